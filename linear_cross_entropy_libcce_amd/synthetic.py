@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the flash cut-cross-entropy head.
+
+This module draws inputs only; it holds none of the head's arithmetic, so both
+the HIP path and the CPU oracle can take its arrays without sharing any code.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
+
+1. packed head words ``wq`` uint32 [V, H*bits/32], each word uniform over all
+   32-bit values -- so every ``bits``-wide code inside it is uniform over
+   [0, 2**bits), the code distribution of the workloads;
+2. per-group scales fp32 [V, H/64], uniform in [lo, hi);
+   biases are derived, not drawn: ``-8*s`` (4-bit) or ``-128*s`` (8-bit),
+   i.e. the affine zero point sits mid-range as in an MLX affine quantizer;
+3. hidden states drawn fp32 N(0, 1), rounded to bf16 (round-to-nearest-even),
+   returned as the raw uint16 bit patterns [M, H];
+4. targets int32 [M]: uniform over [0, V), or truncated Zipf(a) over the
+   vocabulary (P(id = k-1) proportional to k**-a, sampled by inverse CDF);
+5. mask uint8 [M] (1 = supervised token) or None: a contiguous masked prefix,
+   or exactly round(frac*M) masked positions chosen by a seeded permutation.
+
+The five workloads mirror the sizes the pages validate (H=1536 and H=2560 heads
+with V up to 262144; page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts,
+the header comment and the H_MAX note) plus a tail-mask case.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+GROUP = 64
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    H: int
+    V: int
+    bits: int
+    scale_lo: float
+    scale_hi: float
+    softcap: float = 0.0
+    targets: str = "uniform"      # "uniform" | "zipf"
+    zipf_a: float = 1.1
+    mask: str = "none"            # "none" | "prefix" | "random"
+    mask_frac: float = 0.0
+
+    @property
+    def G(self) -> int:
+        return self.H // GROUP
+
+    @property
+    def words_per_row(self) -> int:
+        return self.H * self.bits // 32
+
+
+def _w4(name, M, H, V, **kw):
+    return Workload(name, M, H, V, 4, 0.005, 0.02, **kw)
+
+
+WORKLOADS = {
+    0: _w4("tiny: M=16 H=256 V=4096 4-bit", 16, 256, 4096),
+    1: _w4("M=2048 H=1536 V=65536 4-bit", 2048, 1536, 65536),
+    2: _w4("M=512 H=2560 V=262144 4-bit cap30 prefix-masked", 512, 2560, 262144,
+           softcap=30.0, mask="prefix", mask_frac=0.5),
+    3: Workload("M=8192 H=2560 V=262144 8-bit cap30", 8192, 2560, 262144, 8,
+                0.0005, 0.002, softcap=30.0),
+    4: _w4("M=8192 H=4096 V=151655 4-bit zipf random-masked", 8192, 4096, 151655,
+           targets="zipf", mask="random", mask_frac=0.3),
+}
+
+SEED_BASE = 20261202
+
+
+def seed_for(cfg: int) -> int:
+    return SEED_BASE + cfg
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return the bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _targets(rng, M, V, kind, a):
+    if kind == "uniform":
+        return rng.integers(0, V, size=M, dtype=np.int64).astype(np.int32)
+    if kind == "zipf":
+        w = np.arange(1, V + 1, dtype=np.float64) ** (-a)
+        cdf = np.cumsum(w)
+        cdf /= cdf[-1]
+        u = rng.random(M)
+        return np.minimum(np.searchsorted(cdf, u, side="right"), V - 1).astype(np.int32)
+    raise ValueError(kind)
+
+
+def _mask(rng, M, kind, frac) -> Optional[np.ndarray]:
+    if kind == "none":
+        return None
+    m = np.ones(M, dtype=np.uint8)
+    n = int(round(frac * M))
+    if kind == "prefix":
+        m[:n] = 0
+    elif kind == "random":
+        m[rng.permutation(M)[:n]] = 0
+    else:
+        raise ValueError(kind)
+    return m
+
+
+def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
+    """All arrays of one workload (M may be overridden for reduced cases)."""
+    M = w.M if M is None else M
+    rng = np.random.default_rng(seed)
+    wq = rng.integers(0, 2**32, size=(w.V, w.words_per_row), dtype=np.uint32)
+    scales = rng.uniform(w.scale_lo, w.scale_hi, size=(w.V, w.G)).astype(np.float32)
+    zero_point = np.float32(8.0 if w.bits == 4 else 128.0)
+    biases = (-zero_point * scales).astype(np.float32)
+    h = bf16_bits_from_f32(rng.standard_normal((M, w.H), dtype=np.float32))
+    targets = _targets(rng, M, w.V, w.targets, w.zipf_a)
+    mask = _mask(rng, M, w.mask, w.mask_frac)
+    return dict(h=h, wq=wq, scales=scales, biases=biases, targets=targets, mask=mask,
+                M=M, H=w.H, V=w.V, bits=w.bits, group=GROUP, softcap=float(w.softcap))
+
+
+def make_custom(M, H, V, bits, seed, softcap=0.0, scale_lo=None, scale_hi=None,
+                targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0) -> dict:
+    """A reduced/edge-case workload with the same value distributions."""
+    if scale_lo is None:
+        scale_lo, scale_hi = (0.005, 0.02) if bits == 4 else (0.0005, 0.002)
+    w = Workload("custom", M, H, V, bits, scale_lo, scale_hi, softcap=softcap,
+                 targets=targets, mask=mask, mask_frac=mask_frac)
+    d = make_inputs(w, seed)
+    if h_scale != 1.0:
+        d["h"] = bf16_bits_from_f32(f32_from_bf16_bits(d["h"]) * np.float32(h_scale))
+    return d

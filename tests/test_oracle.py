@@ -1,0 +1,281 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle.
+
+The pages print no worked input->output example, so every pin here is a closed
+form, an invariant, a finite difference, brute force through an independent
+library routine (torch float64 autograd), or a hand-derived value from
+hex-literal packed words.  Each test names the mistake it is meant to catch.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_cross_entropy_libcce_amd import synthetic as syn
+
+GROUP = 64
+
+
+def pack_codes(q, bits):
+    """Test-local packer: element k of a word sits at bits [bits*k, bits*k+bits)."""
+    q = np.asarray(q, dtype=np.uint64)
+    V, H = q.shape
+    per = 32 // bits
+    w = np.zeros((V, H // per), dtype=np.uint64)
+    for k in range(per):
+        w |= q[:, k::per] << np.uint64(bits * k)
+    return w.astype(np.uint32)
+
+
+def bf16(x):
+    return syn.bf16_bits_from_f32(np.asarray(x, dtype=np.float32))
+
+
+def mk(h_f32, q, scales, biases, targets, bits, softcap=0.0, mask=None):
+    h_bits = bf16(h_f32)
+    M, H = h_bits.shape
+    return dict(h=h_bits, wq=pack_codes(q, bits), scales=np.asarray(scales, np.float32),
+                biases=np.asarray(biases, np.float32), targets=np.asarray(targets, np.int32),
+                mask=mask, M=M, H=H, V=q.shape[0], bits=bits, group=GROUP, softcap=softcap)
+
+
+def test_packer_matches_hex_literals():
+    # catches a packer with the element order reversed inside the word
+    assert pack_codes(np.arange(8)[None, :], 4)[0, 0] == 0x76543210
+    assert pack_codes(np.arange(4)[None, :] + 0xA0, 8)[0, 0] == 0xA3A2A1A0
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_code_order_and_group_index_from_hex_words(bits):
+    """h = one-hot at d makes logit v equal to the dequantized element w[v][d].
+
+    Words are written as hex literals and the expected codes read off by hand,
+    so a reversed nibble/byte order, a wrong word index or a wrong group index
+    changes the logits.  H = 128 has two groups with different scales.
+    """
+    H, V = 128, 3
+    per = 32 // bits
+    if bits == 4:
+        row0 = [0x76543210, 0xFEDCBA98] * (H // per // 2)       # q[d] = d % 16
+        row1 = [0x01234567, 0x89ABCDEF] * (H // per // 2)       # q[d] = 7 - d%16 (d%16<8), 23 - d%16 else
+        row2 = [0xFFFFFFFF] * (H // per)                        # q = 15
+        d, expect_q = 69, [5, 2, 15]                            # d=69: word 8 (even), nibble 5
+    else:
+        row0 = [(4 * j + 3) << 24 | (4 * j + 2) << 16 | (4 * j + 1) << 8 | 4 * j for j in range(H // per)]
+        row1 = [0xFFFEFDFC] * (H // per)                        # q[d] = 252 + d%4
+        row2 = [0x00000080] * (H // per)                        # q = 128 at d%4==0 else 0
+        d, expect_q = 69, [69, 252 + 69 % 4, 0]
+    wq = np.array([row0, row1, row2], dtype=np.uint32)
+    scales = np.array([[0.5, 0.25], [0.125, 0.0625], [1.0, 2.0]], np.float32)
+    biases = np.array([[-1.0, 0.5], [0.25, -0.75], [0.0, -3.0]], np.float32)
+    h = np.zeros((1, H), np.float32)
+    h[0, d] = 1.0
+    g = d // GROUP
+    z = [float(scales[v, g]) * expect_q[v] + float(biases[v, g]) for v in range(V)]
+    lse = math.log(sum(math.exp(x) for x in z))
+    for t in range(V):
+        inp = dict(h=bf16(h), wq=wq, scales=scales, biases=biases,
+                   targets=np.array([t], np.int32), mask=None, M=1, H=H, V=V,
+                   bits=bits, group=GROUP, softcap=0.0)
+        logp, l, _ = oracle.cce(inp, backward=False)
+        assert abs(l[0] - lse) < 1e-12 * abs(lse)
+        assert abs(logp[0] - (z[t] - lse)) < 1e-12 * abs(lse)
+
+
+def _rand_case(seed, M, H, V, bits, softcap=0.0, mask=None, targets=None):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 2 ** bits, size=(V, H))
+    s = rng.uniform(0.005, 0.05, size=(V, H // GROUP))
+    b = -(2 ** (bits - 1)) * s + rng.normal(0, 0.01, size=s.shape)
+    h = rng.standard_normal((M, H)).astype(np.float32)
+    t = rng.integers(0, V, size=M) if targets is None else targets
+    return mk(h, q, s, b, t, bits, softcap, mask), q
+
+
+def test_v1_is_certain():
+    inp, _ = _rand_case(1, 3, 64, 1, 4)
+    logp, lse, dh = oracle.cce(inp)
+    assert np.all(np.abs(logp) < 1e-12) and np.all(np.abs(dh) < 1e-12)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 5.0])
+def test_identical_rows_give_uniform_softmax(softcap):
+    # catches a gradient that does not cancel: coefficients must sum to zero
+    inp, q = _rand_case(2, 4, 128, 9, 8, softcap)
+    for k in ("wq", "scales", "biases"):
+        inp[k] = np.repeat(inp[k][:1], inp["V"], axis=0)
+    logp, lse, dh = oracle.cce(inp)
+    assert np.allclose(logp, -math.log(9), atol=1e-12)
+    assert np.max(np.abs(dh)) < 1e-12
+
+
+def test_zero_head():
+    # codes 8 with bias -8*s are exact zeros: lse = log V
+    V, H = 50, 192
+    q = np.full((V, H), 8)
+    s = np.full((V, H // GROUP), 0.0123, np.float32)
+    inp = mk(np.random.default_rng(3).standard_normal((2, H)), q, s, -8 * s, [0, 49], 4)
+    logp, lse, _ = oracle.cce(inp, backward=False)
+    assert np.allclose(lse, math.log(V), atol=1e-12) and np.allclose(logp, -math.log(V), atol=1e-12)
+
+
+def _dense(q, inp):
+    s = np.repeat(inp["scales"].astype(np.float64), GROUP, axis=1)
+    b = np.repeat(inp["biases"].astype(np.float64), GROUP, axis=1)
+    return s * q + b
+
+
+@pytest.mark.parametrize("softcap", [0.0, 3.0])
+def test_two_way_closed_form(softcap):
+    """V = 2: logp_t = -log(1 + e^(y_o - y_t)); dh = g[(1-p_t) c'_t w_t - p_o c'_o w_o]."""
+    inp, q = _rand_case(4, 5, 128, 2, 4, softcap)
+    inp["h"] = bf16(syn.f32_from_bf16_bits(inp["h"]) * 8)   # larger logits, softcap bites
+    g = np.array([1.0, -1.0, 0.5, 2.0, -0.25])
+    logp, lse, dh = oracle.cce(inp, g=g)
+    W = _dense(q, inp)
+    hd = syn.f32_from_bf16_bits(inp["h"]).astype(np.float64)
+    for t in range(5):
+        z = W @ hd[t]
+        y = softcap * np.tanh(z / softcap) if softcap else z
+        c = 1 - np.tanh(z / softcap) ** 2 if softcap else np.ones(2)
+        tt = inp["targets"][t]
+        o = 1 - tt
+        assert abs(logp[t] + math.log1p(math.exp(y[o] - y[tt]))) < 1e-10
+        pt = 1 / (1 + math.exp(y[o] - y[tt]))
+        ref = g[t] * ((1 - pt) * c[tt] * W[tt] - (1 - pt) * c[o] * W[o])
+        assert np.max(np.abs(dh[t] - ref)) < 1e-10 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("softcap", [0.0, 2.0])
+def test_probabilities_sum_to_one_and_lse_bounds(softcap):
+    V = 64
+    inp, _ = _rand_case(5, 1, 64, V, 8, softcap)
+    inp["h"] = np.repeat(inp["h"], V, axis=0)
+    inp["targets"] = np.arange(V, dtype=np.int32)
+    inp["M"] = V
+    logp, lse, _ = oracle.cce(inp, backward=False)
+    assert abs(np.sum(np.exp(logp)) - 1.0) < 1e-12
+    # max_v y_v <= lse <= max_v y_v + log V, with max_v logp_v = max y - lse
+    assert -math.log(V) - 1e-12 <= np.max(logp) <= 1e-12
+
+
+@pytest.mark.parametrize("bits,softcap,target", [(4, 0.0, 3), (8, 4.0, 3), (4, 4.0, -1), (8, 0.0, 17)])
+def test_gradient_matches_central_differences(bits, softcap, target):
+    """dh_t[d] = g * d logp_t / d h_t[d], checked by central differences in fp64.
+
+    The perturbed coordinate is 0 in the base point, so h_d = +-eps is an exact
+    bf16 value.  Catches a wrong sign of g or of the softmax term, a missing
+    softcap derivative, and a one-hot term applied to an out-of-range target.
+    """
+    V, H = 17, 128
+    inp, _ = _rand_case(6, 1, H, V, bits, softcap, targets=[target])
+    inp["h"] = bf16(syn.f32_from_bf16_bits(inp["h"]) * 4)
+    g = np.array([-0.75])
+    eps = 2.0 ** -12
+    for d in (0, 63, 64, 127):
+        base = syn.f32_from_bf16_bits(inp["h"]).copy()
+        base[0, d] = 0.0
+        inp["h"] = bf16(base)
+        _, _, dh = oracle.cce(inp, g=g)
+        vals = []
+        for sgn in (1, -1):
+            p = base.copy()
+            p[0, d] = sgn * eps
+            x = dict(inp, h=bf16(p))
+            lp, _, _ = oracle.cce(x, backward=False)
+            vals.append(lp[0])
+        fd = g[0] * (vals[0] - vals[1]) / (2 * eps)
+        assert abs(fd - dh[0, d]) < 1e-7 * max(1.0, abs(fd)), (d, fd, dh[0, d])
+    if target < 0 or target >= V:
+        lp, lse, _ = oracle.cce(inp, backward=False)
+        assert abs(lp[0] + lse[0]) < 1e-12
+
+
+def test_common_bias_shift_is_invisible_without_softcap():
+    # shifting every head element by the same delta shifts all logits equally
+    inp, _ = _rand_case(7, 6, 128, 33, 4)
+    a = oracle.cce(inp)
+    inp2 = dict(inp, biases=(inp["biases"] + np.float32(0.25)).astype(np.float32))
+    b = oracle.cce(inp2)
+    assert np.allclose(a[0], b[0], atol=1e-9) and np.allclose(a[2], b[2], atol=1e-9)
+
+
+def test_vocab_permutation_and_token_subsets():
+    inp, _ = _rand_case(8, 7, 128, 40, 8, 3.0)
+    g = np.linspace(-1, 2, 7)
+    base = oracle.cce(inp, g=g)
+    perm = np.random.default_rng(9).permutation(40)
+    inv = np.argsort(perm)
+    x = dict(inp, wq=inp["wq"][perm], scales=inp["scales"][perm], biases=inp["biases"][perm],
+             targets=inv[inp["targets"]].astype(np.int32))
+    got = oracle.cce(x, g=g)
+    for a, b in zip(base, got):
+        assert np.allclose(a, b, atol=1e-10)
+    sub = [5, 0, 3]
+    got = oracle.cce(inp, tokens=sub, g=g)
+    for a, b in zip(base, got):
+        assert np.allclose(a[sub], b, atol=0)
+
+
+def test_four_bit_codes_repacked_as_eight_bit():
+    inp, q = _rand_case(10, 3, 192, 21, 4, 2.0)
+    x = dict(inp, wq=pack_codes(q, 8), bits=8)
+    for a, b in zip(oracle.cce(inp), oracle.cce(x)):
+        assert np.array_equal(a, b)
+
+
+def test_linearity_in_g_and_large_cap():
+    inp, _ = _rand_case(11, 4, 128, 30, 4)
+    g = np.array([1.0, 2.0, -3.0, 0.5])
+    _, _, d1 = oracle.cce(inp)
+    _, _, d2 = oracle.cce(inp, g=g)
+    assert np.allclose(d2, d1 * g[:, None], atol=1e-12)
+    a = oracle.cce(inp)
+    b = oracle.cce(inp, softcap=1e6)
+    for u, v in zip(a, b):
+        assert np.allclose(u, v, atol=1e-6)
+
+
+def test_mask_zeroes_exactly_and_isolates():
+    mask = np.array([1, 0, 1, 0, 1], np.uint8)
+    inp, _ = _rand_case(12, 5, 128, 25, 8, 0.0, mask=mask)
+    logp, lse, dh = oracle.cce(inp)
+    assert np.all(logp[mask == 0] == 0) and np.all(lse[mask == 0] == 0)
+    assert np.all(dh[mask == 0] == 0)
+    full = oracle.cce(dict(inp, mask=None))
+    assert np.array_equal(logp[mask == 1], full[0][mask == 1])
+
+
+@pytest.mark.parametrize("bits,softcap", [(4, 0.0), (8, 30.0), (4, 1.5)])
+def test_against_torch_float64_autograd(bits, softcap):
+    """Brute force through torch: log_softmax + gather + autograd on a dense W."""
+    torch = pytest.importorskip("torch")
+    M, H, V = 6, 192, 37
+    inp, q = _rand_case(13, M, H, V, bits, softcap, targets=[0, 5, 36, 17, 17, 2])
+    inp["h"] = bf16(syn.f32_from_bf16_bits(inp["h"]) * 3)
+    g = np.array([1.0, -1.0, 0.3, 2.0, -0.5, 1.0])
+    logp, lse, dh = oracle.cce(inp, g=g)
+    W = torch.tensor(_dense(q, inp), dtype=torch.float64)
+    h = torch.tensor(syn.f32_from_bf16_bits(inp["h"]).astype(np.float64), requires_grad=True)
+    z = h @ W.T
+    y = softcap * torch.tanh(z / softcap) if softcap else z
+    lp = torch.log_softmax(y, dim=1).gather(1, torch.tensor(inp["targets"], dtype=torch.long)[:, None])[:, 0]
+    (lp * torch.tensor(g)).sum().backward()
+    assert np.allclose(logp, lp.detach().numpy(), atol=1e-10)
+    assert np.allclose(lse, torch.logsumexp(y, dim=1).detach().numpy(), atol=1e-10)
+    assert np.allclose(dh, h.grad.numpy(), atol=1e-10)
+
+
+def test_synthetic_recipe_shapes_and_ranges():
+    d = syn.make_inputs(syn.WORKLOADS[0], syn.seed_for(0))
+    assert d["wq"].shape == (4096, 32) and d["wq"].dtype == np.uint32
+    assert d["scales"].shape == (4096, 4) and np.all((d["scales"] >= 0.005) & (d["scales"] < 0.02))
+    assert np.array_equal(d["biases"], (-8 * d["scales"]).astype(np.float32))
+    assert d["h"].shape == (16, 256) and d["h"].dtype == np.uint16
+    assert np.all((d["targets"] >= 0) & (d["targets"] < 4096)) and d["mask"] is None
+    # codes inside the words are uniform: every nibble value appears
+    nib = (d["wq"][:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
+    assert np.all(np.bincount(nib.ravel(), minlength=16) > 0)
+    # bf16 rounding is to nearest, ties to even
+    assert syn.bf16_bits_from_f32(np.array([1.0 + 2 ** -8], np.float32))[0] == 0x3F80
+    assert syn.bf16_bits_from_f32(np.array([1.0 + 3 * 2 ** -8], np.float32))[0] == 0x3F82
