@@ -1,0 +1,130 @@
+/*
+ * cce.h -- C ABI of libcce, the MI355X (gfx950) flash cut-cross-entropy head.
+ *
+ * The operation (page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts, header
+ * comment and flashCceForward / flashCceBackward): for hidden states h [M, H]
+ * and a frozen affine-quantized LM head W [V, H], compute per token
+ *
+ *     y_v   = c(h_t . W_v),  c(z) = cap * tanh(z / cap) if cap > 0 else z
+ *     lse_t = log sum_v exp(y_v)
+ *     logp_t = y_{target_t} - lse_t
+ *
+ * and, for an upstream cotangent g_t = d loss / d logp_t, the gradient
+ *
+ *     dh_t = g_t * d logp_t / d h_t
+ *          = g_t * sum_v (1[v = target_t] - exp(y_v - lse_t)) * c'(z_v) * W_v
+ *
+ * without ever writing the [M, V] logits or a dequantized head to memory.
+ *
+ * Conventions shared by every call:
+ *  - Pointers named "device" are HIP device (or managed) memory on the current
+ *    device; the caller allocates and owns every buffer.  The library keeps no
+ *    pointer after a call returns and never allocates device memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Buffers must stay valid until the stream has passed the work.
+ *    Nothing synchronizes with the host.
+ *  - The library holds no state; calls on different streams are independent
+ *    provided each has its own workspace.  Two calls in flight that share a
+ *    workspace race.
+ *  - On any error return nothing has been enqueued and no output written,
+ *    except CCE_ERR_HIP, which is reported after a failed launch.
+ *  - Masked tokens (mask[t] == 0) get logp = lse = 0 and a zero dh row.
+ *  - A target outside [0, V) matches no vocabulary row: its target term is 0
+ *    (logp = -lse) and it adds no one-hot term to dh.
+ */
+#ifndef LIBCCE_CCE_H
+#define LIBCCE_CCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CCE_ABI_VERSION 1
+
+typedef enum cce_status {
+  CCE_OK = 0,
+  CCE_ERR_INVALID_ARG = 1, /* null pointer, negative size, H % group != 0,
+                              softcap < 0 or not finite, misaligned pointer */
+  CCE_ERR_UNSUPPORTED = 2, /* bits not 4 or 8, group != 64, H or V too large */
+  CCE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
+  CCE_ERR_HIP = 4          /* a HIP launch failed; see cce_status_str */
+} cce_status;
+
+/*
+ * The frozen quantized head (page "mlx-bun 0.0.4 -> 0.0.6",
+ * src/train/flash-cce.ts, the FlashCceHead interface; packing as read by the
+ * forward kernels there).  All pointers are device memory, row-major:
+ *   wq      uint32 [V][H*bits/32]; element d of row v is the unsigned code
+ *           (wq[v][d / (32/bits)] >> (bits * (d % (32/bits)))) & (2^bits - 1),
+ *           i.e. little-endian within each word.  16-byte aligned.
+ *   scales  float  [V][H/group]   (4-byte aligned)
+ *   biases  float  [V][H/group]   (4-byte aligned)
+ * The dequantized element is w[v][d] = scales[v][d/group] * q + biases[v][d/group].
+ *   bits    4 or 8;  group  64;  H a multiple of group, at most 16384;
+ *   V in [1, 2^31 - 1];  softcap >= 0 (0 = no softcap).
+ */
+typedef struct cce_head {
+  const uint32_t *wq;
+  const float *scales;
+  const float *biases;
+  int64_t V;
+  int64_t H;
+  int32_t bits;
+  int32_t group;
+  float softcap;
+} cce_head;
+
+/*
+ * Bytes of device workspace that cce_forward / cce_backward need for this head
+ * and M tokens.  Returns 0 when the head or M is invalid (cce_forward then
+ * reports why).  The value depends only on (V, H, bits, M).
+ */
+size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M);
+size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M);
+
+/*
+ * Forward (page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts,
+ * flashCceForward: vocab-parallel online-softmax partials merged across vocab
+ * blocks into lse, then logp = target logit - lse).
+ *   h          device bf16 [M][H] row-major (raw bf16 bits, 2-byte aligned)
+ *   targets    device int32 [M]
+ *   mask       device uint8 [M] (nonzero = supervised token) or NULL = all
+ *   logp, lse  device float [M], written for every token
+ *   workspace  device, 256-byte aligned, >= cce_forward_workspace_bytes
+ */
+cce_status cce_forward(const cce_head *head, const void *h, int64_t M,
+                       const int32_t *targets, const uint8_t *mask,
+                       float *logp, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * Backward (same file, flashCceBackward: recompute the logits, form the
+ * coefficient g * (onehot - softmax) * c', contract it with W, summing over
+ * vocabulary blocks).
+ *   lse        device float [M], as written by cce_forward for these inputs
+ *   g          device float [M] cotangent of logp, or NULL = all ones
+ *              (for a loss of -sum_t logp_t pass g = -1)
+ *   dh         device float [M][H], fully overwritten
+ *   workspace  device, 256-byte aligned, >= cce_backward_workspace_bytes
+ * Other arguments as for cce_forward.
+ */
+cce_status cce_backward(const cce_head *head, const void *h, int64_t M,
+                        const int32_t *targets, const uint8_t *mask,
+                        const float *lse, const float *g, float *dh,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text of a status (for CCE_ERR_HIP, of the last HIP error
+ * seen by this thread).  The pointer stays valid until the thread's next call. */
+const char *cce_status_str(cce_status status);
+
+/* CCE_ABI_VERSION of the loaded library. */
+int cce_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCCE_CCE_H */

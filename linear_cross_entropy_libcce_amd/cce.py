@@ -1,0 +1,177 @@
+"""Thin Python binding of libcce (include/cce.h), same names as the C ABI.
+
+Argument marshalling only: every step of the head runs in the HIP kernels of
+libcce.so.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if libcce.so cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcce.so")
+
+CCE_OK, CCE_ERR_INVALID_ARG, CCE_ERR_UNSUPPORTED, CCE_ERR_WORKSPACE, CCE_ERR_HIP = range(5)
+
+EXPORTS = ("cce_forward", "cce_backward", "cce_forward_workspace_bytes",
+           "cce_backward_workspace_bytes", "cce_status_str", "cce_abi_version")
+
+
+class cce_head(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("softcap", ctypes.c_float)]
+
+
+class CceError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__("libcce status %d: %s" % (status, text))
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libcce.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libcce.so not built (%s); run linear_cross_entropy_libcce_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    HP = ctypes.POINTER(cce_head)
+    lib.cce_forward.restype = ctypes.c_int
+    lib.cce_forward.argtypes = [HP, P, I64, P, P, P, P, P, SZ, P]
+    lib.cce_backward.restype = ctypes.c_int
+    lib.cce_backward.argtypes = [HP, P, I64, P, P, P, P, P, P, SZ, P]
+    lib.cce_forward_workspace_bytes.restype = SZ
+    lib.cce_forward_workspace_bytes.argtypes = [HP, I64]
+    lib.cce_backward_workspace_bytes.restype = SZ
+    lib.cce_backward_workspace_bytes.argtypes = [HP, I64]
+    lib.cce_status_str.restype = ctypes.c_char_p
+    lib.cce_status_str.argtypes = [ctypes.c_int]
+    lib.cce_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != CCE_OK:
+        raise CceError(status, load().cce_status_str(status).decode())
+
+
+@dataclasses.dataclass
+class Head:
+    """Device tensors of a quantized head: wq uint32-as-int32 [V, H*bits/32],
+    scales/biases float32 [V, H/64]."""
+    wq: "object"
+    scales: "object"
+    biases: "object"
+    bits: int
+    softcap: float = 0.0
+    group: int = 64
+
+    @property
+    def V(self) -> int:
+        return int(self.scales.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.scales.shape[1]) * self.group
+
+    def c_struct(self) -> cce_head:
+        return cce_head(self.wq.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+                        self.V, self.H, self.bits, self.group, float(self.softcap))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _expect(t, dtype, device, shape, name):
+    if t.dtype != dtype or t.device != device or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s (got %s %s %s)"
+                         % (name, dtype, tuple(shape), device, t.dtype, tuple(t.shape), t.device))
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    import torch
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise CceError(CCE_ERR_WORKSPACE, "workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def forward_workspace_bytes(head: Head, M: int) -> int:
+    return int(load().cce_forward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def backward_workspace_bytes(head: Head, M: int) -> int:
+    return int(load().cce_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
+    """(logp, lse), each float32 [M], for bf16 h [M, H] and int32 targets [M]."""
+    import torch
+    lib = load()
+    M, dev = int(h.shape[0]), h.device
+    _expect(h, torch.bfloat16, dev, (M, head.H), "h")
+    _expect(targets, torch.int32, dev, (M,), "targets")
+    if mask is not None:
+        _expect(mask, torch.uint8, dev, (M,), "mask")
+    logp, lse = out if out is not None else (torch.empty(M, dtype=torch.float32, device=dev),
+                                             torch.empty(M, dtype=torch.float32, device=dev))
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_forward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_forward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse
+
+
+def cce_backward(h, head: Head, targets, lse, g=None, mask=None, workspace=None, out=None):
+    """dh float32 [M, H] = g * d logp / d h (g = None means all ones)."""
+    import torch
+    lib = load()
+    M, dev = int(h.shape[0]), h.device
+    _expect(h, torch.bfloat16, dev, (M, head.H), "h")
+    _expect(targets, torch.int32, dev, (M,), "targets")
+    _expect(lse, torch.float32, dev, (M,), "lse")
+    if g is not None:
+        _expect(g, torch.float32, dev, (M,), "g")
+    if mask is not None:
+        _expect(mask, torch.uint8, dev, (M,), "mask")
+    dh = out if out is not None else torch.empty((M, head.H), dtype=torch.float32, device=dev)
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
+                            _ptr(dh), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return dh
+
+
+def head_from_numpy(inp: dict, device="cuda") -> Head:
+    """Upload the head arrays of a synthetic.make_inputs dict."""
+    import torch
+    wq = torch.from_numpy(inp["wq"].view("int32")).to(device)
+    return Head(wq=wq, scales=torch.from_numpy(inp["scales"]).to(device),
+                biases=torch.from_numpy(inp["biases"]).to(device), bits=int(inp["bits"]),
+                softcap=float(inp["softcap"]), group=int(inp["group"]))
+
+
+def tokens_from_numpy(inp: dict, device="cuda"):
+    """(h bf16 [M,H], targets int32 [M], mask uint8 [M] or None) on the device."""
+    import torch
+    h = torch.from_numpy(inp["h"].view("int16")).to(device).view(torch.bfloat16)
+    t = torch.from_numpy(inp["targets"]).to(device)
+    m = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).to(device)
+    return h, t, m

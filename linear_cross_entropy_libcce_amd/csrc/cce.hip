@@ -1,0 +1,284 @@
+// cce.hip -- host side of libcce: argument validation, launch planning,
+// workspace carving and the launch sequence on the caller's stream.
+// The C ABI is declared in include/cce.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "cce.h"
+#include "cce_device.h"
+
+namespace {
+
+using namespace cce;
+
+constexpr int64_t MAX_H = 16384;
+constexpr int64_t MAX_M = (int64_t)1 << 24;
+constexpr size_t COEFF_BUDGET = (size_t)256 << 20;  // bytes of one coefficient chunk
+constexpr int TARGET_WGS = 512;                     // two rounds of 256 CUs
+
+thread_local char g_err[256];
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int64_t M, M_pad, V, H;
+  int G, Kb, Ka, NB, bits, wpr, TT, tiles;
+  float cap;
+  // forward
+  int nsplit, tiles_per_split;
+  // backward
+  int chunk_tiles, nchunks, ksplit, k_tiles, HT;
+  int64_t ld_coeff;
+  // workspace offsets (bytes)
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
+};
+
+cce_status check_head(const cce_head *hd) {
+  if (!hd || !hd->wq || !hd->scales || !hd->biases) return CCE_ERR_INVALID_ARG;
+  if (hd->V < 1 || hd->H < 1) return CCE_ERR_INVALID_ARG;
+  if (!(hd->softcap >= 0.0f) || !std::isfinite(hd->softcap)) return CCE_ERR_INVALID_ARG;
+  if (hd->bits != 4 && hd->bits != 8) return CCE_ERR_UNSUPPORTED;
+  if (hd->group != KSTEP) return CCE_ERR_UNSUPPORTED;
+  if (hd->H % hd->group != 0) return CCE_ERR_INVALID_ARG;
+  if (hd->H > MAX_H || hd->V > (int64_t)INT32_MAX - BN) return CCE_ERR_UNSUPPORTED;
+  if (((uintptr_t)hd->wq & 15) || ((uintptr_t)hd->scales & 3) || ((uintptr_t)hd->biases & 3))
+    return CCE_ERR_INVALID_ARG;
+  return CCE_OK;
+}
+
+Plan make_plan(const cce_head *hd, int64_t M) {
+  Plan p{};
+  p.M = M;
+  p.M_pad = std::max<int64_t>(BM, cdiv(M, BM) * BM);
+  p.V = hd->V;
+  p.H = hd->H;
+  p.bits = hd->bits;
+  p.cap = hd->softcap;
+  p.G = (int)(p.H / KSTEP);
+  p.Kb = (int)(cdiv(3 * p.G, KSTEP) * KSTEP);
+  p.Ka = p.Kb + (int)p.H;
+  p.NB = p.Kb / KSTEP;
+  p.wpr = (int)(p.H * p.bits / 32);
+  p.TT = (int)(p.M_pad / BM);
+  p.tiles = (int)cdiv(p.V, BN);
+
+  p.nsplit = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(1, cdiv(TARGET_WGS, p.TT)));
+  p.tiles_per_split = (int)cdiv(p.tiles, p.nsplit);
+  p.nsplit = (int)cdiv(p.tiles, p.tiles_per_split);
+
+  const int64_t per_tile = p.M_pad * BN * 2;
+  p.chunk_tiles = (int)std::max<int64_t>(1, std::min<int64_t>(p.tiles, (int64_t)COEFF_BUDGET / per_tile));
+  p.nchunks = (int)cdiv(p.tiles, p.chunk_tiles);
+  p.ld_coeff = (int64_t)p.chunk_tiles * BN;
+  p.HT = (int)cdiv(p.H, DT);
+  p.ksplit = (int)std::min<int64_t>(p.chunk_tiles, std::max<int64_t>(1, cdiv(TARGET_WGS, (int64_t)p.TT * p.HT)));
+  p.k_tiles = (int)cdiv(p.chunk_tiles, p.ksplit);
+  p.ksplit = (int)cdiv(p.chunk_tiles, p.k_tiles);
+
+  size_t o = 0;
+  p.o_cnt = o;  o = align_up(o + 256, 256);
+  p.o_idx = o;  o = align_up(o + sizeof(int) * p.M_pad, 256);
+  p.o_inv = o;  o = align_up(o + sizeof(int) * std::max<int64_t>(M, 1), 256);
+  p.o_tok = o;  o = align_up(o + sizeof(TokRec) * p.M_pad, 256);
+  p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
+  const size_t common = o;
+  p.o_part = common;
+  p.fwd_bytes = align_up(common + sizeof(float) * 2 * p.nsplit * p.M_pad, 256);
+  p.o_coeff = common;
+  o = align_up(common + (size_t)2 * p.M_pad * p.ld_coeff, 256);
+  p.o_dhp = o;
+  p.bwd_bytes = align_up(o + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
+  return p;
+}
+
+cce_status check_common(const cce_head *hd, const void *h, int64_t M, const int32_t *targets,
+                        void *workspace) {
+  cce_status s = check_head(hd);
+  if (s != CCE_OK) return s;
+  if (M < 0) return CCE_ERR_INVALID_ARG;
+  if (M > MAX_M) return CCE_ERR_UNSUPPORTED;
+  if (M == 0) return CCE_OK;
+  if (!h || !targets) return CCE_ERR_INVALID_ARG;
+  if (((uintptr_t)h & 1) || ((uintptr_t)targets & 3)) return CCE_ERR_INVALID_ARG;
+  if (workspace && ((uintptr_t)workspace & 255)) return CCE_ERR_INVALID_ARG;
+  return CCE_OK;
+}
+
+cce_status hip_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return CCE_OK;
+  std::snprintf(g_err, sizeof g_err, "HIP error: %s", hipGetErrorString(e));
+  return CCE_ERR_HIP;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// compaction, augmented rows and token records, target logits
+void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_t *targets,
+                  const uint8_t *mask, const float *lse, const float *g, void *ws, hipStream_t st,
+                  bool bwd) {
+  int *cnt = ws_at<int>(ws, p.o_cnt);
+  int *idx = ws_at<int>(ws, p.o_idx);
+  int *inv = ws_at<int>(ws, p.o_inv);
+  TokRec *tok = ws_at<TokRec>(ws, p.o_tok);
+  uint16_t *haug = ws_at<uint16_t>(ws, p.o_haug);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt);
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)p.M_pad), dim3(256), 0, st, (const uint16_t *)h, (int)p.H, p.G,
+                     p.Kb, p.Ka, (const int *)idx, targets, lse, g, tok, haug);
+  const dim3 tg((unsigned)cdiv(p.M_pad, 4));
+  if (p.bits == 4)
+    hipLaunchKernelGGL(k_target<4>, tg, dim3(256), 0, st, (const uint16_t *)haug, p.Ka, p.Kb, (int)p.H, p.G,
+                       hd->wq, p.wpr, hd->scales, hd->biases, p.V, p.cap, (const int *)cnt, tok, (int)p.M_pad,
+                       bwd ? 1 : 0);
+  else
+    hipLaunchKernelGGL(k_target<8>, tg, dim3(256), 0, st, (const uint16_t *)haug, p.Ka, p.Kb, (int)p.H, p.G,
+                       hd->wq, p.wpr, hd->scales, hd->biases, p.V, p.cap, (const int *)cnt, tok, (int)p.M_pad,
+                       bwd ? 1 : 0);
+}
+
+TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
+  TileArgs a{};
+  a.haug = ws_at<const uint16_t>(ws, p.o_haug);
+  a.wq = hd->wq;
+  a.scales = hd->scales;
+  a.biases = hd->biases;
+  a.cnt = ws_at<const int>(ws, p.o_cnt);
+  a.tok = ws_at<const TokRec>(ws, p.o_tok);
+  a.V = p.V;
+  a.G = p.G;
+  a.Ka = p.Ka;
+  a.NB = p.NB;
+  a.wpr = p.wpr;
+  a.M_pad = (int)p.M_pad;
+  a.cap = p.cap;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cce_abi_version(void) { return CCE_ABI_VERSION; }
+
+const char *cce_status_str(cce_status s) {
+  switch (s) {
+    case CCE_OK: return "ok";
+    case CCE_ERR_INVALID_ARG: return "invalid argument";
+    case CCE_ERR_UNSUPPORTED: return "unsupported head configuration";
+    case CCE_ERR_WORKSPACE: return "workspace missing or too small";
+    case CCE_ERR_HIP: return g_err[0] ? g_err : "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M) {
+  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(head, M).fwd_bytes;
+}
+
+size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M) {
+  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(head, M).bwd_bytes;
+}
+
+cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                       const uint8_t *mask, float *logp, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  cce_status s = check_common(head, h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  if (!logp || !lse || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3)) return CCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(head, M);
+  if (!workspace || workspace_bytes < p.fwd_bytes) return CCE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  launch_front(p, head, h, targets, mask, nullptr, nullptr, workspace, st, false);
+  TileArgs a = tile_args(p, head, workspace);
+  a.part = ws_at<float>(workspace, p.o_part);
+  a.range_tile0 = 0;
+  a.range_tiles = p.tiles;
+  a.tiles_per_wg = p.tiles_per_split;
+  const dim3 grid((unsigned)p.TT, (unsigned)p.nsplit);
+  if (p.bits == 4)
+    hipLaunchKernelGGL((k_tile<4, false>), grid, dim3(NTHREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_tile<8, false>), grid, dim3(NTHREADS), 0, st, a);
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)cdiv(M, 256)), dim3(256), 0, st,
+                     (const float *)a.part, p.nsplit, (int)p.M_pad, ws_at<const int>(workspace, p.o_inv),
+                     ws_at<const TokRec>(workspace, p.o_tok), (int)M, logp, lse);
+  return hip_status();
+}
+
+cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                        const uint8_t *mask, const float *lse, const float *g, float *dh,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  cce_status s = check_common(head, h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  if (!lse || !dh || ((uintptr_t)lse & 3) || ((uintptr_t)dh & 3) || ((uintptr_t)g & 3))
+    return CCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(head, M);
+  if (!workspace || workspace_bytes < p.bwd_bytes) return CCE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  launch_front(p, head, h, targets, mask, lse, g, workspace, st, true);
+  TileArgs a = tile_args(p, head, workspace);
+  a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
+  a.ld_coeff = p.ld_coeff;
+  a.tiles_per_wg = 1;
+
+  GemmArgs ga{};
+  ga.coeff = a.coeff;
+  ga.ld_coeff = p.ld_coeff;
+  ga.wq = head->wq;
+  ga.scales = head->scales;
+  ga.biases = head->biases;
+  ga.cnt = a.cnt;
+  ga.dh_part = ws_at<float>(workspace, p.o_dhp);
+  ga.V = p.V;
+  ga.H = (int)p.H;
+  ga.G = p.G;
+  ga.wpr = p.wpr;
+  ga.M_pad = (int)p.M_pad;
+  ga.tiles_per_split = p.k_tiles;
+
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+    a.range_tile0 = t0;
+    a.range_tiles = nt;
+    const dim3 g1((unsigned)p.TT, (unsigned)nt);
+    if (p.bits == 4)
+      hipLaunchKernelGGL((k_tile<4, true>), g1, dim3(NTHREADS), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_tile<8, true>), g1, dim3(NTHREADS), 0, st, a);
+    ga.chunk_tile0 = t0;
+    ga.chunk_tiles = nt;
+    ga.accumulate = c > 0;
+    const dim3 g2((unsigned)p.TT, (unsigned)p.HT, (unsigned)p.ksplit);
+    if (p.bits == 4)
+      hipLaunchKernelGGL(k_dh_gemm<4>, g2, dim3(NTHREADS), 0, st, ga);
+    else
+      hipLaunchKernelGGL(k_dh_gemm<8>, g2, dim3(NTHREADS), 0, st, ga);
+  }
+  const dim3 gr((unsigned)M, (unsigned)cdiv(p.H, 256));
+  if (p.bits == 4)
+    hipLaunchKernelGGL(k_dh_reduce<4>, gr, dim3(256), 0, st, (const float *)ga.dh_part, p.ksplit, (int)p.M_pad,
+                       (int)p.H, p.G, ws_at<const int>(workspace, p.o_inv), ws_at<const TokRec>(workspace, p.o_tok),
+                       head->wq, p.wpr, head->scales, head->biases, p.V, dh);
+  else
+    hipLaunchKernelGGL(k_dh_reduce<8>, gr, dim3(256), 0, st, (const float *)ga.dh_part, p.ksplit, (int)p.M_pad,
+                       (int)p.H, p.G, ws_at<const int>(workspace, p.o_inv), ws_at<const TokRec>(workspace, p.o_tok),
+                       head->wq, p.wpr, head->scales, head->biases, p.V, dh);
+  return hip_status();
+}
+
+}  // extern "C"

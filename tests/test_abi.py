@@ -1,0 +1,98 @@
+"""The C ABI without a GPU: the library loads, exports what include/cce.h
+declares, and rejects bad arguments with status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_libcce_amd import build, cce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    build.build(force=False)
+    return cce.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "cce.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(cce_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(cce.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.cce_abi_version() == 1
+
+
+def head(**kw):
+    d = dict(wq=0x1000, scales=0x2000, biases=0x3000, V=1000, H=256, bits=4, group=64, softcap=0.0)
+    d.update(kw)
+    return cce.cce_head(**d)
+
+
+def fwd(lib, hd, M=4, h=0x4000, targets=0x5000, logp=0x6000, lse=0x7000, ws=None, nbytes=None):
+    if ws is None:
+        ws, nbytes = 0x100000, 1 << 40
+    return lib.cce_forward(ctypes.byref(hd), h, M, targets, None, logp, lse, ws, nbytes, None)
+
+
+def test_workspace_sizes(lib):
+    hd = head()
+    a = lib.cce_forward_workspace_bytes(ctypes.byref(hd), 16)
+    b = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 16)
+    assert a > 0 and b > 0 and a % 256 == 0 and b % 256 == 0
+    assert lib.cce_forward_workspace_bytes(ctypes.byref(hd), 100000) > a
+    assert lib.cce_forward_workspace_bytes(ctypes.byref(head(bits=5)), 16) == 0
+    assert lib.cce_backward_workspace_bytes(ctypes.byref(hd), -1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=5), cce.CCE_ERR_UNSUPPORTED),
+    (dict(bits=2), cce.CCE_ERR_UNSUPPORTED),
+    (dict(group=32), cce.CCE_ERR_UNSUPPORTED),
+    (dict(H=100), cce.CCE_ERR_INVALID_ARG),      # not a multiple of the group
+    (dict(H=32768), cce.CCE_ERR_UNSUPPORTED),
+    (dict(V=0), cce.CCE_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), cce.CCE_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), cce.CCE_ERR_INVALID_ARG),
+    (dict(softcap=float("nan")), cce.CCE_ERR_INVALID_ARG),
+    (dict(wq=0), cce.CCE_ERR_INVALID_ARG),
+    (dict(wq=0x1004), cce.CCE_ERR_INVALID_ARG),  # not 16-byte aligned
+    (dict(scales=0), cce.CCE_ERR_INVALID_ARG),
+])
+def test_bad_head_is_rejected(lib, kw, status):
+    assert fwd(lib, head(**kw)) == status
+
+
+def test_bad_token_arguments_are_rejected(lib):
+    hd = head()
+    assert fwd(lib, hd, M=-1) == cce.CCE_ERR_INVALID_ARG
+    assert fwd(lib, hd, h=0) == cce.CCE_ERR_INVALID_ARG
+    assert fwd(lib, hd, h=0x4001) == cce.CCE_ERR_INVALID_ARG
+    assert fwd(lib, hd, targets=0) == cce.CCE_ERR_INVALID_ARG
+    assert fwd(lib, hd, logp=0) == cce.CCE_ERR_INVALID_ARG
+    assert fwd(lib, hd, ws=0x100010, nbytes=1 << 40) == cce.CCE_ERR_INVALID_ARG   # misaligned workspace
+    need = lib.cce_forward_workspace_bytes(ctypes.byref(hd), 4)
+    assert fwd(lib, hd, ws=0x100000, nbytes=need - 1) == cce.CCE_ERR_WORKSPACE
+    assert lib.cce_forward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x6000, 0x7000, None, 1 << 40, None) \
+        == cce.CCE_ERR_WORKSPACE
+    # M = 0 is a successful no-op
+    assert fwd(lib, hd, M=0, h=0, targets=0) == cce.CCE_OK
+    bneed = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 4)
+    assert lib.cce_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0, None, 0x8000, 0x100000, bneed, None) \
+        == cce.CCE_ERR_INVALID_ARG   # lse missing
+    assert lib.cce_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, 0x9002, 0x8000, 0x100000, bneed,
+                            None) == cce.CCE_ERR_INVALID_ARG   # misaligned g
+    assert lib.cce_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x100000, bneed - 256,
+                            None) == cce.CCE_ERR_WORKSPACE
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.cce_status_str(s)

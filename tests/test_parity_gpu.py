@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (stated for the head): |logp_gpu - logp_oracle| <= 5e-3 and the
+same for lse, max over supervised tokens; masked tokens exactly 0; dh relative
+L2 error ||dh_gpu - dh_oracle||_F / ||dh_oracle||_F <= 1e-2 over the compared
+rows, masked rows exactly 0.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_cross_entropy_libcce_amd import cce
+from linear_cross_entropy_libcce_amd import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+LOGP_TOL = 5e-3
+DH_TOL = 1e-2
+
+
+def say(msg):
+    print("[parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cce.load()
+    return torch
+
+
+def run_gpu(torch, inp, g=None, backward=True):
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    gg = None if g is None else torch.from_numpy(np.asarray(g, np.float32)).cuda()
+    logp, lse = cce.cce_forward(h, head, t, m)
+    dh = cce.cce_backward(h, head, t, lse, gg, m) if backward else None
+    torch.cuda.synchronize()
+    out = (logp.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+           None if dh is None else dh.cpu().numpy().astype(np.float64))
+    del head, h, t, m, logp, lse, dh
+    return out
+
+
+def check(inp, gpu, orc, rows, tag):
+    glogp, glse, gdh = gpu
+    ologp, olse, odh = orc
+    mask = inp["mask"]
+    active = np.ones(len(rows), bool) if mask is None else mask[rows] != 0
+    rows = np.asarray(rows)
+    el = np.abs(glogp[rows] - ologp)[active]
+    es = np.abs(glse[rows] - olse)[active]
+    say("%s: max|dlogp|=%.3g max|dlse|=%.3g over %d tokens" % (tag, el.max(initial=0), es.max(initial=0),
+                                                               active.sum()))
+    assert np.all(np.isfinite(glogp)) and np.all(np.isfinite(glse))
+    assert el.max(initial=0) <= LOGP_TOL and es.max(initial=0) <= LOGP_TOL
+    if mask is not None:
+        assert np.all(glogp[mask == 0] == 0) and np.all(glse[mask == 0] == 0)
+    if gdh is not None:
+        assert np.all(np.isfinite(gdh))
+        if mask is not None:
+            assert np.all(gdh[mask == 0] == 0)
+        a, b = gdh[rows][active], odh[active]
+        if a.size:
+            num, den = np.linalg.norm(a - b), np.linalg.norm(b)
+            rel = num / den if den > 0 else num
+            row = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+            say("%s: dh rel L2 = %.3g (worst row %.3g)" % (tag, rel, row.max()))
+            assert rel <= DH_TOL
+
+
+SMALL = {
+    "H256_V1000_4bit": dict(M=600, H=256, V=1000, bits=4),
+    "H1536_V777_8bit_cap_zipf_randmask": dict(M=300, H=1536, V=777, bits=8, softcap=30.0, targets="zipf",
+                                             mask="random", mask_frac=0.3),
+    "H2560_V400_4bit_cap_prefixmask": dict(M=520, H=2560, V=400, bits=4, softcap=30.0, mask="prefix",
+                                          mask_frac=0.5),
+    "H4096_V300_4bit": dict(M=257, H=4096, V=300, bits=4),
+    "H2560_V260_8bit_cap_small_scales": dict(M=140, H=2560, V=260, bits=8, softcap=30.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_reduced_case_against_full_oracle(torch_cuda, name):
+    kw = SMALL[name]
+    inp = syn.make_custom(seed=zlib.crc32(name.encode()) % 1000, **kw)
+    g = np.random.default_rng(1).uniform(-2, 2, size=kw["M"])
+    say("case %s: GPU fwd+bwd" % name)
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    orc = oracle.cce(inp, g=g)
+    check(inp, gpu, orc, np.arange(kw["M"]), name)
+
+
+def test_workload0_full(torch_cuda):
+    inp = syn.make_inputs(syn.WORKLOADS[0], syn.seed_for(0))
+    say("workload 0 (M=16 H=256 V=4096): GPU fwd+bwd")
+    gpu = run_gpu(torch_cuda, inp)
+    check(inp, gpu, oracle.cce(inp), np.arange(16), "workload0")
+
+
+def sample_rows(inp, n, seed):
+    M = inp["M"]
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1, M // 2}
+    if inp["mask"] is not None:
+        rows |= set(np.flatnonzero(inp["mask"] == 0)[:2].tolist())
+        act = np.flatnonzero(inp["mask"] != 0)
+        rows |= {int(act[0]), int(act[-1])}
+    rows |= set(rng.choice(M, size=n, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_workload_sampled(torch_cuda, cfg):
+    w = syn.WORKLOADS[cfg]
+    say("workload %d (%s): generating inputs" % (cfg, w.name))
+    inp = syn.make_inputs(w, syn.seed_for(cfg))
+    say("workload %d: GPU fwd+bwd at full size" % cfg)
+    gpu = run_gpu(torch_cuda, inp)
+    rows = sample_rows(inp, 6, cfg)
+    say("workload %d: oracle on %d sampled tokens" % (cfg, len(rows)))
+    orc = oracle.cce(inp, tokens=rows)
+    check(inp, gpu, orc, rows, "workload%d" % cfg)
+    # properties that hold for every token
+    glogp, glse, gdh = gpu
+    act = np.ones(inp["M"], bool) if inp["mask"] is None else inp["mask"] != 0
+    assert np.all(glogp[act] <= 1e-6) and np.all(np.isfinite(glse))
+    assert np.all(np.isfinite(gdh))
+
+
+EDGE = {
+    "M1": dict(M=1, H=128, V=300, bits=4),
+    "M2": dict(M=2, H=128, V=300, bits=8),
+    "M3": dict(M=3, H=192, V=300, bits=4, softcap=5.0),
+    "M4": dict(M=4, H=64, V=129, bits=8),
+    "M255": dict(M=255, H=64, V=130, bits=4),
+    "M256": dict(M=256, H=64, V=128, bits=4),
+    "M257": dict(M=257, H=64, V=127, bits=8),
+    "V1": dict(M=5, H=64, V=1, bits=4),
+    "V2": dict(M=5, H=128, V=2, bits=8, softcap=3.0),
+    "V65": dict(M=7, H=320, V=65, bits=4),
+    "H64": dict(M=33, H=64, V=1000, bits=8),
+    "H320_ragged_dh_tile": dict(M=40, H=320, V=200, bits=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_shapes(torch_cuda, name):
+    kw = EDGE[name]
+    inp = syn.make_custom(seed=7, **kw)
+    g = np.random.default_rng(2).uniform(-1, 1, size=kw["M"])
+    say("edge %s: GPU fwd+bwd" % name)
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(kw["M"]), name)
+
+
+def test_all_masked_and_out_of_range_targets(torch_cuda):
+    inp = syn.make_custom(M=20, H=128, V=500, bits=4, seed=3)
+    inp["mask"] = np.zeros(20, np.uint8)
+    say("edge all-masked: GPU fwd+bwd")
+    logp, lse, dh = run_gpu(torch_cuda, inp)
+    assert np.all(logp == 0) and np.all(lse == 0) and np.all(dh == 0)
+    inp["mask"] = None
+    inp["targets"] = np.array([-1, 500, 2 ** 31 - 1, -(2 ** 31)] + list(range(16)), np.int32)
+    say("edge out-of-range targets: GPU fwd+bwd")
+    gpu = run_gpu(torch_cuda, inp)
+    orc = oracle.cce(inp)
+    check(inp, gpu, orc, np.arange(20), "oob-targets")
+    assert np.allclose(gpu[0][:4], -gpu[1][:4], atol=1e-6)
+
+
+def test_repeat_runs_are_bitwise_identical(torch_cuda):
+    inp = syn.make_custom(M=300, H=512, V=3000, bits=8, seed=11, softcap=30.0)
+    say("determinism: two GPU runs")
+    a = run_gpu(torch_cuda, inp)
+    b = run_gpu(torch_cuda, inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
