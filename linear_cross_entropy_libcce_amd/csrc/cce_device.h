@@ -13,9 +13,12 @@
 //    kernel, lifted onto the matrix cores).  The bias term sum_g b[v,g]*S[t,g]
 //    (S = per-group sum of h) rides along as extra K columns: hi/lo bf16
 //    splits S_hi*b_hi + S_lo*b_hi + S_hi*b_lo, accumulated directly.
-//  * The backward contracts bf16 coefficients with a bf16-dequantized head tile
-//    (s*q + b rounded once, in LDS); fp32 accumulation.  The one-hot part of
-//    the coefficient is split off and added in fp32 in the final reduction.
+//  * The backward contracts bf16 coefficients -g*p*c' with a bf16-dequantized
+//    head tile (s*q + b rounded once, in LDS), fp32 accumulation.  The target
+//    column's whole term g*(1 - p_t)*c'_t*w_t is kept out of that path and
+//    added in fp32, with 1 - p_t = -expm1(y_t - lse): exact for a flat softmax
+//    (where that term dominates) and for a peaked one (where it is a small
+//    difference of large numbers).
 //
 // Tile roles: a workgroup is 4 waves (256 threads).  MFMA v_mfma_f32_16x16x32_bf16
 // lane layout (verified on gfx950): operand lane l holds row l%16, K elements
@@ -42,7 +45,7 @@ constexpr int MAX_G = 256;     // H <= 16384
 struct TokRec {
   float lse;   // backward: lse of the token (0 for padding rows)
   float g;     // backward: cotangent (0 for padding rows)
-  float tval;  // forward: softcapped target logit; backward: g * c'(z_target)
+  float tval;  // forward: softcapped target logit; backward: target coefficient
   int tgt;     // target id, -1 for padding rows
 };
 
@@ -169,7 +172,8 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t *h, int H, int G, i
 // ---------------------------------------------------------------------------
 // Target logit of each compacted row, in fp32 straight from the packed row:
 // z = sum_g (s * sum_{d in g} h_d q_d + b * S_g).  One wave per row.
-// Forward: tval = c(z).  Backward: tval = g * c'(z), the one-hot coefficient.
+// Forward: tval = c(z).  Backward: tval = g * (1 - exp(c(z) - lse)) * c'(z),
+// the target column's coefficient.
 template <int BITS>
 __global__ void __launch_bounds__(256) k_target(const uint16_t *haug, int Ka, int Kb, int H, int G,
                                                 const uint32_t *wq, int wpr, const float *scales,
@@ -194,12 +198,13 @@ __global__ void __launch_bounds__(256) k_target(const uint16_t *haug, int Ka, in
       part += scales[(size_t)tgt * G + gg] * A + biases[(size_t)tgt * G + gg] * S;
     }
     const float z = wave_sum(part);
+    float y = z, dc = 1.0f;
     if (cap > 0.0f) {
       const float th = tanhf(z / cap);
-      out = bwd ? tok[r].g * (1.0f - th * th) : cap * th;
-    } else {
-      out = bwd ? tok[r].g : z;
+      y = cap * th;
+      dc = 1.0f - th * th;
     }
+    out = bwd ? tok[r].g * -expm1f(y - tok[r].lse) * dc : y;
   }
   if (lane == 0) tok[r].tval = out;
 }
@@ -310,7 +315,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_tile(TileArgs a) {
   for (int ti = 0; ti < 4; ++ti) hp[ti] = a.haug + (size_t)(tok0 + ti * 16 + l16) * a.Ka + lq * 8;
 
   float run_m[4], run_s[4];
-  float lse_t[4], gneg_t[4];
+  float lse_t[4], g_t[4];
+  int64_t tgt_t[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     run_m[ti] = -INFINITY;
@@ -318,7 +324,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_tile(TileArgs a) {
     if (BWD) {
       const TokRec rec = a.tok[tok0 + ti * 16 + l16];
       lse_t[ti] = rec.lse;
-      gneg_t[ti] = -rec.g;
+      g_t[ti] = rec.g;
+      tgt_t[ti] = rec.tgt;
     }
   }
 
@@ -436,8 +443,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_tile(TileArgs a) {
                 y = cap * th;
                 dc = 1.0f - th * th;
               }
-              const float val = gneg_t[ti] * __expf(y - lse_t[ti]) * dc;
-              c[h2 * 4 + j] = (v < a.V) ? val : 0.0f;
+              // -g * softmax * c'; the target column is left out here and its
+              // whole term g * (1 - p) * c' * w is added in fp32 by k_dh_reduce.
+              const float val = -g_t[ti] * __expf(y - lse_t[ti]) * dc;
+              c[h2 * 4 + j] = (v < a.V && v != tgt_t[ti]) ? val : 0.0f;
             }
           // packet (p2, lq): rows {32*p2 + 4*lq + 0..3} then {32*p2 + 16 + 4*lq + 0..3}
           *(u32x4_t *)(crow + (p2 * 4 + lq) * 8) =
@@ -648,7 +657,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_dh_gemm(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dh[t][:] = sum_k dh_part[k][r][:] + g*c'(z_target) * w[target][:] (fp32),
+// dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
 // zero rows for masked tokens.
 template <int BITS>
 __global__ void __launch_bounds__(256) k_dh_reduce(const float *dh_part, int ksplit, int M_pad, int H, int G,
@@ -663,7 +672,7 @@ __global__ void __launch_bounds__(256) k_dh_reduce(const float *dh_part, int ksp
   if (r >= 0) {
     for (int k = 0; k < ksplit; ++k) acc += dh_part[((size_t)k * M_pad + r) * H + d];
     const TokRec rec = tok[r];
-    if (rec.tval != 0.0f && rec.tgt >= 0 && (int64_t)rec.tgt < V) {
+    if (rec.tgt >= 0 && (int64_t)rec.tgt < V) {
       const size_t gi = (size_t)rec.tgt * G + d / KSTEP;
       const float q = (float)code_at<BITS>(wq + (size_t)rec.tgt * wpr, d);
       acc += rec.tval * (scales[gi] * q + biases[gi]);

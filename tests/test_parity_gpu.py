@@ -182,3 +182,19 @@ def test_repeat_runs_are_bitwise_identical(torch_cuda):
     b = run_gpu(torch_cuda, inp)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 30.0])
+def test_peaked_softmax(torch_cuda, softcap):
+    """Target probability near 1: dh = g (1 - p_t) c'_t w_t - ..., a small
+    difference of large terms; the coefficient must be formed before rounding."""
+    inp = syn.make_custom(M=64, H=256, V=300, bits=4, seed=5, softcap=softcap)
+    hf = np.abs(syn.f32_from_bf16_bits(inp["h"]))
+    inp["h"] = syn.bf16_bits_from_f32(hf)
+    inp["targets"][:48] = 7
+    inp["biases"][7] += np.float32(0.07)
+    say("peaked softmax (cap %g): GPU fwd+bwd" % softcap)
+    gpu = run_gpu(torch_cuda, inp)
+    orc = oracle.cce(inp)
+    assert np.exp(orc[0][:48]).min() > 0.95   # the case really is peaked
+    check(inp, gpu, orc, np.arange(64), "peaked")
