@@ -1,0 +1,164 @@
+#!/usr/bin/env python3
+"""Throughput of libcce's flash cut-cross-entropy head, forward + backward.
+
+One step = cce_forward + cce_backward (g = 1) over one batch of the synthetic
+workload M=8192 tokens, H=2560, V=262144, 8-bit affine head (group 64),
+softcap 30 -- the largest single-GPU workload at H=2560, V=262144.  Inputs are
+resident in HBM and workspaces preallocated before the timed region.
+
+Prints one JSON line.  `value` is supervised tokens per second of fwd+bwd.
+`roofline` is for the kernel family with the most time per step, timed live
+with HIP events on the launch stream (include/cce_profile.h), against the
+MI355X dense bf16 MFMA peak.  `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload's tokens.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, seconds, M_eff):
+    """The oracle, untuned, on a bounded token sample; scaled to tokens/s."""
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle
+    act = np.arange(inp["M"]) if inp["mask"] is None else np.flatnonzero(inp["mask"])
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    oracle.cce(inp, tokens=act[:1])
+    per_tok = time.perf_counter() - t0
+    n = int(max(1, min(64, seconds / max(per_tok, 1e-3))))
+    toks = rng.choice(act, size=n, replace=False)
+    t0 = time.perf_counter()
+    oracle.cce(inp, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "fwd+bwd of %d random supervised tokens of the full workload (%.1f s)" % (n, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the head is data-parallel over tokens with no "
+              "communication, so a %d-GPU run is %d independent copies of this one; "
+              "run with --gpus 1." % (args.gpus, args.gpus), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_cross_entropy_libcce_amd import cce
+    from linear_cross_entropy_libcce_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    log("generating workload %d (%s)" % (args.workload, w.name))
+    inp = syn.make_inputs(w, syn.seed_for(args.workload))
+    M, H, V = inp["M"], inp["H"], inp["V"]
+    M_eff = M if inp["mask"] is None else int(inp["mask"].sum())
+    dev = torch.device("cuda:0")
+    head = cce.head_from_numpy(inp, dev)
+    h, t, m = cce.tokens_from_numpy(inp, dev)
+    ws_f = torch.empty(cce.forward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(cce.backward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
+    logp = torch.empty(M, dtype=torch.float32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev)
+    dh = torch.empty((M, H), dtype=torch.float32, device=dev)
+
+    def step():
+        cce.cce_forward(h, head, t, m, workspace=ws_f, out=(logp, lse))
+        cce.cce_backward(h, head, t, lse, None, m, workspace=ws_b, out=dh)
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log("timing %d steps" % args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    log("%.3f ms/step (wall %.3f ms/step)" % (ms, 1e3 * wall / args.steps))
+
+    # per-kernel timing pass (same steps, events around every launch)
+    log("per-kernel timing pass")
+    cce.profile_read()
+    cce.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = cce.profile_read()
+    cce.profile_enable(False)
+    per_step = {k: (n / args.steps, tot / args.steps) for k, (n, tot) in prof.items()}
+    for k, (n, tot) in sorted(per_step.items(), key=lambda kv: -kv[1][1]):
+        log("  %-10s %5.1f launches/step  %8.3f ms/step" % (k, n, tot))
+
+    alg_flops = 6.0 * M_eff * V * H          # forward logits + backward recompute + dh
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+    per_kernel_flops = {"tile_fwd": 2.0 * M_eff * V * H, "tile_bwd": 2.0 * M_eff * V * H,
+                        "dh_gemm": 2.0 * M_eff * V * H}
+    dom = max(per_step, key=lambda k: per_step[k][1])
+    n_l, t_l = per_step[dom]
+    roof = None
+    if dom in per_kernel_flops:
+        flop_launch = per_kernel_flops[dom] / n_l
+        achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flop_per_launch": flop_launch, "avg_launch_ms": round(t_l / n_l, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a token sample (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, M_eff)
+
+    out = {
+        "metric": "CCE fwd+bwd tokens/s and % bf16 MFMA peak at H=2560,V=262144",
+        "value": round(M_eff / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V, "bits": inp["bits"],
+                   "group": 64, "softcap": inp["softcap"], "g": 1.0},
+        "tflops": round(tflops, 1),
+        "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "kernel_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

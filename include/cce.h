@@ -80,7 +80,8 @@ typedef struct cce_head {
 /*
  * Bytes of device workspace that cce_forward / cce_backward need for this head
  * and M tokens.  Returns 0 when the head or M is invalid (cce_forward then
- * reports why).  The value depends only on (V, H, bits, M).
+ * reports why).  The value depends only on (V, H, bits, M) and the compute
+ * unit count of the current device (the launch plan fills whole rounds).
  */
 size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M);
 size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M);
@@ -89,7 +90,7 @@ size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M);
  * Forward (page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts,
  * flashCceForward: vocab-parallel online-softmax partials merged across vocab
  * blocks into lse, then logp = target logit - lse).
- *   h          device bf16 [M][H] row-major (raw bf16 bits, 2-byte aligned)
+ *   h          device bf16 [M][H] row-major (raw bf16 bits, 16-byte aligned)
  *   targets    device int32 [M]
  *   mask       device uint8 [M] (nonzero = supervised token) or NULL = all
  *   logp, lse  device float [M], written for every token

@@ -17,13 +17,18 @@ LIB_PATH = os.path.join(_PKG, "libcce.so")
 CCE_OK, CCE_ERR_INVALID_ARG, CCE_ERR_UNSUPPORTED, CCE_ERR_WORKSPACE, CCE_ERR_HIP = range(5)
 
 EXPORTS = ("cce_forward", "cce_backward", "cce_forward_workspace_bytes",
-           "cce_backward_workspace_bytes", "cce_status_str", "cce_abi_version")
+           "cce_backward_workspace_bytes", "cce_status_str", "cce_abi_version",
+           "cce_profile_enable", "cce_profile_read")
 
 
 class cce_head(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("softcap", ctypes.c_float)]
+
+
+class cce_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class CceError(RuntimeError):
@@ -56,6 +61,10 @@ def load(path: str = LIB_PATH):
     lib.cce_status_str.restype = ctypes.c_char_p
     lib.cce_status_str.argtypes = [ctypes.c_int]
     lib.cce_abi_version.restype = ctypes.c_int
+    lib.cce_profile_enable.restype = ctypes.c_int
+    lib.cce_profile_enable.argtypes = [ctypes.c_int]
+    lib.cce_profile_read.restype = ctypes.c_int
+    lib.cce_profile_read.argtypes = [ctypes.POINTER(cce_kernel_time), ctypes.c_int]
     _lib = lib
     return lib
 
@@ -175,3 +184,17 @@ def tokens_from_numpy(inp: dict, device="cuda"):
     t = torch.from_numpy(inp["targets"]).to(device)
     m = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).to(device)
     return h, t, m
+
+
+def profile_enable(on: bool) -> bool:
+    """Opt-in per-kernel event timing (include/cce_profile.h); returns the old state."""
+    return bool(load().cce_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel family: (launches, total_ms)} since the last read (waits for the GPU)."""
+    buf = (cce_kernel_time * 32)()
+    n = load().cce_profile_read(buf, 32)
+    if n < 0:
+        raise CceError(CCE_ERR_HIP, "event timing failed")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}

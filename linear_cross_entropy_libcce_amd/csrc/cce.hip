@@ -8,8 +8,12 @@
 #include <cstdio>
 #include <cstring>
 
+#include <mutex>
+#include <vector>
+
 #include "cce.h"
 #include "cce_device.h"
+#include "cce_profile.h"
 
 namespace {
 
@@ -18,11 +22,58 @@ using namespace cce;
 constexpr int64_t MAX_H = 16384;
 constexpr int64_t MAX_M = (int64_t)1 << 24;
 constexpr size_t COEFF_BUDGET = (size_t)256 << 20;  // bytes of one coefficient chunk
-constexpr int TARGET_WGS = 512;                     // two rounds of 256 CUs
 
 thread_local char g_err[256];
 
+// ---- opt-in launch timing (cce_profile.h) ----------------------------------
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+int g_prof_on = 0;
+
+struct ProfScope {
+  ProfRec r{nullptr, nullptr, nullptr};
+  hipStream_t st;
+  ProfScope(const char *name, hipStream_t s) : st(s) {
+    if (!g_prof_on) return;
+    r.name = name;
+    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) {
+      r.name = nullptr;
+      return;
+    }
+    (void)hipEventRecord(r.a, st);
+  }
+  ~ProfScope() {
+    if (!r.name) return;
+    (void)hipEventRecord(r.b, st);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof.push_back(r);
+  }
+};
+
+#define CCE_LAUNCH(NAME, STREAM, CALL)    \
+  do {                                    \
+    ProfScope prof_scope_(NAME, STREAM);  \
+    CALL;                                 \
+  } while (0)
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
@@ -32,7 +83,7 @@ struct Plan {
   // forward
   int nsplit, tiles_per_split;
   // backward
-  int chunk_tiles, nchunks, ksplit, k_tiles, HT;
+  int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;
   int64_t ld_coeff;
   // workspace offsets (bytes)
   size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
@@ -45,7 +96,7 @@ cce_status check_head(const cce_head *hd) {
   if (hd->bits != 4 && hd->bits != 8) return CCE_ERR_UNSUPPORTED;
   if (hd->group != KSTEP) return CCE_ERR_UNSUPPORTED;
   if (hd->H % hd->group != 0) return CCE_ERR_INVALID_ARG;
-  if (hd->H > MAX_H || hd->V > (int64_t)INT32_MAX - BN) return CCE_ERR_UNSUPPORTED;
+  if (hd->H > MAX_H || hd->V > (int64_t)INT32_MAX - BNT) return CCE_ERR_UNSUPPORTED;
   if (((uintptr_t)hd->wq & 15) || ((uintptr_t)hd->scales & 3) || ((uintptr_t)hd->biases & 3))
     return CCE_ERR_INVALID_ARG;
   return CCE_OK;
@@ -65,20 +116,38 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.NB = p.Kb / KSTEP;
   p.wpr = (int)(p.H * p.bits / 32);
   p.TT = (int)(p.M_pad / BM);
-  p.tiles = (int)cdiv(p.V, BN);
+  p.tiles = (int)cdiv(p.V, BNT);
+  const int64_t cus = device_cus();
 
-  p.nsplit = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(1, cdiv(TARGET_WGS, p.TT)));
+  // forward: about one round of tile workgroups (one per CU)
+  p.nsplit = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(1, cdiv(cus, p.TT)));
   p.tiles_per_split = (int)cdiv(p.tiles, p.nsplit);
   p.nsplit = (int)cdiv(p.tiles, p.tiles_per_split);
 
-  const int64_t per_tile = p.M_pad * BN * 2;
+  // backward: coefficient chunks of at most COEFF_BUDGET bytes
+  const int64_t per_tile = p.M_pad * BNT * 2;
   p.chunk_tiles = (int)std::max<int64_t>(1, std::min<int64_t>(p.tiles, (int64_t)COEFF_BUDGET / per_tile));
   p.nchunks = (int)cdiv(p.tiles, p.chunk_tiles);
-  p.ld_coeff = (int64_t)p.chunk_tiles * BN;
+  p.ld_coeff = (int64_t)p.chunk_tiles * BNT;
+  p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(4, (int64_t)p.TT * p.chunk_tiles / (2 * cus)));
   p.HT = (int)cdiv(p.H, DT);
-  p.ksplit = (int)std::min<int64_t>(p.chunk_tiles, std::max<int64_t>(1, cdiv(TARGET_WGS, (int64_t)p.TT * p.HT)));
-  p.k_tiles = (int)cdiv(p.chunk_tiles, p.ksplit);
-  p.ksplit = (int)cdiv(p.chunk_tiles, p.k_tiles);
+  // Vocabulary splits of the dh contraction (in 128-row units): the fewest that
+  // fill whole rounds of resident workgroups (2 per CU) to >= 90%; each split
+  // adds one dh slab.
+  const int gchunk = 2 * p.chunk_tiles;
+  {
+    const int64_t slots = 2 * cus;
+    const int64_t base = (int64_t)p.TT * p.HT;
+    int best = 1;
+    for (int ks = 1; ks <= 8 && ks <= gchunk; ++ks) {
+      best = ks;
+      const int64_t n = base * ks;
+      if ((double)n / (double)(cdiv(n, slots) * slots) >= 0.9) break;
+    }
+    p.ksplit = best;
+  }
+  p.k_tiles = (int)cdiv(gchunk, p.ksplit);
+  p.ksplit = (int)cdiv(gchunk, p.k_tiles);
 
   size_t o = 0;
   p.o_cnt = o;  o = align_up(o + 256, 256);
@@ -88,7 +157,7 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   const size_t common = o;
   p.o_part = common;
-  p.fwd_bytes = align_up(common + sizeof(float) * 2 * p.nsplit * p.M_pad, 256);
+  p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * p.nsplit) * p.M_pad, 256);
   p.o_coeff = common;
   o = align_up(common + (size_t)2 * p.M_pad * p.ld_coeff, 256);
   p.o_dhp = o;
@@ -104,7 +173,7 @@ cce_status check_common(const cce_head *hd, const void *h, int64_t M, const int3
   if (M > MAX_M) return CCE_ERR_UNSUPPORTED;
   if (M == 0) return CCE_OK;
   if (!h || !targets) return CCE_ERR_INVALID_ARG;
-  if (((uintptr_t)h & 1) || ((uintptr_t)targets & 3)) return CCE_ERR_INVALID_ARG;
+  if (((uintptr_t)h & 15) || ((uintptr_t)targets & 3)) return CCE_ERR_INVALID_ARG;
   if (workspace && ((uintptr_t)workspace & 255)) return CCE_ERR_INVALID_ARG;
   return CCE_OK;
 }
@@ -130,18 +199,11 @@ void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_
   int *inv = ws_at<int>(ws, p.o_inv);
   TokRec *tok = ws_at<TokRec>(ws, p.o_tok);
   uint16_t *haug = ws_at<uint16_t>(ws, p.o_haug);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt);
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)p.M_pad), dim3(256), 0, st, (const uint16_t *)h, (int)p.H, p.G,
-                     p.Kb, p.Ka, (const int *)idx, targets, lse, g, tok, haug);
-  const dim3 tg((unsigned)cdiv(p.M_pad, 4));
-  if (p.bits == 4)
-    hipLaunchKernelGGL(k_target<4>, tg, dim3(256), 0, st, (const uint16_t *)haug, p.Ka, p.Kb, (int)p.H, p.G,
-                       hd->wq, p.wpr, hd->scales, hd->biases, p.V, p.cap, (const int *)cnt, tok, (int)p.M_pad,
-                       bwd ? 1 : 0);
-  else
-    hipLaunchKernelGGL(k_target<8>, tg, dim3(256), 0, st, (const uint16_t *)haug, p.Ka, p.Kb, (int)p.H, p.G,
-                       hd->wq, p.wpr, hd->scales, hd->biases, p.V, p.cap, (const int *)cnt, tok, (int)p.M_pad,
-                       bwd ? 1 : 0);
+  CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
+  CCE_LAUNCH("prep", st, launch_prep(st, (int)p.M_pad, (const uint16_t *)h, (int)p.H, p.G, p.Kb, p.Ka, idx, targets,
+                                     lse, g, tok, haug));
+  CCE_LAUNCH("target", st, launch_target(st, p.bits, (int)p.M_pad, (const uint16_t *)h, idx, (int)p.H, p.G, hd->wq,
+                                         p.wpr, hd->scales, hd->biases, p.V, p.cap, cnt, tok, bwd ? 1 : 0));
 }
 
 TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
@@ -158,7 +220,10 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.NB = p.NB;
   a.wpr = p.wpr;
   a.M_pad = (int)p.M_pad;
+  a.ks16 = p.Ka / 16;
+  a.ksv = p.ld_coeff / 16;
   a.cap = p.cap;
+  a.inv_cap = p.cap > 0.0f ? 1.0f / p.cap : 0.0f;
   return a;
 }
 
@@ -206,14 +271,12 @@ cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int
   a.range_tile0 = 0;
   a.range_tiles = p.tiles;
   a.tiles_per_wg = p.tiles_per_split;
-  const dim3 grid((unsigned)p.TT, (unsigned)p.nsplit);
-  if (p.bits == 4)
-    hipLaunchKernelGGL((k_tile<4, false>), grid, dim3(NTHREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_tile<8, false>), grid, dim3(NTHREADS), 0, st, a);
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)cdiv(M, 256)), dim3(256), 0, st,
-                     (const float *)a.part, p.nsplit, (int)p.M_pad, ws_at<const int>(workspace, p.o_inv),
-                     ws_at<const TokRec>(workspace, p.o_tok), (int)M, logp, lse);
+  a.nwr = p.nsplit;
+  a.nblocks = p.TT * p.nsplit;
+  const dim3 grid((unsigned)(cdiv(a.nblocks, 8) * 8));
+  CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, false, grid, a));
+  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, 2 * p.nsplit, (int)p.M_pad, ws_at<const int>(workspace, p.o_inv),
+                                       ws_at<const TokRec>(workspace, p.o_tok), logp, lse));
   return hip_status();
 }
 
@@ -233,7 +296,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   TileArgs a = tile_args(p, head, workspace);
   a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
   a.ld_coeff = p.ld_coeff;
-  a.tiles_per_wg = 1;
+  a.tiles_per_wg = p.bwd_tpw;
 
   GemmArgs ga{};
   ga.coeff = a.coeff;
@@ -249,36 +312,64 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   ga.wpr = p.wpr;
   ga.M_pad = (int)p.M_pad;
   ga.tiles_per_split = p.k_tiles;
+  ga.HT = p.HT;
+  ga.ksplit = p.ksplit;
+  ga.nblocks = p.TT * p.HT * p.ksplit;
+  const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
 
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * p.chunk_tiles;
     const int nt = std::min(p.chunk_tiles, p.tiles - t0);
     a.range_tile0 = t0;
     a.range_tiles = nt;
-    const dim3 g1((unsigned)p.TT, (unsigned)nt);
-    if (p.bits == 4)
-      hipLaunchKernelGGL((k_tile<4, true>), g1, dim3(NTHREADS), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_tile<8, true>), g1, dim3(NTHREADS), 0, st, a);
-    ga.chunk_tile0 = t0;
-    ga.chunk_tiles = nt;
+    a.nwr = (int)cdiv(nt, p.bwd_tpw);
+    a.nblocks = p.TT * a.nwr;
+    const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
+    CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, true, g1, a));
+    ga.chunk_tile0 = 2 * t0;  // the dh contraction counts 128-row vocabulary tiles
+    ga.chunk_tiles = 2 * nt;
     ga.accumulate = c > 0;
-    const dim3 g2((unsigned)p.TT, (unsigned)p.HT, (unsigned)p.ksplit);
-    if (p.bits == 4)
-      hipLaunchKernelGGL(k_dh_gemm<4>, g2, dim3(NTHREADS), 0, st, ga);
-    else
-      hipLaunchKernelGGL(k_dh_gemm<8>, g2, dim3(NTHREADS), 0, st, ga);
+    CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
   }
-  const dim3 gr((unsigned)M, (unsigned)cdiv(p.H, 256));
-  if (p.bits == 4)
-    hipLaunchKernelGGL(k_dh_reduce<4>, gr, dim3(256), 0, st, (const float *)ga.dh_part, p.ksplit, (int)p.M_pad,
-                       (int)p.H, p.G, ws_at<const int>(workspace, p.o_inv), ws_at<const TokRec>(workspace, p.o_tok),
-                       head->wq, p.wpr, head->scales, head->biases, p.V, dh);
-  else
-    hipLaunchKernelGGL(k_dh_reduce<8>, gr, dim3(256), 0, st, (const float *)ga.dh_part, p.ksplit, (int)p.M_pad,
-                       (int)p.H, p.G, ws_at<const int>(workspace, p.o_inv), ws_at<const TokRec>(workspace, p.o_tok),
-                       head->wq, p.wpr, head->scales, head->biases, p.V, dh);
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga.dh_part, p.ksplit, (int)p.M_pad, (int)p.H, p.G,
+                                               ws_at<const int>(workspace, p.o_inv),
+                                               ws_at<const TokRec>(workspace, p.o_tok), head->wq, p.wpr, head->scales,
+                                               head->biases, p.V, dh));
   return hip_status();
+}
+
+int cce_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  const int prev = g_prof_on;
+  g_prof_on = on ? 1 : 0;
+  return prev;
+}
+
+int cce_profile_read(cce_kernel_time *out, int max) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  int n = 0, rc = 0;
+  for (const ProfRec &r : recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) rc = -1;
+    int i = 0;
+    while (i < n && std::strncmp(out[i].name, r.name, sizeof out[i].name) != 0) ++i;
+    if (i == n && n < max && out) {
+      std::memset(&out[n], 0, sizeof out[n]);
+      std::strncpy(out[n].name, r.name, sizeof out[n].name - 1);
+      ++n;
+    }
+    if (i < n) {
+      out[i].launches += 1;
+      out[i].total_ms += ms;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  return rc < 0 ? -1 : n;
 }
 
 }  // extern "C"

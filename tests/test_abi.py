@@ -18,8 +18,13 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "cce.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(cce_\w+)\s*\(", text, re.M)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(cce_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -91,6 +96,11 @@ def test_bad_token_arguments_are_rejected(lib):
                             None) == cce.CCE_ERR_INVALID_ARG   # misaligned g
     assert lib.cce_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x100000, bneed - 256,
                             None) == cce.CCE_ERR_WORKSPACE
+
+
+def test_profile_api_without_launches(lib):
+    assert lib.cce_profile_enable(0) == 0
+    assert cce.profile_read() == {}
 
 
 def test_status_strings(lib):
