@@ -25,6 +25,37 @@ sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30        # calibration copy: reads and writes exactly this many bytes
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_M8192_H2560_V262144_8bit.txt")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; a traffic measurement is valid only for them."""
+    import hashlib
+    d = os.path.join(ROOT, "linear_cross_entropy_libcce_amd", "csrc")
+    hsh = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        hsh.update(f.encode())
+        hsh.update(open(os.path.join(d, f), "rb").read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["%s.fetch_bytes_per_launch" % kernel]) + float(kv["%s.write_bytes_per_launch" % kernel])
+    except KeyError:
+        return None
 
 
 def log(msg):
@@ -57,6 +88,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain device copy of COPY_BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the head is data-parallel over tokens with no "
@@ -67,6 +100,15 @@ def main():
     import torch
     from linear_cross_entropy_libcce_amd import cce
     from linear_cross_entropy_libcce_amd import synthetic as syn
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy of %d bytes done" % COPY_BYTES)
 
     w = syn.WORKLOADS[args.workload]
     log("generating workload %d (%s)" % (args.workload, w.name))
@@ -127,8 +169,11 @@ def main():
     if dom in per_kernel_flops:
         flop_launch = per_kernel_flops[dom] / n_l
         achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
+        tb = measured_traffic(dom) if args.workload == 3 else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": tb,
+                "traffic_GB_per_s": None if tb is None else round(tb / (t_l / n_l * 1e-3) / 1e9, 1),
                 "flop_per_launch": flop_launch, "avg_launch_ms": round(t_l / n_l, 4)}
 
     cpu = None
