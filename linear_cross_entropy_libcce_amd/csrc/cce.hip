@@ -86,7 +86,7 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_bunit, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
 };
 
 cce_status check_head(const cce_head *hd) {
@@ -155,6 +155,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_inv = o;  o = align_up(o + sizeof(int) * std::max<int64_t>(M, 1), 256);
   p.o_tok = o;  o = align_up(o + sizeof(TokRec) * p.M_pad, 256);
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
+  p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
+  p.o_bunit = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   const size_t common = o;
   p.o_part = common;
   p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * p.nsplit) * p.M_pad, 256);
@@ -202,6 +204,8 @@ void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_
   CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
   CCE_LAUNCH("prep", st, launch_prep(st, (int)p.M_pad, (const uint16_t *)h, (int)p.H, p.G, p.Kb, p.Ka, idx, targets,
                                      lse, g, tok, haug));
+  CCE_LAUNCH("bias_op", st, launch_bias_operand(st, p.bits, hd->biases, hd->scales, p.V, p.G, p.Kb, ws_at<uint8_t>(ws, p.o_baug),
+                                                           ws_at<float>(ws, p.o_bunit)));
   CCE_LAUNCH("target", st, launch_target(st, p.bits, (int)p.M_pad, (const uint16_t *)h, idx, (int)p.H, p.G, hd->wq,
                                          p.wpr, hd->scales, hd->biases, p.V, p.cap, cnt, tok, bwd ? 1 : 0));
 }
@@ -209,6 +213,8 @@ void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_
 TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   TileArgs a{};
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
+  a.baug = ws_at<const uint8_t>(ws, p.o_baug);
+  a.bunit = ws_at<const float>(ws, p.o_bunit);
   a.wq = hd->wq;
   a.scales = hd->scales;
   a.biases = hd->biases;
@@ -217,6 +223,7 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.V = p.V;
   a.G = p.G;
   a.Ka = p.Ka;
+  a.Kb = p.Kb;
   a.NB = p.NB;
   a.wpr = p.wpr;
   a.M_pad = (int)p.M_pad;

@@ -20,9 +20,9 @@
 //    (where that term dominates) and for a peaked one (where it is a small
 //    difference of large numbers).
 //
-// Tile roles: a workgroup is 4 waves (256 threads).  MFMA v_mfma_f32_16x16x32_bf16
-// lane layout (verified on gfx950): operand lane l holds row l%16, K elements
-// 8*(l/16)..+8; result lane l holds column l%16, rows 4*(l/16)+0..3.
+// MFMA v_mfma_f32_32x32x16_bf16 lane layout (verified on gfx950): operand
+// lane l holds row l%32, K elements 8*(l/32)..+8; result lane l holds column
+// l%32, rows 8i + 4*(l/32) + j in element 4i + j (i, j in 0..3).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -83,6 +83,12 @@ __device__ __forceinline__ void unpack8(uint32_t w, uint32_t *o) {
   o[1] = pack_rne((float)((w >> 16) & 0xFFu), (float)(w >> 24));
 }
 
+// 4 signed bytes of one word -> 2 dwords of exact bf16 pairs.
+__device__ __forceinline__ void unpack8s(uint32_t w, uint32_t *o) {
+  o[0] = pack_rne((float)((int)(w << 24) >> 24), (float)((int)(w << 16) >> 24));
+  o[1] = pack_rne((float)((int)(w << 8) >> 24), (float)((int)w >> 24));
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t code_at(const uint32_t *row, int d) {
   constexpr int PER = 32 / BITS;
@@ -105,7 +111,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 struct TileArgs {
-  const uint16_t *haug;  // [M_pad][Ka] bf16
+  const uint16_t *haug;  // [M_pad][Ka] bf16, fragment-major
+  const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
+  const float *bunit;    // [V] fixed-point unit of each row's biases
   const uint32_t *wq;
   const float *scales;
   const float *biases;
@@ -115,7 +123,7 @@ struct TileArgs {
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
   int64_t V;
-  int G, Ka, NB, wpr, M_pad;
+  int G, Ka, Kb, NB, wpr, M_pad;
   int64_t ks16;          // Ka / 16 (fragment-major h rows)
   int64_t ksv;           // ld_coeff / 16 (fragment-major coefficient chunk)
   int range_tile0, range_tiles, tiles_per_wg, nwr, nblocks;
@@ -136,6 +144,21 @@ struct GemmArgs {
   int HT, ksplit, nblocks;
   int accumulate;
 };
+
+// Raw buffer resource over [base, base + bytes): a lane whose byte offset is
+// at or past `bytes` reads zeros (and its write is dropped), so ragged tails
+// need no per-lane predicate.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float buf_loadf(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 
 // Linear block id -> work id, so that consecutive work ids share an XCD
 // (blocks are dispatched to the 8 XCDs round-robin).  nb_grid % 8 == 0.
@@ -174,6 +197,8 @@ void launch_prep(hipStream_t st, int M_pad, const uint16_t *h, int H, int G, int
 void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const int *idx, int H, int G,
                    const uint32_t *wq, int wpr, const float *scales, const float *biases, int64_t V, float cap,
                    const int *cnt, TokRec *tok, int bwd);
+void launch_bias_operand(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G,
+                         int Kb, uint8_t *baug, float *bunit);
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
 void launch_merge(hipStream_t st, int M, const float *part, int nsplit, int M_pad, const int *inv,
                   const TokRec *tok, float *logp, float *lse);

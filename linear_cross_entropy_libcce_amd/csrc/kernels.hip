@@ -43,8 +43,10 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 // ---------------------------------------------------------------------------
 // Per compacted row r: gather h, write the augmented row [bias block | h] in
 // fragment-major layout, and the token record.  Bias block column kk
-// (part = kk / G, gi = kk % G): part 0 -> S_hi[gi], 1 -> S_lo[gi], 2 -> S_hi[gi],
-// else 0, with S = per-group sum of h.  h rows are 16-byte aligned.
+// (part = kk / G, gi = kk % G): part 0 -> 256 S_hi[gi], 1 -> 256 S_lo[gi],
+// 2 -> S_hi[gi], else 0, with S = per-group sum of h split into bf16 hi + lo
+// (the head side holds the matching fixed-point digits of the biases).  h rows
+// are 16-byte aligned.
 __global__ void __launch_bounds__(256) k_prep(const uint16_t *h, int H, int G, int Kb, int Ka,
                                               const int *idx, const int32_t *targets,
                                               const float *lse, const float *g, TokRec *tok,
@@ -80,7 +82,8 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t *h, int H, int G, i
         if (part < 3) {
           const float S = sS[gi];
           const uint32_t hi = bf16_rne(S);
-          val = (part == 1) ? bf16_rne(S - bf16_to_f32(hi)) : hi;
+          const float x = (part == 1) ? 256.0f * (S - bf16_to_f32(hi)) : bf16_to_f32(hi) * (part == 0 ? 256.0f : 1.0f);
+          val = bf16_rne(x);
         }
         pr2[u] = val;
       }

@@ -9,12 +9,20 @@ namespace cce {
 // The logit tile: 256 tokens x 256 vocabulary rows per workgroup of 8 waves,
 // K = Ka (bias block, then H).  Wave w owns tokens [64(w%4), +64) and vocab
 // rows [128(w/4), +128) of the tile as 2 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = vocabulary rows).  The
-// code tile is unpacked once into LDS (double buffered, one group per step)
-// and shared by the eight waves; the token operand is loaded straight from
-// the augmented rows into registers (the two waves of a token group load the
-// same rows, served once by L2), reloaded for the next step right after its
-// last use.
+// v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = vocabulary rows).
+//
+// Per K step (one quantization group of 64):
+//  * the code tile of the step is in LDS as bf16 (double buffered) and shared
+//    by the eight waves;
+//  * the token operand comes straight from the fragment-major augmented rows
+//    into registers, one step ahead;
+//  * the producer (every thread: one vocabulary row, one half of the step)
+//    unpacks the codes of the NEXT step into the other LDS buffer, in four
+//    slices placed between the MFMAs, from words it loaded TWO steps ahead
+//    (two register sets, alternating), so global latency is covered by a
+//    full step of MFMA work and the unpack rides in the MFMA shadow.
+// All global reads are raw buffer loads: rows past V read as zeros, so there
+// is no per-lane predicate and no branch in the step.
 //
 // Scale fold without a second accumulator: the accumulator is kept in units of
 // the current group's scale, acc <- acc * (s_{g-1} / s_g) + A_g, so the MFMA
@@ -23,91 +31,94 @@ namespace cce {
 // 1; a scale of exactly 0 is replaced by 1e-30, whose contribution is nil.)
 
 constexpr int ZROW = 36;  // padded fp32 row stride of the per-wave transpose scratch (32 columns)
+constexpr float LOG2E = 1.4426950408889634f;
+
+enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2 };
+
+// One step's worth of head data for one producer thread: 32 K values of one
+// vocabulary row (4-bit: 4 words, 8-bit and bias block: 8 words of bytes), and
+// the row's scale of that step (the bias block's: its fixed-point unit).
+struct ProdRegs {
+  uint32_t w[8];
+  float s;
+};
 
 template <int BITS>
 struct Producer {
-  // Thread tid stages row tid/2 (of BNT), K half tid%2 (32 codes) of each
-  // step, and (tid even) that row's scale ratio.
-  static constexpr int NW = BITS;  // words per thread per step
-  uint32_t w[NW];
-  float s;
-  float s_prev;
+  int prow, phalf;
 
-  __device__ __forceinline__ void load(const TileArgs &a, int64_t v0, int step, int prow, int phalf) {
-    const int64_t v = v0 + prow;
-    const bool ok = v < a.V;
-    if (step >= a.NB) {
-      const int g = step - a.NB;
-      const uint32_t *src = a.wq + (size_t)v * a.wpr + g * (2 * BITS) + phalf * BITS;
+  // Issue the loads of step `step` of the vocabulary tile at v0: a bias-block
+  // step (step < NB: fixed-point digits and unit) or group step - NB (codes
+  // and scale).  Both kinds are two 16-byte loads and one scalar per thread;
+  // the source is chosen with wave-uniform selects, so no branch.
+  __device__ __forceinline__ void load(const TileArgs &a, int64_t v0, int step, ProdRegs &p) const {
+    const int64_t rows = a.V - v0 < BNT ? a.V - v0 : BNT;
+    const bool bias = step < a.NB;
+    const int g = step - a.NB;
+    const rsrc_t rw = bias ? make_rsrc(a.baug + v0 * a.Kb, rows * a.Kb)
+                           : make_rsrc(a.wq + v0 * a.wpr, rows * a.wpr * 4);
+    const int vo = bias ? prow * a.Kb + phalf * 32 : prow * a.wpr * 4 + phalf * BITS * 4;
+    const int so = bias ? step * 64 : g * (8 * BITS);
 #pragma unroll
-      for (int i = 0; i < NW; i += 4) {
-        const u32x4_t x = ok ? *(const u32x4_t *)(src + i) : u32x4_t{0, 0, 0, 0};
-        w[i] = x[0]; w[i + 1] = x[1]; w[i + 2] = x[2]; w[i + 3] = x[3];
-      }
-      s = ok ? a.scales[(size_t)v * a.G + g] : 1.0f;
+    for (int i = 0; i < 2; ++i) {
+      const u32x4_t x = buf_load16(rw, vo + 16 * i, so);
+      p.w[4 * i] = x[0]; p.w[4 * i + 1] = x[1]; p.w[4 * i + 2] = x[2]; p.w[4 * i + 3] = x[3];
     }
+    const rsrc_t rs = bias ? make_rsrc(a.bunit + v0, rows * 4) : make_rsrc(a.scales + v0 * a.G, rows * a.G * 4);
+    p.s = buf_loadf(rs, bias ? prow * 4 : prow * a.G * 4, bias ? 0 : g * 4);
   }
 
-  __device__ __forceinline__ void store(const TileArgs &a, int64_t v0, int step, int prow, int phalf,
-                                        uint16_t *sw, float *sr, float *slast) {
-    uint32_t o[16];
-    if (step >= a.NB) {
-      if (BITS == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unpack4(w[i], o + 4 * i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) unpack8(w[i], o + 2 * i);
-      }
-      if (phalf == 0) {
-        const float se = scale_eff(s);
-        sr[prow] = __fdividef((step == a.NB) ? 1.0f : s_prev, se);
-        s_prev = se;
-        if (step == a.NB + a.G - 1) slast[prow] = se;
-      }
+  // Slice `part` (8 K values = 16 bytes) of this thread's LDS row.  Bytes are
+  // stored offset by 128 (8-bit codes as they come, bias digits written so);
+  // flipping the top bit gives the signed value q - 128 (resp. the digit),
+  // one sign-extending convert per byte.  4-bit codes stay unsigned.
+  __device__ __forceinline__ void store(bool bias, int part, const ProdRegs &p, uint16_t *sw) const {
+    uint32_t o[4];
+    if (BITS == 8 || bias) {
+      unpack8s(p.w[2 * part] ^ 0x80808080u, o);
+      unpack8s(p.w[2 * part + 1] ^ 0x80808080u, o + 2);
     } else {
-      // bias block chunk: hi/lo splits of the fp32 biases (part 0,1 -> hi; 2 -> lo)
-      const int64_t v = v0 + prow;
-      const bool ok = v < a.V;
-      const float *brow = a.biases + (size_t)(ok ? v : 0) * a.G;
-      const int kk0 = step * KSTEP + phalf * 32;
-      int part = kk0 / a.G;
-      int gi = kk0 - part * a.G;
-      uint32_t val[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        uint32_t x = 0;
-        if (ok && part < 3) {
-          const float b = brow[gi];
-          const uint32_t hi = bf16_rne(b);
-          x = (part == 2) ? bf16_rne(b - bf16_to_f32(hi)) : hi;
-        }
-        val[e] = x;
-        if (++gi == a.G) { gi = 0; ++part; }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[e] = val[2 * e] | (val[2 * e + 1] << 16);
-      if (phalf == 0) sr[prow] = 1.0f;
+      unpack4(p.w[part], o);
     }
-    uint16_t *dst = sw + prow * WROW + phalf * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(u32x4_t *)(dst + 8 * i) = u32x4_t{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    *(u32x4_t *)(sw + prow * WROW + phalf * 32 + 8 * part) = u32x4_t{o[0], o[1], o[2], o[3]};
+  }
+
+  // Fold ratio of step `step` (and the last group's scale); s_prev carries the
+  // previous step's effective scale of this row.  The bias block accumulates
+  // in units of the row's fixed-point unit; the first group's fold converts
+  // them.
+  __device__ __forceinline__ void ratio(const TileArgs &a, int step, const ProdRegs &p, float &s_prev,
+                                        float *sr, float *slast) const {
+    if (phalf != 0) return;
+    const float se = scale_eff(p.s);
+    sr[prow] = (step < a.NB) ? 1.0f : __fdividef(s_prev, se);
+    if (step == a.NB + a.G - 1) slast[prow] = se;
+    s_prev = se;
   }
 };
 
-template <int BITS, bool BWD>
+// Softcapped logit and its derivative from the exponential form of tanh:
+// t = e^{-2|z|/cap}, th = sign(z) (1 - t) / (1 + t), c = cap * th, c' = 1 - th^2.
+__device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) {
+  const float t = __builtin_amdgcn_exp2f(fabsf(z) * c1);
+  const float th = copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), z);
+  dc = 1.0f - th * th;
+  return cap * th;
+}
+
+template <int BITS, int MODE>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
+  constexpr bool BWD = MODE == MODE_BWD;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   if (bid >= a.nblocks) return;
   const int tt = bid / a.nwr, wr = bid % a.nwr;
   if (tt * BM >= a.cnt[0]) return;
   const int tile_begin = wr * a.tiles_per_wg;
   const int tile_end = min(tile_begin + a.tiles_per_wg, a.range_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int tg = wave & 3, vh = wave >> 2;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int prow = tid >> 1, phalf = tid & 1;
   const int steps = a.NB + a.G;
 
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * WROW];
@@ -117,47 +128,195 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 
   const int tok0 = tt * BM + tg * 64;
   const int vcol0 = vh * 128;  // this wave's first vocabulary row within the tile
-  // fragment-major h rows: one 1 KiB block per (32 tokens, 16 K), 4 per step
-  const uint16_t *hp0 = a.haug + ((size_t)(tok0 >> 5) * a.ks16 * 64 + lane) * 8;
-  const uint16_t *hp1 = hp0 + (size_t)a.ks16 * 512;
+  // fragment-major h rows of the workgroup's 256 tokens: one 1 KiB block per
+  // (32 tokens, 16 K); this wave's two token blocks start at hv0, hv0 + hstride.
+  const rsrc_t rh = make_rsrc(a.haug + (size_t)(tt * BM >> 5) * a.ks16 * 512, (int64_t)8 * a.ks16 * 1024);
+  const int hv0 = ((tg * 2) * (int)a.ks16 * 64 + lane) * 16;
+  const int hstride = (int)a.ks16 * 1024;
   float *zs = sZ[wave];
 
   float run_m = -INFINITY, run_s = 0.0f;
-  float lse_t = 0.0f, g_t = 0.0f;
-  int64_t tgt_t = -1;
+  float lse2 = 0.0f, g_t = 0.0f;
+  int tgt_t = -1;
   if (BWD) {
     const TokRec rec = a.tok[tok0 + lane];
-    lse_t = rec.lse;
+    lse2 = rec.lse * LOG2E;
     g_t = rec.g;
     tgt_t = rec.tgt;
   }
+  const float c1 = -2.0f * LOG2E * a.inv_cap;  // t = exp2(|z| * c1)
+  const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 * u / (1 + t))
 
   const int total = (tile_end - tile_begin) * steps;
   if (total > 0) {
     Producer<BITS> pr;
-    pr.s_prev = 1.0f;
+    pr.prow = tid >> 1;
+    pr.phalf = tid & 1;
+    ProdRegs P0, P1;
+    float s_prev = 1.0f;
     f32x16_t acc[2][4];
     bf16x8_t hA[2][4];
+
+    // step `n` (<= steps) steps after (tile, st)
+    auto coords = [&](int tile, int st, int n, int64_t &v0, int &step) {
+      int s2 = st + n, t2 = tile;
+      if (s2 >= steps) { s2 -= steps; ++t2; }
+      v0 = (int64_t)(a.range_tile0 + t2) * BNT;
+      step = s2;
+    };
     {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile_begin) * BNT;
-      pr.load(a, v0, 0, prow, phalf);
-      pr.store(a, v0, 0, prow, phalf, sW[0], sR[0], sLast);
+      int64_t v1; int s1;
+      coords(tile_begin, 0, 1, v1, s1);
+      pr.load(a, v0, 0, P0);
+      pr.load(a, v1, s1, P1);
+#pragma unroll
+      for (int part = 0; part < 4; ++part) pr.store(true, part, P0, sW[0]);
+      pr.ratio(a, 0, P0, s_prev, sR[0], sLast);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        hA[0][ks] = *(const bf16x8_t *)(hp0 + ks * 512);
-        hA[1][ks] = *(const bf16x8_t *)(hp1 + ks * 512);
+        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, 0));
+        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, 0));
       }
       __syncthreads();
     }
-    int st = 0, tile = tile_begin;
-    for (int idx = 0; idx < total; ++idx) {
-      const int cb = idx & 1;
-      const bool more = idx + 1 < total;
-      const int nst = (st + 1 == steps) ? 0 : st + 1;
-      const int ntile = (st + 1 == steps) ? tile + 1 : tile;
+
+    // The MFMA work of one step on LDS buffer cb, with the producer slices of
+    // the next step (words in `cur`) placed between the MFMAs and the loads of
+    // the step after next (into `nxt`) issued first.
+    auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt) {
+      const bool sbias = sn < a.NB;
+      pr.load(a, vnn, snn, nxt);
+      const uint16_t *sw = sW[cb] + (vcol0 + l32) * WROW + lh * 8;
+      float r[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+      const int hnext = sn * 4096;
+      // B operand of column block c for k-step ks + 1 is read as soon as its
+      // two MFMAs of k-step ks are issued; a scheduling barrier after each
+      // k-step keeps this order (left free, the compiler hoists every LDS read
+      // and unpack and runs out of registers).
+      bf16x8_t bq[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + c * 32 * WROW);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            if (ks == 0) acc[rb][c] *= r[c];
+            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
+          }
+          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + c * 32 * WROW + (ks + 1) * 16);
+        }
+        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
+        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
+        pr.store(sbias, ks, cur, sW[cb ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pr.ratio(a, sn, cur, s_prev, sR[cb ^ 1], sLast);
+    };
+
+    // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
+    // (in units of s_last) of token row rb*32 + 8i + 4*lh + j and vocab row
+    // v0 + vcol0 + c*32 + l32.  Transposed per wave through its own LDS
+    // scratch so that lane = token, then streamed in chunks of 16 columns.
+    // The scratch is private to the wave: in-order LDS access within a wave
+    // needs no workgroup barrier.
+    auto epilogue = [&](int tile) {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile) * BNT;
-      const int64_t nv0 = (int64_t)(a.range_tile0 + ntile) * BNT;
-      if (more) pr.load(a, nv0, nst, prow, phalf);
+      const bool full = v0 + BNT <= a.V;
+      float sl[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sl[c] = sLast[vcol0 + c * 32 + l32];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              zs[(rb * 32 + 8 * i + 4 * lh + j) * ZROW + l32] = acc[rb][c][4 * i + j] * sl[c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+        for (int k0 = 0; k0 < 32; k0 += 16) {
+          float z[16];
+#pragma unroll
+          for (int k = 0; k < 16; k += 4) {
+            const f32x4_t x = *(const f32x4_t *)(zs + lane * ZROW + k0 + k);
+            z[k] = x[0]; z[k + 1] = x[1]; z[k + 2] = x[2]; z[k + 3] = x[3];
+          }
+          const int64_t vb = v0 + vcol0 + c * 32 + k0;
+          const int nv = full ? 16 : (int)(a.V - vb < 0 ? 0 : (a.V - vb < 16 ? a.V - vb : 16));
+          if (MODE == MODE_FWD_CAP) {
+            // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum.
+            float ssum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              const float t = __builtin_amdgcn_exp2f(fabsf(z[k]) * c1);
+              const float u = z[k] >= 0.0f ? t : 1.0f;
+              const float e = __builtin_amdgcn_exp2f(c2 * u * __builtin_amdgcn_rcpf(1.0f + t));
+              ssum += (k < nv) ? e : 0.0f;
+            }
+            run_s += ssum;
+          } else if (MODE == MODE_FWD) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              z[k] = (k < nv) ? z[k] : -INFINITY;
+              tmax = fmaxf(tmax, z[k]);
+            }
+            const float mnew = fmaxf(run_m, tmax);
+            if (mnew != -INFINITY) {
+              const float mb = mnew * LOG2E;
+              float ssum = 0.0f;
+#pragma unroll
+              for (int k = 0; k < 16; ++k) ssum += __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -mb));
+              run_s = run_s * __builtin_amdgcn_exp2f((run_m - mnew) * LOG2E) + ssum;
+              run_m = mnew;
+            }
+          } else {
+            // -g * softmax * c'; the target column is left out here and its
+            // whole term g * (1 - p) * c' * w is added in fp32 by k_dh_reduce.
+            const int64_t dtk = (int64_t)tgt_t - vb;  // target's position in this chunk, or -1
+            const int tk = (dtk >= 0 && dtk < 16) ? (int)dtk : -1;
+            uint32_t pk[8];
+#pragma unroll
+            for (int k = 0; k < 16; k += 2) {
+              float cv[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                float dc = 1.0f, y = z[k + u];
+                if (a.cap > 0.0f) y = cap_d(z[k + u], c1, a.cap, dc);
+                const float val = -g_t * __builtin_amdgcn_exp2f(fmaf(y, LOG2E, -lse2)) * dc;
+                cv[u] = (k + u < nv && k + u != tk) ? val : 0.0f;
+              }
+              pk[k / 2] = pack_rne(cv[0], cv[1]);
+            }
+            // fragment-major chunk: these 16 vocab rows are K chunks 2m, 2m+1
+            const int64_t vloc = (int64_t)tile * BNT + vcol0 + c * 32 + k0;
+            const int cm = (int)(vloc >> 3);
+            *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm, a.ksv)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+            *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + 1, a.ksv)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    };
+
+    // One step: MFMAs on buffer idx & 1, then the tile's epilogue after its
+    // last step.
+    auto do_step = [&](int idx, int tile, int st, ProdRegs &cur, ProdRegs &nxt) {
+      int64_t vn, vnn;
+      int sn, snn;
+      coords(tile, st, 1, vn, sn);    // next step: unpacked now
+      coords(tile, st, 2, vnn, snn);  // step after next: loaded now
       if (st == 0) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -166,122 +325,89 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
-      const uint16_t *sw = sW[cb] + (vcol0 + l32) * WROW + lh * 8;
-      float r[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8_t bq[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + c * 32 * WROW + ks * 16);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            if (ks == 0) acc[rb][c] *= r[c];
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
-          }
-        if (more) {
-          hA[0][ks] = *(const bf16x8_t *)(hp0 + (size_t)(nst * 4 + ks) * 512);
-          hA[1][ks] = *(const bf16x8_t *)(hp1 + (size_t)(nst * 4 + ks) * 512);
-        }
-      }
-      if (more) pr.store(a, nv0, nst, prow, phalf, sW[cb ^ 1], sR[cb ^ 1], sLast);
-
-      if (st == steps - 1) {
-        // ---- epilogue of this vocabulary tile.  acc[rb][c][4i+j] is the logit
-        // (in units of s_last) of token row rb*32 + 8i + 4*lh + j and vocab row
-        // v0 + vcol0 + c*32 + l32.  Transpose per wave through LDS so that lane = token,
-        // then stream the row in chunks of 16.
-        float sl[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sl[c] = sLast[vcol0 + c * 32 + l32];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // one 32-column block of the tile: [64 tokens x 32 vocab rows]
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                zs[(rb * 32 + 8 * i + 4 * lh + j) * ZROW + l32] = acc[rb][c][4 * i + j] * sl[c];
-          __syncthreads();
-#pragma unroll
-          for (int k0 = 0; k0 < 32; k0 += 16) {
-            float z[16];
-#pragma unroll
-            for (int k = 0; k < 16; k += 4) {
-              const f32x4_t x = *(const f32x4_t *)(zs + lane * ZROW + k0 + k);
-              z[k] = x[0]; z[k + 1] = x[1]; z[k + 2] = x[2]; z[k + 3] = x[3];
-            }
-            const int64_t vb = v0 + vcol0 + c * 32 + k0;
-            if (!BWD) {
-              float tmax = -INFINITY;
-#pragma unroll
-              for (int k = 0; k < 16; ++k) {
-                float y = softcap(z[k], a.cap, a.inv_cap);
-                y = (vb + k < a.V) ? y : -INFINITY;
-                z[k] = y;
-                tmax = fmaxf(tmax, y);
-              }
-              const float mnew = fmaxf(run_m, tmax);
-              if (mnew != -INFINITY) {
-                float ssum = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) ssum += __expf(z[k] - mnew);
-                run_s = run_s * __expf(run_m - mnew) + ssum;
-                run_m = mnew;
-              }
-            } else {
-              // -g * softmax * c'; the target column is left out here and its
-              // whole term g * (1 - p) * c' * w is added in fp32 by k_dh_reduce.
-              uint32_t pk[8];
-#pragma unroll
-              for (int k = 0; k < 16; k += 2) {
-                float c2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                  float dc;
-                  const float y = softcap_d(z[k + u], a.cap, a.inv_cap, dc);
-                  const int64_t v = vb + k + u;
-                  const float val = -g_t * __expf(y - lse_t) * dc;
-                  c2[u] = (v < a.V && v != tgt_t) ? val : 0.0f;
-                }
-                pk[k / 2] = pack_rne(c2[0], c2[1]);
-              }
-              // fragment-major chunk: these 16 vocab rows are K chunks 2m, 2m+1
-              const int64_t vloc = (int64_t)tile * BNT + vcol0 + c * 32 + k0;
-              const int cm = (int)(vloc >> 3);
-              *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm, a.ksv)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-              *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + 1, a.ksv)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
-            }
-          }
-          __syncthreads();
-        }
-      }
+      mfma_step(idx & 1, sn, vnn, snn, cur, nxt);
+      if (st == steps - 1) epilogue(tile);
       __syncthreads();
-      st = nst;
-      tile = ntile;
+    };
+
+    int st = 0, tile = tile_begin;
+    auto advance = [&]() {
+      if (++st == steps) { st = 0; ++tile; }
+    };
+    int idx = 0;
+    for (; idx + 1 < total; idx += 2) {
+      do_step(idx, tile, st, P1, P0);
+      advance();
+      do_step(idx + 1, tile, st, P0, P1);
+      advance();
     }
+    if (idx < total) do_step(idx, tile, st, P1, P0);
   }
 
   if (!BWD) {
     float *dst = a.part + ((size_t)(2 * wr + vh) * a.M_pad + tok0 + lane) * 2;
-    dst[0] = run_m;
+    dst[0] = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
     dst[1] = run_s;
   }
 }
 
-void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
-  if (bits == 4) {
-    if (bwd) hipLaunchKernelGGL((k_tile<4, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_tile<4, false>), grid, dim3(TW), 0, st, a);
-  } else {
-    if (bwd) hipLaunchKernelGGL((k_tile<8, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_tile<8, false>), grid, dim3(TW), 0, st, a);
+// Head side of the bias block.  The block carries sum_g b'[v][g] * S[t][g]
+// (S the group sum of h) with b' = b + 128 s for 8-bit heads, whose codes the
+// tile uses as q - 128, and b' = b for 4-bit heads.  Row v's b' is written in
+// 16-bit fixed point, b' ~= u_v * n, u_v = max_g |b'| / 32639,
+// n = 256 d1 + d0 with signed digits d1, d0 in [-128, 127] (exact in bf16),
+// stored as bytes offset by 128.  Column kk of the block (part = kk / G,
+// gi = kk % G) holds d1 for parts 0 and 1 and d0 for part 2, zero past 3G; the
+// token side holds [256 S_hi, 256 S_lo, S_hi] (S split into bf16 hi + lo), so
+// the block sums u_v^-1 * sum_g b' S up to the dropped d0 * S_lo term and the
+// fixed-point rounding, both below 2^-16 of max|b'| * |S| per group.  One wave
+// per row.
+__global__ void __launch_bounds__(256) k_bias_operand(const float *biases, const float *scales, float shift,
+                                                      int64_t V, int G, int Kb, uint8_t *baug, float *bunit) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= V) return;
+  const float *brow = biases + v * G;
+  const float *srow = scales + v * G;
+  float m = 0.0f;
+  for (int g = lane; g < G; g += 64) m = fmaxf(m, fabsf(fmaf(shift, srow[g], brow[g])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float u = m / 32639.0f;
+  const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+  for (int kk = lane; kk < Kb; kk += 64) {
+    const int part = kk / G, gi = kk - part * G;
+    int digit = 0;
+    if (part < 3) {
+      const float b = fmaf(shift, srow[gi], brow[gi]);
+      const int n = (int)fminf(fmaxf(rintf(b * inv), -32639.0f), 32639.0f);
+      const int d1 = (n + 128) >> 8;  // floor((n + 128) / 256), in [-127, 127]
+      digit = (part == 2) ? n - 256 * d1 : d1;
+    }
+    baug[v * Kb + kk] = (uint8_t)(digit + 128);
   }
+  if (lane == 0) bunit[v] = u;
+}
+
+void launch_bias_operand(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G,
+                         int Kb, uint8_t *baug, float *bunit) {
+  hipLaunchKernelGGL(k_bias_operand, dim3((unsigned)((V + 3) / 4)), dim3(256), 0, st, biases, scales,
+                     bits == 8 ? 128.0f : 0.0f, V, G, Kb, baug, bunit);
+}
+
+void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
+  const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
+#define CCE_TILE(B, MD) hipLaunchKernelGGL((k_tile<B, MD>), grid, dim3(TW), 0, st, a)
+  if (bits == 4) {
+    if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
+    else if (mode == MODE_FWD_CAP) CCE_TILE(4, MODE_FWD_CAP);
+    else CCE_TILE(4, MODE_FWD);
+  } else {
+    if (mode == MODE_BWD) CCE_TILE(8, MODE_BWD);
+    else if (mode == MODE_FWD_CAP) CCE_TILE(8, MODE_FWD_CAP);
+    else CCE_TILE(8, MODE_FWD);
+  }
+#undef CCE_TILE
 }
 
 }  // namespace cce
