@@ -1,9 +1,9 @@
 """Compile libcce.so for gfx950 in-tree (hipcc, no JIT cache).
 
-Three translation units: the host API (cce.hip), the logit tile kernel
+Four translation units: the host API (cce.hip), the logit tile kernel
 (tile.hip, built with the VGPR form of MFMA because the VALU rescales its
-accumulator every quantization group) and the other kernels (kernels.hip,
-whose dh-contraction accumulators are best left to AGPRs).
+accumulator every quantization group), the dh contraction (dh.hip, whose
+accumulators are best left to AGPRs) and the small kernels (kernels.hip).
 """
 from __future__ import annotations
 
@@ -19,6 +19,7 @@ UNITS = {
     "cce.hip": [],
     "tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "kernels.hip": [],
+    "dh.hip": [],
 }
 HEADERS = [os.path.join(CSRC, "cce_device.h"), os.path.join(ROOT, "include", "cce.h"),
            os.path.join(ROOT, "include", "cce_profile.h")]

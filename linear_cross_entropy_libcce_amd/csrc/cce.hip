@@ -83,7 +83,7 @@ struct Plan {
   // forward
   int nsplit, tiles_per_split;
   // backward
-  int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;
+  int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: K steps per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
   size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_bunit, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
@@ -130,24 +130,23 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.nchunks = (int)cdiv(p.tiles, p.chunk_tiles);
   p.ld_coeff = (int64_t)p.chunk_tiles * BNT;
   p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(4, (int64_t)p.TT * p.chunk_tiles / (2 * cus)));
-  p.HT = (int)cdiv(p.H, DT);
-  // Vocabulary splits of the dh contraction (in 128-row units): the fewest that
-  // fill whole rounds of resident workgroups (2 per CU) to >= 90%; each split
-  // adds one dh slab.
-  const int gchunk = 2 * p.chunk_tiles;
+  p.HT = (int)cdiv(p.H, 256);
+  // Vocabulary splits of the dh contraction: the fewest that fill whole rounds
+  // of resident workgroups (one per CU) to >= 90%; each split adds one dh slab.
+  const int chunk_steps = p.chunk_tiles * (BNT / KSTEP);
   {
-    const int64_t slots = 2 * cus;
+    const int64_t slots = cus;
     const int64_t base = (int64_t)p.TT * p.HT;
     int best = 1;
-    for (int ks = 1; ks <= 8 && ks <= gchunk; ++ks) {
+    for (int ks = 1; ks <= 8 && ks <= chunk_steps; ++ks) {
       best = ks;
       const int64_t n = base * ks;
       if ((double)n / (double)(cdiv(n, slots) * slots) >= 0.9) break;
     }
     p.ksplit = best;
   }
-  p.k_tiles = (int)cdiv(gchunk, p.ksplit);
-  p.ksplit = (int)cdiv(gchunk, p.k_tiles);
+  p.k_tiles = (int)cdiv(chunk_steps, p.ksplit);  // K steps per split
+  p.ksplit = (int)cdiv(chunk_steps, p.k_tiles);
 
   size_t o = 0;
   p.o_cnt = o;  o = align_up(o + 256, 256);
@@ -307,7 +306,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
 
   GemmArgs ga{};
   ga.coeff = a.coeff;
-  ga.ld_coeff = p.ld_coeff;
+  ga.ksv = p.ld_coeff / 16;
   ga.wq = head->wq;
   ga.scales = head->scales;
   ga.biases = head->biases;
@@ -318,7 +317,8 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   ga.G = p.G;
   ga.wpr = p.wpr;
   ga.M_pad = (int)p.M_pad;
-  ga.tiles_per_split = p.k_tiles;
+  ga.steps_per_split = p.k_tiles;
+  ga.TT = p.TT;
   ga.HT = p.HT;
   ga.ksplit = p.ksplit;
   ga.nblocks = p.TT * p.HT * p.ksplit;
@@ -333,8 +333,8 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
     a.nblocks = p.TT * a.nwr;
     const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
     CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, true, g1, a));
-    ga.chunk_tile0 = 2 * t0;  // the dh contraction counts 128-row vocabulary tiles
-    ga.chunk_tiles = 2 * nt;
+    ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_steps = nt * (BNT / KSTEP);
     ga.accumulate = c > 0;
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
   }

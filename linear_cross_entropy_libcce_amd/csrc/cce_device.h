@@ -35,13 +35,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256;        // tokens per workgroup tile (4 waves x 64)
-constexpr int BN = 128;        // vocabulary rows per dh-contraction tile (coefficient columns)
 constexpr int BNT = 256;       // vocabulary rows per logit tile
 constexpr int TW = 512;        // threads per logit-tile workgroup (8 waves)
 constexpr int KSTEP = 64;      // K per step = one quantization group
-constexpr int NTHREADS = 256;
 constexpr int WROW = KSTEP + 8;  // padded bf16 row stride of the LDS code tile
-constexpr int DT = 128;        // dh columns per workgroup in the dh contraction
 constexpr int MAX_G = 256;     // H <= 16384
 
 // Per-token side data, one 16-byte record per compacted row.
@@ -131,17 +128,19 @@ struct TileArgs {
 };
 
 struct GemmArgs {
-  const uint16_t *coeff;  // fragment-major [M_pad][ld_coeff]
-  int64_t ld_coeff;
+  const uint16_t *coeff;  // fragment-major [M_pad][16 * ksv] bf16 coefficient chunk
+  int64_t ksv;            // K blocks of 16 vocabulary rows per 32-token row block of the chunk
   const uint32_t *wq;
   const float *scales;
   const float *biases;
   const int *cnt;
   float *dh_part;        // [ksplit][M_pad][H]
   int64_t V;
+  int64_t chunk_v0;      // first vocabulary row of the chunk
   int H, G, wpr, M_pad;
-  int chunk_tile0, chunk_tiles, tiles_per_split;
-  int HT, ksplit, nblocks;
+  int chunk_steps;       // 64-row K steps in the chunk
+  int steps_per_split;
+  int TT, HT, ksplit, nblocks;
   int accumulate;
 };
 

@@ -1,0 +1,224 @@
+// dh.hip -- the dh contraction of libcce's backward (the second phase of the
+// page's backward: the coefficients contracted with the head, summed over
+// vocabulary blocks).
+#include "cce_device.h"
+
+namespace cce {
+
+// dh_part[k][t][d] (+)= sum_v coeff[t][v] * bf16(s*q + b)[v][d] over the
+// vocabulary rows of split k of one coefficient chunk.
+//
+// Workgroup: 256 tokens x 256 dh columns, 8 waves; wave w owns tokens
+// [64(w%4), +64) and columns [128(w/4), +128) as 2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = d, K = vocabulary rows).
+// Per K step of 64 vocabulary rows:
+//  * the head tile of the step is dequantized once (s*q + b, rounded to bf16)
+//    into LDS as [d][v], double buffered, and shared by the eight waves;
+//  * the coefficient operand comes straight from the fragment-major chunk
+//    into registers, one step ahead;
+//  * the producer (every thread: 8 vocabulary rows x 4 columns) loads the
+//    head words two steps ahead into alternating register sets and
+//    dequantizes the next step in four slices placed between the MFMAs.
+// Reads are raw buffer loads (rows past V read as zeros), so the step has no
+// per-lane predicate.  Each split owns its fp32 slab: no atomics, and a
+// repeated call gives identical bits.
+
+constexpr int DTW = 256;       // dh columns per workgroup
+constexpr int KSTP = 64;       // vocabulary rows per K step
+constexpr int BROW = KSTP + 8; // padded bf16 row stride of the LDS head tile [d][v]
+
+// Producer mapping: thread (rgp, dc) handles vocabulary rows 8*rgp .. 8*rgp+7
+// of the step and columns 4*dc .. 4*dc+3 of the tile; lanes are 16 dc x 4 rgp,
+// so one load instruction covers 4 rows and the 16-byte LDS writes of 16
+// lanes fall in distinct banks.  Scale and bias of the step's 64 rows x 4
+// groups are loaded once per workgroup (one float per thread: waves 0-3 the
+// scales, 4-7 the biases) into LDS and read back by the dequantizing threads.
+template <int BITS>
+struct DhRegs {
+  uint32_t w[8];  // 8-bit: 4 codes of row e; 4-bit: 4 codes in the low 16 bits
+  float sb;       // one scale or bias of the step, staged through LDS
+};
+
+template <int BITS>
+struct DhProducer {
+  int rgp, dc;    // rows 8*rgp + e, columns 4*dc + k of the tile
+  int wcol;       // byte offset of those columns within a packed row
+  int sbrow, sbg; // the (row, group) of the scale or bias this thread loads for the LDS stage
+  int isb;        // 1: that value is a bias (wave-uniform)
+  int gq0;        // first quantization group of the tile
+
+  __device__ __forceinline__ void load(const GemmArgs &a, int64_t vs, DhRegs<BITS> &p) const {
+    const int64_t rows = a.V - vs < KSTP ? a.V - vs : KSTP;
+    const rsrc_t rw = make_rsrc(a.wq + vs * a.wpr, rows * a.wpr * 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int voff = (8 * rgp + e) * a.wpr * 4 + wcol;
+      if (BITS == 8) p.w[e] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff, 0, 0);
+      else p.w[e] = __builtin_amdgcn_raw_buffer_load_b16(rw, voff, 0, 0);
+    }
+    const rsrc_t rs = make_rsrc((isb ? a.biases : a.scales) + vs * a.G, rows * a.G * 4);
+    p.sb = buf_loadf(rs, (sbrow * a.G + gq0 + sbg) * 4, 0);
+  }
+
+  // LDS stage of the step's scales and biases: [group j][row][scale, bias].
+  __device__ __forceinline__ void stage_sb(const DhRegs<BITS> &p, float *ssb) const {
+    ssb[(sbg * KSTP + sbrow) * 2 + isb] = p.sb;
+  }
+
+  // (scale, bias) of the thread's 8 rows (group j = dc / 16).
+  __device__ __forceinline__ void read_sb(const float *ssb, float (&s)[8], float (&b)[8]) const {
+    const float *src = ssb + ((dc >> 4) * KSTP + 8 * rgp) * 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 x = *(const float2 *)(src + 2 * e);
+      s[e] = x.x;
+      b[e] = x.y;
+    }
+  }
+
+  // Column 4*dc + k: its 8 rows dequantized and stored as one 16-byte run of v.
+  __device__ __forceinline__ void store(int k, const DhRegs<BITS> &p, const float (&s)[8], const float (&b)[8],
+                                        uint16_t *sb) const {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t q = (BITS == 8) ? (p.w[e] >> (8 * k)) & 0xFFu : (p.w[e] >> (4 * k)) & 0xFu;
+      x[e] = fmaf(s[e], (float)q, b[e]);
+    }
+    *(u32x4_t *)(sb + (4 * dc + k) * BROW + 8 * rgp) =
+        u32x4_t{pack_rne(x[0], x[1]), pack_rne(x[2], x[3]), pack_rne(x[4], x[5]), pack_rne(x[6], x[7])};
+  }
+};
+
+template <int BITS>
+__global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  if (bid >= a.nblocks) return;
+  // consecutive work ids share the token tile (and the coefficient rows)
+  const int dt = bid % a.HT;
+  const int tt = (bid / a.HT) % a.TT;
+  const int ks_ = bid / (a.HT * a.TT);
+  if (tt * BM >= a.cnt[0]) return;
+  const int d0 = dt * DTW;
+  const int step0 = ks_ * a.steps_per_split;
+  const int nsteps = min(a.steps_per_split, a.chunk_steps - step0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tg = wave & 3, dh = wave >> 2;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * BROW];
+  __shared__ __attribute__((aligned(16))) float sSB[2][4 * KSTP * 2];
+
+  const int tok0 = tt * BM + tg * 64;
+  // fragment-major coefficients of the workgroup's 256 tokens: one 1 KiB block
+  // per (32 tokens, 16 vocabulary rows)
+  const rsrc_t rc = make_rsrc(a.coeff + (size_t)(tt * BM >> 5) * a.ksv * 512, (int64_t)8 * a.ksv * 1024);
+  const int cv0 = ((tg * 2) * (int)a.ksv * 64 + lane) * 16;
+  const int cstride = (int)a.ksv * 1024;
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
+
+  if (nsteps > 0) {
+    DhProducer<BITS> pr;
+    pr.dc = (lane & 15) + 16 * (wave & 3);
+    pr.rgp = (lane >> 4) + 4 * (wave >> 2);
+    pr.wcol = (d0 + 4 * pr.dc) * BITS / 8;
+    pr.sbrow = (tid & 255) >> 2;
+    pr.sbg = tid & 3;
+    pr.isb = wave >> 2;  // waves 0-3 load scales, 4-7 biases
+    pr.gq0 = d0 / KSTEP;
+    DhRegs<BITS> P0, P1;
+    bf16x8_t cA[2][4];
+    float sc[8], bi[8];
+    // vocabulary row of step i of this split
+    auto vrow = [&](int i) { return a.chunk_v0 + (int64_t)(step0 + i) * KSTP; };
+    // K offset (bytes) of step i in the fragment-major chunk
+    auto koff = [&](int i) { return (step0 + i) * 4 * 1024; };
+
+    pr.load(a, vrow(0), P0);
+    pr.load(a, vrow(1), P1);
+    pr.stage_sb(P0, sSB[0]);
+    pr.stage_sb(P1, sSB[1]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, koff(0)));
+      cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, koff(0)));
+    }
+    __syncthreads();
+    pr.read_sb(sSB[0], sc, bi);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pr.store(k, P0, sc, bi, sB[0]);
+    __syncthreads();
+
+    // Step st: MFMAs on buffer st & 1; dequantize step st + 1 (words in `cur`,
+    // scales in LDS slot (st + 1) & 1) into the other buffer between them;
+    // load step st + 2 into `nxt` and stage its scales in slot st & 1.
+    auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &nxt) {
+      const int cb = st & 1;
+      pr.load(a, vrow(st + 2), nxt);  // past the split: valid rows or zeros, never used
+      pr.read_sb(sSB[cb ^ 1], sc, bi);
+      const uint16_t *sw = sB[cb] + (dh * 128 + l32) * BROW + lh * 8;
+      const int knext = koff(st + 1 < nsteps ? st + 1 : st);
+      bf16x8_t bq[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + c * 32 * BROW);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
+          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + c * 32 * BROW + (ks + 1) * 16);
+        }
+        cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
+        cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));
+        pr.store(ks, cur, sc, bi, sB[cb ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pr.stage_sb(nxt, sSB[cb]);
+      __syncthreads();
+    };
+    int st = 0;
+    for (; st + 1 < nsteps; st += 2) {
+      do_step(st, P1, P0);
+      do_step(st + 1, P0, P1);
+    }
+    if (st < nsteps) do_step(st, P1, P0);
+  } else if (a.accumulate) {
+    return;
+  }
+
+  // result lane layout: column d0 + dh*128 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int d = d0 + dh * 128 + c * 32 + l32;
+    if (d >= a.H) continue;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float *dst = a.dh_part + ((size_t)ks_ * a.M_pad + tok0 + rb * 32 + 8 * i + 4 * lh + j) * a.H + d;
+          const float v = acc[rb][c][4 * i + j];
+          *dst = a.accumulate ? (*dst + v) : v;
+        }
+  }
+}
+
+void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
+  if (bits == 4)
+    hipLaunchKernelGGL(k_dh<4>, grid, dim3(TW), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_dh<8>, grid, dim3(TW), 0, st, a);
+}
+
+}  // namespace cce

@@ -1,5 +1,5 @@
 // kernels.hip -- the small kernels of libcce (compaction, prep, target logit,
-// merge, split reduce) and the dh contraction.
+// merge, split reduce).
 #include "cce_device.h"
 
 namespace cce {
@@ -167,148 +167,6 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nsplit, in
 }
 
 // ---------------------------------------------------------------------------
-// dh contraction: dh_part[k][t][d] (+)= sum_v coeff[t][v] * bf16(s*q + b)[v][d]
-// over the vocabulary rows of split k of one coefficient chunk.  Workgroup:
-// 256 tokens x 128 dh columns; wave w owns tokens [64w, 64w+64) as 2 x 4
-// blocks of v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = d).  The head
-// tile is dequantized once per step into LDS as [d][v] (v contiguous); the
-// coefficient operand is loaded straight from the chunk into registers.
-
-template <int BITS>
-__global__ void __launch_bounds__(NTHREADS, 2) k_dh_gemm(GemmArgs a) {
-  constexpr int KST = 64;                        // vocabulary rows per K step
-  constexpr int SPT = BN / KST;                  // K steps per 128-row vocab tile
-  constexpr int BROW = KST + 8;                  // padded LDS row stride (bf16)
-  constexpr int RPT = 4;                         // vocabulary rows staged per thread
-  constexpr int NRG = KST / RPT;                 // row groups per step
-  constexpr int WC = NTHREADS / NRG;             // 8-column groups of d staged per step
-  constexpr int DPW = 32 / BITS;                 // dh columns per word
-  constexpr int WPT = 8 / DPW;                   // words per row per thread (8 columns of d)
-  constexpr int NKS = KST / 16;                  // MFMA k-steps per K step
-  static_assert(WC * 8 == DT, "each thread stages 8 columns of the dh tile");
-
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  if (bid >= a.nblocks) return;
-  const int ks_ = bid % a.ksplit;
-  const int dt = (bid / a.ksplit) % a.HT;
-  const int tt = bid / (a.ksplit * a.HT);
-  if (tt * BM >= a.cnt[0]) return;
-  const int d0 = dt * DT;
-  const int tile_begin = ks_ * a.tiles_per_split;
-  const int tile_end = min(tile_begin + a.tiles_per_split, a.chunk_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, lh = lane >> 5;
-
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][DT * BROW];
-
-  const int tok0 = tt * BM + wave * 64;
-  // fragment-major coefficient chunk: one 1 KiB block per (32 tokens, 16 vocab rows)
-  const int64_t ksv = a.ld_coeff / 16;
-  const uint16_t *cp0 = a.coeff + ((size_t)(tok0 >> 5) * ksv * 64 + lane) * 8 + (size_t)tile_begin * (BN / 16) * 512;
-  const uint16_t *cp1 = cp0 + (size_t)ksv * 512;
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
-
-  // producer: RPT consecutive vocabulary rows x 8 columns of d (WPT words per
-  // row).  The row group varies fastest across lanes so that the LDS writes of
-  // neighbouring lanes land side by side in one [d] row.
-  const int rg = tid % NRG, wc = tid / NRG;
-  const int dcol = wc * 8;
-  const bool dok = d0 + dcol < a.H;
-  const int gq = (d0 + dcol) / KSTEP;
-  const int64_t wcol = (d0 + dcol) / DPW;
-
-  const int nsteps = (tile_end - tile_begin) * SPT;
-  uint32_t wv[RPT][WPT];
-  float sv[RPT], bv[RPT];
-
-  auto load_step = [&](int step) {
-    const int64_t vb = (int64_t)(a.chunk_tile0 + tile_begin) * BN + (int64_t)step * KST + rg * RPT;
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      const int64_t v = vb + e;
-      const bool ok = dok && v < a.V;
-#pragma unroll
-      for (int u = 0; u < WPT; ++u) wv[e][u] = ok ? a.wq[(size_t)v * a.wpr + wcol + u] : 0u;
-      sv[e] = ok ? a.scales[(size_t)v * a.G + gq] : 0.0f;
-      bv[e] = ok ? a.biases[(size_t)v * a.G + gq] : 0.0f;
-    }
-  };
-  auto store_step = [&](uint16_t *sb) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float x[RPT];
-#pragma unroll
-      for (int e = 0; e < RPT; ++e) {
-        const uint32_t q = (wv[e][k / DPW] >> (BITS * (k % DPW))) & ((1u << BITS) - 1u);
-        x[e] = sv[e] * (float)q + bv[e];
-      }
-      *(uint2 *)(sb + (dcol + k) * BROW + rg * RPT) = make_uint2(pack_rne(x[0], x[1]), pack_rne(x[2], x[3]));
-    }
-  };
-
-  if (nsteps > 0) {
-    bf16x8_t cA[2][NKS];
-    load_step(0);
-    store_step(sB[0]);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      cA[0][ks] = *(const bf16x8_t *)(cp0 + ks * 512);
-      cA[1][ks] = *(const bf16x8_t *)(cp1 + ks * 512);
-    }
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-      const int cb = st & 1;
-      const bool more = st + 1 < nsteps;
-      if (more) load_step(st + 1);
-      const uint16_t *sb = sB[cb] + l32 * BROW + lh * 8;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        bf16x8_t bq[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sb + c * 32 * BROW + ks * 16);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
-        if (more) {
-          cA[0][ks] = *(const bf16x8_t *)(cp0 + (size_t)((st + 1) * NKS + ks) * 512);
-          cA[1][ks] = *(const bf16x8_t *)(cp1 + (size_t)((st + 1) * NKS + ks) * 512);
-        }
-      }
-      if (more) store_step(sB[cb ^ 1]);
-      __syncthreads();
-    }
-  } else if (a.accumulate) {
-    return;
-  }
-
-  // result lane layout: column d0 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = d0 + c * 32 + l32;
-      if (d >= a.H) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float *dst = a.dh_part + ((size_t)ks_ * a.M_pad + tok0 + rb * 32 + 8 * i + 4 * lh + j) * a.H + d;
-          const float v = acc[rb][c][4 * i + j];
-          *dst = a.accumulate ? (*dst + v) : v;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
 // zero rows for masked tokens.
 template <int BITS>
@@ -359,13 +217,6 @@ void launch_merge(hipStream_t st, int M, const float *part, int nsplit, int M_pa
                   const TokRec *tok, float *logp, float *lse) {
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, part, nsplit, M_pad, inv, tok, M,
                      logp, lse);
-}
-
-void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
-  if (bits == 4)
-    hipLaunchKernelGGL(k_dh_gemm<4>, grid, dim3(NTHREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_dh_gemm<8>, grid, dim3(NTHREADS), 0, st, a);
 }
 
 void launch_dh_reduce(hipStream_t st, int bits, int M, const float *dh_part, int ksplit, int M_pad, int H, int G,
