@@ -21,7 +21,7 @@ using namespace cce;
 
 constexpr int64_t MAX_H = 16384;
 constexpr int64_t MAX_M = (int64_t)1 << 24;
-constexpr size_t COEFF_BUDGET = (size_t)256 << 20;  // bytes of one coefficient chunk
+constexpr size_t COEFF_BUDGET = (size_t)1 << 30;  // bytes of one coefficient chunk
 
 thread_local char g_err[256];
 
@@ -86,7 +86,7 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: K steps per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_bunit, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_bunit, o_rt, o_slast, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
 };
 
 cce_status check_head(const cce_head *hd) {
@@ -132,16 +132,22 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(4, (int64_t)p.TT * p.chunk_tiles / (2 * cus)));
   p.HT = (int)cdiv(p.H, 256);
   // Vocabulary splits of the dh contraction: the fewest that fill whole rounds
-  // of resident workgroups (one per CU) to >= 90%; each split adds one dh slab.
+  // of resident workgroups (one per CU) to >= 97%, else the best fill of up
+  // to 8; each split adds one dh slab.
   const int chunk_steps = p.chunk_tiles * (BNT / KSTEP);
   {
     const int64_t slots = cus;
     const int64_t base = (int64_t)p.TT * p.HT;
     int best = 1;
+    double best_fill = 0.0;
     for (int ks = 1; ks <= 8 && ks <= chunk_steps; ++ks) {
-      best = ks;
       const int64_t n = base * ks;
-      if ((double)n / (double)(cdiv(n, slots) * slots) >= 0.9) break;
+      const double fill = (double)n / (double)(cdiv(n, slots) * slots);
+      if (fill > best_fill + 1e-9) {
+        best = ks;
+        best_fill = fill;
+      }
+      if (fill >= 0.97) break;
     }
     p.ksplit = best;
   }
@@ -156,6 +162,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
   p.o_bunit = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
+  p.o_rt = o; o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
+  p.o_slast = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   const size_t common = o;
   p.o_part = common;
   p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * p.nsplit) * p.M_pad, 256);
@@ -205,6 +213,8 @@ void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_
                                      lse, g, tok, haug));
   CCE_LAUNCH("bias_op", st, launch_bias_operand(st, p.bits, hd->biases, hd->scales, p.V, p.G, p.Kb, ws_at<uint8_t>(ws, p.o_baug),
                                                            ws_at<float>(ws, p.o_bunit)));
+  CCE_LAUNCH("ratio_tab", st, launch_ratio_table(st, hd->scales, ws_at<const float>(ws, p.o_bunit), p.V, p.G, p.NB,
+                                                 ws_at<float>(ws, p.o_rt), ws_at<float>(ws, p.o_slast)));
   CCE_LAUNCH("target", st, launch_target(st, p.bits, (int)p.M_pad, (const uint16_t *)h, idx, (int)p.H, p.G, hd->wq,
                                          p.wpr, hd->scales, hd->biases, p.V, p.cap, cnt, tok, bwd ? 1 : 0));
 }
@@ -214,6 +224,8 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
   a.bunit = ws_at<const float>(ws, p.o_bunit);
+  a.rt = ws_at<const float>(ws, p.o_rt);
+  a.slast = ws_at<const float>(ws, p.o_slast);
   a.wq = hd->wq;
   a.scales = hd->scales;
   a.biases = hd->biases;

@@ -38,7 +38,6 @@ constexpr int BM = 256;        // tokens per workgroup tile (4 waves x 64)
 constexpr int BNT = 256;       // vocabulary rows per logit tile
 constexpr int TW = 512;        // threads per logit-tile workgroup (8 waves)
 constexpr int KSTEP = 64;      // K per step = one quantization group
-constexpr int WROW = KSTEP + 8;  // padded bf16 row stride of the LDS code tile
 constexpr int MAX_G = 256;     // H <= 16384
 
 // Per-token side data, one 16-byte record per compacted row.
@@ -111,6 +110,8 @@ struct TileArgs {
   const uint16_t *haug;  // [M_pad][Ka] bf16, fragment-major
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
   const float *bunit;    // [V] fixed-point unit of each row's biases
+  const float *rt;       // [NB + G][V] fold ratio of every step
+  const float *slast;    // [V] effective scale of the last group
   const uint32_t *wq;
   const float *scales;
   const float *biases;
@@ -198,6 +199,8 @@ void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const
                    const int *cnt, TokRec *tok, int bwd);
 void launch_bias_operand(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G,
                          int Kb, uint8_t *baug, float *bunit);
+void launch_ratio_table(hipStream_t st, const float *scales, const float *bunit, int64_t V, int G, int NB,
+                        float *rt, float *slast);
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
 void launch_merge(hipStream_t st, int M, const float *part, int nsplit, int M_pad, const int *inv,
                   const TokRec *tok, float *logp, float *lse);

@@ -16,84 +16,90 @@ namespace cce {
 //    by the eight waves;
 //  * the token operand comes straight from the fragment-major augmented rows
 //    into registers, one step ahead;
-//  * the producer (every thread: one vocabulary row, one half of the step)
-//    unpacks the codes of the NEXT step into the other LDS buffer, in four
-//    slices placed between the MFMAs, from words it loaded TWO steps ahead
-//    (two register sets, alternating), so global latency is covered by a
-//    full step of MFMA work and the unpack rides in the MFMA shadow.
+//  * the producer (every thread: 16 K values of two vocabulary rows) unpacks
+//    the codes of the NEXT step into the other LDS buffer, in four slices
+//    placed between the MFMAs, from words it loaded at the start of the
+//    previous step (two register sets, alternating), so global latency is
+//    covered by a step of MFMA work and the unpack rides in the MFMA shadow.
 // All global reads are raw buffer loads: rows past V read as zeros, so there
 // is no per-lane predicate and no branch in the step.
 //
 // Scale fold without a second accumulator: the accumulator is kept in units of
 // the current group's scale, acc <- acc * (s_{g-1} / s_g) + A_g, so the MFMA
 // accumulates in place and the VALU does one multiply per element per group.
-// After the last group z = acc * s_last.  (The bias block runs first with scale
-// 1; a scale of exactly 0 is replaced by 1e-30, whose contribution is nil.)
+// After the last group z = acc * s_last.  The ratios come from a table built
+// once per call (k_ratio_table); the bias block runs first with ratio 1 in
+// units of the row's fixed-point unit, and a scale of exactly 0 is replaced by
+// 1e-30, whose contribution is nil.
 
 constexpr int ZROW = 36;  // padded fp32 row stride of the per-wave transpose scratch (32 columns)
 constexpr float LOG2E = 1.4426950408889634f;
 
 enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2 };
 
-// One step's worth of head data for one producer thread: 32 K values of one
-// vocabulary row (4-bit: 4 words, 8-bit and bias block: 8 words of bytes), and
-// the row's scale of that step (the bias block's: its fixed-point unit).
+// One step's worth of head data for one producer thread: 16 K values of each
+// of two vocabulary rows (8-bit codes and bias digits: 4 words per row; 4-bit
+// codes: the first 2 words per row), and the fold ratio of one row.
 struct ProdRegs {
   uint32_t w[8];
-  float s;
+  float r;
 };
 
+// The LDS code tile is [256 rows][64 K] bf16 without padding; the 16-byte
+// chunk c of row n sits at chunk position c ^ ((n >> 1) & 7).  With that
+// swizzle the B-operand reads (32 consecutive rows, one chunk) and the
+// producer writes (4 rows x 4 chunk pairs per 16 lanes) both hit distinct
+// banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// Producer mapping: wave w, lane l loads the 16-byte K slice l & 3 of rows
+// 32w + (l >> 2) and 32w + 16 + (l >> 2), so one load instruction covers 16
+// rows x 64 contiguous bytes.  Threads 0..255 also carry row t's fold ratio.
 template <int BITS>
 struct Producer {
-  int prow, phalf;
+  int row0, q, tid;
 
   // Issue the loads of step `step` of the vocabulary tile at v0: a bias-block
-  // step (step < NB: fixed-point digits and unit) or group step - NB (codes
-  // and scale).  Both kinds are two 16-byte loads and one scalar per thread;
-  // the source is chosen with wave-uniform selects, so no branch.
+  // step (step < NB: fixed-point digits) or group step - NB (codes), and the
+  // fold ratio of the step from the precomputed table.  The source is chosen
+  // with wave-uniform selects, so no branch.
   __device__ __forceinline__ void load(const TileArgs &a, int64_t v0, int step, ProdRegs &p) const {
     const int64_t rows = a.V - v0 < BNT ? a.V - v0 : BNT;
     const bool bias = step < a.NB;
     const int g = step - a.NB;
     const rsrc_t rw = bias ? make_rsrc(a.baug + v0 * a.Kb, rows * a.Kb)
                            : make_rsrc(a.wq + v0 * a.wpr, rows * a.wpr * 4);
-    const int vo = bias ? prow * a.Kb + phalf * 32 : prow * a.wpr * 4 + phalf * BITS * 4;
+    const int rowb = bias ? a.Kb : a.wpr * 4;                // bytes per row
+    const int qb = (bias || BITS == 8) ? 16 : 8;             // bytes per 16 K values
     const int so = bias ? step * 64 : g * (8 * BITS);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4_t x = buf_load16(rw, vo + 16 * i, so);
+      const u32x4_t x = buf_load16(rw, (row0 + 16 * i) * rowb + q * qb, so);
       p.w[4 * i] = x[0]; p.w[4 * i + 1] = x[1]; p.w[4 * i + 2] = x[2]; p.w[4 * i + 3] = x[3];
     }
-    const rsrc_t rs = bias ? make_rsrc(a.bunit + v0, rows * 4) : make_rsrc(a.scales + v0 * a.G, rows * a.G * 4);
-    p.s = buf_loadf(rs, bias ? prow * 4 : prow * a.G * 4, bias ? 0 : g * 4);
+    const rsrc_t rr = make_rsrc(a.rt + (int64_t)step * a.V + v0, rows * 4);
+    p.r = buf_loadf(rr, (tid & (BNT - 1)) * 4, 0);
   }
 
-  // Slice `part` (8 K values = 16 bytes) of this thread's LDS row.  Bytes are
-  // stored offset by 128 (8-bit codes as they come, bias digits written so);
-  // flipping the top bit gives the signed value q - 128 (resp. the digit),
-  // one sign-extending convert per byte.  4-bit codes stay unsigned.
-  __device__ __forceinline__ void store(bool bias, int part, const ProdRegs &p, uint16_t *sw) const {
+  // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
+  // Bytes are stored offset by 128 (8-bit codes as they come, bias digits
+  // written so); flipping the top bit gives the signed value q - 128 (resp.
+  // the digit), one sign-extending convert per byte.  4-bit codes stay
+  // unsigned.
+  __device__ __forceinline__ void store(bool bias, int ks, const ProdRegs &p, uint16_t *sw) const {
+    const int i = ks >> 1, h = ks & 1;
     uint32_t o[4];
     if (BITS == 8 || bias) {
-      unpack8s(p.w[2 * part] ^ 0x80808080u, o);
-      unpack8s(p.w[2 * part + 1] ^ 0x80808080u, o + 2);
+      unpack8s(p.w[4 * i + 2 * h] ^ 0x80808080u, o);
+      unpack8s(p.w[4 * i + 2 * h + 1] ^ 0x80808080u, o + 2);
     } else {
-      unpack4(p.w[part], o);
+      unpack4(p.w[4 * i + h], o);
     }
-    *(u32x4_t *)(sw + prow * WROW + phalf * 32 + 8 * part) = u32x4_t{o[0], o[1], o[2], o[3]};
+    *(u32x4_t *)(sw + swz(row0 + 16 * i, 2 * q + h)) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
 
-  // Fold ratio of step `step` (and the last group's scale); s_prev carries the
-  // previous step's effective scale of this row.  The bias block accumulates
-  // in units of the row's fixed-point unit; the first group's fold converts
-  // them.
-  __device__ __forceinline__ void ratio(const TileArgs &a, int step, const ProdRegs &p, float &s_prev,
-                                        float *sr, float *slast) const {
-    if (phalf != 0) return;
-    const float se = scale_eff(p.s);
-    sr[prow] = (step < a.NB) ? 1.0f : __fdividef(s_prev, se);
-    if (step == a.NB + a.G - 1) slast[prow] = se;
-    s_prev = se;
+  __device__ __forceinline__ void ratio(const ProdRegs &p, float *sr) const {
+    if (tid < BNT) sr[tid] = p.r;
   }
 };
 
@@ -121,9 +127,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int l32 = lane & 31, lh = lane >> 5;
   const int steps = a.NB + a.G;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * WROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KSTEP];
   __shared__ __attribute__((aligned(16))) float sR[2][BNT];
-  __shared__ __attribute__((aligned(16))) float sLast[BNT];
   __shared__ __attribute__((aligned(16))) float sZ[8][64 * ZROW];
 
   const int tok0 = tt * BM + tg * 64;
@@ -150,10 +155,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int total = (tile_end - tile_begin) * steps;
   if (total > 0) {
     Producer<BITS> pr;
-    pr.prow = tid >> 1;
-    pr.phalf = tid & 1;
+    pr.row0 = wave * 32 + (lane >> 2);
+    pr.q = lane & 3;
+    pr.tid = tid;
     ProdRegs P0, P1;
-    float s_prev = 1.0f;
+    // this lane's B-operand chunk offsets (row vcol0 + l32 + 32c, chunk 2ks + lh)
+    int boff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) boff[ks] = swz(vcol0 + l32, 2 * ks + lh);
     f32x16_t acc[2][4];
     bf16x8_t hA[2][4];
 
@@ -172,7 +181,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, v1, s1, P1);
 #pragma unroll
       for (int part = 0; part < 4; ++part) pr.store(true, part, P0, sW[0]);
-      pr.ratio(a, 0, P0, s_prev, sR[0], sLast);
+      pr.ratio(P0, sR[0]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, 0));
@@ -187,7 +196,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt) {
       const bool sbias = sn < a.NB;
       pr.load(a, vnn, snn, nxt);
-      const uint16_t *sw = sW[cb] + (vcol0 + l32) * WROW + lh * 8;
+      const uint16_t *sw = sW[cb];
       float r[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
@@ -198,7 +207,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       // and unpack and runs out of registers).
       bf16x8_t bq[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + c * 32 * WROW);
+      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTEP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -208,14 +217,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             if (ks == 0) acc[rb][c] *= r[c];
             acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
           }
-          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + c * 32 * WROW + (ks + 1) * 16);
+          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTEP);
         }
         hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
         hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
         pr.store(sbias, ks, cur, sW[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pr.ratio(a, sn, cur, s_prev, sR[cb ^ 1], sLast);
+      pr.ratio(cur, sR[cb ^ 1]);
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
@@ -228,8 +237,9 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile) * BNT;
       const bool full = v0 + BNT <= a.V;
       float sl[4];
+      const rsrc_t rl = make_rsrc(a.slast + v0, (a.V - v0 < BNT ? a.V - v0 : BNT) * 4);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sl[c] = sLast[vcol0 + c * 32 + l32];
+      for (int c = 0; c < 4; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -393,6 +403,29 @@ void launch_bias_operand(hipStream_t st, int bits, const float *biases, const fl
                          int Kb, uint8_t *baug, float *bunit) {
   hipLaunchKernelGGL(k_bias_operand, dim3((unsigned)((V + 3) / 4)), dim3(256), 0, st, biases, scales,
                      bits == 8 ? 128.0f : 0.0f, V, G, Kb, baug, bunit);
+}
+
+// Fold ratios of every step, rt[step][v] (1 for the bias steps, then
+// u_v / s_0, s_0 / s_1, ... with effective scales), and s_last[v] = s_{G-1}.
+// One thread per vocabulary row; the table rows are written coalesced.
+__global__ void __launch_bounds__(256) k_ratio_table(const float *scales, const float *bunit, int64_t V, int G,
+                                                     int NB, float *rt, float *slast) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  for (int s = 0; s < NB; ++s) rt[s * V + v] = 1.0f;
+  float prev = scale_eff(bunit[v]);
+  for (int g = 0; g < G; ++g) {
+    const float se = scale_eff(scales[v * G + g]);
+    rt[(NB + g) * V + v] = prev / se;
+    prev = se;
+  }
+  slast[v] = prev;
+}
+
+void launch_ratio_table(hipStream_t st, const float *scales, const float *bunit, int64_t V, int G, int NB,
+                        float *rt, float *slast) {
+  hipLaunchKernelGGL(k_ratio_table, dim3((unsigned)((V + 255) / 256)), dim3(256), 0, st, scales, bunit, V, G, NB,
+                     rt, slast);
 }
 
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
