@@ -13,7 +13,8 @@ namespace cce {
 // v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = d, K = vocabulary rows).
 // Per K step of 64 vocabulary rows:
 //  * the head tile of the step is dequantized once (s*q + b, rounded to bf16)
-//    into LDS as [d][v], double buffered, and shared by the eight waves;
+//    into LDS as [d][v] (swizzled, see dswz), double buffered, and shared by
+//    the eight waves;
 //  * the coefficient operand comes straight from the fragment-major chunk
 //    into registers, one step ahead;
 //  * the producer (every thread: 8 vocabulary rows x 4 columns) loads the
@@ -25,7 +26,14 @@ namespace cce {
 
 constexpr int DTW = 256;       // dh columns per workgroup
 constexpr int KSTP = 64;       // vocabulary rows per K step
-constexpr int BROW = KSTP + 8; // padded bf16 row stride of the LDS head tile [d][v]
+
+// The LDS head tile is [256 d][64 v] bf16 without padding; the 16-byte chunk c
+// (8 vocabulary rows) of row d sits at chunk position c ^ ((d ^ (d >> 2)) & 7).
+// The B-operand reads (consecutive d, one chunk) and the producer writes (d
+// four apart, one chunk) then spread over distinct 16-byte bank groups; the
+// padded alternative puts every fourth producer row on the same banks
+// (measured: 17x more LDS bank-conflict cycles).
+__device__ __forceinline__ int dswz(int d, int chunk) { return d * KSTP + ((chunk ^ ((d ^ (d >> 2)) & 7)) << 3); }
 
 // Producer mapping: thread (rgp, dc) handles vocabulary rows 8*rgp .. 8*rgp+7
 // of the step and columns 4*dc .. 4*dc+3 of the tile; lanes are 16 dc x 4 rgp,
@@ -85,7 +93,7 @@ struct DhProducer {
       const uint32_t q = (BITS == 8) ? (p.w[e] >> (8 * k)) & 0xFFu : (p.w[e] >> (4 * k)) & 0xFu;
       x[e] = fmaf(s[e], (float)q, b[e]);
     }
-    *(u32x4_t *)(sb + (4 * dc + k) * BROW + 8 * rgp) =
+    *(u32x4_t *)(sb + dswz(4 * dc + k, rgp)) =
         u32x4_t{pack_rne(x[0], x[1]), pack_rne(x[2], x[3]), pack_rne(x[4], x[5]), pack_rne(x[6], x[7])};
   }
 };
@@ -107,7 +115,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int tg = wave & 3, dh = wave >> 2;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * BROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * KSTP];
   __shared__ __attribute__((aligned(16))) float sSB[2][4 * KSTP * 2];
 
   const int tok0 = tt * BM + tg * 64;
@@ -135,6 +143,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.isb = wave >> 2;  // waves 0-3 load scales, 4-7 biases
     pr.gq0 = d0 / KSTEP;
     DhRegs<BITS> P0, P1;
+    // this lane's B-operand chunk offsets (row dh*128 + l32 + 32c, chunk 2ks + lh);
+    // the swizzle key of row d + 32c equals that of row d
+    int boff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) boff[ks] = dswz(dh * 128 + l32, 2 * ks + lh);
     bf16x8_t cA[2][4];
     float sc[8], bi[8];
     // vocabulary row of step i of this split
@@ -164,11 +177,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       const int cb = st & 1;
       pr.load(a, vrow(st + 2), nxt);  // past the split: valid rows or zeros, never used
       pr.read_sb(sSB[cb ^ 1], sc, bi);
-      const uint16_t *sw = sB[cb] + (dh * 128 + l32) * BROW + lh * 8;
+      const uint16_t *sw = sB[cb];
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
       bf16x8_t bq[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + c * 32 * BROW);
+      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -176,7 +189,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
-          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + c * 32 * BROW + (ks + 1) * 16);
+          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTP);
         }
         cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
         cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));

@@ -46,10 +46,9 @@ struct ProdRegs {
 };
 
 // The LDS code tile is [256 rows][64 K] bf16 without padding; the 16-byte
-// chunk c of row n sits at chunk position c ^ ((n >> 1) & 7).  With that
-// swizzle the B-operand reads (32 consecutive rows, one chunk) and the
-// producer writes (4 rows x 4 chunk pairs per 16 lanes) both hit distinct
-// banks.
+// chunk c of row n sits at chunk position c ^ ((n >> 1) & 7), which spreads
+// both the B-operand reads (consecutive rows, one chunk) and the producer
+// writes (4 rows x 4 chunk pairs per 16 lanes) over distinct bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 // Producer mapping: wave w, lane l loads the 16-byte K slice l & 3 of rows
