@@ -85,7 +85,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="synthetic workload index (0-4); 3 is the measured configuration")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override M (e.g. 1024: one GPU's share of workload 3 split over 8 GPUs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -111,6 +114,9 @@ def main():
         log("calibration copy of %d bytes done" % COPY_BYTES)
 
     w = syn.WORKLOADS[args.workload]
+    if args.tokens is not None:
+        import dataclasses
+        w = dataclasses.replace(w, M=args.tokens, name="%s, M=%d" % (w.name, args.tokens))
     log("generating workload %d (%s)" % (args.workload, w.name))
     inp = syn.make_inputs(w, syn.seed_for(args.workload))
     M, H, V = inp["M"], inp["H"], inp["V"]
@@ -146,6 +152,21 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log("%.3f ms/step (wall %.3f ms/step)" % (ms, 1e3 * wall / args.steps))
 
+    # forward and backward alone (same inputs), for the split the step hides
+    def timed(fn):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record()
+        for _ in range(args.steps):
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / args.steps
+
+    ms_fwd = timed(lambda: cce.cce_forward(h, head, t, m, workspace=ws_f, out=(logp, lse)))
+    ms_bwd = timed(lambda: cce.cce_backward(h, head, t, lse, None, m, workspace=ws_b, out=dh))
+    log("forward %.3f ms, backward %.3f ms" % (ms_fwd, ms_bwd))
+
     # per-kernel timing pass (same steps, events around every launch)
     log("per-kernel timing pass")
     cce.profile_read()
@@ -160,6 +181,8 @@ def main():
         log("  %-10s %5.1f launches/step  %8.3f ms/step" % (k, n, tot))
 
     alg_flops = 6.0 * M_eff * V * H          # forward logits + backward recompute + dh
+    head_bytes = V * (H * inp["bits"] // 8) + 2 * 4 * V * (H // 64)  # packed codes + fp32 scales and biases
+    head_gbs = 2.0 * head_bytes / (ms * 1e-3) / 1e9                   # the head is read by both passes
     tflops = alg_flops / (ms * 1e-3) / 1e12
     per_kernel_flops = {"tile_fwd": 2.0 * M_eff * V * H, "tile_bwd": 2.0 * M_eff * V * H,
                         "dh_gemm": 2.0 * M_eff * V * H}
@@ -169,7 +192,7 @@ def main():
     if dom in per_kernel_flops:
         flop_launch = per_kernel_flops[dom] / n_l
         achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
-        tb = measured_traffic(dom) if args.workload == 3 else None
+        tb = measured_traffic(dom) if (args.workload == 3 and args.tokens is None) else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": tb,
@@ -196,8 +219,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V, "bits": inp["bits"],
                    "group": 64, "softcap": inp["softcap"], "g": 1.0},
+        "ms_fwd": round(ms_fwd, 4),
+        "ms_bwd": round(ms_bwd, 4),
         "tflops": round(tflops, 1),
         "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "head_GB_per_s": round(head_gbs, 1),
         "kernel_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

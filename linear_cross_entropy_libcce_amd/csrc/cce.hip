@@ -81,12 +81,12 @@ struct Plan {
   int G, Kb, Ka, NB, bits, wpr, TT, tiles;
   float cap;
   // forward
-  int nsplit, tiles_per_split;
+  int nsplit, tiles_per_split, fwd_blocks, max_splits;
   // backward
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: K steps per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_bunit, o_rt, o_slast, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
 };
 
 cce_status check_head(const cce_head *hd) {
@@ -123,6 +123,12 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.nsplit = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(1, cdiv(cus, p.TT)));
   p.tiles_per_split = (int)cdiv(p.tiles, p.nsplit);
   p.nsplit = (int)cdiv(p.tiles, p.tiles_per_split);
+  p.fwd_blocks = p.TT * p.nsplit;
+  // Partial slots per token: the kernels give the launched workgroups to the
+  // active token tiles only (masked tokens are compacted away), so a few
+  // active tiles get more vocabulary splits; bounded to 64 MiB of partials.
+  p.max_splits = (int)std::max<int64_t>(
+      p.nsplit, std::min<int64_t>(std::min<int64_t>(p.tiles, p.fwd_blocks), ((int64_t)64 << 20) / 16 / p.M_pad));
 
   // backward: coefficient chunks of at most COEFF_BUDGET bytes
   const int64_t per_tile = p.M_pad * BNT * 2;
@@ -161,12 +167,11 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_tok = o;  o = align_up(o + sizeof(TokRec) * p.M_pad, 256);
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
-  p.o_bunit = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   p.o_rt = o; o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
   p.o_slast = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   const size_t common = o;
   p.o_part = common;
-  p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * p.nsplit) * p.M_pad, 256);
+  p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
   p.o_coeff = common;
   o = align_up(common + (size_t)2 * p.M_pad * p.ld_coeff, 256);
   p.o_dhp = o;
@@ -211,10 +216,9 @@ void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_
   CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
   CCE_LAUNCH("prep", st, launch_prep(st, (int)p.M_pad, (const uint16_t *)h, (int)p.H, p.G, p.Kb, p.Ka, idx, targets,
                                      lse, g, tok, haug));
-  CCE_LAUNCH("bias_op", st, launch_bias_operand(st, p.bits, hd->biases, hd->scales, p.V, p.G, p.Kb, ws_at<uint8_t>(ws, p.o_baug),
-                                                           ws_at<float>(ws, p.o_bunit)));
-  CCE_LAUNCH("ratio_tab", st, launch_ratio_table(st, hd->scales, ws_at<const float>(ws, p.o_bunit), p.V, p.G, p.NB,
-                                                 ws_at<float>(ws, p.o_rt), ws_at<float>(ws, p.o_slast)));
+  CCE_LAUNCH("head_prep", st, launch_head_prep(st, p.bits, hd->biases, hd->scales, p.V, p.G, p.Kb, p.NB,
+                                               ws_at<uint8_t>(ws, p.o_baug), ws_at<float>(ws, p.o_rt),
+                                               ws_at<float>(ws, p.o_slast)));
   CCE_LAUNCH("target", st, launch_target(st, p.bits, (int)p.M_pad, (const uint16_t *)h, idx, (int)p.H, p.G, hd->wq,
                                          p.wpr, hd->scales, hd->biases, p.V, p.cap, cnt, tok, bwd ? 1 : 0));
 }
@@ -223,7 +227,6 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   TileArgs a{};
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
-  a.bunit = ws_at<const float>(ws, p.o_bunit);
   a.rt = ws_at<const float>(ws, p.o_rt);
   a.slast = ws_at<const float>(ws, p.o_slast);
   a.wq = hd->wq;
@@ -288,12 +291,12 @@ cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int
   a.part = ws_at<float>(workspace, p.o_part);
   a.range_tile0 = 0;
   a.range_tiles = p.tiles;
-  a.tiles_per_wg = p.tiles_per_split;
-  a.nwr = p.nsplit;
-  a.nblocks = p.TT * p.nsplit;
+  a.nblocks = p.fwd_blocks;
+  a.max_splits = p.max_splits;
   const dim3 grid((unsigned)(cdiv(a.nblocks, 8) * 8));
   CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, false, grid, a));
-  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, 2 * p.nsplit, (int)p.M_pad, ws_at<const int>(workspace, p.o_inv),
+  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.tiles, p.max_splits, (int)p.M_pad,
+                                       ws_at<const int>(workspace, p.o_inv), a.cnt,
                                        ws_at<const TokRec>(workspace, p.o_tok), logp, lse));
   return hip_status();
 }
@@ -314,7 +317,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   TileArgs a = tile_args(p, head, workspace);
   a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
   a.ld_coeff = p.ld_coeff;
-  a.tiles_per_wg = p.bwd_tpw;
+  a.max_splits = 1 << 30;
 
   GemmArgs ga{};
   ga.coeff = a.coeff;
@@ -329,7 +332,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   ga.G = p.G;
   ga.wpr = p.wpr;
   ga.M_pad = (int)p.M_pad;
-  ga.steps_per_split = p.k_tiles;
+  ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);
   ga.TT = p.TT;
   ga.HT = p.HT;
   ga.ksplit = p.ksplit;
@@ -341,8 +344,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
     const int nt = std::min(p.chunk_tiles, p.tiles - t0);
     a.range_tile0 = t0;
     a.range_tiles = nt;
-    a.nwr = (int)cdiv(nt, p.bwd_tpw);
-    a.nblocks = p.TT * a.nwr;
+    a.nblocks = p.TT * (int)cdiv(nt, p.bwd_tpw);
     const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
     CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, true, g1, a));
     ga.chunk_v0 = (int64_t)t0 * BNT;
@@ -350,10 +352,8 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
     ga.accumulate = c > 0;
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
   }
-  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga.dh_part, p.ksplit, (int)p.M_pad, (int)p.H, p.G,
-                                               ws_at<const int>(workspace, p.o_inv),
-                                               ws_at<const TokRec>(workspace, p.o_tok), head->wq, p.wpr, head->scales,
-                                               head->biases, p.V, dh));
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, ws_at<const int>(workspace, p.o_inv),
+                                               ws_at<const TokRec>(workspace, p.o_tok), dh));
   return hip_status();
 }
 

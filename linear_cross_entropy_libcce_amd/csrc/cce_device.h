@@ -109,7 +109,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 struct TileArgs {
   const uint16_t *haug;  // [M_pad][Ka] bf16, fragment-major
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
-  const float *bunit;    // [V] fixed-point unit of each row's biases
   const float *rt;       // [NB + G][V] fold ratio of every step
   const float *slast;    // [V] effective scale of the last group
   const uint32_t *wq;
@@ -124,7 +123,9 @@ struct TileArgs {
   int G, Ka, Kb, NB, wpr, M_pad;
   int64_t ks16;          // Ka / 16 (fragment-major h rows)
   int64_t ksv;           // ld_coeff / 16 (fragment-major coefficient chunk)
-  int range_tile0, range_tiles, tiles_per_wg, nwr, nblocks;
+  int range_tile0, range_tiles;
+  int nblocks;           // launched work ids (the split per active token tile is derived on the device)
+  int max_splits;        // forward: capacity of the partial buffer in splits per token
   float cap, inv_cap;
 };
 
@@ -139,9 +140,9 @@ struct GemmArgs {
   int64_t V;
   int64_t chunk_v0;      // first vocabulary row of the chunk
   int H, G, wpr, M_pad;
-  int chunk_steps;       // 64-row K steps in the chunk
-  int steps_per_split;
-  int TT, HT, ksplit, nblocks;
+  int chunk_steps;       // 64-row K steps in this chunk
+  int max_chunk_steps;   // K steps of a full chunk (fixes the split across chunks)
+  int TT, HT, ksplit, nblocks;  // ksplit: slab capacity in units of all TT token tiles
   int accumulate;
 };
 
@@ -158,6 +159,30 @@ __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int voff, int soff) {
 }
 __device__ __forceinline__ float buf_loadf(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// Work split chosen on the device from the supervised-token count (the host
+// does not know it without a synchronization): `nblocks` launched workgroups
+// cover act = ceil(cnt / 256) active token tiles, each with as many splits of
+// `units` (vocabulary tiles or K steps) as fit; the result is also the number
+// of per-token partials to merge.
+__device__ __forceinline__ int active_tiles(const int *cnt) { return (cnt[0] + BM - 1) / BM; }
+__device__ __forceinline__ int splits_for(int nblocks, int act, int units, int cap) {
+  int n = nblocks / (act > 0 ? act : 1);
+  n = n < cap ? n : cap;
+  n = n < units ? n : units;
+  n = n > 1 ? n : 1;
+  const int per = (units + n - 1) / n;
+  return (units + per - 1) / per;
+}
+
+// K splits of the dh contraction for act active token tiles: as many as the
+// launched workgroups allow, bounded by the slab capacity (ks * act <=
+// ksplit * TT, the slabs being laid out over the active rows only).
+__device__ __forceinline__ void dh_split(const GemmArgs &a, int act, int &ks, int &steps_per) {
+  const int cap = a.ksplit * a.TT / (act > 0 ? act : 1);
+  ks = splits_for(a.nblocks / a.HT, act, a.max_chunk_steps, cap);
+  steps_per = (a.max_chunk_steps + ks - 1) / ks;
 }
 
 // Linear block id -> work id, so that consecutive work ids share an XCD
@@ -197,16 +222,13 @@ void launch_prep(hipStream_t st, int M_pad, const uint16_t *h, int H, int G, int
 void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const int *idx, int H, int G,
                    const uint32_t *wq, int wpr, const float *scales, const float *biases, int64_t V, float cap,
                    const int *cnt, TokRec *tok, int bwd);
-void launch_bias_operand(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G,
-                         int Kb, uint8_t *baug, float *bunit);
-void launch_ratio_table(hipStream_t st, const float *scales, const float *bunit, int64_t V, int G, int NB,
-                        float *rt, float *slast);
+void launch_head_prep(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G, int Kb,
+                      int NB, uint8_t *baug, float *rt, float *slast);
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
-void launch_merge(hipStream_t st, int M, const float *part, int nsplit, int M_pad, const int *inv,
-                  const TokRec *tok, float *logp, float *lse);
+void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
+                  const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
-void launch_dh_reduce(hipStream_t st, int bits, int M, const float *dh_part, int ksplit, int M_pad, int H, int G,
-                      const int *inv, const TokRec *tok, const uint32_t *wq, int wpr, const float *scales,
-                      const float *biases, int64_t V, float *dh);
+void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
+                      float *dh);
 
 }  // namespace cce

@@ -5,8 +5,9 @@
 
 namespace cce {
 
-// dh_part[k][t][d] (+)= sum_v coeff[t][v] * bf16(s*q + b)[v][d] over the
-// vocabulary rows of split k of one coefficient chunk.
+// dh_part[k][r][d] (+)= sum_v coeff[r][v] * bf16(s*q + b)[v][d] over the
+// vocabulary rows of split k of one coefficient chunk (slabs of the active
+// rows r < 256 * ceil(cnt / 256), split count from dh_split).
 //
 // Workgroup: 256 tokens x 256 dh columns, 8 waves; wave w owns tokens
 // [64(w%4), +64) and columns [128(w/4), +128) as 2 x 4 blocks of
@@ -101,15 +102,18 @@ struct DhProducer {
 template <int BITS>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  if (bid >= a.nblocks) return;
+  // the launched work ids are spread over the active token tiles only;
   // consecutive work ids share the token tile (and the coefficient rows)
+  const int act = active_tiles(a.cnt);
+  int ksd, steps_per;
+  dh_split(a, act, ksd, steps_per);
+  if (bid >= a.HT * act * ksd) return;
   const int dt = bid % a.HT;
-  const int tt = (bid / a.HT) % a.TT;
-  const int ks_ = bid / (a.HT * a.TT);
-  if (tt * BM >= a.cnt[0]) return;
+  const int tt = (bid / a.HT) % act;
+  const int ks_ = bid / (a.HT * act);
   const int d0 = dt * DTW;
-  const int step0 = ks_ * a.steps_per_split;
-  const int nsteps = min(a.steps_per_split, a.chunk_steps - step0);
+  const int step0 = ks_ * steps_per;
+  const int nsteps = min(steps_per, a.chunk_steps - step0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tg = wave & 3, dh = wave >> 2;
@@ -220,7 +224,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float *dst = a.dh_part + ((size_t)ks_ * a.M_pad + tok0 + rb * 32 + 8 * i + 4 * lh + j) * a.H + d;
+          float *dst = a.dh_part + ((size_t)ks_ * act * BM + tok0 + rb * 32 + 8 * i + 4 * lh + j) * a.H + d;
           const float v = acc[rb][c][4 * i + j];
           *dst = a.accumulate ? (*dst + v) : v;
         }

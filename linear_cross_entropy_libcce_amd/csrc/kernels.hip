@@ -144,8 +144,11 @@ __global__ void __launch_bounds__(256) k_target(const uint16_t *h, const int *id
 // ---------------------------------------------------------------------------
 // Cross-split merge (page "mlx-bun 0.0.4 -> 0.0.6", flashCceForward's host
 // merge): lse = m* + log sum_s s_s exp(m_s - m*), logp = target logit - lse.
-__global__ void __launch_bounds__(256) k_merge(const float *part, int nsplit, int M_pad, const int *inv,
-                                               const TokRec *tok, int M, float *logp, float *lse) {
+__global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int tiles, int max_splits,
+                                               int M_pad, const int *inv, const int *cnt, const TokRec *tok,
+                                               int M, float *logp, float *lse) {
+  // two partials (vocabulary halves of the tile) per split of the forward
+  const int nsplit = 2 * splits_for(nblocks, active_tiles(cnt), tiles, max_splits);
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= M) return;
   const int r = inv[t];
@@ -170,22 +173,23 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nsplit, in
 // dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
 // zero rows for masked tokens.
 template <int BITS>
-__global__ void __launch_bounds__(256) k_dh_reduce(const float *dh_part, int ksplit, int M_pad, int H, int G,
-                                                   const int *inv, const TokRec *tok, const uint32_t *wq,
-                                                   int wpr, const float *scales, const float *biases,
-                                                   int64_t V, float *dh) {
+__global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, const TokRec *tok, float *dh) {
   const int t = blockIdx.x;
   const int d = blockIdx.y * 256 + threadIdx.x;
+  const int H = a.H;
   if (d >= H) return;
   const int r = inv[t];
   float acc = 0.0f;
   if (r >= 0) {
-    for (int k = 0; k < ksplit; ++k) acc += dh_part[((size_t)k * M_pad + r) * H + d];
+    const int act = active_tiles(a.cnt);
+    int ksd, steps_per;
+    dh_split(a, act, ksd, steps_per);
+    for (int k = 0; k < ksd; ++k) acc += a.dh_part[((size_t)k * act * BM + r) * H + d];
     const TokRec rec = tok[r];
-    if (rec.tgt >= 0 && (int64_t)rec.tgt < V) {
-      const size_t gi = (size_t)rec.tgt * G + d / KSTEP;
-      const float q = (float)code_at<BITS>(wq + (size_t)rec.tgt * wpr, d);
-      acc += rec.tval * (scales[gi] * q + biases[gi]);
+    if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
+      const size_t gi = (size_t)rec.tgt * a.G + d / KSTEP;
+      const float q = (float)code_at<BITS>(a.wq + (size_t)rec.tgt * a.wpr, d);
+      acc += rec.tval * (a.scales[gi] * q + a.biases[gi]);
     }
   }
   dh[(size_t)t * H + d] = acc;
@@ -213,22 +217,19 @@ void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const
                        cnt, tok, M_pad, bwd);
 }
 
-void launch_merge(hipStream_t st, int M, const float *part, int nsplit, int M_pad, const int *inv,
-                  const TokRec *tok, float *logp, float *lse) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, part, nsplit, M_pad, inv, tok, M,
-                     logp, lse);
+void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
+                  const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, part, nblocks, tiles, max_splits,
+                     M_pad, inv, cnt, tok, M, logp, lse);
 }
 
-void launch_dh_reduce(hipStream_t st, int bits, int M, const float *dh_part, int ksplit, int M_pad, int H, int G,
-                      const int *inv, const TokRec *tok, const uint32_t *wq, int wpr, const float *scales,
-                      const float *biases, int64_t V, float *dh) {
-  const dim3 grid((unsigned)M, (unsigned)((H + 255) / 256));
+void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
+                      float *dh) {
+  const dim3 grid((unsigned)M, (unsigned)((ga.H + 255) / 256));
   if (bits == 4)
-    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, dh_part, ksplit, M_pad, H, G, inv, tok, wq, wpr,
-                       scales, biases, V, dh);
+    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh);
   else
-    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, dh_part, ksplit, M_pad, H, G, inv, tok, wq, wpr,
-                       scales, biases, V, dh);
+    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh);
 }
 
 }  // namespace cce
