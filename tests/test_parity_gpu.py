@@ -83,6 +83,10 @@ SMALL = {
                                           mask_frac=0.5),
     "H4096_V300_4bit": dict(M=257, H=4096, V=300, bits=4),
     "H2560_V260_8bit_cap_small_scales": dict(M=140, H=2560, V=260, bits=8, softcap=30.0),
+    # M >= 4096 selects the 512-token x 128-row logit tile: ragged token and vocabulary tails there
+    "wide_H256_V700_4bit": dict(M=4200, H=256, V=700, bits=4),
+    "wide_H512_V389_8bit_cap_randmask": dict(M=4500, H=512, V=389, bits=8, softcap=30.0, mask="random",
+                                             mask_frac=0.4),
 }
 
 
