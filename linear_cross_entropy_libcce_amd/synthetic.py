@@ -18,9 +18,17 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
 5. mask uint8 [M] (1 = supervised token) or None: a contiguous masked prefix,
    or exactly round(frac*M) masked positions chosen by a seeded permutation.
 
-The five workloads mirror the sizes the pages validate (H=1536 and H=2560 heads
+A peaked workload multiplies the scales (and so the biases) of the first
+``boost_rows`` vocabulary rows by ``boost`` after step 2.  Their logits then
+dominate every token's softmax, as the frequent tokens of a trained model's
+head do, and most vocabulary blocks carry almost no probability: the regime
+in which the backward's block skip and coefficient filter fire.
+
+Workloads 0-4 mirror the sizes the pages validate (H=1536 and H=2560 heads
 with V up to 262144; page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts,
-the header comment and the H_MAX note) plus a tail-mask case.
+the header comment and the H_MAX note) plus a tail-mask case; workload 5 is
+workload 3's shape with a peaked head and Zipf targets, the stand-in for the
+real text on which the pages measure their backward skips.
 """
 from __future__ import annotations
 
@@ -46,6 +54,8 @@ class Workload:
     zipf_a: float = 1.1
     mask: str = "none"            # "none" | "prefix" | "random"
     mask_frac: float = 0.0
+    boost_rows: int = 0           # peaked head: rows [0, boost_rows) get scales * boost
+    boost: float = 1.0
 
     @property
     def G(self) -> int:
@@ -69,6 +79,8 @@ WORKLOADS = {
                 0.0005, 0.002, softcap=30.0),
     4: _w4("M=8192 H=4096 V=151655 4-bit zipf random-masked", 8192, 4096, 151655,
            targets="zipf", mask="random", mask_frac=0.3),
+    5: Workload("M=8192 H=2560 V=262144 8-bit peaked (rows < 4096 scaled x8) zipf", 8192, 2560, 262144, 8,
+                0.0005, 0.002, targets="zipf", boost_rows=4096, boost=8.0),
 }
 
 SEED_BASE = 20261202
@@ -121,6 +133,8 @@ def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
     rng = np.random.default_rng(seed)
     wq = rng.integers(0, 2**32, size=(w.V, w.words_per_row), dtype=np.uint32)
     scales = rng.uniform(w.scale_lo, w.scale_hi, size=(w.V, w.G)).astype(np.float32)
+    if w.boost_rows > 0:
+        scales[:w.boost_rows] *= np.float32(w.boost)
     zero_point = np.float32(8.0 if w.bits == 4 else 128.0)
     biases = (-zero_point * scales).astype(np.float32)
     h = bf16_bits_from_f32(rng.standard_normal((M, w.H), dtype=np.float32))
@@ -131,12 +145,14 @@ def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
 
 
 def make_custom(M, H, V, bits, seed, softcap=0.0, scale_lo=None, scale_hi=None,
-                targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0) -> dict:
+                targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0,
+                boost_rows=0, boost=1.0) -> dict:
     """A reduced/edge-case workload with the same value distributions."""
     if scale_lo is None:
         scale_lo, scale_hi = (0.005, 0.02) if bits == 4 else (0.0005, 0.002)
     w = Workload("custom", M, H, V, bits, scale_lo, scale_hi, softcap=softcap,
-                 targets=targets, mask=mask, mask_frac=mask_frac)
+                 targets=targets, mask=mask, mask_frac=mask_frac,
+                 boost_rows=boost_rows, boost=boost)
     d = make_inputs(w, seed)
     if h_scale != 1.0:
         d["h"] = bf16_bits_from_f32(f32_from_bf16_bits(d["h"]) * np.float32(h_scale))

@@ -1,12 +1,15 @@
-"""ctypes wrapper of the fp64 CPU oracle (cce_oracle.c).
+"""fp64 CPU oracle: ctypes wrapper of cce_oracle.c, plus the approximate
+backward (block skip, coefficient filter) written out on dense matrices.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the library.  See cce_oracle.c for what
-is computed and which passages of the pages each step follows.
+is computed and which passages of the pages each step follows; the skip rules
+and their readings are described above `cce_skip` below.
 """
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -84,3 +87,141 @@ def cce(inp: dict, tokens: Optional[Sequence[int]] = None, backward: bool = True
     if rc != 0:
         raise ValueError("oracle_cce rejected its arguments (rc=%d)" % rc)
     return logp, lse, dh
+
+
+# ---------------------------------------------------------------------------
+# The approximate backward (opt-in skips), written out on dense fp64 matrices.
+#
+# Page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts, the notes on the two
+# backward skips and the scalar backward kernel's phase 1 / phase 2:
+#   * block early exit: a (token block, vocabulary block) pair contributes
+#     nothing when, for every token of the token block, the largest softmax
+#     probability inside the vocabulary block is below eps and the token's
+#     target lies outside it;
+#   * coefficient filter: the contraction of a (token block, vocabulary block)
+#     pair is skipped when every coefficient in it is below eps in magnitude.
+# Readings fixed here (the pages' blocks are their own kernel tiles):
+#   * token blocks are runs of TOKEN_TILE consecutive supervised tokens (in
+#     index order; masked tokens are not counted); vocabulary blocks are rows
+#     [BLOCK_V*b, BLOCK_V*(b+1)) clipped to V;
+#   * "largest probability below eps" is block_max - lse < log(eps), where
+#     block_max is the largest softcapped logit of the block;
+#   * the filter looks at the non-target coefficients only, and a target's
+#     term g*(1 - p)*c'*w is always kept: dropping it is never "small";
+#   * eps = 0 turns a skip off; both skips on: the block rule first, the
+#     filter on the pairs that stay.
+# Dense [M, V] matrices: small inputs only.
+# ---------------------------------------------------------------------------
+BLOCK_V = 256
+TOKEN_TILE = 256
+
+
+def dequantize(inp: dict) -> np.ndarray:
+    """W[v][d] = scale * q + bias in fp64 from the packed words (little-endian
+    codes within each uint32, per-group scale and bias)."""
+    bits, group = int(inp["bits"]), int(inp["group"])
+    wq = np.asarray(inp["wq"], dtype=np.uint32)
+    V, wpr = wq.shape
+    per = 32 // bits
+    shifts = (np.arange(per, dtype=np.uint32) * bits).astype(np.uint32)
+    q = (wq[:, :, None] >> shifts[None, None, :]) & np.uint32((1 << bits) - 1)
+    q = q.reshape(V, wpr * per).astype(np.float64)
+    s = np.repeat(np.asarray(inp["scales"], np.float64), group, axis=1)
+    b = np.repeat(np.asarray(inp["biases"], np.float64), group, axis=1)
+    return s * q + b
+
+
+def dense(inp: dict, g: Optional[np.ndarray] = None, softcap: Optional[float] = None) -> dict:
+    """Every quantity of the plain definition as dense fp64 matrices over the
+    supervised tokens: z, y, lse, logp, coefficients and the block maxima."""
+    W = dequantize(inp)
+    M, V = int(inp["M"]), int(inp["V"])
+    cap = float(inp["softcap"] if softcap is None else softcap)
+    mk = inp.get("mask")
+    act = np.arange(M) if mk is None else np.flatnonzero(np.asarray(mk) != 0)
+    hb = np.asarray(inp["h"], dtype=np.uint16)[act]
+    hd = (hb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    z = hd @ W.T
+    if cap > 0:
+        th = np.tanh(z / cap)
+        y, dc = cap * th, 1.0 - th * th
+    else:
+        y, dc = z, np.ones_like(z)
+    mx = y.max(axis=1, keepdims=True)
+    lse = (mx + np.log(np.exp(y - mx).sum(axis=1, keepdims=True)))[:, 0]
+    tg = np.asarray(inp["targets"], np.int64)[act]
+    t_in = (tg >= 0) & (tg < V)
+    rows = np.arange(len(act))
+    logp = np.where(t_in, y[rows, np.clip(tg, 0, V - 1)], 0.0) - lse
+    gt = np.ones(len(act)) if g is None else np.asarray(g, np.float64)[act]
+    p = np.exp(y - lse[:, None])
+    coeff = -gt[:, None] * p * dc           # non-target part of every coefficient
+    tcoef = np.zeros(len(act))              # the target's whole coefficient g*(1-p)*c'
+    tcoef[t_in] = gt[t_in] * (1.0 - p[rows[t_in], tg[t_in]]) * dc[rows[t_in], tg[t_in]]
+    coeff[rows[t_in], tg[t_in]] = 0.0
+    nb = (V + BLOCK_V - 1) // BLOCK_V
+    bmax = np.full((len(act), nb), -np.inf)
+    for b in range(nb):
+        bmax[:, b] = y[:, b * BLOCK_V:min(V, (b + 1) * BLOCK_V)].max(axis=1)
+    return dict(W=W, act=act, z=z, y=y, lse=lse, logp=logp, coeff=coeff, tcoef=tcoef, tgt=tg,
+                t_in=t_in, block_max=bmax)
+
+
+def block_max(inp: dict, softcap: Optional[float] = None) -> np.ndarray:
+    """[M, ceil(V/BLOCK_V)] largest softcapped logit per vocabulary block of
+    each token; rows of masked tokens are 0."""
+    d = dense(inp, softcap=softcap)
+    out = np.zeros((int(inp["M"]), d["block_max"].shape[1]))
+    out[d["act"]] = d["block_max"]
+    return out
+
+
+def _pair_cold(bmax_tile, lse_tile, tgt_tile, b, block_eps):
+    """Block rule for one (token tile, vocabulary block b) pair."""
+    lo, hi = b * BLOCK_V, (b + 1) * BLOCK_V
+    if np.any((tgt_tile >= lo) & (tgt_tile < hi)):
+        return False
+    return bool(np.all(bmax_tile[:, b] - lse_tile < math.log(block_eps)))
+
+
+def _pair_filtered(coeff_pair, filter_eps):
+    """Filter rule for one pair: every non-target coefficient below eps."""
+    return bool(np.max(np.abs(coeff_pair), initial=0.0) < filter_eps)
+
+
+def cce_skip(inp: dict, g: Optional[np.ndarray] = None, block_eps: float = 0.0,
+             filter_eps: float = 0.0, softcap: Optional[float] = None):
+    """(logp, lse, dh, dropped) over all M tokens with the two skips applied.
+
+    `dropped` is the boolean [n_token_tiles, n_blocks] table of the pairs whose
+    non-target coefficients were left out.
+    """
+    d = dense(inp, g=g, softcap=softcap)
+    M, V, H = int(inp["M"]), int(inp["V"]), int(inp["H"])
+    coeff = d["coeff"].copy()
+    n = len(d["act"])
+    nt = (n + TOKEN_TILE - 1) // TOKEN_TILE
+    nb = d["block_max"].shape[1]
+    dropped = np.zeros((nt, nb), dtype=bool)
+    for k in range(nt):
+        r0, r1 = k * TOKEN_TILE, min(n, (k + 1) * TOKEN_TILE)
+        for b in range(nb):
+            c0, c1 = b * BLOCK_V, min(V, (b + 1) * BLOCK_V)
+            drop = block_eps > 0 and _pair_cold(d["block_max"][r0:r1], d["lse"][r0:r1],
+                                                d["tgt"][r0:r1], b, block_eps)
+            if not drop and filter_eps > 0:
+                drop = _pair_filtered(coeff[r0:r1, c0:c1], filter_eps)
+            if drop:
+                coeff[r0:r1, c0:c1] = 0.0
+                dropped[k, b] = True
+    W = d["W"]
+    dh_act = coeff @ W
+    ti = np.flatnonzero(d["t_in"])
+    dh_act[ti] += d["tcoef"][ti, None] * W[d["tgt"][ti]]
+    logp = np.zeros(M)
+    lse = np.zeros(M)
+    dh = np.zeros((M, H))
+    logp[d["act"]] = d["logp"]
+    lse[d["act"]] = d["lse"]
+    dh[d["act"]] = dh_act
+    return logp, lse, dh, dropped
