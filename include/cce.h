@@ -42,7 +42,12 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 1
+#define CCE_ABI_VERSION 2
+
+/* Vocabulary rows per block of block_max, and supervised tokens per token
+ * tile of the backward skips (both are the kernels' tile sizes). */
+#define CCE_BLOCK_V 256
+#define CCE_TOKEN_TILE 256
 
 typedef enum cce_status {
   CCE_OK = 0,
@@ -116,6 +121,58 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M,
                         const int32_t *targets, const uint8_t *mask,
                         const float *lse, const float *g, float *dh,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward that also writes the per-block maxima the backward's block skip
+ * reads (page "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts, the notes on
+ * the blockMax vocabulary-block early exit of the backward).
+ *   block_max  device float [M][ceil(V / CCE_BLOCK_V)] (4-byte aligned) or
+ *              NULL, which makes the call cce_forward.  block_max[t][b] is the
+ *              largest softcapped logit y_v over the rows v in
+ *              [CCE_BLOCK_V*b, min(V, CCE_BLOCK_V*(b+1))); rows of masked
+ *              tokens are 0.
+ * Other arguments, the workspace size and the errors are those of cce_forward.
+ */
+cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M,
+                          const int32_t *targets, const uint8_t *mask,
+                          float *logp, float *lse, float *block_max,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Opt-in approximations of the backward (same file: the coefficient filter
+ * and the block early exit of the backward kernels; both default to off).
+ * Token tiles are runs of CCE_TOKEN_TILE consecutive supervised tokens (in
+ * index order), vocabulary blocks those of block_max.  For a (token tile,
+ * block) pair:
+ *   block_eps   > 0: the pair is left out when, for every token of the tile,
+ *               block_max - lse < log(block_eps) (its largest probability in
+ *               the block is below block_eps) and its target is outside the
+ *               block.  Needs block_max.
+ *   filter_eps  > 0: the pair is left out when every non-target coefficient
+ *               g * p_v * c'(z_v) in it is below filter_eps in magnitude.
+ * "Left out" drops the pair's non-target coefficients; every target's term
+ * g * (1 - p) * c' * w_target is always kept.  0 turns a skip off; both on:
+ * the block rule first, then the filter on the pairs that remain.
+ */
+typedef struct cce_skip {
+  float block_eps;
+  float filter_eps;
+} cce_skip;
+
+/*
+ * Backward with the skips of `skip` (NULL or both eps 0: exactly cce_backward).
+ *   block_max  as written by cce_forward_ex for these inputs; needed (non-NULL)
+ *              when skip->block_eps > 0, else ignored
+ * Other arguments and the workspace size are those of cce_backward.  Errors
+ * as cce_backward, plus CCE_ERR_INVALID_ARG for a negative or non-finite eps
+ * or block_eps > 0 without block_max.
+ */
+cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M,
+                           const int32_t *targets, const uint8_t *mask,
+                           const float *lse, const float *g,
+                           const float *block_max, const cce_skip *skip,
+                           float *dh, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* Human-readable text of a status (for CCE_ERR_HIP, of the last HIP error
  * seen by this thread).  The pointer stays valid until the thread's next call. */

@@ -16,15 +16,22 @@ LIB_PATH = os.path.join(_PKG, "libcce.so")
 
 CCE_OK, CCE_ERR_INVALID_ARG, CCE_ERR_UNSUPPORTED, CCE_ERR_WORKSPACE, CCE_ERR_HIP = range(5)
 
-EXPORTS = ("cce_forward", "cce_backward", "cce_forward_workspace_bytes",
-           "cce_backward_workspace_bytes", "cce_status_str", "cce_abi_version",
-           "cce_profile_enable", "cce_profile_read")
+EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
+           "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_status_str",
+           "cce_abi_version", "cce_profile_enable", "cce_profile_read")
+
+BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
+TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
 
 
 class cce_head(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("softcap", ctypes.c_float)]
+
+
+class cce_skip(ctypes.Structure):
+    _fields_ = [("block_eps", ctypes.c_float), ("filter_eps", ctypes.c_float)]
 
 
 class cce_kernel_time(ctypes.Structure):
@@ -54,6 +61,10 @@ def load(path: str = LIB_PATH):
     lib.cce_forward.argtypes = [HP, P, I64, P, P, P, P, P, SZ, P]
     lib.cce_backward.restype = ctypes.c_int
     lib.cce_backward.argtypes = [HP, P, I64, P, P, P, P, P, P, SZ, P]
+    lib.cce_forward_ex.restype = ctypes.c_int
+    lib.cce_forward_ex.argtypes = [HP, P, I64, P, P, P, P, P, P, SZ, P]
+    lib.cce_backward_ex.restype = ctypes.c_int
+    lib.cce_backward_ex.argtypes = [HP, P, I64, P, P, P, P, P, ctypes.POINTER(cce_skip), P, P, SZ, P]
     lib.cce_forward_workspace_bytes.restype = SZ
     lib.cce_forward_workspace_bytes.argtypes = [HP, I64]
     lib.cce_backward_workspace_bytes.restype = SZ
@@ -130,17 +141,41 @@ def backward_workspace_bytes(head: Head, M: int) -> int:
     return int(load().cce_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
 
 
-def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
-    """(logp, lse), each float32 [M], for bf16 h [M, H] and int32 targets [M]."""
+def n_blocks(head: Head) -> int:
+    """Blocks per row of block_max: ceil(V / BLOCK_V)."""
+    return (head.V + BLOCK_V - 1) // BLOCK_V
+
+
+def _tokens(h, head: Head, targets, mask):
     import torch
-    lib = load()
     M, dev = int(h.shape[0]), h.device
     _expect(h, torch.bfloat16, dev, (M, head.H), "h")
     _expect(targets, torch.int32, dev, (M,), "targets")
     if mask is not None:
         _expect(mask, torch.uint8, dev, (M,), "mask")
-    logp, lse = out if out is not None else (torch.empty(M, dtype=torch.float32, device=dev),
-                                             torch.empty(M, dtype=torch.float32, device=dev))
+    return M, dev
+
+
+def _fwd_out(M, dev, out):
+    import torch
+    if out is not None:
+        return out
+    return torch.empty(M, dtype=torch.float32, device=dev), torch.empty(M, dtype=torch.float32, device=dev)
+
+
+def _bwd_in(head: Head, M, dev, lse, g, out):
+    import torch
+    _expect(lse, torch.float32, dev, (M,), "lse")
+    if g is not None:
+        _expect(g, torch.float32, dev, (M,), "g")
+    return out if out is not None else torch.empty((M, head.H), dtype=torch.float32, device=dev)
+
+
+def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
+    """(logp, lse), each float32 [M], for bf16 h [M, H] and int32 targets [M]."""
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    logp, lse = _fwd_out(M, dev, out)
     hs = head.c_struct()
     ws = _workspace(lib.cce_forward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
     _check(lib.cce_forward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
@@ -148,23 +183,53 @@ def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
     return logp, lse
 
 
-def cce_backward(h, head: Head, targets, lse, g=None, mask=None, workspace=None, out=None):
-    """dh float32 [M, H] = g * d logp / d h (g = None means all ones)."""
+def cce_forward_ex(h, head: Head, targets, mask=None, block_max=True, workspace=None, out=None):
+    """(logp, lse, block_max): block_max float32 [M, n_blocks(head)], allocated
+    (True), given as a tensor to write into, or not produced (None)."""
     import torch
     lib = load()
-    M, dev = int(h.shape[0]), h.device
-    _expect(h, torch.bfloat16, dev, (M, head.H), "h")
-    _expect(targets, torch.int32, dev, (M,), "targets")
-    _expect(lse, torch.float32, dev, (M,), "lse")
-    if g is not None:
-        _expect(g, torch.float32, dev, (M,), "g")
-    if mask is not None:
-        _expect(mask, torch.uint8, dev, (M,), "mask")
-    dh = out if out is not None else torch.empty((M, head.H), dtype=torch.float32, device=dev)
+    M, dev = _tokens(h, head, targets, mask)
+    logp, lse = _fwd_out(M, dev, out)
+    bmx = None
+    if block_max is True:
+        bmx = torch.empty((M, n_blocks(head)), dtype=torch.float32, device=dev)
+    elif block_max is not None and block_max is not False:
+        _expect(block_max, torch.float32, dev, (M, n_blocks(head)), "block_max")
+        bmx = block_max
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_forward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_forward_ex(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
+                              _ptr(bmx), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse, bmx
+
+
+def cce_backward(h, head: Head, targets, lse, g=None, mask=None, workspace=None, out=None):
+    """dh float32 [M, H] = g * d logp / d h (g = None means all ones)."""
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    dh = _bwd_in(head, M, dev, lse, g, out)
     hs = head.c_struct()
     ws = _workspace(lib.cce_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
     _check(lib.cce_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
                             _ptr(dh), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return dh
+
+
+def cce_backward_ex(h, head: Head, targets, lse, g=None, mask=None, block_max=None, block_eps=0.0,
+                    filter_eps=0.0, workspace=None, out=None):
+    """dh with the opt-in skips (block_eps needs block_max from cce_forward_ex)."""
+    import torch
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    dh = _bwd_in(head, M, dev, lse, g, out)
+    if block_max is not None:
+        _expect(block_max, torch.float32, dev, (M, n_blocks(head)), "block_max")
+    hs = head.c_struct()
+    sk = cce_skip(float(block_eps), float(filter_eps))
+    ws = _workspace(lib.cce_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_backward_ex(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
+                               _ptr(block_max), ctypes.byref(sk), _ptr(dh), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(dev)))
     return dh
 
 

@@ -22,6 +22,7 @@ using namespace cce;
 constexpr int64_t MAX_H = 16384;
 constexpr int64_t MAX_M = (int64_t)1 << 24;
 constexpr size_t COEFF_BUDGET = (size_t)1 << 30;  // bytes of one coefficient chunk
+constexpr int64_t MAX_CHUNK_TILES = 2048;          // vocabulary tiles of one coefficient chunk
 
 thread_local char g_err[256];
 
@@ -83,10 +84,11 @@ struct Plan {
   // forward
   int nsplit, tiles_per_split, fwd_blocks, max_splits;
   // backward
-  int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: K steps per dh split
+  int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, fwd_bytes, bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, o_fl, fwd_bytes,
+      bwd_bytes;
 };
 
 cce_status check_head(const cce_head *hd) {
@@ -132,7 +134,9 @@ Plan make_plan(const cce_head *hd, int64_t M) {
 
   // backward: coefficient chunks of at most COEFF_BUDGET bytes
   const int64_t per_tile = p.M_pad * BNT * 2;
-  p.chunk_tiles = (int)std::max<int64_t>(1, std::min<int64_t>(p.tiles, (int64_t)COEFF_BUDGET / per_tile));
+  // (at most MAX_CHUNK_TILES: a dh split lists its flagged tiles in LDS)
+  p.chunk_tiles = (int)std::max<int64_t>(
+      1, std::min<int64_t>(std::min<int64_t>(p.tiles, MAX_CHUNK_TILES), (int64_t)COEFF_BUDGET / per_tile));
   p.nchunks = (int)cdiv(p.tiles, p.chunk_tiles);
   p.ld_coeff = (int64_t)p.chunk_tiles * BNT;
   p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(4, (int64_t)p.TT * p.chunk_tiles / (2 * cus)));
@@ -140,13 +144,12 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   // Vocabulary splits of the dh contraction: the fewest that fill whole rounds
   // of resident workgroups (one per CU) to >= 97%, else the best fill of up
   // to 8; each split adds one dh slab.
-  const int chunk_steps = p.chunk_tiles * (BNT / KSTEP);
   {
     const int64_t slots = cus;
     const int64_t base = (int64_t)p.TT * p.HT;
     int best = 1;
     double best_fill = 0.0;
-    for (int ks = 1; ks <= 8 && ks <= chunk_steps; ++ks) {
+    for (int ks = 1; ks <= 8 && ks <= p.chunk_tiles; ++ks) {
       const int64_t n = base * ks;
       const double fill = (double)n / (double)(cdiv(n, slots) * slots);
       if (fill > best_fill + 1e-9) {
@@ -157,8 +160,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     }
     p.ksplit = best;
   }
-  p.k_tiles = (int)cdiv(chunk_steps, p.ksplit);  // K steps per split
-  p.ksplit = (int)cdiv(chunk_steps, p.k_tiles);
+  p.k_tiles = (int)cdiv(p.chunk_tiles, p.ksplit);  // splits hold whole tiles
+  p.ksplit = (int)cdiv(p.chunk_tiles, p.k_tiles);
 
   size_t o = 0;
   p.o_cnt = o;  o = align_up(o + 256, 256);
@@ -175,7 +178,9 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_coeff = common;
   o = align_up(common + (size_t)2 * p.M_pad * p.ld_coeff, 256);
   p.o_dhp = o;
-  p.bwd_bytes = align_up(o + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
+  o = align_up(o + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
+  p.o_fl = o;  // pair flags of the skips: [TT][tiles] bytes
+  p.bwd_bytes = align_up(o + (size_t)p.TT * p.tiles, 256);
   return p;
 }
 
@@ -278,10 +283,18 @@ size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M) {
 cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                        const uint8_t *mask, float *logp, float *lse, void *workspace,
                        size_t workspace_bytes, void *stream) {
+  return cce_forward_ex(head, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                          const uint8_t *mask, float *logp, float *lse, float *block_max, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   cce_status s = check_common(head, h, M, targets, workspace);
   if (s != CCE_OK || M == 0) return s;
-  if (!logp || !lse || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3)) return CCE_ERR_INVALID_ARG;
+  if (!logp || !lse || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3) || ((uintptr_t)block_max & 3))
+    return CCE_ERR_INVALID_ARG;
   const Plan p = make_plan(head, M);
+  if (block_max && cdiv(p.tiles, 256) * M > INT32_MAX) return CCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.fwd_bytes) return CCE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
@@ -293,22 +306,45 @@ cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int
   a.range_tiles = p.tiles;
   a.nblocks = p.fwd_blocks;
   a.max_splits = p.max_splits;
+  a.bmx = block_max;
+  a.idx = ws_at<const int>(workspace, p.o_idx);
+  a.nbv = p.tiles;
   const dim3 grid((unsigned)(cdiv(a.nblocks, 8) * 8));
   CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, false, grid, a));
   CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.tiles, p.max_splits, (int)p.M_pad,
                                        ws_at<const int>(workspace, p.o_inv), a.cnt,
                                        ws_at<const TokRec>(workspace, p.o_tok), logp, lse));
+  if (block_max && mask)
+    CCE_LAUNCH("bmx_mask", st, launch_bmx_mask(st, (int)M, p.tiles, ws_at<const int>(workspace, p.o_inv), block_max));
   return hip_status();
 }
 
 cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                         const uint8_t *mask, const float *lse, const float *g, float *dh,
                         void *workspace, size_t workspace_bytes, void *stream) {
+  return cce_backward_ex(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, workspace, workspace_bytes,
+                         stream);
+}
+
+cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                           const uint8_t *mask, const float *lse, const float *g, const float *block_max,
+                           const cce_skip *skip, float *dh, void *workspace, size_t workspace_bytes,
+                           void *stream) {
   cce_status s = check_common(head, h, M, targets, workspace);
   if (s != CCE_OK || M == 0) return s;
   if (!lse || !dh || ((uintptr_t)lse & 3) || ((uintptr_t)dh & 3) || ((uintptr_t)g & 3))
     return CCE_ERR_INVALID_ARG;
+  float block_eps = 0.0f, filter_eps = 0.0f;
+  if (skip) {
+    block_eps = skip->block_eps;
+    filter_eps = skip->filter_eps;
+    if (!(block_eps >= 0.0f) || !std::isfinite(block_eps) || !(filter_eps >= 0.0f) || !std::isfinite(filter_eps))
+      return CCE_ERR_INVALID_ARG;
+    if (block_eps > 0.0f && (!block_max || ((uintptr_t)block_max & 3))) return CCE_ERR_INVALID_ARG;
+  }
   const Plan p = make_plan(head, M);
+  const bool use_fl = block_eps > 0.0f || filter_eps > 0.0f;
+  if (use_fl && cdiv(p.tiles, 64) * p.TT > INT32_MAX) return CCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.bwd_bytes) return CCE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
@@ -318,6 +354,14 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
   a.ld_coeff = p.ld_coeff;
   a.max_splits = 1 << 30;
+  uint8_t *fl = use_fl ? ws_at<uint8_t>(workspace, p.o_fl) : nullptr;
+  if (fl)
+    CCE_LAUNCH("warm", st, launch_warm(st, p.TT, p.tiles, a.cnt, ws_at<const int>(workspace, p.o_idx), a.tok,
+                                       block_max, p.tiles, block_eps > 0.0f ? std::log(block_eps) : 0.0f,
+                                       block_eps > 0.0f ? 1 : 0, fl));
+  a.fl = fl;
+  a.fl_ld = p.tiles;
+  a.filter_eps = filter_eps;
 
   GemmArgs ga{};
   ga.coeff = a.coeff;
@@ -337,6 +381,8 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
   ga.HT = p.HT;
   ga.ksplit = p.ksplit;
   ga.nblocks = p.TT * p.HT * p.ksplit;
+  ga.fl = fl;
+  ga.fl_ld = p.tiles;
   const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
 
   for (int c = 0; c < p.nchunks; ++c) {
@@ -348,6 +394,7 @@ cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const in
     const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
     CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, true, g1, a));
     ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_tile0 = t0;
     ga.chunk_steps = nt * (BNT / KSTEP);
     ga.accumulate = c > 0;
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));

@@ -127,6 +127,18 @@ struct TileArgs {
   int nblocks;           // launched work ids (the split per active token tile is derived on the device)
   int max_splits;        // forward: capacity of the partial buffer in splits per token
   float cap, inv_cap;
+  // forward, optional: block_max[idx[r]][tile] = largest softcapped logit of
+  // vocabulary tile `tile` for compacted row r (nbv = tiles per row)
+  float *bmx;
+  const int *idx;
+  int64_t nbv;
+  // backward, optional: fl[tt * fl_ld + tile] = 1 while the (token tile,
+  // vocabulary tile) pair is needed; cold pairs (0) are not computed, and the
+  // coefficient filter clears the pairs whose non-target |coefficients| all
+  // stay below filter_eps (0 = no filter)
+  uint8_t *fl;
+  int64_t fl_ld;
+  float filter_eps;
 };
 
 struct GemmArgs {
@@ -144,6 +156,11 @@ struct GemmArgs {
   int max_chunk_steps;   // K steps of a full chunk (fixes the split across chunks)
   int TT, HT, ksplit, nblocks;  // ksplit: slab capacity in units of all TT token tiles
   int accumulate;
+  // optional pair flags of the skips (as in TileArgs): a split contracts only
+  // the vocabulary tiles whose flag is set for its token tile
+  const uint8_t *fl;
+  int64_t fl_ld;
+  int chunk_tile0;       // first vocabulary tile of the chunk
 };
 
 // Raw buffer resource over [base, base + bytes): a lane whose byte offset is
@@ -179,10 +196,13 @@ __device__ __forceinline__ int splits_for(int nblocks, int act, int units, int c
 // K splits of the dh contraction for act active token tiles: as many as the
 // launched workgroups allow, bounded by the slab capacity (ks * act <=
 // ksplit * TT, the slabs being laid out over the active rows only).
+// Splits hold whole vocabulary tiles (4 K steps each; chunk_steps is a
+// multiple of 4), so that a split can leave out the cold tiles of the skips.
 __device__ __forceinline__ void dh_split(const GemmArgs &a, int act, int &ks, int &steps_per) {
   const int cap = a.ksplit * a.TT / (act > 0 ? act : 1);
-  ks = splits_for(a.nblocks / a.HT, act, a.max_chunk_steps, cap);
-  steps_per = (a.max_chunk_steps + ks - 1) / ks;
+  const int tiles = a.max_chunk_steps >> 2;
+  ks = splits_for(a.nblocks / a.HT, act, tiles, cap);
+  steps_per = 4 * ((tiles + ks - 1) / ks);
 }
 
 // Linear block id -> work id, so that consecutive work ids share an XCD
@@ -225,6 +245,9 @@ void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const
 void launch_head_prep(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G, int Kb,
                       int NB, uint8_t *baug, float *rt, float *slast);
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
+void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
+                 const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl);
+void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *bmx);
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
                   const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);

@@ -24,6 +24,9 @@ namespace cce {
 // Reads are raw buffer loads (rows past V read as zeros), so the step has no
 // per-lane predicate.  Each split owns its fp32 slab: no atomics, and a
 // repeated call gives identical bits.
+// SKIP (second instantiation): the split contracts only the vocabulary tiles
+// of its range whose pair flag is set for its token tile; their K steps are
+// listed in LDS first, in order.
 
 constexpr int DTW = 256;       // dh columns per workgroup
 constexpr int KSTP = 64;       // vocabulary rows per K step
@@ -99,7 +102,9 @@ struct DhProducer {
   }
 };
 
-template <int BITS>
+constexpr int MAX_LIST = 2048;  // vocabulary tiles per split (a chunk holds at most 2048)
+
+template <int BITS, bool SKIP>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only;
@@ -113,7 +118,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int ks_ = bid / (a.HT * act);
   const int d0 = dt * DTW;
   const int step0 = ks_ * steps_per;
-  const int nsteps = min(steps_per, a.chunk_steps - step0);
+  int nsteps = min(steps_per, a.chunk_steps - step0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tg = wave & 3, dh = wave >> 2;
@@ -121,6 +126,43 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * KSTP];
   __shared__ __attribute__((aligned(16))) float sSB[2][4 * KSTP * 2];
+  __shared__ uint16_t sList[SKIP ? MAX_LIST : 1];
+  __shared__ int sCount[SKIP ? 9 : 1];
+
+  if (SKIP) {
+    // flagged tiles of [step0 / 4, (step0 + nsteps) / 4), compacted in order:
+    // thread i owns tiles 4i .. 4i+3 of the range, counts them, and a
+    // workgroup scan (waves, then across the 8 wave totals) places them
+    const int t0 = step0 >> 2, nt = nsteps > 0 ? nsteps >> 2 : 0;
+    const uint8_t *frow = a.fl + (int64_t)tt * a.fl_ld + a.chunk_tile0 + t0;
+    int mine = 0;
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * tid + j;
+      mine += (t < nt && frow[t] != 0) ? 1 : 0;
+    }
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) sCount[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += sCount[w];
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 8; ++w) tot += sCount[w];
+      sCount[8] = tot;
+    }
+    int pos = base + incl - mine;
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * tid + j;
+      if (t < nt && frow[t] != 0) sList[pos++] = (uint16_t)(t0 + t);
+    }
+    __syncthreads();
+    nsteps = 4 * sCount[8];
+  }
 
   const int tok0 = tt * BM + tg * 64;
   // fragment-major coefficients of the workgroup's 256 tokens: one 1 KiB block
@@ -154,10 +196,16 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     for (int ks = 0; ks < 4; ++ks) boff[ks] = dswz(dh * 128 + l32, 2 * ks + lh);
     bf16x8_t cA[2][4];
     float sc[8], bi[8];
+    // chunk K step of step i of this split (past the end: the last one)
+    auto cstep = [&](int i) {
+      if (!SKIP) return step0 + i;
+      const int c = i < nsteps ? i : nsteps - 1;
+      return 4 * (int)sList[c >> 2] + (c & 3);
+    };
     // vocabulary row of step i of this split
-    auto vrow = [&](int i) { return a.chunk_v0 + (int64_t)(step0 + i) * KSTP; };
+    auto vrow = [&](int i) { return a.chunk_v0 + (int64_t)cstep(i) * KSTP; };
     // K offset (bytes) of step i in the fragment-major chunk
-    auto koff = [&](int i) { return (step0 + i) * 4 * 1024; };
+    auto koff = [&](int i) { return cstep(i) * 4 * 1024; };
 
     pr.load(a, vrow(0), P0);
     pr.load(a, vrow(1), P1);
@@ -232,10 +280,14 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 }
 
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
-  if (bits == 4)
-    hipLaunchKernelGGL(k_dh<4>, grid, dim3(TW), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_dh<8>, grid, dim3(TW), 0, st, a);
+  const bool skip = a.fl != nullptr;
+  if (bits == 4) {
+    if (skip) hipLaunchKernelGGL((k_dh<4, true>), grid, dim3(TW), 0, st, a);
+    else hipLaunchKernelGGL((k_dh<4, false>), grid, dim3(TW), 0, st, a);
+  } else {
+    if (skip) hipLaunchKernelGGL((k_dh<8, true>), grid, dim3(TW), 0, st, a);
+    else hipLaunchKernelGGL((k_dh<8, false>), grid, dim3(TW), 0, st, a);
+  }
 }
 
 }  // namespace cce

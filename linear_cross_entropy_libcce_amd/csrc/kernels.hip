@@ -170,6 +170,53 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, i
 }
 
 // ---------------------------------------------------------------------------
+// Pair flags of the backward skips (page "mlx-bun 0.0.4 -> 0.0.6",
+// src/train/flash-cce.ts, the block early exit of the backward kernels): the
+// (token tile tt, vocabulary tile b) pair is needed unless, for every
+// supervised token of the tile, block_max - lse < log(eps) and the target is
+// outside the tile.  block_on = 0 marks every pair needed (filter only).
+// Workgroup: one token tile x 64 vocabulary tiles; thread (b = tid % 64,
+// quarter = tid / 64) scans every fourth token of the tile, the quarters are
+// OR-ed through LDS.  Reads of block_max are 64 consecutive floats per wave.
+__global__ void __launch_bounds__(256) k_warm(const int *cnt, const int *idx, const TokRec *tok, const float *bmx,
+                                              int64_t nbv, int64_t tiles, float log_eps, int block_on, uint8_t *fl) {
+  __shared__ int sW[4][64];
+  const int64_t nbc = (tiles + 63) / 64;
+  const int tt = (int)(blockIdx.x / nbc);
+  const int n = cnt[0];
+  if (tt * BM >= n) return;
+  const int bl = threadIdx.x & 63, qt = threadIdx.x >> 6;
+  const int64_t b = (int64_t)(blockIdx.x % nbc) * 64 + bl;
+  int warm = block_on ? 0 : 1;
+  if (block_on && b < tiles) {
+    const int64_t lo = b * BNT;
+    for (int j = qt; j < BM; j += 4) {
+      const int r = tt * BM + j;
+      if (r >= n) break;
+      const TokRec rec = tok[r];
+      const bool hot = bmx[(int64_t)idx[r] * nbv + b] - rec.lse >= log_eps;
+      const bool holds = rec.tgt >= lo && rec.tgt < lo + BNT;
+      if (hot || holds) {
+        warm = 1;
+        break;
+      }
+    }
+  }
+  sW[qt][bl] = warm;
+  __syncthreads();
+  if (qt == 0 && b < tiles)
+    fl[(int64_t)tt * tiles + b] = (uint8_t)(sW[0][bl] | sW[1][bl] | sW[2][bl] | sW[3][bl]);
+}
+
+// block_max rows of masked tokens are 0.
+__global__ void __launch_bounds__(256) k_bmx_mask(int64_t nbv, const int *inv, float *bmx) {
+  const int64_t nbc = (nbv + 255) / 256;
+  const int t = (int)(blockIdx.x / nbc);
+  const int64_t b = (int64_t)(blockIdx.x % nbc) * 256 + threadIdx.x;
+  if (b < nbv && inv[t] < 0) bmx[(int64_t)t * nbv + b] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
 // dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
 // zero rows for masked tokens.
 template <int BITS>
@@ -221,6 +268,17 @@ void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int til
                   const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, part, nblocks, tiles, max_splits,
                      M_pad, inv, cnt, tok, M, logp, lse);
+}
+
+void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
+                 const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl) {
+  const dim3 grid((unsigned)(((tiles + 63) / 64) * TT));
+  hipLaunchKernelGGL(k_warm, grid, dim3(256), 0, st, cnt, idx, tok, bmx, nbv, tiles, log_eps, block_on, fl);
+}
+
+void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *bmx) {
+  const dim3 grid((unsigned)(((nbv + 255) / 256) * M));
+  hipLaunchKernelGGL(k_bmx_mask, grid, dim3(256), 0, st, nbv, inv, bmx);
 }
 
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,

@@ -31,6 +31,14 @@ namespace cce {
 // once per call (k_head_prep); the bias block runs first with ratio 1 in
 // units of the row's fixed-point unit, and a scale of exactly 0 is replaced by
 // 1e-30, whose contribution is nil.
+//
+// EXTRA (a second instantiation, so the plain passes carry none of it):
+//  * forward: the largest logit of every (token, vocabulary tile), written to
+//    block_max after the softcap (monotonic, so the max commutes with it);
+//  * backward: the (token tile, vocabulary tile) pairs whose flag is clear
+//    are skipped (no MFMA work, no coefficients), and with a filter the flag
+//    of a computed pair is cleared when all its non-target |coefficients|
+//    are below filter_eps.  The dh contraction reads the same flags.
 
 constexpr int ZROW = 36;  // padded fp32 row stride of the per-wave transpose scratch (32 columns)
 constexpr float LOG2E = 1.4426950408889634f;
@@ -111,7 +119,7 @@ __device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) 
   return cap * th;
 }
 
-template <int BITS, int MODE>
+template <int BITS, int MODE, bool EXTRA>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -132,6 +140,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KSTEP];
   __shared__ __attribute__((aligned(16))) float sR[2][BNT];
   __shared__ __attribute__((aligned(16))) float sZ[8][64 * ZROW];
+  __shared__ float sX[2][BM];  // EXTRA: per-wave tile maxima, read after the step's barrier
 
   const int tok0 = tt * BM + tg * 64;
   const int vcol0 = vh * 128;  // this wave's first vocabulary row within the tile
@@ -154,7 +163,20 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const float c1 = -2.0f * LOG2E * a.inv_cap;  // t = exp2(|z| * c1)
   const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 * u / (1 + t))
 
-  const int total = (tile_end - tile_begin) * steps;
+  // EXTRA backward: walk the flagged tiles of the range only
+  const uint8_t *fl_row = (BWD && EXTRA) ? a.fl + (int64_t)tt * a.fl_ld + a.range_tile0 : nullptr;
+  auto next_tile = [&](int t) {
+    ++t;
+    if (BWD && EXTRA)
+      while (t < tile_end && fl_row[t] == 0) ++t;
+    return t;
+  };
+  int n_tiles = tile_end - tile_begin;
+  if (BWD && EXTRA) {
+    n_tiles = 0;
+    for (int t = tile_begin; t < tile_end; ++t) n_tiles += fl_row[t] != 0;
+  }
+  const int total = n_tiles * steps;
   if (total > 0) {
     Producer<BITS> pr;
     pr.row0 = wave * 32 + (lane >> 2);
@@ -171,14 +193,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     // step `n` (<= steps) steps after (tile, st)
     auto coords = [&](int tile, int st, int n, int64_t &v0, int &step) {
       int s2 = st + n, t2 = tile;
-      if (s2 >= steps) { s2 -= steps; ++t2; }
+      if (s2 >= steps) { s2 -= steps; t2 = next_tile(tile); }
       v0 = (int64_t)(a.range_tile0 + t2) * BNT;
       step = s2;
     };
+    const int first_tile = next_tile(tile_begin - 1);
     {
-      const int64_t v0 = (int64_t)(a.range_tile0 + tile_begin) * BNT;
+      const int64_t v0 = (int64_t)(a.range_tile0 + first_tile) * BNT;
       int64_t v1; int s1;
-      coords(tile_begin, 0, 1, v1, s1);
+      coords(first_tile, 0, 1, v1, s1);
       pr.load(a, v0, 0, P0);
       pr.load(a, v1, s1, P1);
 #pragma unroll
@@ -238,6 +261,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     auto epilogue = [&](int tile) {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile) * BNT;
       const bool full = v0 + BNT <= a.V;
+      float xm = BWD ? 0.0f : -INFINITY;  // EXTRA: max logit (forward) or max |coefficient| (backward)
       float sl[4];
       const rsrc_t rl = make_rsrc(a.slast + v0, (a.V - v0 < BNT ? a.V - v0 : BNT) * 4);
 #pragma unroll
@@ -273,6 +297,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               const float u = z[k] >= 0.0f ? t : 1.0f;
               const float e = __builtin_amdgcn_exp2f(c2 * u * __builtin_amdgcn_rcpf(1.0f + t));
               ssum += (k < nv) ? e : 0.0f;
+              if (EXTRA) xm = fmaxf(xm, (k < nv) ? z[k] : -INFINITY);
             }
             run_s += ssum;
           } else if (MODE == MODE_FWD) {
@@ -282,6 +307,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               z[k] = (k < nv) ? z[k] : -INFINITY;
               tmax = fmaxf(tmax, z[k]);
             }
+            if (EXTRA) xm = fmaxf(xm, tmax);
             const float mnew = fmaxf(run_m, tmax);
             if (mnew != -INFINITY) {
               const float mb = mnew * LOG2E;
@@ -306,6 +332,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
                 if (a.cap > 0.0f) y = cap_d(z[k + u], c1, a.cap, dc);
                 const float val = -g_t * __builtin_amdgcn_exp2f(fmaf(y, LOG2E, -lse2)) * dc;
                 cv[u] = (k + u < nv && k + u != tk) ? val : 0.0f;
+                if (EXTRA) xm = fmaxf(xm, fabsf(cv[u]));
               }
               pk[k / 2] = pack_rne(cv[0], cv[1]);
             }
@@ -319,6 +346,35 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      if (EXTRA) {
+        if (BWD) {
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) xm = fmaxf(xm, __shfl_xor(xm, o, 64));
+          if (lane == 0) sX[0][wave] = xm;
+        } else {
+          sX[vh][tg * 64 + lane] = xm;
+        }
+      }
+    };
+
+    // EXTRA, after the barrier that follows the epilogue of `tile`: combine
+    // the waves' maxima of the tile (the next epilogue that rewrites sX is at
+    // least one more barrier away).
+    auto tile_extra = [&](int tile) {
+      if (!BWD) {
+        const int r = tok0 + lane;
+        if (vh == 0 && r < a.cnt[0]) {
+          const float m = fmaxf(sX[0][tg * 64 + lane], sX[1][tg * 64 + lane]);
+          float dc;
+          const float y = (a.cap > 0.0f) ? cap_d(m, c1, a.cap, dc) : m;
+          a.bmx[(int64_t)a.idx[r] * a.nbv + a.range_tile0 + tile] = y;
+        }
+      } else if (a.filter_eps > 0.0f && tid == 0) {
+        float m = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) m = fmaxf(m, sX[0][w]);
+        if (m < a.filter_eps) a.fl[(int64_t)tt * a.fl_ld + a.range_tile0 + tile] = 0;
       }
     };
 
@@ -340,11 +396,12 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       mfma_step(idx & 1, sn, vnn, snn, cur, nxt);
       if (st == steps - 1) epilogue(tile);
       __syncthreads();
+      if (EXTRA && st == steps - 1) tile_extra(tile);
     };
 
-    int st = 0, tile = tile_begin;
+    int st = 0, tile = first_tile;
     auto advance = [&]() {
-      if (++st == steps) { st = 0; ++tile; }
+      if (++st == steps) { st = 0; tile = next_tile(tile); }
     };
     int idx = 0;
     for (; idx + 1 < total; idx += 2) {
@@ -432,7 +489,12 @@ void launch_head_prep(hipStream_t st, int bits, const float *biases, const float
 
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
   const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
-#define CCE_TILE(B, MD) hipLaunchKernelGGL((k_tile<B, MD>), grid, dim3(TW), 0, st, a)
+  const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
+#define CCE_TILE(B, MD)                                                          \
+  do {                                                                           \
+    if (extra) hipLaunchKernelGGL((k_tile<B, MD, true>), grid, dim3(TW), 0, st, a); \
+    else hipLaunchKernelGGL((k_tile<B, MD, false>), grid, dim3(TW), 0, st, a);      \
+  } while (0)
   if (bits == 4) {
     if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(4, MODE_FWD_CAP);

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 1
+    assert lib.cce_abi_version() == 2
 
 
 def head(**kw):
@@ -96,6 +96,30 @@ def test_bad_token_arguments_are_rejected(lib):
                             None) == cce.CCE_ERR_INVALID_ARG   # misaligned g
     assert lib.cce_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x100000, bneed - 256,
                             None) == cce.CCE_ERR_WORKSPACE
+
+
+def bwd_ex(lib, hd, block_max=None, skip=None, ws=0x100000, nbytes=None):
+    if nbytes is None:
+        nbytes = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 4)
+    sk = None if skip is None else ctypes.byref(cce.cce_skip(*skip))
+    return lib.cce_backward_ex(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, block_max, sk, 0x8000,
+                               ws, nbytes, None)
+
+
+def test_bad_skip_arguments_are_rejected(lib):
+    hd = head()
+    for sk in [(-1.0, 0.0), (0.0, -1e-5), (float("nan"), 0.0), (0.0, float("inf"))]:
+        assert bwd_ex(lib, hd, block_max=0xA000, skip=sk) == cce.CCE_ERR_INVALID_ARG, sk
+    # the block skip needs block_max (4-byte aligned); the filter alone does not
+    assert bwd_ex(lib, hd, block_max=None, skip=(1e-5, 0.0)) == cce.CCE_ERR_INVALID_ARG
+    assert bwd_ex(lib, hd, block_max=0xA002, skip=(1e-5, 0.0)) == cce.CCE_ERR_INVALID_ARG
+    need = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 4)
+    assert bwd_ex(lib, hd, skip=(0.0, 1e-5), nbytes=need - 256) == cce.CCE_ERR_WORKSPACE
+    # the forward's block_max must be 4-byte aligned
+    assert lib.cce_forward_ex(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x6000, 0x7000, 0xA002, 0x100000,
+                              1 << 40, None) == cce.CCE_ERR_INVALID_ARG
+    assert lib.cce_forward_ex(ctypes.byref(hd), 0x4000, 0, 0, None, 0x6000, 0x7000, 0xA000, 0x100000,
+                              1 << 40, None) == cce.CCE_OK    # M = 0
 
 
 def test_profile_api_without_launches(lib):
