@@ -200,7 +200,8 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     auto cstep = [&](int i) {
       if (!SKIP) return step0 + i;
       const int c = i < nsteps ? i : nsteps - 1;
-      return 4 * (int)sList[c >> 2] + (c & 3);
+      // the list entry is the same for every lane: keep it scalar (it forms buffer bases)
+      return 4 * __builtin_amdgcn_readfirstlane((int)sList[c >> 2]) + (c & 3);
     };
     // vocabulary row of step i of this split
     auto vrow = [&](int i) { return a.chunk_v0 + (int64_t)cstep(i) * KSTP; };

@@ -116,18 +116,19 @@ BLOCK_V = 256
 TOKEN_TILE = 256
 
 
-def dequantize(inp: dict) -> np.ndarray:
+def dequantize(inp: dict, v0: int = 0, v1: Optional[int] = None) -> np.ndarray:
     """W[v][d] = scale * q + bias in fp64 from the packed words (little-endian
-    codes within each uint32, per-group scale and bias)."""
+    codes within each uint32, per-group scale and bias), rows [v0, v1)."""
     bits, group = int(inp["bits"]), int(inp["group"])
-    wq = np.asarray(inp["wq"], dtype=np.uint32)
+    v1 = int(inp["V"]) if v1 is None else v1
+    wq = np.asarray(inp["wq"], dtype=np.uint32)[v0:v1]
     V, wpr = wq.shape
     per = 32 // bits
     shifts = (np.arange(per, dtype=np.uint32) * bits).astype(np.uint32)
     q = (wq[:, :, None] >> shifts[None, None, :]) & np.uint32((1 << bits) - 1)
     q = q.reshape(V, wpr * per).astype(np.float64)
-    s = np.repeat(np.asarray(inp["scales"], np.float64), group, axis=1)
-    b = np.repeat(np.asarray(inp["biases"], np.float64), group, axis=1)
+    s = np.repeat(np.asarray(inp["scales"][v0:v1], np.float64), group, axis=1)
+    b = np.repeat(np.asarray(inp["biases"][v0:v1], np.float64), group, axis=1)
     return s * q + b
 
 
@@ -167,12 +168,33 @@ def dense(inp: dict, g: Optional[np.ndarray] = None, softcap: Optional[float] = 
                 t_in=t_in, block_max=bmax)
 
 
-def block_max(inp: dict, softcap: Optional[float] = None) -> np.ndarray:
+def block_max(inp: dict, softcap: Optional[float] = None, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
     """[M, ceil(V/BLOCK_V)] largest softcapped logit per vocabulary block of
-    each token; rows of masked tokens are 0."""
-    d = dense(inp, softcap=softcap)
-    out = np.zeros((int(inp["M"]), d["block_max"].shape[1]))
-    out[d["act"]] = d["block_max"]
+    each token; rows of masked tokens are 0.  With `tokens`, only those rows
+    ([len(tokens), n_blocks]), computed over the head in row chunks so that a
+    full-size head fits in memory."""
+    if tokens is None:
+        d = dense(inp, softcap=softcap)
+        out = np.zeros((int(inp["M"]), d["block_max"].shape[1]))
+        out[d["act"]] = d["block_max"]
+        return out
+    V = int(inp["V"])
+    cap = float(inp["softcap"] if softcap is None else softcap)
+    tok = np.asarray(tokens, np.int64)
+    hb = np.asarray(inp["h"], dtype=np.uint16)[tok]
+    hd = (hb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nb = (V + BLOCK_V - 1) // BLOCK_V
+    out = np.zeros((len(tok), nb))
+    step = 64 * BLOCK_V
+    for v0 in range(0, V, step):
+        v1 = min(V, v0 + step)
+        z = hd @ dequantize(inp, v0, v1).T
+        y = cap * np.tanh(z / cap) if cap > 0 else z
+        for b in range(v0 // BLOCK_V, (v1 + BLOCK_V - 1) // BLOCK_V):
+            out[:, b] = y[:, b * BLOCK_V - v0:min(v1, (b + 1) * BLOCK_V) - v0].max(axis=1)
+    mk = inp.get("mask")
+    if mk is not None:
+        out[np.asarray(mk)[tok] == 0] = 0.0
     return out
 
 

@@ -213,3 +213,24 @@ def test_skip_rule_mutants(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, "mutant survived: " + name
+
+
+def test_sampled_block_max_matches_dense():
+    # the row-chunked path (used at full size) against the dense one: catches a
+    # block cut wrong at a chunk boundary (V = 20000 is ragged against both the
+    # 16384-row chunks and the 256-row blocks) and masked rows left non-zero
+    d = syn.make_custom(300, 128, 20000, 8, 3, boost_rows=128, boost=8.0, targets="zipf", mask="random",
+                        mask_frac=0.3, softcap=20.0)
+    rows = [0, 5, 7, 150, 299]
+    full = oracle.block_max(d)
+    part = oracle.block_max(d, tokens=rows)
+    assert part.shape == (len(rows), (20000 + 255) // 256)
+    assert np.array_equal(full[rows], part)
+    # a block's maximum is attained by one of its rows: the largest softcapped
+    # logit read straight off the dense logits of the plain definition
+    y = oracle.dense(d)["y"]
+    act = np.flatnonzero(d["mask"] != 0)
+    r = int(np.searchsorted(act, 150))
+    assert act[r] == 150 or d["mask"][150] == 0
+    if d["mask"][150] != 0:
+        np.testing.assert_allclose(full[150, 78], y[r, 78 * 256:20000].max(), rtol=0, atol=0)

@@ -133,3 +133,40 @@ def test_tiny_eps_keeps_exact_tolerance(torch_cuda):
     rel = np.linalg.norm(gdh - exact) / np.linalg.norm(exact)
     say("eps 1e-5: GPU skip vs exact oracle %.3g" % rel)
     assert rel <= DH_TOL
+
+
+def test_peaked_workload_full_size(torch_cuda):
+    # the full-size peaked workload in bench's launch configuration: exact
+    # forward/backward within the head's tolerances on sampled tokens, block
+    # maxima on those tokens, and the skipped backward at the pages' eps
+    # (1e-5, 1e-5) within the exact dh tolerance
+    cfg = 5
+    w = syn.WORKLOADS[cfg]
+    say("workload %d (%s): generating inputs" % (cfg, w.name))
+    inp = syn.make_inputs(w, syn.seed_for(cfg))
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    say("workload %d: GPU forward with block maxima, exact and skipped backward" % cfg)
+    logp, lse, bmx = cce.cce_forward_ex(h, head, t, m, block_max=True)
+    dh_exact = cce.cce_backward(h, head, t, lse, None, m)
+    dh_skip = cce.cce_backward_ex(h, head, t, lse, None, m, block_max=bmx, block_eps=1e-5, filter_eps=1e-5)
+    torch_cuda.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    rows = np.array(sorted({0, inp["M"] - 1, inp["M"] // 2} | set(rng.choice(inp["M"], 5, replace=False).tolist())))
+    say("workload %d: oracle on %d sampled tokens" % (cfg, len(rows)))
+    ologp, olse, odh = oracle.cce(inp, tokens=rows)
+    glogp = logp.cpu().numpy()[rows].astype(np.float64)
+    glse = lse.cpu().numpy()[rows].astype(np.float64)
+    assert np.abs(glogp - ologp).max() <= 5e-3 and np.abs(glse - olse).max() <= 5e-3
+    ge = dh_exact.cpu().numpy()[rows].astype(np.float64)
+    gs = dh_skip.cpu().numpy()[rows].astype(np.float64)
+    rel_e = np.linalg.norm(ge - odh) / np.linalg.norm(odh)
+    rel_s = np.linalg.norm(gs - odh) / np.linalg.norm(odh)
+    say("workload %d: dh rel L2 exact %.3g, skipped %.3g" % (cfg, rel_e, rel_s))
+    assert rel_e <= DH_TOL and rel_s <= DH_TOL
+    say("workload %d: oracle block maxima of the sampled tokens" % cfg)
+    ob = oracle.block_max(inp, tokens=rows)
+    gb = bmx.cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(gb - ob).max()
+    say("workload %d: max|d block_max| = %.3g" % (cfg, err))
+    assert err <= LOGIT_TOL
