@@ -210,22 +210,40 @@ T *ws_at(void *ws, size_t off) {
 }
 
 // compaction, augmented rows and token records, target logits
-void launch_front(const Plan &p, const cce_head *hd, const void *h, const int32_t *targets,
-                  const uint8_t *mask, const float *lse, const float *g, void *ws, hipStream_t st,
-                  bool bwd) {
+void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32_t *targets,
+                   const uint8_t *mask, const float *lse, const float *g, void *ws, hipStream_t st,
+                   bool bwd) {
   int *cnt = ws_at<int>(ws, p.o_cnt);
   int *idx = ws_at<int>(ws, p.o_idx);
   int *inv = ws_at<int>(ws, p.o_inv);
   TokRec *tok = ws_at<TokRec>(ws, p.o_tok);
   uint16_t *haug = ws_at<uint16_t>(ws, p.o_haug);
   CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
-  CCE_LAUNCH("prep", st, launch_prep(st, (int)p.M_pad, (const uint16_t *)h, (int)p.H, p.G, p.Kb, p.Ka, idx, targets,
-                                     lse, g, tok, haug));
-  CCE_LAUNCH("head_prep", st, launch_head_prep(st, p.bits, hd->biases, hd->scales, p.V, p.G, p.Kb, p.NB,
-                                               ws_at<uint8_t>(ws, p.o_baug), ws_at<float>(ws, p.o_rt),
-                                               ws_at<float>(ws, p.o_slast)));
-  CCE_LAUNCH("target", st, launch_target(st, p.bits, (int)p.M_pad, (const uint16_t *)h, idx, (int)p.H, p.G, hd->wq,
-                                         p.wpr, hd->scales, hd->biases, p.V, p.cap, cnt, tok, bwd ? 1 : 0));
+  FrontArgs f{};
+  f.h = (const uint16_t *)h;
+  f.idx = idx;
+  f.targets = targets;
+  f.lse = lse;
+  f.g = g;
+  f.wq = hd->wq;
+  f.scales = hd->scales;
+  f.biases = hd->biases;
+  f.tok = tok;
+  f.haug = haug;
+  f.baug = ws_at<uint8_t>(ws, p.o_baug);
+  f.rt = ws_at<float>(ws, p.o_rt);
+  f.slast = ws_at<float>(ws, p.o_slast);
+  f.V = p.V;
+  f.H = (int)p.H;
+  f.G = p.G;
+  f.Kb = p.Kb;
+  f.Ka = p.Ka;
+  f.NB = p.NB;
+  f.wpr = p.wpr;
+  f.M_pad = (int)p.M_pad;
+  f.cap = p.cap;
+  f.bwd = bwd ? 1 : 0;
+  CCE_LAUNCH("front", st, launch_front(st, p.bits, f));
 }
 
 TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
@@ -299,7 +317,7 @@ cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
 
-  launch_front(p, head, h, targets, mask, nullptr, nullptr, workspace, st, false);
+  enqueue_front(p, head, h, targets, mask, nullptr, nullptr, workspace, st, false);
   TileArgs a = tile_args(p, head, workspace);
   a.part = ws_at<float>(workspace, p.o_part);
   a.range_tile0 = 0;
@@ -349,7 +367,7 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
 
-  launch_front(p, head, h, targets, mask, lse, g, workspace, st, true);
+  enqueue_front(p, head, h, targets, mask, lse, g, workspace, st, true);
   TileArgs a = tile_args(p, head, workspace);
   a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
   a.ld_coeff = p.ld_coeff;

@@ -141,6 +141,24 @@ struct TileArgs {
   float filter_eps;
 };
 
+// Arguments of the front launch (token rows, target logit, head side).
+struct FrontArgs {
+  const uint16_t *h;       // [M][H] bf16
+  const int *idx;          // [M_pad] compacted row -> token (-1: padding)
+  const int32_t *targets;
+  const float *lse, *g;    // backward only (lse NULL in the forward)
+  const uint32_t *wq;
+  const float *scales, *biases;
+  TokRec *tok;
+  uint16_t *haug;
+  uint8_t *baug;           // head side: bias-block digits, fold ratios, last scale
+  float *rt, *slast;
+  int64_t V;
+  int H, G, Kb, Ka, NB, wpr, M_pad;
+  float cap;
+  int bwd;
+};
+
 struct GemmArgs {
   const uint16_t *coeff;  // fragment-major [M_pad][16 * ksv] bf16 coefficient chunk
   int64_t ksv;            // K blocks of 16 vocabulary rows per 32-token row block of the chunk
@@ -237,13 +255,7 @@ __device__ __forceinline__ float softcap_d(float z, float cap, float inv_cap, fl
 
 // Launch entry points of the kernel translation units (host side).
 void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt);
-void launch_prep(hipStream_t st, int M_pad, const uint16_t *h, int H, int G, int Kb, int Ka, const int *idx,
-                 const int32_t *targets, const float *lse, const float *g, TokRec *tok, uint16_t *haug);
-void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const int *idx, int H, int G,
-                   const uint32_t *wq, int wpr, const float *scales, const float *biases, int64_t V, float cap,
-                   const int *cnt, TokRec *tok, int bwd);
-void launch_head_prep(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G, int Kb,
-                      int NB, uint8_t *baug, float *rt, float *slast);
+void launch_front(hipStream_t st, int bits, const FrontArgs &f);
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
                  const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl);

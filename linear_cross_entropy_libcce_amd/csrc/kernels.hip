@@ -41,33 +41,120 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 }
 
 // ---------------------------------------------------------------------------
-// Per compacted row r: gather h, write the augmented row [bias block | h] in
-// fragment-major layout, and the token record.  Bias block column kk
-// (part = kk / G, gi = kk % G): part 0 -> 256 S_hi[gi], 1 -> 256 S_lo[gi],
-// 2 -> S_hi[gi], else 0, with S = per-group sum of h split into bf16 hi + lo
-// (the head side holds the matching fixed-point digits of the biases).  h rows
-// are 16-byte aligned.
-__global__ void __launch_bounds__(256) k_prep(const uint16_t *h, int H, int G, int Kb, int Ka,
-                                              const int *idx, const int32_t *targets,
-                                              const float *lse, const float *g, TokRec *tok,
-                                              uint16_t *haug) {
-  __shared__ float sS[MAX_G];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int src = idx[r];
-  const int64_t ks16 = Ka / 16;
-  const int nch = H / 8;  // 16-byte chunks of the h part; 8 per group
-  for (int c = tid; c < nch; c += 256) {
-    const u32x4_t x = (src >= 0) ? *(const u32x4_t *)(h + (size_t)src * H + 8 * c) : u32x4_t{0, 0, 0, 0};
-    *(u32x4_t *)(haug + frag_slot(r, Kb / 8 + c, ks16)) = x;
-    float part = 0.0f;
+// The front of every call, one launch (after the compaction):
+//
+// Workgroups [0, M_pad): compacted row r.  Gather h, write the augmented row
+// [bias block | h] in fragment-major layout and the token record, and the
+// target logit in fp32 straight from the packed target row,
+// z = sum_g (s * sum_{d in g} h_d q_d + b * S_g): forward tval = c(z),
+// backward tval = g * (1 - exp(c(z) - lse)) * c'(z), the target column's
+// coefficient.  Bias block column kk (part = kk / G, gi = kk % G): part 0 ->
+// 256 S_hi[gi], 1 -> 256 S_lo[gi], 2 -> S_hi[gi], else 0, with S = per-group
+// sum of h split into bf16 hi + lo (the head side holds the matching
+// fixed-point digits of the biases).  h rows are 16-byte aligned.
+//
+// Workgroups [M_pad, M_pad + ceil(V / 64)): the head side, 64 rows each.
+// Per-call head preparation (the head is frozen, so this depends on the head
+// only):
+//
+// * Head side of the bias block.  The block carries sum_g b'[v][g] * S[t][g]
+//   (S the group sum of h) with b' = b + 128 s for 8-bit heads, whose codes
+//   the tile uses as q - 128, and b' = b for 4-bit heads.  Row v's b' is
+//   written in 16-bit fixed point, b' ~= u_v * n, u_v = max_g |b'| / 32639,
+//   n = 256 d1 + d0 with signed digits d1, d0 in [-128, 127] (exact in bf16),
+//   stored as bytes offset by 128.  Column kk of the block (part = kk / G,
+//   gi = kk % G) holds d1 for parts 0 and 1 and d0 for part 2, zero past 3G;
+//   the token side holds [256 S_hi, 256 S_lo, S_hi] (S split into bf16 hi +
+//   lo), so the block sums u_v^-1 * sum_g b' S up to the dropped d0 * S_lo
+//   term and the fixed-point rounding, both below 2^-16 of max|b'| * |S| per
+//   group.
+// * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
+//   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
+// One workgroup per 64 rows: each wave writes the digits of 16 rows (lanes
+// over the row's groups and block columns, coalesced), then the ratio table
+// is written with lanes over rows (coalesced) and the four waves over groups.
+__device__ void head_prep_block(int64_t blk, const float *biases, const float *scales, float shift, int64_t V, int G,
+                                int Kb, int NB, uint8_t *baug, float *rt, float *slast, float *su) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t v0 = blk * 64;
+  for (int i = 0; i < 16; ++i) {
+    const int rl = wave * 16 + i;
+    const int64_t v = v0 + rl;
+    if (v >= V) break;
+    const float *brow = biases + v * G;
+    const float *srow = scales + v * G;
+    float m = 0.0f;
+    for (int g = lane; g < G; g += 64) m = fmaxf(m, fabsf(fmaf(shift, srow[g], brow[g])));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part += bf16_to_f32(x[e] & 0xFFFFu) + bf16_to_f32(x[e] >> 16);
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float u = m / 32639.0f;
+    const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+    for (int kk = lane; kk < Kb; kk += 64) {
+      const int part = kk / G, gi = kk - part * G;
+      int digit = 0;
+      if (part < 3) {
+        const float b = fmaf(shift, srow[gi], brow[gi]);
+        const int n = (int)fminf(fmaxf(rintf(b * inv), -32639.0f), 32639.0f);
+        const int d1 = (n + 128) >> 8;  // floor((n + 128) / 256), in [-127, 127]
+        digit = (part == 2) ? n - 256 * d1 : d1;
+      }
+      baug[v * Kb + kk] = (uint8_t)(digit + 128);
+    }
+    if (lane == 0) su[rl] = u;
+  }
+  __syncthreads();
+  const int64_t v = v0 + lane;
+  if (v >= V) return;
+  const float *srow = scales + v * G;
+  for (int s2 = wave; s2 < NB; s2 += 4) rt[s2 * V + v] = 1.0f;
+  for (int g = wave; g < G; g += 4) {
+    const float prev = scale_eff(g == 0 ? su[lane] : srow[g - 1]);
+    rt[(NB + g) * V + v] = prev / scale_eff(srow[g]);
+  }
+  if (wave == 0) slast[v] = scale_eff(srow[G - 1]);
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256) k_front(FrontArgs f) {
+  __shared__ float sS[MAX_G];
+  __shared__ float sRed[4];
+  const int tid = threadIdx.x;
+  if (blockIdx.x >= (unsigned)f.M_pad) {
+    head_prep_block((int64_t)blockIdx.x - f.M_pad, f.biases, f.scales, BITS == 8 ? 128.0f : 0.0f, f.V, f.G, f.Kb,
+                    f.NB, f.baug, f.rt, f.slast, sS);
+    return;
+  }
+  const int r = blockIdx.x;
+  const int src = f.idx[r];
+  const int H = f.H, G = f.G, Kb = f.Kb;
+  const int64_t ks16 = f.Ka / 16;
+  const int nch = H / 8;  // 16-byte chunks of the h part; 8 per group
+  const int tgt = (src >= 0) ? f.targets[src] : -1;
+  const bool has_t = src >= 0 && tgt >= 0 && (int64_t)tgt < f.V;
+  const uint32_t *wrow = f.wq + (size_t)(has_t ? tgt : 0) * f.wpr;
+  float zpart = 0.0f;
+  for (int c = tid; c < nch; c += 256) {
+    const u32x4_t x = (src >= 0) ? *(const u32x4_t *)(f.h + (size_t)src * H + 8 * c) : u32x4_t{0, 0, 0, 0};
+    *(u32x4_t *)(f.haug + frag_slot(r, Kb / 8 + c, ks16)) = x;
+    float part = 0.0f, dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_to_f32(x[e] & 0xFFFFu), hi = bf16_to_f32(x[e] >> 16);
+      part += lo + hi;
+      if (has_t) dot += lo * (float)code_at<BITS>(wrow, 8 * c + 2 * e) + hi * (float)code_at<BITS>(wrow, 8 * c + 2 * e + 1);
+    }
+    if (has_t) {
+      const size_t gi = (size_t)tgt * G + (c >> 3);
+      zpart += f.scales[gi] * dot + f.biases[gi] * part;
+    }
     // the 8 chunks of one group sit in 8 consecutive lanes
     part += __shfl_xor(part, 1, 8);
     part += __shfl_xor(part, 2, 8);
     part += __shfl_xor(part, 4, 8);
     if ((c & 7) == 0) sS[c >> 3] = part;
   }
+  zpart = wave_sum(zpart);
+  if ((tid & 63) == 0) sRed[tid >> 6] = zpart;
   __syncthreads();
   for (int c = tid; c < Kb / 8; c += 256) {
     uint32_t o[4];
@@ -89,80 +176,64 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t *h, int H, int G, i
       }
       o[e] = pr2[0] | (pr2[1] << 16);
     }
-    *(u32x4_t *)(haug + frag_slot(r, c, ks16)) = u32x4_t{o[0], o[1], o[2], o[3]};
+    *(u32x4_t *)(f.haug + frag_slot(r, c, ks16)) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
   if (tid == 0) {
     TokRec rec;
-    rec.lse = (src >= 0 && lse) ? lse[src] : 0.0f;
-    rec.g = (src >= 0) ? (g ? g[src] : 1.0f) : 0.0f;
-    rec.tval = 0.0f;
-    rec.tgt = (src >= 0) ? targets[src] : -1;
-    tok[r] = rec;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Target logit of each compacted row, in fp32 straight from the packed row:
-// z = sum_g (s * sum_{d in g} h_d q_d + b * S_g).  One wave per row.
-// Forward: tval = c(z).  Backward: tval = g * (1 - exp(c(z) - lse)) * c'(z),
-// the target column's coefficient.
-template <int BITS>
-__global__ void __launch_bounds__(256) k_target(const uint16_t *h, const int *idx, int H, int G,
-                                                const uint32_t *wq, int wpr, const float *scales,
-                                                const float *biases, int64_t V, float cap,
-                                                const int *cnt, TokRec *tok, int M_pad, int bwd) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= M_pad) return;
-  const int tgt = tok[r].tgt;
-  float out = 0.0f;
-  if (r < cnt[0] && tgt >= 0 && (int64_t)tgt < V) {
-    float part = 0.0f;
-    const uint32_t *wrow = wq + (size_t)tgt * wpr;
-    const uint16_t *hrow = h + (size_t)idx[r] * H;
-    for (int gg = lane; gg < G; gg += 64) {
-      float A = 0.0f, S = 0.0f;
-      for (int d = gg * KSTEP; d < gg * KSTEP + KSTEP; ++d) {
-        const float x = bf16_to_f32(hrow[d]);
-        A += x * (float)code_at<BITS>(wrow, d);
-        S += x;
+    rec.lse = (src >= 0 && f.lse) ? f.lse[src] : 0.0f;
+    rec.g = (src >= 0) ? (f.g ? f.g[src] : 1.0f) : 0.0f;
+    rec.tgt = tgt;
+    float out = 0.0f;
+    if (has_t) {
+      const float z = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+      float y = z, dc = 1.0f;
+      if (f.cap > 0.0f) {
+        const float th = tanhf(z / f.cap);
+        y = f.cap * th;
+        dc = 1.0f - th * th;
       }
-      part += scales[(size_t)tgt * G + gg] * A + biases[(size_t)tgt * G + gg] * S;
+      out = f.bwd ? rec.g * -expm1f(y - rec.lse) * dc : y;
     }
-    const float z = wave_sum(part);
-    float y = z, dc = 1.0f;
-    if (cap > 0.0f) {
-      const float th = tanhf(z / cap);
-      y = cap * th;
-      dc = 1.0f - th * th;
-    }
-    out = bwd ? tok[r].g * -expm1f(y - tok[r].lse) * dc : y;
+    rec.tval = out;
+    f.tok[r] = rec;
   }
-  if (lane == 0) tok[r].tval = out;
 }
 
 // ---------------------------------------------------------------------------
 // Cross-split merge (page "mlx-bun 0.0.4 -> 0.0.6", flashCceForward's host
 // merge): lse = m* + log sum_s s_s exp(m_s - m*), logp = target logit - lse.
+// A group of L lanes per token (L the power of two >= the split count, at
+// most 64) reads the token's partials in parallel and reduces with shuffles;
+// one token per thread when there are few splits, a wave per token when a
+// few supervised tokens carry hundreds of splits.
 __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int tiles, int max_splits,
                                                int M_pad, const int *inv, const int *cnt, const TokRec *tok,
                                                int M, float *logp, float *lse) {
   // two partials (vocabulary halves of the tile) per split of the forward
   const int nsplit = 2 * splits_for(nblocks, active_tiles(cnt), tiles, max_splits);
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= M) return;
-  const int r = inv[t];
+  int L = 1;
+  while (L < nsplit && L < 64) L <<= 1;
+  const int per_block = 256 / L;
+  if (blockIdx.x * per_block >= M) return;  // the grid is sized for L = 64
+  const int t = blockIdx.x * per_block + threadIdx.x / L;
+  const int sl = threadIdx.x % L;
+  const int r = t < M ? inv[t] : -1;
+  float mx = -INFINITY;
+  if (r >= 0)
+    for (int s = sl; s < nsplit; s += L) mx = fmaxf(mx, part[((size_t)s * M_pad + r) * 2]);
+  for (int o = L >> 1; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, L));
+  float se = 0.0f;
+  if (r >= 0)
+    for (int s = sl; s < nsplit; s += L) {
+      const float m = part[((size_t)s * M_pad + r) * 2];
+      if (m != -INFINITY) se += part[((size_t)s * M_pad + r) * 2 + 1] * __expf(m - mx);
+    }
+  for (int o = L >> 1; o >= 1; o >>= 1) se += __shfl_xor(se, o, L);
+  if (t >= M || sl != 0) return;
   if (r < 0) {
     logp[t] = 0.0f;
     lse[t] = 0.0f;
     return;
-  }
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part[((size_t)s * M_pad + r) * 2]);
-  float se = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float m = part[((size_t)s * M_pad + r) * 2];
-    if (m != -INFINITY) se += part[((size_t)s * M_pad + r) * 2 + 1] * __expf(m - mx);
   }
   const float l = mx + logf(se);
   lse[t] = l;
@@ -246,27 +317,17 @@ void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, M, M_pad, idx, inv, cnt);
 }
 
-void launch_prep(hipStream_t st, int M_pad, const uint16_t *h, int H, int G, int Kb, int Ka, const int *idx,
-                 const int32_t *targets, const float *lse, const float *g, TokRec *tok, uint16_t *haug) {
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)M_pad), dim3(256), 0, st, h, H, G, Kb, Ka, idx, targets, lse, g, tok,
-                     haug);
-}
-
-void launch_target(hipStream_t st, int bits, int M_pad, const uint16_t *h, const int *idx, int H, int G,
-                   const uint32_t *wq, int wpr, const float *scales, const float *biases, int64_t V, float cap,
-                   const int *cnt, TokRec *tok, int bwd) {
-  const dim3 grid((unsigned)((M_pad + 3) / 4));
+void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
+  const dim3 grid((unsigned)(f.M_pad + (f.V + 63) / 64));
   if (bits == 4)
-    hipLaunchKernelGGL(k_target<4>, grid, dim3(256), 0, st, h, idx, H, G, wq, wpr, scales, biases, V, cap,
-                       cnt, tok, M_pad, bwd);
+    hipLaunchKernelGGL(k_front<4>, grid, dim3(256), 0, st, f);
   else
-    hipLaunchKernelGGL(k_target<8>, grid, dim3(256), 0, st, h, idx, H, G, wq, wpr, scales, biases, V, cap,
-                       cnt, tok, M_pad, bwd);
+    hipLaunchKernelGGL(k_front<8>, grid, dim3(256), 0, st, f);
 }
 
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
                   const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, part, nblocks, tiles, max_splits,
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, part, nblocks, tiles, max_splits,
                      M_pad, inv, cnt, tok, M, logp, lse);
 }
 

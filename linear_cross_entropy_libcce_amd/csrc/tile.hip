@@ -28,9 +28,9 @@ namespace cce {
 // the current group's scale, acc <- acc * (s_{g-1} / s_g) + A_g, so the MFMA
 // accumulates in place and the VALU does one multiply per element per group.
 // After the last group z = acc * s_last.  The ratios come from a table built
-// once per call (k_head_prep); the bias block runs first with ratio 1 in
-// units of the row's fixed-point unit, and a scale of exactly 0 is replaced by
-// 1e-30, whose contribution is nil.
+// once per call (the head side of the front launch); the bias block runs
+// first with ratio 1 in units of the row's fixed-point unit, and a scale of
+// exactly 0 is replaced by 1e-30, whose contribution is nil.
 //
 // EXTRA (a second instantiation, so the plain passes carry none of it):
 //  * forward: the largest logit of every (token, vocabulary tile), written to
@@ -418,73 +418,6 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     dst[0] = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
     dst[1] = run_s;
   }
-}
-
-// Per-call head preparation (the head is frozen, so this depends on the head
-// only):
-//
-// * Head side of the bias block.  The block carries sum_g b'[v][g] * S[t][g]
-//   (S the group sum of h) with b' = b + 128 s for 8-bit heads, whose codes
-//   the tile uses as q - 128, and b' = b for 4-bit heads.  Row v's b' is
-//   written in 16-bit fixed point, b' ~= u_v * n, u_v = max_g |b'| / 32639,
-//   n = 256 d1 + d0 with signed digits d1, d0 in [-128, 127] (exact in bf16),
-//   stored as bytes offset by 128.  Column kk of the block (part = kk / G,
-//   gi = kk % G) holds d1 for parts 0 and 1 and d0 for part 2, zero past 3G;
-//   the token side holds [256 S_hi, 256 S_lo, S_hi] (S split into bf16 hi +
-//   lo), so the block sums u_v^-1 * sum_g b' S up to the dropped d0 * S_lo
-//   term and the fixed-point rounding, both below 2^-16 of max|b'| * |S| per
-//   group.
-// * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
-//   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
-// One workgroup per 64 rows: each wave writes the digits of 16 rows (lanes
-// over the row's groups and block columns, coalesced), then the ratio table
-// is written with lanes over rows (coalesced) and the four waves over groups.
-__global__ void __launch_bounds__(256) k_head_prep(const float *biases, const float *scales, float shift, int64_t V,
-                                                   int G, int Kb, int NB, uint8_t *baug, float *rt, float *slast) {
-  __shared__ float su[64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t v0 = (int64_t)blockIdx.x * 64;
-  for (int i = 0; i < 16; ++i) {
-    const int rl = wave * 16 + i;
-    const int64_t v = v0 + rl;
-    if (v >= V) break;
-    const float *brow = biases + v * G;
-    const float *srow = scales + v * G;
-    float m = 0.0f;
-    for (int g = lane; g < G; g += 64) m = fmaxf(m, fabsf(fmaf(shift, srow[g], brow[g])));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float u = m / 32639.0f;
-    const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
-    for (int kk = lane; kk < Kb; kk += 64) {
-      const int part = kk / G, gi = kk - part * G;
-      int digit = 0;
-      if (part < 3) {
-        const float b = fmaf(shift, srow[gi], brow[gi]);
-        const int n = (int)fminf(fmaxf(rintf(b * inv), -32639.0f), 32639.0f);
-        const int d1 = (n + 128) >> 8;  // floor((n + 128) / 256), in [-127, 127]
-        digit = (part == 2) ? n - 256 * d1 : d1;
-      }
-      baug[v * Kb + kk] = (uint8_t)(digit + 128);
-    }
-    if (lane == 0) su[rl] = u;
-  }
-  __syncthreads();
-  const int64_t v = v0 + lane;
-  if (v >= V) return;
-  const float *srow = scales + v * G;
-  for (int s2 = wave; s2 < NB; s2 += 4) rt[s2 * V + v] = 1.0f;
-  for (int g = wave; g < G; g += 4) {
-    const float prev = scale_eff(g == 0 ? su[lane] : srow[g - 1]);
-    rt[(NB + g) * V + v] = prev / scale_eff(srow[g]);
-  }
-  if (wave == 0) slast[v] = scale_eff(srow[G - 1]);
-}
-
-void launch_head_prep(hipStream_t st, int bits, const float *biases, const float *scales, int64_t V, int G, int Kb,
-                      int NB, uint8_t *baug, float *rt, float *slast) {
-  hipLaunchKernelGGL(k_head_prep, dim3((unsigned)((V + 63) / 64)), dim3(256), 0, st, biases, scales,
-                     bits == 8 ? 128.0f : 0.0f, V, G, Kb, NB, baug, rt, slast);
 }
 
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
