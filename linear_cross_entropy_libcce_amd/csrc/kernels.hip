@@ -70,58 +70,78 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 //   group.
 // * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
 //   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
-// One workgroup per 64 rows: each wave writes the digits of 16 rows (lanes
-// over the row's groups and block columns, coalesced), then the ratio table
-// is written with lanes over rows (coalesced) and the four waves over groups.
+// One workgroup per 64 rows, three flat passes: (1) |b'| of every (row,
+// group) with a shared-memory max per row; (2) the digits, lanes over
+// consecutive (row, group) pairs so that the loads and the byte stores of a
+// wave are contiguous; (3) the ratio table, whose layout is [step][V] (read
+// that way by the tile): the scales of 64 groups at a time are staged in LDS
+// with contiguous loads, then written with lanes over rows.
+constexpr int HP_ROWS = 64, HP_COLS = 64, HP_LD = HP_COLS + 1;
+
 __device__ void head_prep_block(int64_t blk, const float *biases, const float *scales, float shift, int64_t V, int G,
-                                int Kb, int NB, uint8_t *baug, float *rt, float *slast, float *su) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t v0 = blk * 64;
-  for (int i = 0; i < 16; ++i) {
-    const int rl = wave * 16 + i;
-    const int64_t v = v0 + rl;
-    if (v >= V) break;
-    const float *brow = biases + v * G;
-    const float *srow = scales + v * G;
-    float m = 0.0f;
-    for (int g = lane; g < G; g += 64) m = fmaxf(m, fabsf(fmaf(shift, srow[g], brow[g])));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float u = m / 32639.0f;
-    const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
-    for (int kk = lane; kk < Kb; kk += 64) {
-      const int part = kk / G, gi = kk - part * G;
-      int digit = 0;
-      if (part < 3) {
-        const float b = fmaf(shift, srow[gi], brow[gi]);
-        const int n = (int)fminf(fmaxf(rintf(b * inv), -32639.0f), 32639.0f);
-        const int d1 = (n + 128) >> 8;  // floor((n + 128) / 256), in [-127, 127]
-        digit = (part == 2) ? n - 256 * d1 : d1;
-      }
-      baug[v * Kb + kk] = (uint8_t)(digit + 128);
-    }
-    if (lane == 0) su[rl] = u;
+                                int Kb, int NB, uint8_t *baug, float *rt, float *slast, float *su, float *sT) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t v0 = blk * HP_ROWS;
+  const int rows = (int)(V - v0 < HP_ROWS ? V - v0 : HP_ROWS);
+  unsigned *smax = reinterpret_cast<unsigned *>(su);
+  float *sprev = su + HP_ROWS;
+  if (tid < HP_ROWS) smax[tid] = 0u;
+  __syncthreads();
+  const float *brow = biases + v0 * G, *srow = scales + v0 * G;
+  const int n = rows * G;
+  for (int i = tid; i < n; i += 256) {
+    const float bp = fmaf(shift, srow[i], brow[i]);
+    atomicMax(&smax[i / G], __float_as_uint(fabsf(bp)));  // |b'| >= 0: integer order is float order
   }
   __syncthreads();
-  const int64_t v = v0 + lane;
-  if (v >= V) return;
-  const float *srow = scales + v * G;
-  for (int s2 = wave; s2 < NB; s2 += 4) rt[s2 * V + v] = 1.0f;
-  for (int g = wave; g < G; g += 4) {
-    const float prev = scale_eff(g == 0 ? su[lane] : srow[g - 1]);
-    rt[(NB + g) * V + v] = prev / scale_eff(srow[g]);
+  for (int i = tid; i < n; i += 256) {
+    const int r = i / G, gi = i - r * G;
+    const float u = __uint_as_float(smax[r]) / 32639.0f;
+    const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+    const float bp = fmaf(shift, srow[i], brow[i]);
+    const int q = (int)fminf(fmaxf(rintf(bp * inv), -32639.0f), 32639.0f);
+    const int d1 = (q + 128) >> 8;  // floor((q + 128) / 256), in [-127, 127]
+    uint8_t *row = baug + (v0 + r) * Kb;
+    row[gi] = (uint8_t)(d1 + 128);
+    row[G + gi] = (uint8_t)(d1 + 128);
+    row[2 * G + gi] = (uint8_t)(q - 256 * d1 + 128);
   }
-  if (wave == 0) slast[v] = scale_eff(srow[G - 1]);
+  const int pad = Kb - 3 * G;
+  for (int i = tid; i < rows * pad; i += 256) baug[(v0 + i / pad) * Kb + 3 * G + i % pad] = (uint8_t)128;
+  const int64_t v = v0 + lane;
+  if (wave == 0 && lane < rows) {
+    sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
+    for (int s2 = 0; s2 < NB; ++s2) rt[s2 * V + v] = 1.0f;
+  }
+  for (int c0 = 0; c0 < G; c0 += HP_COLS) {
+    const int cw = G - c0 < HP_COLS ? G - c0 : HP_COLS;
+    __syncthreads();  // sprev written, the previous chunk's reads done
+    for (int i = tid; i < rows * cw; i += 256) {
+      const int r = i / cw, gl = i - r * cw;
+      sT[r * HP_LD + gl] = srow[(int64_t)r * G + c0 + gl];
+    }
+    __syncthreads();
+    if (lane < rows) {
+      for (int gl = wave; gl < cw; gl += 4) {
+        const float prev = gl > 0 ? sT[lane * HP_LD + gl - 1] : sprev[lane];
+        rt[(int64_t)(NB + c0 + gl) * V + v] = scale_eff(prev) / scale_eff(sT[lane * HP_LD + gl]);
+      }
+    }
+    __syncthreads();
+    if (tid < rows) sprev[tid] = sT[tid * HP_LD + cw - 1];
+  }
+  if (tid < rows) slast[v0 + tid] = scale_eff(sprev[tid]);
 }
 
 template <int BITS>
 __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
   __shared__ float sS[MAX_G];
   __shared__ float sRed[4];
+  __shared__ float sT[HP_ROWS * HP_LD];
   const int tid = threadIdx.x;
   if (blockIdx.x >= (unsigned)f.M_pad) {
     head_prep_block((int64_t)blockIdx.x - f.M_pad, f.biases, f.scales, BITS == 8 ? 128.0f : 0.0f, f.V, f.G, f.Kb,
-                    f.NB, f.baug, f.rt, f.slast, sS);
+                    f.NB, f.baug, f.rt, f.slast, sS, sT);
     return;
   }
   const int r = blockIdx.x;
@@ -318,7 +338,7 @@ void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *
 }
 
 void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
-  const dim3 grid((unsigned)(f.M_pad + (f.V + 63) / 64));
+  const dim3 grid((unsigned)(f.M_pad + (f.V + HP_ROWS - 1) / HP_ROWS));
   if (bits == 4)
     hipLaunchKernelGGL(k_front<4>, grid, dim3(256), 0, st, f);
   else
