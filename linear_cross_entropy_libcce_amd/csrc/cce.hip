@@ -23,6 +23,7 @@ constexpr int64_t MAX_H = 16384;
 constexpr int64_t MAX_M = (int64_t)1 << 24;
 constexpr size_t COEFF_BUDGET = (size_t)1 << 30;  // bytes of one coefficient chunk
 constexpr int64_t MAX_CHUNK_TILES = 2048;          // vocabulary tiles of one coefficient chunk
+constexpr int64_t FUSED_COMPACT_MAX_M = 2048;      // tokens compacted inside the front launch
 
 thread_local char g_err[256];
 
@@ -218,8 +219,17 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   int *inv = ws_at<int>(ws, p.o_inv);
   TokRec *tok = ws_at<TokRec>(ws, p.o_tok);
   uint16_t *haug = ws_at<uint16_t>(ws, p.o_haug);
-  CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
+  // up to this many tokens the front's row blocks compact the mask themselves
+  // (each scans all M mask bytes), one launch fewer
+  const bool fuse = p.M <= FUSED_COMPACT_MAX_M;
+  if (!fuse) CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
   FrontArgs f{};
+  f.compact = fuse ? 1 : 0;
+  f.M = (int)p.M;
+  f.mask = mask;
+  f.idx_out = idx;
+  f.inv = inv;
+  f.cnt = cnt;
   f.h = (const uint16_t *)h;
   f.idx = idx;
   f.targets = targets;

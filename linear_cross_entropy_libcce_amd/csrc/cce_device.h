@@ -157,6 +157,11 @@ struct FrontArgs {
   int H, G, Kb, Ka, NB, wpr, M_pad;
   float cap;
   int bwd;
+  // compact != 0: the row blocks compact the mask themselves (small M) and
+  // write idx_out, inv and cnt; otherwise idx comes from the compaction launch
+  int compact, M;
+  const uint8_t *mask;
+  int *idx_out, *inv, *cnt;
 };
 
 struct GemmArgs {

@@ -145,7 +145,49 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
     return;
   }
   const int r = blockIdx.x;
-  const int src = f.idx[r];
+  int src;
+  if (f.compact) {
+    // small M: every row block compacts for itself (no separate launch).
+    // Thread i scans its slice of the mask; a block scan of the slice counts
+    // gives the rank of every slice start.  Row block r takes the r-th
+    // supervised token as its source, and fixes inv of token r (r < M).
+    __shared__ int sC[4], sSrc;
+    const int M = f.M, per = (M + 255) / 256;
+    const int t0 = tid * per, t1 = min(M, t0 + per);
+    int c = 0;
+    for (int t = t0; t < t1; ++t) c += f.mask ? (f.mask[t] != 0) : 1;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if ((tid & 63) >= o) incl += y;
+    }
+    if ((tid & 63) == 63) sC[tid >> 6] = incl;
+    if (tid == 0) sSrc = -1;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < (tid >> 6); ++w) base += sC[w];
+    const int excl = base + incl - c;
+    if (r >= excl && r < excl + c) {  // the r-th supervised token is in this slice
+      int k = excl;
+      for (int t = t0; t < t1; ++t)
+        if (!f.mask || f.mask[t] != 0) {
+          if (k == r) sSrc = t;
+          ++k;
+        }
+    }
+    if (r < M && r >= t0 && r < t1) {  // rank of token r
+      int k = excl;
+      for (int t = t0; t < r; ++t) k += f.mask ? (f.mask[t] != 0) : 1;
+      f.inv[r] = (!f.mask || f.mask[r] != 0) ? k : -1;
+    }
+    if (r == 0 && tid == 0) f.cnt[0] = sC[0] + sC[1] + sC[2] + sC[3];
+    __syncthreads();
+    src = sSrc;
+    if (tid == 0) f.idx_out[r] = src;
+  } else {
+    src = f.idx[r];
+  }
   const int H = f.H, G = f.G, Kb = f.Kb;
   const int64_t ks16 = f.Ka / 16;
   const int nch = H / 8;  // 16-byte chunks of the h part; 8 per group
