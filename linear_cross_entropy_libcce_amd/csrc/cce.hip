@@ -144,13 +144,17 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.HT = (int)cdiv(p.H, 256);
   // Vocabulary splits of the dh contraction: the fewest that fill whole rounds
   // of resident workgroups (one per CU) to >= 97%, else the best fill of up
-  // to 8; each split adds one dh slab.
+  // to 8 -- or, when 8 splits cannot fill one round (few token tiles), of up
+  // to a round's worth; each split adds one dh slab, at most 4 GiB of slabs.
   {
     const int64_t slots = cus;
     const int64_t base = (int64_t)p.TT * p.HT;
+    const int64_t slab = p.M_pad * p.H * (int64_t)sizeof(float);
+    const int64_t reach = base * 8 >= slots ? 8 : std::min<int64_t>(64, cdiv(slots, base));
+    const int max_ks = (int)std::max<int64_t>(1, std::min<int64_t>(reach, ((int64_t)4 << 30) / slab));
     int best = 1;
     double best_fill = 0.0;
-    for (int ks = 1; ks <= 8 && ks <= p.chunk_tiles; ++ks) {
+    for (int ks = 1; ks <= max_ks && ks <= p.chunk_tiles; ++ks) {
       const int64_t n = base * ks;
       const double fill = (double)n / (double)(cdiv(n, slots) * slots);
       if (fill > best_fill + 1e-9) {
@@ -278,6 +282,7 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.ksv = p.ld_coeff / 16;
   a.cap = p.cap;
   a.inv_cap = p.cap > 0.0f ? 1.0f / p.cap : 0.0f;
+  a.small = p.M <= 64 ? 1 : 0;
   return a;
 }
 
@@ -411,6 +416,7 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   ga.nblocks = p.TT * p.HT * p.ksplit;
   ga.fl = fl;
   ga.fl_ld = p.tiles;
+  ga.small = a.small;
   const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
 
   for (int c = 0; c < p.nchunks; ++c) {

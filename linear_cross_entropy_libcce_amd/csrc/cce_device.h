@@ -139,6 +139,7 @@ struct TileArgs {
   uint8_t *fl;
   int64_t fl_ld;
   float filter_eps;
+  int small;             // at most 64 tokens: only token group 0 of the tile multiplies
 };
 
 // Arguments of the front launch (token rows, target logit, head side).
@@ -184,6 +185,7 @@ struct GemmArgs {
   const uint8_t *fl;
   int64_t fl_ld;
   int chunk_tile0;       // first vocabulary tile of the chunk
+  int small;             // as in TileArgs
 };
 
 // Raw buffer resource over [base, base + bytes): a lane whose byte offset is

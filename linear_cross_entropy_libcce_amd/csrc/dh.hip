@@ -10,7 +10,7 @@ namespace cce {
 // rows r < 256 * ceil(cnt / 256), split count from dh_split).
 //
 // Workgroup: 256 tokens x 256 dh columns, 8 waves; wave w owns tokens
-// [64(w%4), +64) and columns [128(w/4), +128) as 2 x 4 blocks of
+// [64(w/2), +64) and columns [128(w%2), +128) as 2 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = d, K = vocabulary rows).
 // Per K step of 64 vocabulary rows:
 //  * the head tile of the step is dequantized once (s*q + b, rounded to bf16)
@@ -24,6 +24,7 @@ namespace cce {
 // Reads are raw buffer loads (rows past V read as zeros), so the step has no
 // per-lane predicate.  Each split owns its fp32 slab: no atomics, and a
 // repeated call gives identical bits.
+// SMALL (at most 64 tokens): only the two waves of token group 0 multiply.
 // SKIP (second instantiation): the split contracts only the vocabulary tiles
 // of its range whose pair flag is set for its token tile; their K steps are
 // listed in LDS first, in order.
@@ -104,7 +105,7 @@ struct DhProducer {
 
 constexpr int MAX_LIST = 2048;  // vocabulary tiles per split (a chunk holds at most 2048)
 
-template <int BITS, bool SKIP>
+template <int BITS, bool SKIP, bool SMALL>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only;
@@ -121,7 +122,8 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   int nsteps = min(steps_per, a.chunk_steps - step0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tg = wave & 3, dh = wave >> 2;
+  const int tg = wave >> 1, dh = wave & 1;  // the two waves of a token group sit on two SIMDs
+  const bool live = SMALL ? tg == 0 : true;  // at most 64 tokens: token group 0 only
   const int l32 = lane & 31, lh = lane >> 5;
 
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * KSTP];
@@ -233,19 +235,22 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       const uint16_t *sw = sB[cb];
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
       bf16x8_t bq[4];
+      if (live)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
+        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        if (live) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < 4; ++c) {
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
-          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTP);
+            for (int rb = 0; rb < 2; ++rb)
+              acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
+            if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTP);
+          }
+          cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
+          cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));
         }
-        cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
-        cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));
         pr.store(ks, cur, sc, bi, sB[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -261,6 +266,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   } else if (a.accumulate) {
     return;
   }
+  if (!live) return;  // rows of padding tokens only
 
   // result lane layout: column d0 + dh*128 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j
 #pragma unroll
@@ -281,13 +287,15 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 }
 
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
-  const bool skip = a.fl != nullptr;
+  const bool skip = a.fl != nullptr, small = !skip && a.small;
   if (bits == 4) {
-    if (skip) hipLaunchKernelGGL((k_dh<4, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_dh<4, false>), grid, dim3(TW), 0, st, a);
+    if (skip) hipLaunchKernelGGL((k_dh<4, true, false>), grid, dim3(TW), 0, st, a);
+    else if (small) hipLaunchKernelGGL((k_dh<4, false, true>), grid, dim3(TW), 0, st, a);
+    else hipLaunchKernelGGL((k_dh<4, false, false>), grid, dim3(TW), 0, st, a);
   } else {
-    if (skip) hipLaunchKernelGGL((k_dh<8, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_dh<8, false>), grid, dim3(TW), 0, st, a);
+    if (skip) hipLaunchKernelGGL((k_dh<8, true, false>), grid, dim3(TW), 0, st, a);
+    else if (small) hipLaunchKernelGGL((k_dh<8, false, true>), grid, dim3(TW), 0, st, a);
+    else hipLaunchKernelGGL((k_dh<8, false, false>), grid, dim3(TW), 0, st, a);
   }
 }
 

@@ -7,8 +7,8 @@ namespace cce {
 
 // ---------------------------------------------------------------------------
 // The logit tile: 256 tokens x 256 vocabulary rows per workgroup of 8 waves,
-// K = Ka (bias block, then H).  Wave w owns tokens [64(w%4), +64) and vocab
-// rows [128(w/4), +128) of the tile as 2 x 4 blocks of
+// K = Ka (bias block, then H).  Wave w owns tokens [64(w/2), +64) and vocab
+// rows [128(w%2), +128) of the tile as 2 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = vocabulary rows).
 //
 // Per K step (one quantization group of 64):
@@ -32,7 +32,10 @@ namespace cce {
 // first with ratio 1 in units of the row's fixed-point unit, and a scale of
 // exactly 0 is replaced by 1e-30, whose contribution is nil.
 //
-// EXTRA (a second instantiation, so the plain passes carry none of it):
+// VAR_SMALL (at most 64 tokens): only the two waves of token group 0 carry
+// MFMA work and epilogues; the other six still produce the code tiles.
+//
+// VAR_EXTRA (a second instantiation, so the plain passes carry none of it):
 //  * forward: the largest logit of every (token, vocabulary tile), written to
 //    block_max after the softcap (monotonic, so the max commutes with it);
 //  * backward: the (token tile, vocabulary tile) pairs whose flag is clear
@@ -44,6 +47,7 @@ constexpr int ZROW = 36;  // padded fp32 row stride of the per-wave transpose sc
 constexpr float LOG2E = 1.4426950408889634f;
 
 enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2 };
+enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
 
 // One step's worth of head data for one producer thread: 16 K values of each
 // of two vocabulary rows (8-bit codes and bias digits: 4 words per row; 4-bit
@@ -119,9 +123,10 @@ __device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) 
   return cap * th;
 }
 
-template <int BITS, int MODE, bool EXTRA>
+template <int BITS, int MODE, int VAR>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
+  constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only
   const int act = active_tiles(a.cnt);
@@ -133,7 +138,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int tile_end = min(tile_begin + tpw, a.range_tiles);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int tg = wave & 3, vh = wave >> 2;
+  const int tg = wave >> 1, vh = wave & 1;  // the two waves of a token group sit on two SIMDs
+  const bool live = SMALL ? tg == 0 : true;  // this wave's tokens can be supervised
   const int l32 = lane & 31, lh = lane >> 5;
   const int steps = a.NB + a.G;
 
@@ -223,29 +229,33 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[4];
+      if (live)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+        for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
       const int hnext = sn * 4096;
       // B operand of column block c for k-step ks + 1 is read as soon as its
       // two MFMAs of k-step ks are issued; a scheduling barrier after each
       // k-step keeps this order (left free, the compiler hoists every LDS read
       // and unpack and runs out of registers).
       bf16x8_t bq[4];
+      if (live)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTEP);
+        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTEP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        if (live) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < 4; ++c) {
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            if (ks == 0) acc[rb][c] *= r[c];
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
+            for (int rb = 0; rb < 2; ++rb) {
+              if (ks == 0) acc[rb][c] *= r[c];
+              acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
+            }
+            if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTEP);
           }
-          if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTEP);
+          hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
+          hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
         }
-        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
-        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
         pr.store(sbias, ks, cur, sW[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -394,7 +404,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
       mfma_step(idx & 1, sn, vnn, snn, cur, nxt);
-      if (st == steps - 1) epilogue(tile);
+      if (live && st == steps - 1) epilogue(tile);
       __syncthreads();
       if (EXTRA && st == steps - 1) tile_extra(tile);
     };
@@ -413,7 +423,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     if (idx < total) do_step(idx, tile, st, P1, P0);
   }
 
-  if (!BWD) {
+  if (!BWD && live) {
     float *dst = a.part + ((size_t)(2 * wr + vh) * a.M_pad + tok0 + lane) * 2;
     dst[0] = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
     dst[1] = run_s;
@@ -423,10 +433,12 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
   const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
   const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
-#define CCE_TILE(B, MD)                                                          \
-  do {                                                                           \
-    if (extra) hipLaunchKernelGGL((k_tile<B, MD, true>), grid, dim3(TW), 0, st, a); \
-    else hipLaunchKernelGGL((k_tile<B, MD, false>), grid, dim3(TW), 0, st, a);      \
+  const int var = extra ? VAR_EXTRA : (a.small ? VAR_SMALL : VAR_PLAIN);
+#define CCE_TILE(B, MD)                                                                        \
+  do {                                                                                         \
+    if (var == VAR_EXTRA) hipLaunchKernelGGL((k_tile<B, MD, VAR_EXTRA>), grid, dim3(TW), 0, st, a); \
+    else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL>), grid, dim3(TW), 0, st, a); \
+    else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN>), grid, dim3(TW), 0, st, a);            \
   } while (0)
   if (bits == 4) {
     if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
