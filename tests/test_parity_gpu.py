@@ -202,3 +202,17 @@ def test_peaked_softmax(torch_cuda, softcap):
     orc = oracle.cce(inp)
     assert np.exp(orc[0][:48]).min() > 0.95   # the case really is peaked
     check(inp, gpu, orc, np.arange(64), "peaked")
+
+
+@pytest.mark.parametrize("M", [40, 64, 65])
+def test_small_m_on_the_full_head(torch_cuda, M):
+    # the small-M launch (M <= 64: only the first token group multiplies, many
+    # dh splits) and its neighbour M = 65, on workload 3's full head; every
+    # token against the oracle
+    w = syn.WORKLOADS[3]
+    say("small M=%d on workload 3's head: generating inputs" % M)
+    inp = syn.make_inputs(w, syn.seed_for(3), M=M)
+    g = np.random.default_rng(M).uniform(-1.5, 1.5, size=M)
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    say("small M=%d: oracle on all tokens" % M)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "smallM%d" % M)
