@@ -8,9 +8,13 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
 1. packed head words ``wq`` uint32 [V, H*bits/32], each word uniform over all
    32-bit values -- so every ``bits``-wide code inside it is uniform over
    [0, 2**bits), the code distribution of the workloads;
-2. per-group scales fp32 [V, H/64], uniform in [lo, hi);
-   biases are derived, not drawn: ``-8*s`` (4-bit) or ``-128*s`` (8-bit),
-   i.e. the affine zero point sits mid-range as in an MLX affine quantizer;
+2. per-group scales fp32 [V, H/group] (group 64 unless stated), uniform in
+   [lo, hi); biases are derived, not drawn: ``-8*s`` (4-bit) or ``-128*s``
+   (8-bit), i.e. the affine zero point sits mid-range as in an MLX affine
+   quantizer.  With bf16 / fp16 storage the scales are rounded to that type
+   (nearest, ties to even) before the biases are derived, and both are
+   returned as raw 16-bit patterns (exact in the narrow type: the zero points
+   are powers of two);
 3. hidden states drawn fp32 N(0, 1), rounded to bf16 (round-to-nearest-even),
    returned as the raw uint16 bit patterns [M, H];
 4. targets int32 [M]: uniform over [0, V), or truncated Zipf(a) over the
@@ -56,10 +60,12 @@ class Workload:
     mask_frac: float = 0.0
     boost_rows: int = 0           # peaked head: rows [0, boost_rows) get scales * boost
     boost: float = 1.0
+    group: int = GROUP            # quantization group: 32, 64 or 128
+    sb_dtype: str = "f32"         # storage of scales and biases: "f32" | "bf16" | "f16"
 
     @property
     def G(self) -> int:
-        return self.H // GROUP
+        return self.H // self.group
 
     @property
     def words_per_row(self) -> int:
@@ -101,6 +107,15 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def sb_as_f32(a: np.ndarray, sb_dtype: str) -> np.ndarray:
+    """Scales or biases as fp32 (exact widening of the stored type)."""
+    if sb_dtype == "f32":
+        return np.asarray(a, np.float32)
+    if sb_dtype == "bf16":
+        return f32_from_bf16_bits(np.asarray(a, np.uint16))
+    return np.asarray(a, np.uint16).view(np.float16).astype(np.float32)
+
+
 def _targets(rng, M, V, kind, a):
     if kind == "uniform":
         return rng.integers(0, V, size=M, dtype=np.int64).astype(np.int32)
@@ -135,24 +150,32 @@ def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
     scales = rng.uniform(w.scale_lo, w.scale_hi, size=(w.V, w.G)).astype(np.float32)
     if w.boost_rows > 0:
         scales[:w.boost_rows] *= np.float32(w.boost)
+    if w.sb_dtype == "bf16":
+        scales = f32_from_bf16_bits(bf16_bits_from_f32(scales))
+    elif w.sb_dtype == "f16":
+        scales = scales.astype(np.float16).astype(np.float32)
     zero_point = np.float32(8.0 if w.bits == 4 else 128.0)
     biases = (-zero_point * scales).astype(np.float32)
+    if w.sb_dtype == "bf16":
+        scales, biases = bf16_bits_from_f32(scales), bf16_bits_from_f32(biases)
+    elif w.sb_dtype == "f16":
+        scales, biases = scales.astype(np.float16).view(np.uint16), biases.astype(np.float16).view(np.uint16)
     h = bf16_bits_from_f32(rng.standard_normal((M, w.H), dtype=np.float32))
     targets = _targets(rng, M, w.V, w.targets, w.zipf_a)
     mask = _mask(rng, M, w.mask, w.mask_frac)
     return dict(h=h, wq=wq, scales=scales, biases=biases, targets=targets, mask=mask,
-                M=M, H=w.H, V=w.V, bits=w.bits, group=GROUP, softcap=float(w.softcap))
+                M=M, H=w.H, V=w.V, bits=w.bits, group=w.group, softcap=float(w.softcap), sb_dtype=w.sb_dtype)
 
 
 def make_custom(M, H, V, bits, seed, softcap=0.0, scale_lo=None, scale_hi=None,
                 targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0,
-                boost_rows=0, boost=1.0) -> dict:
+                boost_rows=0, boost=1.0, group=GROUP, sb_dtype="f32") -> dict:
     """A reduced/edge-case workload with the same value distributions."""
     if scale_lo is None:
         scale_lo, scale_hi = (0.005, 0.02) if bits == 4 else (0.0005, 0.002)
     w = Workload("custom", M, H, V, bits, scale_lo, scale_hi, softcap=softcap,
                  targets=targets, mask=mask, mask_frac=mask_frac,
-                 boost_rows=boost_rows, boost=boost)
+                 boost_rows=boost_rows, boost=boost, group=group, sb_dtype=sb_dtype)
     d = make_inputs(w, seed)
     if h_scale != 1.0:
         d["h"] = bf16_bits_from_f32(f32_from_bf16_bits(d["h"]) * np.float32(h_scale))

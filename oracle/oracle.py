@@ -54,6 +54,19 @@ def threads() -> int:
     return int(_load().oracle_threads())
 
 
+def _sb_f32(a, sb_dtype: str) -> np.ndarray:
+    """Stored scales or biases widened exactly to fp32 (fp32, or the raw bits
+    of bf16 / fp16)."""
+    if sb_dtype == "f32":
+        return np.asarray(a, np.float32)
+    b = np.asarray(a, np.uint16)
+    if sb_dtype == "bf16":
+        return (b.astype(np.uint32) << 16).view(np.float32)
+    if sb_dtype == "f16":
+        return b.view(np.float16).astype(np.float32)
+    raise ValueError(sb_dtype)
+
+
 def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -68,8 +81,8 @@ def cce(inp: dict, tokens: Optional[Sequence[int]] = None, backward: bool = True
     lib = _load() if lib is None else lib
     h = np.ascontiguousarray(inp["h"], dtype=np.uint16)
     wq = np.ascontiguousarray(inp["wq"], dtype=np.uint32)
-    sc = np.ascontiguousarray(inp["scales"], dtype=np.float32)
-    bi = np.ascontiguousarray(inp["biases"], dtype=np.float32)
+    sc = np.ascontiguousarray(_sb_f32(inp["scales"], inp.get("sb_dtype", "f32")))
+    bi = np.ascontiguousarray(_sb_f32(inp["biases"], inp.get("sb_dtype", "f32")))
     tg = np.ascontiguousarray(inp["targets"], dtype=np.int32)
     mk = inp.get("mask")
     mk = None if mk is None else np.ascontiguousarray(mk, dtype=np.uint8)
@@ -127,8 +140,9 @@ def dequantize(inp: dict, v0: int = 0, v1: Optional[int] = None) -> np.ndarray:
     shifts = (np.arange(per, dtype=np.uint32) * bits).astype(np.uint32)
     q = (wq[:, :, None] >> shifts[None, None, :]) & np.uint32((1 << bits) - 1)
     q = q.reshape(V, wpr * per).astype(np.float64)
-    s = np.repeat(np.asarray(inp["scales"][v0:v1], np.float64), group, axis=1)
-    b = np.repeat(np.asarray(inp["biases"][v0:v1], np.float64), group, axis=1)
+    sbt = inp.get("sb_dtype", "f32")
+    s = np.repeat(_sb_f32(inp["scales"][v0:v1], sbt).astype(np.float64), group, axis=1)
+    b = np.repeat(_sb_f32(inp["biases"][v0:v1], sbt).astype(np.float64), group, axis=1)
     return s * q + b
 
 

@@ -82,6 +82,47 @@ def test_code_order_and_group_index_from_hex_words(bits):
         assert abs(logp[0] - (z[t] - lse)) < 1e-12 * abs(lse)
 
 
+# (value, bf16 bits, fp16 bits), read off by hand
+SB_TABLE_S = [(0.5, 0x3F00, 0x3800), (0.25, 0x3E80, 0x3400), (0.125, 0x3E00, 0x3000),
+              (2.0, 0x4000, 0x4000), (0.75, 0x3F40, 0x3A00), (1.5, 0x3FC0, 0x3E00)]
+SB_TABLE_B = [(-1.0, 0xBF80, 0xBC00), (0.5, 0x3F00, 0x3800), (-0.75, 0xBF40, 0xBA00),
+              (0.0, 0x0000, 0x0000), (-3.0, 0xC040, 0xC200), (0.25, 0x3E80, 0x3400)]
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("sb_dtype", ["f32", "bf16", "f16"])
+def test_group_size_and_scale_storage(group, sb_dtype):
+    """h = one-hot at d makes logit v = s[v][d // group] * q[v][d] + b[v][d // group].
+
+    Scales and biases come from a hand-written table, given as fp32 values or
+    as their bf16 / fp16 bit patterns; a wrong group index (d // 64 instead of
+    d // group), a truncating or misread 16-bit widening changes the logits.
+    """
+    H, V, bits = 128, 3, 8
+    ng = H // group
+    d_all = np.arange(H)
+    q = np.array([(3 * d_all + 50 * v) % 256 for v in range(V)])
+    pick = lambda table, v, g: table[(v * ng + g + v) % len(table)]
+    col = {"f32": 0, "bf16": 1, "f16": 2}[sb_dtype]
+    sc = np.array([[pick(SB_TABLE_S, v, g)[col] for g in range(ng)] for v in range(V)])
+    bi = np.array([[pick(SB_TABLE_B, v, g)[col] for g in range(ng)] for v in range(V)])
+    sv = np.array([[pick(SB_TABLE_S, v, g)[0] for g in range(ng)] for v in range(V)])
+    bv = np.array([[pick(SB_TABLE_B, v, g)[0] for g in range(ng)] for v in range(V)])
+    store = (lambda a: a.astype(np.float32)) if sb_dtype == "f32" else (lambda a: a.astype(np.uint16))
+    for d in (5, 37, 69, 101):
+        h = np.zeros((1, H), np.float32)
+        h[0, d] = 1.0
+        z = [sv[v, d // group] * q[v, d] + bv[v, d // group] for v in range(V)]
+        lse = math.log(sum(math.exp(x) for x in z))
+        for t in range(V):
+            inp = dict(h=bf16(h), wq=pack_codes(q, bits), scales=store(sc), biases=store(bi),
+                       targets=np.array([t], np.int32), mask=None, M=1, H=H, V=V, bits=bits,
+                       group=group, softcap=0.0, sb_dtype=sb_dtype)
+            logp, l, _ = oracle.cce(inp, backward=False)
+            assert abs(l[0] - lse) < 1e-12 * abs(lse)
+            assert abs(logp[0] - (z[t] - lse)) < 1e-12 * max(1.0, abs(lse))
+
+
 def _rand_case(seed, M, H, V, bits, softcap=0.0, mask=None, targets=None):
     rng = np.random.default_rng(seed)
     q = rng.integers(0, 2 ** bits, size=(V, H))

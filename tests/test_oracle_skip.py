@@ -63,12 +63,16 @@ def block_sum(d, rows, t):
     return (p[rows, None] * W[rows]).sum(axis=0)
 
 
-@pytest.mark.parametrize("seed,bits,cap,mask", [(1, 4, 0.0, "none"), (2, 8, 20.0, "random")])
-def test_dense_path_matches_c_oracle(seed, bits, cap, mask):
+@pytest.mark.parametrize("seed,bits,cap,mask,group,sbt", [(1, 4, 0.0, "none", 64, "f32"),
+                                                      (2, 8, 20.0, "random", 64, "f32"),
+                                                      (3, 8, 0.0, "none", 32, "bf16"),
+                                                      (4, 4, 10.0, "random", 128, "f16")])
+def test_dense_path_matches_c_oracle(seed, bits, cap, mask, group, sbt):
     # catches a numpy dequantization or a softmax/coefficient that differs from
-    # the pinned C oracle (code order, group axis, sign of the softmax term)
+    # the pinned C oracle (code order, group axis, 16-bit widening, sign of the
+    # softmax term)
     d = syn.make_custom(300, 128, 700, bits, seed, softcap=cap, mask=mask, mask_frac=0.3,
-                        boost_rows=64, boost=4.0)
+                        boost_rows=64, boost=4.0, group=group, sb_dtype=sbt)
     g = np.linspace(-1.5, 1.0, d["M"])
     l0, s0, h0 = oracle.cce(d, g=g)
     l1, s1, h1, dropped = oracle.cce_skip(d, g=g)
