@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 2
+#define CCE_ABI_VERSION 3
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -53,10 +53,18 @@ typedef enum cce_status {
   CCE_OK = 0,
   CCE_ERR_INVALID_ARG = 1, /* null pointer, negative size, H % group != 0,
                               softcap < 0 or not finite, misaligned pointer */
-  CCE_ERR_UNSUPPORTED = 2, /* bits not 4 or 8, group != 64, H or V too large */
+  CCE_ERR_UNSUPPORTED = 2, /* bits not 4 or 8, group not 32/64/128, scale
+                              dtype unknown, H or V too large */
   CCE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
   CCE_ERR_HIP = 4          /* a HIP launch failed; see cce_status_str */
 } cce_status;
+
+/* Storage type of the per-group scales and biases. */
+typedef enum cce_sb_dtype {
+  CCE_SB_F32 = 0,
+  CCE_SB_BF16 = 1,
+  CCE_SB_F16 = 2
+} cce_sb_dtype;
 
 /*
  * The frozen quantized head (page "mlx-bun 0.0.4 -> 0.0.6",
@@ -65,21 +73,27 @@ typedef enum cce_status {
  *   wq      uint32 [V][H*bits/32]; element d of row v is the unsigned code
  *           (wq[v][d / (32/bits)] >> (bits * (d % (32/bits)))) & (2^bits - 1),
  *           i.e. little-endian within each word.  16-byte aligned.
- *   scales  float  [V][H/group]   (4-byte aligned)
- *   biases  float  [V][H/group]   (4-byte aligned)
- * The dequantized element is w[v][d] = scales[v][d/group] * q + biases[v][d/group].
- *   bits    4 or 8;  group  64;  H a multiple of group, at most 16384;
- *   V in [1, 2^31 - 1];  softcap >= 0 (0 = no softcap).
+ *   scales  [V][H/group] of sb_dtype (aligned to its size)
+ *   biases  [V][H/group] of sb_dtype (aligned to its size)
+ * The dequantized element is w[v][d] = scales[v][d/group] * q + biases[v][d/group],
+ * with the stored scale and bias widened exactly to fp32.
+ *   bits    4 or 8;  group  32, 64 or 128 (the group sizes of MLX's affine
+ *           quantizer, which the page's kernels accept);  H a multiple of
+ *           group and of 64, at most 16384;  V in [1, 2^31 - 1];
+ *   softcap >= 0 (0 = no softcap);
+ *   sb_dtype  CCE_SB_F32 (what the page's host casts to), CCE_SB_BF16 or
+ *           CCE_SB_F16 (the model-dtype storage of MLX heads, read as is).
  */
 typedef struct cce_head {
   const uint32_t *wq;
-  const float *scales;
-  const float *biases;
+  const void *scales;
+  const void *biases;
   int64_t V;
   int64_t H;
   int32_t bits;
   int32_t group;
   float softcap;
+  int32_t sb_dtype;
 } cce_head;
 
 /*

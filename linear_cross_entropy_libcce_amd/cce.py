@@ -24,10 +24,13 @@ BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
 
 
+SB_DTYPES = {"f32": 0, "bf16": 1, "f16": 2}   # cce_sb_dtype
+
+
 class cce_head(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("softcap", ctypes.c_float)]
+                ("group", ctypes.c_int32), ("softcap", ctypes.c_float), ("sb_dtype", ctypes.c_int32)]
 
 
 class cce_skip(ctypes.Structure):
@@ -88,13 +91,15 @@ def _check(status: int):
 @dataclasses.dataclass
 class Head:
     """Device tensors of a quantized head: wq uint32-as-int32 [V, H*bits/32],
-    scales/biases float32 [V, H/64]."""
+    scales/biases [V, H/group] stored as float32, or as bf16 / fp16 (torch
+    bfloat16 / float16, or their raw bits in int16 with sb_dtype set)."""
     wq: "object"
     scales: "object"
     biases: "object"
     bits: int
     softcap: float = 0.0
     group: int = 64
+    sb_dtype: str = "f32"
 
     @property
     def V(self) -> int:
@@ -106,7 +111,7 @@ class Head:
 
     def c_struct(self) -> cce_head:
         return cce_head(self.wq.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
-                        self.V, self.H, self.bits, self.group, float(self.softcap))
+                        self.V, self.H, self.bits, self.group, float(self.softcap), SB_DTYPES[self.sb_dtype])
 
 
 def _ptr(t) -> Optional[int]:
@@ -237,9 +242,12 @@ def head_from_numpy(inp: dict, device="cuda") -> Head:
     """Upload the head arrays of a synthetic.make_inputs dict."""
     import torch
     wq = torch.from_numpy(inp["wq"].view("int32")).to(device)
-    return Head(wq=wq, scales=torch.from_numpy(inp["scales"]).to(device),
-                biases=torch.from_numpy(inp["biases"]).to(device), bits=int(inp["bits"]),
-                softcap=float(inp["softcap"]), group=int(inp["group"]))
+    sbt = inp.get("sb_dtype", "f32")
+
+    def up(a):
+        return torch.from_numpy(a if sbt == "f32" else a.view("int16")).to(device)
+    return Head(wq=wq, scales=up(inp["scales"]), biases=up(inp["biases"]), bits=int(inp["bits"]),
+                softcap=float(inp["softcap"]), group=int(inp["group"]), sb_dtype=sbt)
 
 
 def tokens_from_numpy(inp: dict, device="cuda"):

@@ -80,7 +80,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
   int64_t M, M_pad, V, H;
-  int G, Kb, Ka, NB, bits, wpr, TT, tiles;
+  int G, Kb, Ka, NB, bits, wpr, TT, tiles;  // G: 64-wide K steps of h (H / 64)
+  int gs, Gq, sbt;                           // quantization group, groups per row, scale/bias dtype
   float cap;
   // forward
   int nsplit, tiles_per_split, fwd_blocks, max_splits;
@@ -88,8 +89,8 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, o_fl, fwd_bytes,
-      bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_rt2, o_slast, o_part, o_coeff, o_dhp, o_fl,
+      fwd_bytes, bwd_bytes;
 };
 
 cce_status check_head(const cce_head *hd) {
@@ -97,10 +98,14 @@ cce_status check_head(const cce_head *hd) {
   if (hd->V < 1 || hd->H < 1) return CCE_ERR_INVALID_ARG;
   if (!(hd->softcap >= 0.0f) || !std::isfinite(hd->softcap)) return CCE_ERR_INVALID_ARG;
   if (hd->bits != 4 && hd->bits != 8) return CCE_ERR_UNSUPPORTED;
-  if (hd->group != KSTEP) return CCE_ERR_UNSUPPORTED;
+  if (hd->group != 32 && hd->group != 64 && hd->group != 128) return CCE_ERR_UNSUPPORTED;
+  if (hd->sb_dtype != CCE_SB_F32 && hd->sb_dtype != CCE_SB_BF16 && hd->sb_dtype != CCE_SB_F16)
+    return CCE_ERR_UNSUPPORTED;
   if (hd->H % hd->group != 0) return CCE_ERR_INVALID_ARG;
+  if (hd->H % KSTEP != 0) return CCE_ERR_UNSUPPORTED;  // group 32 with H an odd multiple of 32
   if (hd->H > MAX_H || hd->V > (int64_t)INT32_MAX - BNT) return CCE_ERR_UNSUPPORTED;
-  if (((uintptr_t)hd->wq & 15) || ((uintptr_t)hd->scales & 3) || ((uintptr_t)hd->biases & 3))
+  const uintptr_t sal = hd->sb_dtype == CCE_SB_F32 ? 3 : 1;
+  if (((uintptr_t)hd->wq & 15) || ((uintptr_t)hd->scales & sal) || ((uintptr_t)hd->biases & sal))
     return CCE_ERR_INVALID_ARG;
   return CCE_OK;
 }
@@ -114,7 +119,11 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.bits = hd->bits;
   p.cap = hd->softcap;
   p.G = (int)(p.H / KSTEP);
-  p.Kb = (int)(cdiv(3 * p.G, KSTEP) * KSTEP);
+  p.gs = hd->group;
+  p.Gq = (int)(p.H / p.gs);
+  p.sbt = hd->sb_dtype;
+  // bias block: three columns per quantization group (fixed-point digits x S hi/lo)
+  p.Kb = (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
   p.Ka = p.Kb + (int)p.H;
   p.NB = p.Kb / KSTEP;
   p.wpr = (int)(p.H * p.bits / 32);
@@ -176,6 +185,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
   p.o_rt = o; o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
+  p.o_rt2 = o;  // group 32: the fold ratio in the middle of every step
+  if (p.gs == 32) o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
   p.o_slast = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   const size_t common = o;
   p.o_part = common;
@@ -246,6 +257,10 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   f.haug = haug;
   f.baug = ws_at<uint8_t>(ws, p.o_baug);
   f.rt = ws_at<float>(ws, p.o_rt);
+  f.rt2 = p.gs == 32 ? ws_at<float>(ws, p.o_rt2) : nullptr;
+  f.gs = p.gs;
+  f.Gq = p.Gq;
+  f.sbt = p.sbt;
   f.slast = ws_at<float>(ws, p.o_slast);
   f.V = p.V;
   f.H = (int)p.H;
@@ -265,10 +280,9 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
   a.rt = ws_at<const float>(ws, p.o_rt);
+  a.rt2 = p.gs == 32 ? ws_at<const float>(ws, p.o_rt2) : nullptr;
   a.slast = ws_at<const float>(ws, p.o_slast);
   a.wq = hd->wq;
-  a.scales = hd->scales;
-  a.biases = hd->biases;
   a.cnt = ws_at<const int>(ws, p.o_cnt);
   a.tok = ws_at<const TokRec>(ws, p.o_tok);
   a.V = p.V;
@@ -407,6 +421,9 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   ga.V = p.V;
   ga.H = (int)p.H;
   ga.G = p.G;
+  ga.gs = p.gs;
+  ga.Gq = p.Gq;
+  ga.sbt = p.sbt;
   ga.wpr = p.wpr;
   ga.M_pad = (int)p.M_pad;
   ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);

@@ -38,7 +38,8 @@ constexpr int BM = 256;        // tokens per workgroup tile (4 waves x 64)
 constexpr int BNT = 256;       // vocabulary rows per logit tile
 constexpr int TW = 512;        // threads per logit-tile workgroup (8 waves)
 constexpr int KSTEP = 64;      // K per step = one quantization group
-constexpr int MAX_G = 256;     // H <= 16384
+constexpr int MAX_G = 256;     // H <= 16384: K steps of 64
+constexpr int MAX_GQ = 512;    // quantization groups per row (group >= 32)
 
 // Per-token side data, one 16-byte record per compacted row.
 struct TokRec {
@@ -109,18 +110,17 @@ __device__ __forceinline__ float wave_sum(float x) {
 struct TileArgs {
   const uint16_t *haug;  // [M_pad][Ka] bf16, fragment-major
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
-  const float *rt;       // [NB + G][V] fold ratio of every step
+  const float *rt;       // [NB + G][V] fold ratio of every step (before its first K column)
+  const float *rt2;      // group 32: [NB + G][V] fold ratio at the step's K column 32 (else unused)
   const float *slast;    // [V] effective scale of the last group
   const uint32_t *wq;
-  const float *scales;
-  const float *biases;
   const int *cnt;
   const TokRec *tok;
   float *part;           // forward: [nwr][M_pad] x (max, sumexp)
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
   int64_t V;
-  int G, Ka, Kb, NB, wpr, M_pad;
+  int G, Ka, Kb, NB, wpr, M_pad;  // G: 64-wide K steps of the h part (H / 64)
   int64_t ks16;          // Ka / 16 (fragment-major h rows)
   int64_t ksv;           // ld_coeff / 16 (fragment-major coefficient chunk)
   int range_tile0, range_tiles;
@@ -149,13 +149,14 @@ struct FrontArgs {
   const int32_t *targets;
   const float *lse, *g;    // backward only (lse NULL in the forward)
   const uint32_t *wq;
-  const float *scales, *biases;
+  const void *scales, *biases;  // [V][Gq] of sbt
   TokRec *tok;
   uint16_t *haug;
   uint8_t *baug;           // head side: bias-block digits, fold ratios, last scale
-  float *rt, *slast;
+  float *rt, *rt2, *slast;
   int64_t V;
   int H, G, Kb, Ka, NB, wpr, M_pad;
+  int gs, Gq, sbt;         // quantization group, groups per row, scale/bias dtype
   float cap;
   int bwd;
   // compact != 0: the row blocks compact the mask themselves (small M) and
@@ -169,13 +170,14 @@ struct GemmArgs {
   const uint16_t *coeff;  // fragment-major [M_pad][16 * ksv] bf16 coefficient chunk
   int64_t ksv;            // K blocks of 16 vocabulary rows per 32-token row block of the chunk
   const uint32_t *wq;
-  const float *scales;
-  const float *biases;
+  const void *scales;     // [V][Gq] of sbt
+  const void *biases;
   const int *cnt;
   float *dh_part;        // [ksplit][M_pad][H]
   int64_t V;
   int64_t chunk_v0;      // first vocabulary row of the chunk
-  int H, G, wpr, M_pad;
+  int H, G, wpr, M_pad;  // G: H / 64
+  int gs, Gq, sbt;       // quantization group, groups per row, scale/bias dtype
   int chunk_steps;       // 64-row K steps in this chunk
   int max_chunk_steps;   // K steps of a full chunk (fixes the split across chunks)
   int TT, HT, ksplit, nblocks;  // ksplit: slab capacity in units of all TT token tiles
@@ -234,6 +236,19 @@ __device__ __forceinline__ void dh_split(const GemmArgs &a, int act, int &ks, in
 // (blocks are dispatched to the 8 XCDs round-robin).  nb_grid % 8 == 0.
 __device__ __forceinline__ int xcd_remap(int b, int nb_grid) {
   return (b & 7) * (nb_grid >> 3) + (b >> 3);
+}
+
+// Scales and biases are stored as fp32, bf16 or fp16 (SB_*); all widen
+// exactly to fp32.
+enum { SB_F32 = 0, SB_BF16 = 1, SB_F16 = 2 };
+__device__ __forceinline__ float sb_widen(uint32_t bits, int sbt) {
+  if (sbt == SB_F32) return __uint_as_float(bits);
+  if (sbt == SB_BF16) return __uint_as_float(bits << 16);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ float ld_sb(const void *base, int64_t i, int sbt) {
+  if (sbt == SB_F32) return static_cast<const float *>(base)[i];
+  return sb_widen(static_cast<const uint16_t *>(base)[i], sbt);
 }
 
 __device__ __forceinline__ float scale_eff(float s) { return (fabsf(s) < 1e-30f) ? 1e-30f : s; }

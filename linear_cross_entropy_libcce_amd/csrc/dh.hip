@@ -43,22 +43,33 @@ __device__ __forceinline__ int dswz(int d, int chunk) { return d * KSTP + ((chun
 // Producer mapping: thread (rgp, dc) handles vocabulary rows 8*rgp .. 8*rgp+7
 // of the step and columns 4*dc .. 4*dc+3 of the tile; lanes are 16 dc x 4 rgp,
 // so one load instruction covers 4 rows and the 16-byte LDS writes of 16
-// lanes fall in distinct banks.  Scale and bias of the step's 64 rows x 4
-// groups are loaded once per workgroup (one float per thread: waves 0-3 the
-// scales, 4-7 the biases) into LDS and read back by the dequantizing threads.
+// lanes fall in distinct banks.  The scales and biases of the step's 64 rows
+// x (256 / group) groups are loaded once per workgroup (value e = tid + 512 k:
+// scales then biases, rows, then groups fastest, so the loads are contiguous)
+// into LDS and read back by the dequantizing threads.
+constexpr int SB_SLOT = 2 * 8 * KSTP;  // floats of one staged step: 2 x (up to 8 groups) x 64 rows
+
 template <int BITS>
 struct DhRegs {
   uint32_t w[8];  // 8-bit: 4 codes of row e; 4-bit: 4 codes in the low 16 bits
-  float sb;       // one scale or bias of the step, staged through LDS
+  float sb[2];    // scales or biases of the step this thread stages
 };
 
 template <int BITS>
 struct DhProducer {
   int rgp, dc;    // rows 8*rgp + e, columns 4*dc + k of the tile
   int wcol;       // byte offset of those columns within a packed row
-  int sbrow, sbg; // the (row, group) of the scale or bias this thread loads for the LDS stage
-  int isb;        // 1: that value is a bias (wave-uniform)
+  int tid;
   int gq0;        // first quantization group of the tile
+  int lg;         // log2 of the groups per tile row (256 / group: 1, 2 or 3)
+  int gsh;        // log2(group / 4): the group of column block dc is dc >> gsh
+
+  // staged value e: (is a bias, row, group within the tile)
+  __device__ __forceinline__ void sb_slot(int e, int &isb, int &row, int &g) const {
+    isb = e >> (6 + lg);
+    row = (e >> lg) & (KSTP - 1);
+    g = e & ((1 << lg) - 1);
+  }
 
   __device__ __forceinline__ void load(const GemmArgs &a, int64_t vs, DhRegs<BITS> &p) const {
     const int64_t rows = a.V - vs < KSTP ? a.V - vs : KSTP;
@@ -69,18 +80,39 @@ struct DhProducer {
       if (BITS == 8) p.w[e] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff, 0, 0);
       else p.w[e] = __builtin_amdgcn_raw_buffer_load_b16(rw, voff, 0, 0);
     }
-    const rsrc_t rs = make_rsrc((isb ? a.biases : a.scales) + vs * a.G, rows * a.G * 4);
-    p.sb = buf_loadf(rs, (sbrow * a.G + gq0 + sbg) * 4, 0);
+    const int esz = a.sbt == SB_F32 ? 4 : 2;
+    const int64_t nb = rows * a.Gq * esz;
+    const rsrc_t rsc = make_rsrc(static_cast<const char *>(a.scales) + vs * a.Gq * esz, nb);
+    const rsrc_t rbi = make_rsrc(static_cast<const char *>(a.biases) + vs * a.Gq * esz, nb);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + 512 * k;
+      int isb, row, g;
+      sb_slot(e, isb, row, g);
+      const int off = (row * a.Gq + gq0 + g) * esz;
+      uint32_t x = 0;
+      if (e < (2 * KSTP) << lg) {
+        if (esz == 4) x = __builtin_amdgcn_raw_buffer_load_b32(isb ? rbi : rsc, off, 0, 0);
+        else x = __builtin_amdgcn_raw_buffer_load_b16(isb ? rbi : rsc, off, 0, 0);
+      }
+      p.sb[k] = sb_widen(x, a.sbt);
+    }
   }
 
   // LDS stage of the step's scales and biases: [group j][row][scale, bias].
   __device__ __forceinline__ void stage_sb(const DhRegs<BITS> &p, float *ssb) const {
-    ssb[(sbg * KSTP + sbrow) * 2 + isb] = p.sb;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + 512 * k;
+      int isb, row, g;
+      sb_slot(e, isb, row, g);
+      if (e < (2 * KSTP) << lg) ssb[(g * KSTP + row) * 2 + isb] = p.sb[k];
+    }
   }
 
-  // (scale, bias) of the thread's 8 rows (group j = dc / 16).
+  // (scale, bias) of the thread's 8 rows (group j = 4 dc / group).
   __device__ __forceinline__ void read_sb(const float *ssb, float (&s)[8], float (&b)[8]) const {
-    const float *src = ssb + ((dc >> 4) * KSTP + 8 * rgp) * 2;
+    const float *src = ssb + ((dc >> gsh) * KSTP + 8 * rgp) * 2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 x = *(const float2 *)(src + 2 * e);
@@ -127,7 +159,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int l32 = lane & 31, lh = lane >> 5;
 
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * KSTP];
-  __shared__ __attribute__((aligned(16))) float sSB[2][4 * KSTP * 2];
+  __shared__ __attribute__((aligned(16))) float sSB[2][SB_SLOT];
   __shared__ uint16_t sList[SKIP ? MAX_LIST : 1];
   __shared__ int sCount[SKIP ? 9 : 1];
 
@@ -186,10 +218,10 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.dc = (lane & 15) + 16 * (wave & 3);
     pr.rgp = (lane >> 4) + 4 * (wave >> 2);
     pr.wcol = (d0 + 4 * pr.dc) * BITS / 8;
-    pr.sbrow = (tid & 255) >> 2;
-    pr.sbg = tid & 3;
-    pr.isb = wave >> 2;  // waves 0-3 load scales, 4-7 biases
-    pr.gq0 = d0 / KSTEP;
+    pr.tid = tid;
+    pr.gq0 = d0 / a.gs;
+    pr.lg = a.gs == 32 ? 3 : (a.gs == 64 ? 2 : 1);
+    pr.gsh = a.gs == 32 ? 3 : (a.gs == 64 ? 4 : 5);
     DhRegs<BITS> P0, P1;
     // this lane's B-operand chunk offsets (row dh*128 + l32 + 32c, chunk 2ks + lh);
     // the swizzle key of row d + 32c equals that of row d

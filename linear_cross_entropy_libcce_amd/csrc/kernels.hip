@@ -78,8 +78,9 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 // with contiguous loads, then written with lanes over rows.
 constexpr int HP_ROWS = 64, HP_COLS = 64, HP_LD = HP_COLS + 1;
 
-__device__ void head_prep_block(int64_t blk, const float *biases, const float *scales, float shift, int64_t V, int G,
-                                int Kb, int NB, uint8_t *baug, float *rt, float *slast, float *su, float *sT) {
+__device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, float *su, float *sT) {
+  const int64_t V = f.V;
+  const int Gq = f.Gq, Kb = f.Kb, NB = f.NB, sbt = f.sbt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t v0 = blk * HP_ROWS;
   const int rows = (int)(V - v0 < HP_ROWS ? V - v0 : HP_ROWS);
@@ -87,61 +88,75 @@ __device__ void head_prep_block(int64_t blk, const float *biases, const float *s
   float *sprev = su + HP_ROWS;
   if (tid < HP_ROWS) smax[tid] = 0u;
   __syncthreads();
-  const float *brow = biases + v0 * G, *srow = scales + v0 * G;
-  const int n = rows * G;
+  const int64_t e0 = v0 * Gq;  // first (row, group) element of the block
+  const int n = rows * Gq;
   for (int i = tid; i < n; i += 256) {
-    const float bp = fmaf(shift, srow[i], brow[i]);
-    atomicMax(&smax[i / G], __float_as_uint(fabsf(bp)));  // |b'| >= 0: integer order is float order
+    const float bp = fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt));
+    atomicMax(&smax[i / Gq], __float_as_uint(fabsf(bp)));  // |b'| >= 0: integer order is float order
   }
   __syncthreads();
   for (int i = tid; i < n; i += 256) {
-    const int r = i / G, gi = i - r * G;
+    const int r = i / Gq, gi = i - r * Gq;
     const float u = __uint_as_float(smax[r]) / 32639.0f;
     const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
-    const float bp = fmaf(shift, srow[i], brow[i]);
+    const float bp = fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt));
     const int q = (int)fminf(fmaxf(rintf(bp * inv), -32639.0f), 32639.0f);
     const int d1 = (q + 128) >> 8;  // floor((q + 128) / 256), in [-127, 127]
-    uint8_t *row = baug + (v0 + r) * Kb;
+    uint8_t *row = f.baug + (v0 + r) * Kb;
     row[gi] = (uint8_t)(d1 + 128);
-    row[G + gi] = (uint8_t)(d1 + 128);
-    row[2 * G + gi] = (uint8_t)(q - 256 * d1 + 128);
+    row[Gq + gi] = (uint8_t)(d1 + 128);
+    row[2 * Gq + gi] = (uint8_t)(q - 256 * d1 + 128);
   }
-  const int pad = Kb - 3 * G;
-  for (int i = tid; i < rows * pad; i += 256) baug[(v0 + i / pad) * Kb + 3 * G + i % pad] = (uint8_t)128;
+  const int pad = Kb - 3 * Gq;
+  for (int i = tid; i < rows * pad; i += 256) f.baug[(v0 + i / pad) * Kb + 3 * Gq + i % pad] = (uint8_t)128;
   const int64_t v = v0 + lane;
   if (wave == 0 && lane < rows) {
     sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
-    for (int s2 = 0; s2 < NB; ++s2) rt[s2 * V + v] = 1.0f;
+    for (int s2 = 0; s2 < NB; ++s2) {
+      f.rt[s2 * V + v] = 1.0f;
+      if (f.gs == 32) f.rt2[s2 * V + v] = 1.0f;
+    }
   }
-  for (int c0 = 0; c0 < G; c0 += HP_COLS) {
-    const int cw = G - c0 < HP_COLS ? G - c0 : HP_COLS;
+  // group g's entry ratio s_{g-1} / s_g goes to the K step where g starts:
+  // group 64 -> step g; 128 -> step 2g (and ratio 1 at step 2g + 1);
+  // 32 -> step g/2 (even g) or the middle of step g/2 (odd g, table rt2)
+  for (int c0 = 0; c0 < Gq; c0 += HP_COLS) {
+    const int cw = Gq - c0 < HP_COLS ? Gq - c0 : HP_COLS;
     __syncthreads();  // sprev written, the previous chunk's reads done
     for (int i = tid; i < rows * cw; i += 256) {
       const int r = i / cw, gl = i - r * cw;
-      sT[r * HP_LD + gl] = srow[(int64_t)r * G + c0 + gl];
+      sT[r * HP_LD + gl] = ld_sb(f.scales, e0 + (int64_t)r * Gq + c0 + gl, sbt);
     }
     __syncthreads();
     if (lane < rows) {
       for (int gl = wave; gl < cw; gl += 4) {
+        const int g = c0 + gl;
         const float prev = gl > 0 ? sT[lane * HP_LD + gl - 1] : sprev[lane];
-        rt[(int64_t)(NB + c0 + gl) * V + v] = scale_eff(prev) / scale_eff(sT[lane * HP_LD + gl]);
+        const float e = scale_eff(prev) / scale_eff(sT[lane * HP_LD + gl]);
+        if (f.gs == 64) {
+          f.rt[(int64_t)(NB + g) * V + v] = e;
+        } else if (f.gs == 128) {
+          f.rt[(int64_t)(NB + 2 * g) * V + v] = e;
+          f.rt[(int64_t)(NB + 2 * g + 1) * V + v] = 1.0f;
+        } else {
+          ((g & 1) ? f.rt2 : f.rt)[(int64_t)(NB + (g >> 1)) * V + v] = e;
+        }
       }
     }
     __syncthreads();
     if (tid < rows) sprev[tid] = sT[tid * HP_LD + cw - 1];
   }
-  if (tid < rows) slast[v0 + tid] = scale_eff(sprev[tid]);
+  if (tid < rows) f.slast[v0 + tid] = scale_eff(sprev[tid]);
 }
 
 template <int BITS>
 __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
-  __shared__ float sS[MAX_G];
+  __shared__ float sS[MAX_GQ];
   __shared__ float sRed[4];
   __shared__ float sT[HP_ROWS * HP_LD];
   const int tid = threadIdx.x;
   if (blockIdx.x >= (unsigned)f.M_pad) {
-    head_prep_block((int64_t)blockIdx.x - f.M_pad, f.biases, f.scales, BITS == 8 ? 128.0f : 0.0f, f.V, f.G, f.Kb,
-                    f.NB, f.baug, f.rt, f.slast, sS, sT);
+    head_prep_block((int64_t)blockIdx.x - f.M_pad, f, BITS == 8 ? 128.0f : 0.0f, sS, sT);
     return;
   }
   const int r = blockIdx.x;
@@ -188,9 +203,10 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
   } else {
     src = f.idx[r];
   }
-  const int H = f.H, G = f.G, Kb = f.Kb;
+  const int H = f.H, Gq = f.Gq, Kb = f.Kb;
   const int64_t ks16 = f.Ka / 16;
-  const int nch = H / 8;  // 16-byte chunks of the h part; 8 per group
+  const int nch = H / 8;     // 16-byte chunks of the h part
+  const int cpg = f.gs / 8;  // chunks per quantization group (4, 8 or 16)
   const int tgt = (src >= 0) ? f.targets[src] : -1;
   const bool has_t = src >= 0 && tgt >= 0 && (int64_t)tgt < f.V;
   const uint32_t *wrow = f.wq + (size_t)(has_t ? tgt : 0) * f.wpr;
@@ -206,14 +222,12 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
       if (has_t) dot += lo * (float)code_at<BITS>(wrow, 8 * c + 2 * e) + hi * (float)code_at<BITS>(wrow, 8 * c + 2 * e + 1);
     }
     if (has_t) {
-      const size_t gi = (size_t)tgt * G + (c >> 3);
-      zpart += f.scales[gi] * dot + f.biases[gi] * part;
+      const int64_t gi = (int64_t)tgt * Gq + c / cpg;
+      zpart += ld_sb(f.scales, gi, f.sbt) * dot + ld_sb(f.biases, gi, f.sbt) * part;
     }
-    // the 8 chunks of one group sit in 8 consecutive lanes
-    part += __shfl_xor(part, 1, 8);
-    part += __shfl_xor(part, 2, 8);
-    part += __shfl_xor(part, 4, 8);
-    if ((c & 7) == 0) sS[c >> 3] = part;
+    // the chunks of one group sit in cpg consecutive lanes
+    for (int o = 1; o < cpg; o <<= 1) part += __shfl_xor(part, o, 16);
+    if (c % cpg == 0) sS[c / cpg] = part;
   }
   zpart = wave_sum(zpart);
   if ((tid & 63) == 0) sRed[tid >> 6] = zpart;
@@ -226,7 +240,7 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int kk = 8 * c + 2 * e + u;
-        const int part = kk / G, gi = kk - part * G;
+        const int part = kk / Gq, gi = kk - part * Gq;
         uint32_t val = 0;
         if (part < 3) {
           const float S = sS[gi];
@@ -367,9 +381,9 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     for (int k = 0; k < ksd; ++k) acc += a.dh_part[((size_t)k * act * BM + r) * H + d];
     const TokRec rec = tok[r];
     if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
-      const size_t gi = (size_t)rec.tgt * a.G + d / KSTEP;
+      const int64_t gi = (int64_t)rec.tgt * a.Gq + d / a.gs;
       const float q = (float)code_at<BITS>(a.wq + (size_t)rec.tgt * a.wpr, d);
-      acc += rec.tval * (a.scales[gi] * q + a.biases[gi]);
+      acc += rec.tval * (ld_sb(a.scales, gi, a.sbt) * q + ld_sb(a.biases, gi, a.sbt));
     }
   }
   dh[(size_t)t * H + d] = acc;

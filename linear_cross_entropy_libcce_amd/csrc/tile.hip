@@ -54,7 +54,7 @@ enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
 // codes: the first 2 words per row), and the fold ratio of one row.
 struct ProdRegs {
   uint32_t w[8];
-  float r;
+  float r, r2;  // fold ratios at the step's K columns 0 and (group 32 only) 32
 };
 
 // The LDS code tile is [256 rows][64 K] bf16 without padding; the 16-byte
@@ -66,7 +66,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chu
 // Producer mapping: wave w, lane l loads the 16-byte K slice l & 3 of rows
 // 32w + (l >> 2) and 32w + 16 + (l >> 2), so one load instruction covers 16
 // rows x 64 contiguous bytes.  Threads 0..255 also carry row t's fold ratio.
-template <int BITS>
+template <int BITS, bool GS32>
 struct Producer {
   int row0, q, tid;
 
@@ -90,6 +90,10 @@ struct Producer {
     }
     const rsrc_t rr = make_rsrc(a.rt + (int64_t)step * a.V + v0, rows * 4);
     p.r = buf_loadf(rr, (tid & (BNT - 1)) * 4, 0);
+    if (GS32) {
+      const rsrc_t rr2 = make_rsrc(a.rt2 + (int64_t)step * a.V + v0, rows * 4);
+      p.r2 = buf_loadf(rr2, (tid & (BNT - 1)) * 4, 0);
+    }
   }
 
   // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
@@ -110,7 +114,10 @@ struct Producer {
   }
 
   __device__ __forceinline__ void ratio(const ProdRegs &p, float *sr) const {
-    if (tid < BNT) sr[tid] = p.r;
+    if (tid < BNT) {
+      sr[tid] = p.r;
+      if (GS32) sr[BNT + tid] = p.r2;  // sr is [K column 0, 32][row] of one buffer
+    }
   }
 };
 
@@ -123,7 +130,7 @@ __device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) 
   return cap * th;
 }
 
-template <int BITS, int MODE, int VAR>
+template <int BITS, int MODE, int VAR, bool GS32>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
   constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
@@ -144,7 +151,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int steps = a.NB + a.G;
 
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KSTEP];
-  __shared__ __attribute__((aligned(16))) float sR[2][BNT];
+  __shared__ __attribute__((aligned(16))) float sR[2][GS32 ? 2 : 1][BNT];  // [buffer][K column 0, 32][row]
   __shared__ __attribute__((aligned(16))) float sZ[8][64 * ZROW];
   __shared__ float sX[2][BM];  // EXTRA: per-wave tile maxima, read after the step's barrier
 
@@ -184,7 +191,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   }
   const int total = n_tiles * steps;
   if (total > 0) {
-    Producer<BITS> pr;
+    Producer<BITS, GS32> pr;
     pr.row0 = wave * 32 + (lane >> 2);
     pr.q = lane & 3;
     pr.tid = tid;
@@ -212,7 +219,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, v1, s1, P1);
 #pragma unroll
       for (int part = 0; part < 4; ++part) pr.store(true, part, P0, sW[0]);
-      pr.ratio(P0, sR[0]);
+      pr.ratio(P0, sR[0][0]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, 0));
@@ -231,7 +238,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       float r[4];
       if (live)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+        for (int c = 0; c < 4; ++c) r[c] = sR[cb][0][vcol0 + c * 32 + l32];
       const int hnext = sn * 4096;
       // B operand of column block c for k-step ks + 1 is read as soon as its
       // two MFMAs of k-step ks are issued; a scheduling barrier after each
@@ -249,6 +256,10 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               if (ks == 0) acc[rb][c] *= r[c];
+              if (GS32 && ks == 2) {  // group 32: the second group of the step
+                if (rb == 0) r[c] = sR[cb][GS32 ? 1 : 0][vcol0 + c * 32 + l32];
+                acc[rb][c] *= r[c];
+              }
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             }
             if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTEP);
@@ -259,7 +270,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         pr.store(sbias, ks, cur, sW[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pr.ratio(cur, sR[cb ^ 1]);
+      pr.ratio(cur, sR[cb ^ 1][0]);
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
@@ -433,12 +444,19 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
   const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
   const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
-  const int var = extra ? VAR_EXTRA : (a.small ? VAR_SMALL : VAR_PLAIN);
-#define CCE_TILE(B, MD)                                                                        \
-  do {                                                                                         \
-    if (var == VAR_EXTRA) hipLaunchKernelGGL((k_tile<B, MD, VAR_EXTRA>), grid, dim3(TW), 0, st, a); \
-    else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL>), grid, dim3(TW), 0, st, a); \
-    else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN>), grid, dim3(TW), 0, st, a);            \
+  const bool gs32 = a.rt2 != nullptr;
+  // group 32 has no small-M instantiation (the plain one is correct there)
+  const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? VAR_SMALL : VAR_PLAIN);
+#define CCE_TILE(B, MD)                                                                                          \
+  do {                                                                                                           \
+    if (gs32) {                                                                                                  \
+      if (var == VAR_EXTRA) hipLaunchKernelGGL((k_tile<B, MD, VAR_EXTRA, true>), grid, dim3(TW), 0, st, a);      \
+      else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);                       \
+    } else {                                                                                                     \
+      if (var == VAR_EXTRA) hipLaunchKernelGGL((k_tile<B, MD, VAR_EXTRA, false>), grid, dim3(TW), 0, st, a);     \
+      else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL, false>), grid, dim3(TW), 0, st, a); \
+      else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                      \
+    }                                                                                                            \
   } while (0)
   if (bits == 4) {
     if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);

@@ -32,11 +32,11 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 2
+    assert lib.cce_abi_version() == 3
 
 
 def head(**kw):
-    d = dict(wq=0x1000, scales=0x2000, biases=0x3000, V=1000, H=256, bits=4, group=64, softcap=0.0)
+    d = dict(wq=0x1000, scales=0x2000, biases=0x3000, V=1000, H=256, bits=4, group=64, softcap=0.0, sb_dtype=0)
     d.update(kw)
     return cce.cce_head(**d)
 
@@ -60,7 +60,12 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=5), cce.CCE_ERR_UNSUPPORTED),
     (dict(bits=2), cce.CCE_ERR_UNSUPPORTED),
-    (dict(group=32), cce.CCE_ERR_UNSUPPORTED),
+    (dict(group=16), cce.CCE_ERR_UNSUPPORTED),
+    (dict(group=256), cce.CCE_ERR_UNSUPPORTED),
+    (dict(group=32, H=96), cce.CCE_ERR_UNSUPPORTED),   # a multiple of the group, not of the 64-wide K step
+    (dict(sb_dtype=3), cce.CCE_ERR_UNSUPPORTED),
+    (dict(sb_dtype=0, scales=0x2002), cce.CCE_ERR_INVALID_ARG),   # fp32 scales need 4-byte alignment
+    (dict(sb_dtype=1, scales=0x2001), cce.CCE_ERR_INVALID_ARG),   # 16-bit ones 2-byte alignment
     (dict(H=100), cce.CCE_ERR_INVALID_ARG),      # not a multiple of the group
     (dict(H=32768), cce.CCE_ERR_UNSUPPORTED),
     (dict(V=0), cce.CCE_ERR_INVALID_ARG),

@@ -83,10 +83,20 @@ SMALL = {
                                           mask_frac=0.5),
     "H4096_V300_4bit": dict(M=257, H=4096, V=300, bits=4),
     "H2560_V260_8bit_cap_small_scales": dict(M=140, H=2560, V=260, bits=8, softcap=30.0),
-    # M >= 4096 selects the 512-token x 128-row logit tile: ragged token and vocabulary tails there
+    # M above 4096: many token tiles, ragged token and vocabulary tails
     "wide_H256_V700_4bit": dict(M=4200, H=256, V=700, bits=4),
     "wide_H512_V389_8bit_cap_randmask": dict(M=4500, H=512, V=389, bits=8, softcap=30.0, mask="random",
                                              mask_frac=0.4),
+    # quantization groups of 32 (two folds per K step) and 128, bf16 / fp16 scales and biases
+    "H512_V900_8bit_group32": dict(M=300, H=512, V=900, bits=8, group=32),
+    "H768_V700_4bit_cap_group32_bf16_randmask": dict(M=400, H=768, V=700, bits=4, softcap=30.0, group=32,
+                                                     sb_dtype="bf16", mask="random", mask_frac=0.3),
+    "H1024_V600_8bit_group128_f16": dict(M=270, H=1024, V=600, bits=8, group=128, sb_dtype="f16"),
+    "H384_V500_4bit_group128_bf16_zipf": dict(M=100, H=384, V=500, bits=4, group=128, sb_dtype="bf16",
+                                              targets="zipf"),
+    "H2560_V300_8bit_cap_f16": dict(M=200, H=2560, V=300, bits=8, softcap=30.0, sb_dtype="f16"),
+    "M40_H512_V900_8bit_group32": dict(M=40, H=512, V=900, bits=8, group=32),
+    "M50_H640_V333_4bit_group128_bf16": dict(M=50, H=640, V=333, bits=4, group=128, sb_dtype="bf16"),
 }
 
 
