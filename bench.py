@@ -89,6 +89,9 @@ def main():
                     help="synthetic workload index (0-4); 3 is the measured configuration")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override M (e.g. 1024: one GPU's share of workload 3 split over 8 GPUs)")
+    ap.add_argument("--group", type=int, default=None, help="override the quantization group (32, 64, 128)")
+    ap.add_argument("--sb-dtype", type=str, default=None, choices=["f32", "bf16", "f16"],
+                    help="override the storage of scales and biases")
     ap.add_argument("--skip", type=str, default=None, metavar="BLOCK_EPS,FILTER_EPS",
                     help="opt-in backward skips (e.g. 1e-5,1e-5): forward with block maxima, backward skipping")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -116,9 +119,13 @@ def main():
         log("calibration copy of %d bytes done" % COPY_BYTES)
 
     w = syn.WORKLOADS[args.workload]
+    import dataclasses
     if args.tokens is not None:
-        import dataclasses
         w = dataclasses.replace(w, M=args.tokens, name="%s, M=%d" % (w.name, args.tokens))
+    if args.group is not None:
+        w = dataclasses.replace(w, group=args.group, name="%s, group %d" % (w.name, args.group))
+    if args.sb_dtype is not None:
+        w = dataclasses.replace(w, sb_dtype=args.sb_dtype, name="%s, %s scales" % (w.name, args.sb_dtype))
     log("generating workload %d (%s)" % (args.workload, w.name))
     inp = syn.make_inputs(w, syn.seed_for(args.workload))
     M, H, V = inp["M"], inp["H"], inp["V"]
@@ -200,7 +207,8 @@ def main():
         log("  %-10s %5.1f launches/step  %8.3f ms/step" % (k, n, tot))
 
     alg_flops = 6.0 * M_eff * V * H          # forward logits + backward recompute + dh
-    head_bytes = V * (H * inp["bits"] // 8) + 2 * 4 * V * (H // 64)  # packed codes + fp32 scales and biases
+    sb_size = 4 if inp.get("sb_dtype", "f32") == "f32" else 2
+    head_bytes = V * (H * inp["bits"] // 8) + 2 * sb_size * V * (H // inp["group"])  # packed codes + scales and biases
     head_gbs = 2.0 * head_bytes / (ms * 1e-3) / 1e9                   # the head is read by both passes
     tflops = alg_flops / (ms * 1e-3) / 1e12
     per_kernel_flops = {"tile_fwd": 2.0 * M_eff * V * H, "tile_bwd": 2.0 * M_eff * V * H,
@@ -211,7 +219,8 @@ def main():
     if dom in per_kernel_flops:
         flop_launch = per_kernel_flops[dom] / n_l
         achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
-        tb = measured_traffic(dom) if (args.workload == 3 and args.tokens is None and not args.skip) else None
+        default_cfg = args.tokens is None and not args.skip and args.group is None and args.sb_dtype is None
+        tb = measured_traffic(dom) if (args.workload == 3 and default_cfg) else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": tb,
@@ -239,7 +248,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V, "bits": inp["bits"],
-                   "group": 64, "softcap": inp["softcap"], "g": 1.0,
+                   "group": inp["group"], "sb_dtype": inp.get("sb_dtype", "f32"), "softcap": inp["softcap"], "g": 1.0,
                    "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps}},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),

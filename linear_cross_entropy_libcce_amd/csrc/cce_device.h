@@ -241,10 +241,12 @@ __device__ __forceinline__ int xcd_remap(int b, int nb_grid) {
 // Scales and biases are stored as fp32, bf16 or fp16 (SB_*); all widen
 // exactly to fp32.
 enum { SB_F32 = 0, SB_BF16 = 1, SB_F16 = 2 };
+// (selects, no branches: this sits in the dh contraction's main loop)
 __device__ __forceinline__ float sb_widen(uint32_t bits, int sbt) {
-  if (sbt == SB_F32) return __uint_as_float(bits);
-  if (sbt == SB_BF16) return __uint_as_float(bits << 16);
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  const float bf = __uint_as_float(bits << 16);
+  const float f = __uint_as_float(bits);
+  return sbt == SB_F32 ? f : (sbt == SB_BF16 ? bf : hf);
 }
 __device__ __forceinline__ float ld_sb(const void *base, int64_t i, int sbt) {
   if (sbt == SB_F32) return static_cast<const float *>(base)[i];

@@ -44,31 +44,36 @@ __device__ __forceinline__ int dswz(int d, int chunk) { return d * KSTP + ((chun
 // of the step and columns 4*dc .. 4*dc+3 of the tile; lanes are 16 dc x 4 rgp,
 // so one load instruction covers 4 rows and the 16-byte LDS writes of 16
 // lanes fall in distinct banks.  The scales and biases of the step's 64 rows
-// x (256 / group) groups are loaded once per workgroup (value e = tid + 512 k:
-// scales then biases, rows, then groups fastest, so the loads are contiguous)
-// into LDS and read back by the dequantizing threads.
+// x 2^LG groups (LG = log2(256 / group)) are loaded once per workgroup (value
+// e = tid + 512 k: scales then biases, rows, then groups fastest, so the
+// loads are contiguous) into LDS and read back by the dequantizing threads.
+// SBW is the stored width of a scale or bias (4: fp32, 2: bf16 or fp16).
 constexpr int SB_SLOT = 2 * 8 * KSTP;  // floats of one staged step: 2 x (up to 8 groups) x 64 rows
 
 template <int BITS>
 struct DhRegs {
   uint32_t w[8];  // 8-bit: 4 codes of row e; 4-bit: 4 codes in the low 16 bits
-  float sb[2];    // scales or biases of the step this thread stages
+  uint32_t sb[2]; // raw bits of the scales or biases this thread stages (widened when staged,
+                  // so the load is not waited for before the step's end)
 };
 
-template <int BITS>
+template <int BITS, int LG, int SBW>
 struct DhProducer {
+  static constexpr int NVAL = (2 * KSTP) << LG;      // staged values per step
+  static constexpr int NK = (NVAL + 511) / 512;      // per thread (1 or 2; half the threads for LG = 1)
+  static constexpr int GSH = 6 - LG;                 // column block dc lies in group dc >> GSH
   int rgp, dc;    // rows 8*rgp + e, columns 4*dc + k of the tile
   int wcol;       // byte offset of those columns within a packed row
   int tid;
   int gq0;        // first quantization group of the tile
-  int lg;         // log2 of the groups per tile row (256 / group: 1, 2 or 3)
-  int gsh;        // log2(group / 4): the group of column block dc is dc >> gsh
 
   // staged value e: (is a bias, row, group within the tile)
   __device__ __forceinline__ void sb_slot(int e, int &isb, int &row, int &g) const {
-    isb = e >> (6 + lg);
-    row = (e >> lg) & (KSTP - 1);
-    g = e & ((1 << lg) - 1);
+    // a run of 64 << LG >= 128 consecutive values shares isb, so it is
+    // uniform in a wave: keep it scalar (it selects the buffer base)
+    isb = __builtin_amdgcn_readfirstlane(e >> (6 + LG));
+    row = (e >> LG) & (KSTP - 1);
+    g = e & ((1 << LG) - 1);
   }
 
   __device__ __forceinline__ void load(const GemmArgs &a, int64_t vs, DhRegs<BITS> &p) const {
@@ -80,39 +85,36 @@ struct DhProducer {
       if (BITS == 8) p.w[e] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff, 0, 0);
       else p.w[e] = __builtin_amdgcn_raw_buffer_load_b16(rw, voff, 0, 0);
     }
-    const int esz = a.sbt == SB_F32 ? 4 : 2;
-    const int64_t nb = rows * a.Gq * esz;
-    const rsrc_t rsc = make_rsrc(static_cast<const char *>(a.scales) + vs * a.Gq * esz, nb);
-    const rsrc_t rbi = make_rsrc(static_cast<const char *>(a.biases) + vs * a.Gq * esz, nb);
+    const int64_t nb = rows * a.Gq * SBW;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
       const int e = tid + 512 * k;
       int isb, row, g;
       sb_slot(e, isb, row, g);
-      const int off = (row * a.Gq + gq0 + g) * esz;
-      uint32_t x = 0;
-      if (e < (2 * KSTP) << lg) {
-        if (esz == 4) x = __builtin_amdgcn_raw_buffer_load_b32(isb ? rbi : rsc, off, 0, 0);
-        else x = __builtin_amdgcn_raw_buffer_load_b16(isb ? rbi : rsc, off, 0, 0);
+      const rsrc_t rs = make_rsrc(static_cast<const char *>(isb ? a.biases : a.scales) + vs * a.Gq * SBW, nb);
+      const int off = (row * a.Gq + gq0 + g) * SBW;
+      if (NVAL >= 512 || e < NVAL) {
+        if (SBW == 4) p.sb[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        else p.sb[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
       }
-      p.sb[k] = sb_widen(x, a.sbt);
     }
   }
 
   // LDS stage of the step's scales and biases: [group j][row][scale, bias].
-  __device__ __forceinline__ void stage_sb(const DhRegs<BITS> &p, float *ssb) const {
+  __device__ __forceinline__ void stage_sb(const DhRegs<BITS> &p, float *ssb, int sbt) const {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
       const int e = tid + 512 * k;
       int isb, row, g;
       sb_slot(e, isb, row, g);
-      if (e < (2 * KSTP) << lg) ssb[(g * KSTP + row) * 2 + isb] = p.sb[k];
+      if (NVAL >= 512 || e < NVAL)
+        ssb[(g * KSTP + row) * 2 + isb] = SBW == 4 ? __uint_as_float(p.sb[k]) : sb_widen(p.sb[k], sbt);
     }
   }
 
   // (scale, bias) of the thread's 8 rows (group j = 4 dc / group).
   __device__ __forceinline__ void read_sb(const float *ssb, float (&s)[8], float (&b)[8]) const {
-    const float *src = ssb + ((dc >> gsh) * KSTP + 8 * rgp) * 2;
+    const float *src = ssb + ((dc >> GSH) * KSTP + 8 * rgp) * 2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 x = *(const float2 *)(src + 2 * e);
@@ -137,7 +139,7 @@ struct DhProducer {
 
 constexpr int MAX_LIST = 2048;  // vocabulary tiles per split (a chunk holds at most 2048)
 
-template <int BITS, bool SKIP, bool SMALL>
+template <int BITS, bool SKIP, bool SMALL, int LG, int SBW>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only;
@@ -214,14 +216,12 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
 
   if (nsteps > 0) {
-    DhProducer<BITS> pr;
+    DhProducer<BITS, LG, SBW> pr;
     pr.dc = (lane & 15) + 16 * (wave & 3);
     pr.rgp = (lane >> 4) + 4 * (wave >> 2);
     pr.wcol = (d0 + 4 * pr.dc) * BITS / 8;
     pr.tid = tid;
     pr.gq0 = d0 / a.gs;
-    pr.lg = a.gs == 32 ? 3 : (a.gs == 64 ? 2 : 1);
-    pr.gsh = a.gs == 32 ? 3 : (a.gs == 64 ? 4 : 5);
     DhRegs<BITS> P0, P1;
     // this lane's B-operand chunk offsets (row dh*128 + l32 + 32c, chunk 2ks + lh);
     // the swizzle key of row d + 32c equals that of row d
@@ -244,8 +244,8 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 
     pr.load(a, vrow(0), P0);
     pr.load(a, vrow(1), P1);
-    pr.stage_sb(P0, sSB[0]);
-    pr.stage_sb(P1, sSB[1]);
+    pr.stage_sb(P0, sSB[0], a.sbt);
+    pr.stage_sb(P1, sSB[1], a.sbt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, koff(0)));
@@ -286,7 +286,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
         pr.store(ks, cur, sc, bi, sB[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pr.stage_sb(nxt, sSB[cb]);
+      pr.stage_sb(nxt, sSB[cb], a.sbt);
       __syncthreads();
     };
     int st = 0;
@@ -318,17 +318,42 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   }
 }
 
-void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
-  const bool skip = a.fl != nullptr, small = !skip && a.small;
-  if (bits == 4) {
-    if (skip) hipLaunchKernelGGL((k_dh<4, true, false>), grid, dim3(TW), 0, st, a);
-    else if (small) hipLaunchKernelGGL((k_dh<4, false, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_dh<4, false, false>), grid, dim3(TW), 0, st, a);
-  } else {
-    if (skip) hipLaunchKernelGGL((k_dh<8, true, false>), grid, dim3(TW), 0, st, a);
-    else if (small) hipLaunchKernelGGL((k_dh<8, false, true>), grid, dim3(TW), 0, st, a);
-    else hipLaunchKernelGGL((k_dh<8, false, false>), grid, dim3(TW), 0, st, a);
+template <int B, int LG, int SBW>
+static void launch_dh_variant(hipStream_t st, dim3 grid, const GemmArgs &a, bool skip, bool small) {
+  if (skip) {
+    hipLaunchKernelGGL((k_dh<B, true, false, LG, SBW>), grid, dim3(TW), 0, st, a);
+    return;
   }
+  if constexpr (LG == 2 && SBW == 4) {
+    if (small) {
+      hipLaunchKernelGGL((k_dh<B, false, true, LG, SBW>), grid, dim3(TW), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_dh<B, false, false, LG, SBW>), grid, dim3(TW), 0, st, a);
+}
+
+template <int B>
+static void launch_dh_bits(hipStream_t st, dim3 grid, const GemmArgs &a) {
+  const bool skip = a.fl != nullptr;
+  const bool wide = a.sbt == SB_F32;
+  // the small-M instantiation exists for the default storage only (group 64, fp32)
+  const bool small = !skip && a.small && a.gs == KSTEP && wide;
+  if (a.gs == 64) {
+    if (wide) launch_dh_variant<B, 2, 4>(st, grid, a, skip, small);
+    else launch_dh_variant<B, 2, 2>(st, grid, a, skip, false);
+  } else if (a.gs == 32) {
+    if (wide) launch_dh_variant<B, 3, 4>(st, grid, a, skip, false);
+    else launch_dh_variant<B, 3, 2>(st, grid, a, skip, false);
+  } else {
+    if (wide) launch_dh_variant<B, 1, 4>(st, grid, a, skip, false);
+    else launch_dh_variant<B, 1, 2>(st, grid, a, skip, false);
+  }
+}
+
+void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
+  if (bits == 4) launch_dh_bits<4>(st, grid, a);
+  else launch_dh_bits<8>(st, grid, a);
 }
 
 }  // namespace cce
