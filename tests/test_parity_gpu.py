@@ -161,6 +161,12 @@ EDGE = {
     "V65": dict(M=7, H=320, V=65, bits=4),
     "H64": dict(M=33, H=64, V=1000, bits=8),
     "H320_ragged_dh_tile": dict(M=40, H=320, V=200, bits=4),
+    # the largest H (256 K steps, a 12-step bias block), with group 32 the most groups (512)
+    "H16384_V200_8bit_cap": dict(M=20, H=16384, V=200, bits=8, softcap=30.0),
+    "H16384_V100_4bit_group32": dict(M=10, H=16384, V=100, bits=4, group=32),
+    # one row in the last vocabulary tile; the compaction launch just past the fused threshold
+    "V65537_tail_row": dict(M=30, H=128, V=65537, bits=4),
+    "M2049_separate_compaction": dict(M=2049, H=64, V=300, bits=8, mask="random", mask_frac=0.5),
 }
 
 
@@ -187,6 +193,29 @@ def test_all_masked_and_out_of_range_targets(torch_cuda):
     orc = oracle.cce(inp)
     check(inp, gpu, orc, np.arange(20), "oob-targets")
     assert np.allclose(gpu[0][:4], -gpu[1][:4], atol=1e-6)
+
+
+def test_workspace_reuse_across_sizes(torch_cuda):
+    # one caller-owned workspace (sized for the larger call) serves calls of
+    # different M back to back, forward and backward, with results equal to
+    # calls on fresh workspaces
+    import torch
+    big = syn.make_custom(M=600, H=256, V=900, bits=8, seed=21, softcap=30.0)
+    small = syn.make_custom(M=70, H=256, V=900, bits=8, seed=22, softcap=30.0)
+    head = cce.head_from_numpy(big)
+    wsf = torch.empty(cce.forward_workspace_bytes(head, 600), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(cce.backward_workspace_bytes(head, 600), dtype=torch.uint8, device="cuda")
+    outs = []
+    for inp in (big, small, big):
+        h, t, m = cce.tokens_from_numpy(inp)
+        logp, lse = cce.cce_forward(h, head, t, m, workspace=wsf)
+        dh = cce.cce_backward(h, head, t, lse, None, m, workspace=wsb)
+        logp0, lse0 = cce.cce_forward(h, head, t, m)
+        dh0 = cce.cce_backward(h, head, t, lse0, None, m)
+        torch.cuda.synchronize()
+        assert torch.equal(logp, logp0) and torch.equal(lse, lse0) and torch.equal(dh, dh0)
+        outs.append(logp.cpu().numpy())
+    assert np.array_equal(outs[0], outs[2])
 
 
 def test_repeat_runs_are_bitwise_identical(torch_cuda):
