@@ -167,6 +167,8 @@ EDGE = {
     # one row in the last vocabulary tile; the compaction launch just past the fused threshold
     "V65537_tail_row": dict(M=30, H=128, V=65537, bits=4),
     "M2049_separate_compaction": dict(M=2049, H=64, V=300, bits=8, mask="random", mask_frac=0.5),
+    # more than 2048 vocabulary tiles: two coefficient chunks (the later one accumulates into the slabs)
+    "V600000_two_chunks": dict(M=20, H=64, V=600000, bits=8, softcap=20.0),
 }
 
 

@@ -170,3 +170,29 @@ def test_peaked_workload_full_size(torch_cuda):
     err = np.abs(gb - ob).max()
     say("workload %d: max|d block_max| = %.3g" % (cfg, err))
     assert err <= LOGIT_TOL
+
+
+def two_chunk_head():
+    """V = 530000 (2071 vocabulary tiles: two coefficient chunks of at most
+    2048).  Block 3 (in the first chunk) and block 2052 (in the second) have
+    8x scales, so they are hot for every token; the flat rest is cold at
+    block_eps = 2e-2 except where targets fall.  Reading the second chunk's
+    flags at a wrong offset drops block 2052 or keeps cold ones."""
+    inp = syn.make_custom(M=40, H=64, V=530000, bits=8, seed=74, targets="zipf")
+    for b in (3, 2052):
+        inp["scales"][256 * b:256 * b + 256] *= np.float32(8.0)
+    inp["biases"] = (-128.0 * inp["scales"]).astype(np.float32)
+    return inp
+
+
+def test_skips_across_two_coefficient_chunks(torch_cuda):
+    inp = two_chunk_head()
+    g = np.linspace(-1.0, 1.5, inp["M"])
+    say("two chunks: block_eps=2e-2")
+    _, gdh = gpu_run(torch_cuda, inp, g, 2e-2, 0.0)
+    _, _, odh, dropped = oracle.cce_skip(inp, g=g, block_eps=2e-2)
+    rel = np.linalg.norm(gdh - odh) / np.linalg.norm(odh)
+    say("two chunks: %d of %d pairs dropped (blocks 3, 2052 kept: %s), GPU vs oracle %.3g"
+        % (dropped.sum(), dropped.size, (not dropped[0, 3]) and (not dropped[0, 2052]), rel))
+    assert not dropped[0, 3] and not dropped[0, 2052] and dropped.sum() > 1000
+    assert rel <= DH_TOL
