@@ -21,7 +21,7 @@ using namespace cce;
 
 constexpr int64_t MAX_H = 16384;
 constexpr int64_t MAX_M = (int64_t)1 << 24;
-constexpr size_t COEFF_BUDGET = (size_t)4 << 30;  // bytes of one coefficient chunk
+constexpr size_t COEFF_BUDGET = (size_t)1 << 30;  // bytes of one coefficient chunk
 constexpr int64_t MAX_CHUNK_TILES = 2048;          // vocabulary tiles of one coefficient chunk
 constexpr int64_t FUSED_COMPACT_MAX_M = 2048;      // tokens compacted inside the front launch
 
