@@ -94,6 +94,8 @@ def main():
                     help="override the storage of scales and biases")
     ap.add_argument("--skip", type=str, default=None, metavar="BLOCK_EPS,FILTER_EPS",
                     help="opt-in backward skips (e.g. 1e-5,1e-5): forward with block maxima, backward skipping")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (launch-bound small M)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -164,6 +166,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    timed_step = step
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        timed_step = graph.replay
+        log("captured one step in a HIP graph")
 
     log("timing %d steps" % args.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -171,7 +186,7 @@ def main():
     wall0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        step()
+        timed_step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -249,7 +264,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V, "bits": inp["bits"],
                    "group": inp["group"], "sb_dtype": inp.get("sb_dtype", "f32"), "softcap": inp["softcap"], "g": 1.0,
-                   "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps}},
+                   "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps},
+                   "hip_graph": bool(args.graph)},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),
         "tflops": round(tflops, 1),

@@ -22,7 +22,9 @@
  *    pointer after a call returns and never allocates device memory.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Buffers must stay valid until the stream has passed the work.
- *    Nothing synchronizes with the host.
+ *    Nothing synchronizes with the host.  A call only enqueues kernels (no
+ *    allocation, memset or host synchronization), so it can be captured in a
+ *    HIP graph and replayed with the same buffers.
  *  - The library holds no state; calls on different streams are independent
  *    provided each has its own workspace.  Two calls in flight that share a
  *    workspace race.

@@ -257,3 +257,45 @@ def test_small_m_on_the_full_head(torch_cuda, M):
     gpu = run_gpu(torch_cuda, inp, g=g)
     say("small M=%d: oracle on all tokens" % M)
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "smallM%d" % M)
+
+
+def test_hip_graph_capture_and_replay(torch_cuda):
+    # the calls enqueue kernels only (no allocation, no host synchronization,
+    # no memset), so a forward + backward can be captured in a HIP graph; every
+    # replay, with eager work and synchronizations between them, must match
+    # the eager result bit for bit
+    import torch
+    inp = syn.make_custom(M=300, H=512, V=2000, bits=8, seed=31, softcap=30.0, mask="random", mask_frac=0.2)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    M, H = inp["M"], inp["H"]
+    wsf = torch.empty(cce.forward_workspace_bytes(head, M), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(cce.backward_workspace_bytes(head, M), dtype=torch.uint8, device="cuda")
+    logp = torch.empty(M, dtype=torch.float32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    dh = torch.empty((M, H), dtype=torch.float32, device="cuda")
+
+    def step():
+        cce.cce_forward(h, head, t, m, workspace=wsf, out=(logp, lse))
+        cce.cce_backward(h, head, t, lse, None, m, workspace=wsb, out=dh)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                      # warm-up on a side stream, as graph capture wants
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = (logp.clone(), lse.clone(), dh.clone())
+    say("graph: capture forward + backward")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        logp.zero_(); lse.zero_(); dh.zero_()
+        junk = torch.randn(1000, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("graph: replay %d" % rep)
+        assert torch.equal(logp, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(dh, ref[2])
+    del junk
