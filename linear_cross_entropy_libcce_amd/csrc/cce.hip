@@ -80,7 +80,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
   int64_t M, M_pad, V, H;
-  int G, Kb, Ka, NB, bits, wpr, TT, tiles;  // G: 64-wide K steps of h (H / 64)
+  int G, Kb, Ka, NB, bits, wpr, TT, tiles;  // NB, G: tile K steps (kw columns) of the bias block and of h
+  int kw;                                   // 64, or 32 for quantization group 32 (one group per step)
   int gs, Gq, sbt;                           // quantization group, groups per row, scale/bias dtype
   float cap;
   // forward
@@ -89,7 +90,7 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_rt2, o_slast, o_part, o_coeff, o_dhp, o_fl,
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, o_fl,
       fwd_bytes, bwd_bytes;
 };
 
@@ -118,14 +119,15 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.H = hd->H;
   p.bits = hd->bits;
   p.cap = hd->softcap;
-  p.G = (int)(p.H / KSTEP);
   p.gs = hd->group;
+  p.kw = p.gs == 32 ? 32 : KSTEP;
+  p.G = (int)(p.H / p.kw);
   p.Gq = (int)(p.H / p.gs);
   p.sbt = hd->sb_dtype;
   // bias block: three columns per quantization group (fixed-point digits x S hi/lo)
   p.Kb = (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
   p.Ka = p.Kb + (int)p.H;
-  p.NB = p.Kb / KSTEP;
+  p.NB = p.Kb / p.kw;
   p.wpr = (int)(p.H * p.bits / 32);
   p.TT = (int)(p.M_pad / BM);
   p.tiles = (int)cdiv(p.V, BNT);
@@ -185,8 +187,6 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
   p.o_rt = o; o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
-  p.o_rt2 = o;  // group 32: the fold ratio in the middle of every step
-  if (p.gs == 32) o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
   p.o_slast = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
   const size_t common = o;
   p.o_part = common;
@@ -257,7 +257,6 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   f.haug = haug;
   f.baug = ws_at<uint8_t>(ws, p.o_baug);
   f.rt = ws_at<float>(ws, p.o_rt);
-  f.rt2 = p.gs == 32 ? ws_at<float>(ws, p.o_rt2) : nullptr;
   f.gs = p.gs;
   f.Gq = p.Gq;
   f.sbt = p.sbt;
@@ -280,7 +279,6 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
   a.rt = ws_at<const float>(ws, p.o_rt);
-  a.rt2 = p.gs == 32 ? ws_at<const float>(ws, p.o_rt2) : nullptr;
   a.slast = ws_at<const float>(ws, p.o_slast);
   a.wq = hd->wq;
   a.cnt = ws_at<const int>(ws, p.o_cnt);
@@ -290,6 +288,7 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.Ka = p.Ka;
   a.Kb = p.Kb;
   a.NB = p.NB;
+  a.kw = p.kw;
   a.wpr = p.wpr;
   a.M_pad = (int)p.M_pad;
   a.ks16 = p.Ka / 16;
@@ -420,7 +419,6 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   ga.dh_part = ws_at<float>(workspace, p.o_dhp);
   ga.V = p.V;
   ga.H = (int)p.H;
-  ga.G = p.G;
   ga.gs = p.gs;
   ga.Gq = p.Gq;
   ga.sbt = p.sbt;

@@ -111,7 +111,6 @@ struct TileArgs {
   const uint16_t *haug;  // [M_pad][Ka] bf16, fragment-major
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
   const float *rt;       // [NB + G][V] fold ratio of every step (before its first K column)
-  const float *rt2;      // group 32: [NB + G][V] fold ratio at the step's K column 32 (else unused)
   const float *slast;    // [V] effective scale of the last group
   const uint32_t *wq;
   const int *cnt;
@@ -120,7 +119,8 @@ struct TileArgs {
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
   int64_t V;
-  int G, Ka, Kb, NB, wpr, M_pad;  // G: 64-wide K steps of the h part (H / 64)
+  int G, Ka, Kb, NB, wpr, M_pad;  // NB, G: K steps of the bias block and of h (kw columns each)
+  int kw;                // K columns per step: 64, or 32 for quantization group 32
   int64_t ks16;          // Ka / 16 (fragment-major h rows)
   int64_t ksv;           // ld_coeff / 16 (fragment-major coefficient chunk)
   int range_tile0, range_tiles;
@@ -153,9 +153,9 @@ struct FrontArgs {
   TokRec *tok;
   uint16_t *haug;
   uint8_t *baug;           // head side: bias-block digits, fold ratios, last scale
-  float *rt, *rt2, *slast;
+  float *rt, *slast;
   int64_t V;
-  int H, G, Kb, Ka, NB, wpr, M_pad;
+  int H, G, Kb, Ka, NB, wpr, M_pad;  // NB, G: tile K steps of the bias block and of h
   int gs, Gq, sbt;         // quantization group, groups per row, scale/bias dtype
   float cap;
   int bwd;
@@ -176,7 +176,7 @@ struct GemmArgs {
   float *dh_part;        // [ksplit][M_pad][H]
   int64_t V;
   int64_t chunk_v0;      // first vocabulary row of the chunk
-  int H, G, wpr, M_pad;  // G: H / 64
+  int H, wpr, M_pad;
   int gs, Gq, sbt;       // quantization group, groups per row, scale/bias dtype
   int chunk_steps;       // 64-row K steps in this chunk
   int max_chunk_steps;   // K steps of a full chunk (fixes the split across chunks)

@@ -112,14 +112,11 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
   const int64_t v = v0 + lane;
   if (wave == 0 && lane < rows) {
     sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
-    for (int s2 = 0; s2 < NB; ++s2) {
-      f.rt[s2 * V + v] = 1.0f;
-      if (f.gs == 32) f.rt2[s2 * V + v] = 1.0f;
-    }
+    for (int s2 = 0; s2 < NB; ++s2) f.rt[s2 * V + v] = 1.0f;
   }
   // group g's entry ratio s_{g-1} / s_g goes to the K step where g starts:
-  // group 64 -> step g; 128 -> step 2g (and ratio 1 at step 2g + 1);
-  // 32 -> step g/2 (even g) or the middle of step g/2 (odd g, table rt2)
+  // groups 32 and 64 -> step g (a step is one group: 32- or 64-wide);
+  // 128 -> step 2g (and ratio 1 at step 2g + 1)
   for (int c0 = 0; c0 < Gq; c0 += HP_COLS) {
     const int cw = Gq - c0 < HP_COLS ? Gq - c0 : HP_COLS;
     __syncthreads();  // sprev written, the previous chunk's reads done
@@ -133,13 +130,11 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
         const int g = c0 + gl;
         const float prev = gl > 0 ? sT[lane * HP_LD + gl - 1] : sprev[lane];
         const float e = scale_eff(prev) / scale_eff(sT[lane * HP_LD + gl]);
-        if (f.gs == 64) {
-          f.rt[(int64_t)(NB + g) * V + v] = e;
-        } else if (f.gs == 128) {
+        if (f.gs == 128) {
           f.rt[(int64_t)(NB + 2 * g) * V + v] = e;
           f.rt[(int64_t)(NB + 2 * g + 1) * V + v] = 1.0f;
         } else {
-          ((g & 1) ? f.rt2 : f.rt)[(int64_t)(NB + (g >> 1)) * V + v] = e;
+          f.rt[(int64_t)(NB + g) * V + v] = e;
         }
       }
     }

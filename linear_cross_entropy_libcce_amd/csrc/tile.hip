@@ -51,23 +51,35 @@ enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
 
 // One step's worth of head data for one producer thread: 16 K values of each
 // of two vocabulary rows (8-bit codes and bias digits: 4 words per row; 4-bit
-// codes: the first 2 words per row), and the fold ratio of one row.
+// codes: the first 2 words per row) -- or, with 32-wide steps, 16 K values of
+// one row -- and the fold ratio of one row.
 struct ProdRegs {
   uint32_t w[8];
-  float r, r2;  // fold ratios at the step's K columns 0 and (group 32 only) 32
+  float r;
 };
 
-// The LDS code tile is [256 rows][64 K] bf16 without padding; the 16-byte
-// chunk c of row n sits at chunk position c ^ ((n >> 1) & 7), which spreads
-// both the B-operand reads (consecutive rows, one chunk) and the producer
-// writes (4 rows x 4 chunk pairs per 16 lanes) over distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// The LDS code tile is [256 rows][KW K] bf16 without padding.  KW = 64: the
+// 16-byte chunk c of row n sits at chunk position c ^ ((n >> 1) & 7), which
+// spreads both the B-operand reads (consecutive rows, one chunk) and the
+// producer writes (4 rows x 4 chunk pairs per 16 lanes) over distinct bank
+// groups.  KW = 32 (group 32: one K step per quantization group, one fold per
+// step): chunk c of row n at c ^ ((n >> 2) & 3), so that 16 consecutive rows
+// of one chunk cover all 64 banks.
+template <int KW>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if (KW == 64) return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+  return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
 
-// Producer mapping: wave w, lane l loads the 16-byte K slice l & 3 of rows
-// 32w + (l >> 2) and 32w + 16 + (l >> 2), so one load instruction covers 16
-// rows x 64 contiguous bytes.  Threads 0..255 also carry row t's fold ratio.
+// Producer mapping, KW = 64: wave w, lane l loads the 16-byte K slice l & 3 of
+// rows 32w + (l >> 2) and 32w + 16 + (l >> 2), so one load instruction covers
+// 16 rows x 64 contiguous bytes.  KW = 32: thread t loads the K half t & 1 of
+// row t >> 1 (16 values: 16 bytes of 8-bit codes or digits, 8 of 4-bit
+// codes), one load instruction covering 32 rows x 32 K.  Threads 0..255 also
+// carry row t's fold ratio.
 template <int BITS, bool GS32>
 struct Producer {
+  static constexpr int KW = GS32 ? 32 : 64;
   int row0, q, tid;
 
   // Issue the loads of step `step` of the vocabulary tile at v0: a bias-block
@@ -82,18 +94,26 @@ struct Producer {
                            : make_rsrc(a.wq + v0 * a.wpr, rows * a.wpr * 4);
     const int rowb = bias ? a.Kb : a.wpr * 4;                // bytes per row
     const int qb = (bias || BITS == 8) ? 16 : 8;             // bytes per 16 K values
-    const int so = bias ? step * 64 : g * (8 * BITS);
+    const int so = bias ? step * KW : g * (KW * BITS / 8);
+    if (GS32) {
+      // row tid >> 1, K half tid & 1
+      const int voff = (tid >> 1) * rowb + (tid & 1) * qb;
+      if (bias || BITS == 8) {
+        const u32x4_t x = buf_load16(rw, voff, so);
+        p.w[0] = x[0]; p.w[1] = x[1]; p.w[2] = x[2]; p.w[3] = x[3];
+      } else {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rw, voff, so, 0);
+        p.w[0] = x[0]; p.w[1] = x[1];
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4_t x = buf_load16(rw, (row0 + 16 * i) * rowb + q * qb, so);
-      p.w[4 * i] = x[0]; p.w[4 * i + 1] = x[1]; p.w[4 * i + 2] = x[2]; p.w[4 * i + 3] = x[3];
+      for (int i = 0; i < 2; ++i) {
+        const u32x4_t x = buf_load16(rw, (row0 + 16 * i) * rowb + q * qb, so);
+        p.w[4 * i] = x[0]; p.w[4 * i + 1] = x[1]; p.w[4 * i + 2] = x[2]; p.w[4 * i + 3] = x[3];
+      }
     }
     const rsrc_t rr = make_rsrc(a.rt + (int64_t)step * a.V + v0, rows * 4);
     p.r = buf_loadf(rr, (tid & (BNT - 1)) * 4, 0);
-    if (GS32) {
-      const rsrc_t rr2 = make_rsrc(a.rt2 + (int64_t)step * a.V + v0, rows * 4);
-      p.r2 = buf_loadf(rr2, (tid & (BNT - 1)) * 4, 0);
-    }
   }
 
   // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
@@ -101,8 +121,9 @@ struct Producer {
   // written so); flipping the top bit gives the signed value q - 128 (resp.
   // the digit), one sign-extending convert per byte.  4-bit codes stay
   // unsigned.
+  // KW = 32: slice ks (0, 1) is K chunk 2 (tid & 1) + ks of row tid >> 1.
   __device__ __forceinline__ void store(bool bias, int ks, const ProdRegs &p, uint16_t *sw) const {
-    const int i = ks >> 1, h = ks & 1;
+    const int i = GS32 ? 0 : ks >> 1, h = ks & 1;
     uint32_t o[4];
     if (BITS == 8 || bias) {
       unpack8s(p.w[4 * i + 2 * h] ^ 0x80808080u, o);
@@ -110,14 +131,12 @@ struct Producer {
     } else {
       unpack4(p.w[4 * i + h], o);
     }
-    *(u32x4_t *)(sw + swz(row0 + 16 * i, 2 * q + h)) = u32x4_t{o[0], o[1], o[2], o[3]};
+    const int off = GS32 ? swz<KW>(tid >> 1, 2 * (tid & 1) + h) : swz<KW>(row0 + 16 * i, 2 * q + h);
+    *(u32x4_t *)(sw + off) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
 
   __device__ __forceinline__ void ratio(const ProdRegs &p, float *sr) const {
-    if (tid < BNT) {
-      sr[tid] = p.r;
-      if (GS32) sr[BNT + tid] = p.r2;  // sr is [K column 0, 32][row] of one buffer
-    }
+    if (tid < BNT) sr[tid] = p.r;
   }
 };
 
@@ -133,6 +152,8 @@ __device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) 
 template <int BITS, int MODE, int VAR, bool GS32>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
+  constexpr int KW = GS32 ? 32 : 64;  // K columns per step (one quantization group)
+  constexpr int NKS = KW / 16;        // MFMA k-steps per step
   constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only
@@ -150,8 +171,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int l32 = lane & 31, lh = lane >> 5;
   const int steps = a.NB + a.G;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KSTEP];
-  __shared__ __attribute__((aligned(16))) float sR[2][GS32 ? 2 : 1][BNT];  // [buffer][K column 0, 32][row]
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KW];
+  __shared__ __attribute__((aligned(16))) float sR[2][BNT];
   __shared__ __attribute__((aligned(16))) float sZ[8][64 * ZROW];
   __shared__ float sX[2][BM];  // EXTRA: per-wave tile maxima, read after the step's barrier
 
@@ -197,11 +218,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     pr.tid = tid;
     ProdRegs P0, P1;
     // this lane's B-operand chunk offsets (row vcol0 + l32 + 32c, chunk 2ks + lh)
-    int boff[4];
+    int boff[NKS];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) boff[ks] = swz(vcol0 + l32, 2 * ks + lh);
+    for (int ks = 0; ks < NKS; ++ks) boff[ks] = swz<KW>(vcol0 + l32, 2 * ks + lh);
     f32x16_t acc[2][4];
-    bf16x8_t hA[2][4];
+    bf16x8_t hA[2][NKS];
 
     // step `n` (<= steps) steps after (tile, st)
     auto coords = [&](int tile, int st, int n, int64_t &v0, int &step) {
@@ -218,10 +239,10 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, v0, 0, P0);
       pr.load(a, v1, s1, P1);
 #pragma unroll
-      for (int part = 0; part < 4; ++part) pr.store(true, part, P0, sW[0]);
-      pr.ratio(P0, sR[0][0]);
+      for (int part = 0; part < NKS; ++part) pr.store(true, part, P0, sW[0]);
+      pr.ratio(P0, sR[0]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, 0));
         hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, 0));
       }
@@ -238,8 +259,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       float r[4];
       if (live)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r[c] = sR[cb][0][vcol0 + c * 32 + l32];
-      const int hnext = sn * 4096;
+        for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+      const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
       // B operand of column block c for k-step ks + 1 is read as soon as its
       // two MFMAs of k-step ks are issued; a scheduling barrier after each
       // k-step keeps this order (left free, the compiler hoists every LDS read
@@ -247,22 +268,18 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       bf16x8_t bq[4];
       if (live)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTEP);
+        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KW);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         if (live) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               if (ks == 0) acc[rb][c] *= r[c];
-              if (GS32 && ks == 2) {  // group 32: the second group of the step
-                if (rb == 0) r[c] = sR[cb][GS32 ? 1 : 0][vcol0 + c * 32 + l32];
-                acc[rb][c] *= r[c];
-              }
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             }
-            if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTEP);
+            if (ks < NKS - 1) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KW);
           }
           hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
           hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
@@ -270,7 +287,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         pr.store(sbias, ks, cur, sW[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pr.ratio(cur, sR[cb ^ 1][0]);
+      pr.ratio(cur, sR[cb ^ 1]);
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
@@ -444,7 +461,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
   const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
   const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
-  const bool gs32 = a.rt2 != nullptr;
+  const bool gs32 = a.kw == 32;
   // group 32 has no small-M instantiation (the plain one is correct there)
   const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? VAR_SMALL : VAR_PLAIN);
 #define CCE_TILE(B, MD)                                                                                          \
