@@ -196,6 +196,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   }
   const float c1 = -2.0f * LOG2E * a.inv_cap;  // t = exp2(|z| * c1)
   const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 * u / (1 + t))
+  const float capl2 = LOG2E * a.cap;           // c(z) * log2(e) = capl2 * tanh(z / cap)
+  const float ng = -g_t, ng4 = -4.0f * g_t;    // backward coefficient factors
 
   // EXTRA backward: walk the flagged tiles of the range only
   const uint8_t *fl_row = (BWD && EXTRA) ? a.fl + (int64_t)tt * a.fl_ld + a.range_tile0 : nullptr;
@@ -360,19 +362,32 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             // whole term g * (1 - p) * c' * w is added in fp32 by k_dh_reduce.
             const int64_t dtk = (int64_t)tgt_t - vb;  // target's position in this chunk, or -1
             const int tk = (dtk >= 0 && dtk < 16) ? (int)dtk : -1;
+            float cv[16];
+            if (a.cap > 0.0f) {
+              // with t = e^{-2|z|/cap} and r = 1/(1+t): tanh(|z|/cap) = 2r - 1 and
+              // c'(z) = 1 - tanh^2 = 4 t r^2 (no cancellation for large |z|)
+#pragma unroll
+              for (int k = 0; k < 16; ++k) {
+                const float t = __builtin_amdgcn_exp2f(fabsf(z[k]) * c1);
+                const float r = __builtin_amdgcn_rcpf(1.0f + t);
+                const float arg = fmaf(copysignf(capl2, z[k]), fmaf(2.0f, r, -1.0f), -lse2);
+                cv[k] = __builtin_amdgcn_exp2f(arg) * (t * r) * (r * ng4);
+              }
+            } else {
+#pragma unroll
+              for (int k = 0; k < 16; ++k) cv[k] = __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -lse2)) * ng;
+            }
+            // a ragged chunk, or a lane whose target falls in it: the whole
+            // wave takes the masking pass (the common case skips it)
+            if (EXTRA || nv < 16 || __builtin_amdgcn_ballot_w64(tk >= 0) != 0) {
+#pragma unroll
+              for (int k = 0; k < 16; ++k) cv[k] = (k < nv && k != tk) ? cv[k] : 0.0f;
+            }
             uint32_t pk[8];
 #pragma unroll
             for (int k = 0; k < 16; k += 2) {
-              float cv[2];
-#pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                float dc = 1.0f, y = z[k + u];
-                if (a.cap > 0.0f) y = cap_d(z[k + u], c1, a.cap, dc);
-                const float val = -g_t * __builtin_amdgcn_exp2f(fmaf(y, LOG2E, -lse2)) * dc;
-                cv[u] = (k + u < nv && k + u != tk) ? val : 0.0f;
-                if (EXTRA) xm = fmaxf(xm, fabsf(cv[u]));
-              }
-              pk[k / 2] = pack_rne(cv[0], cv[1]);
+              if (EXTRA) xm = fmaxf(xm, fmaxf(fabsf(cv[k]), fabsf(cv[k + 1])));
+              pk[k / 2] = pack_rne(cv[k], cv[k + 1]);
             }
             // fragment-major chunk: these 16 vocab rows are K chunks 2m, 2m+1
             const int64_t vloc = (int64_t)tile * BNT + vcol0 + c * 32 + k0;
