@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 3
+#define CCE_ABI_VERSION 4
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -175,20 +175,31 @@ typedef struct cce_skip {
   float filter_eps;
 } cce_skip;
 
+/* Element type of the dh written by cce_backward_ex. */
+typedef enum cce_dh_dtype {
+  CCE_DH_F32 = 0,
+  CCE_DH_BF16 = 1 /* the fp32 sum rounded to nearest, ties to even */
+} cce_dh_dtype;
+
 /*
- * Backward with the skips of `skip` (NULL or both eps 0: exactly cce_backward).
+ * Backward with the skips of `skip` (NULL or both eps 0: exactly cce_backward)
+ * and a choice of output type (the page's training loop keeps dh in the
+ * model's dtype; this saves the caller a conversion pass).
  *   block_max  as written by cce_forward_ex for these inputs; needed (non-NULL)
  *              when skip->block_eps > 0, else ignored
+ *   dh         device [M][H] of dh_dtype (aligned to its size), fully
+ *              overwritten; every element is the fp32 value cce_backward
+ *              would write, rounded once when dh_dtype is CCE_DH_BF16
  * Other arguments and the workspace size are those of cce_backward.  Errors
- * as cce_backward, plus CCE_ERR_INVALID_ARG for a negative or non-finite eps
- * or block_eps > 0 without block_max.
+ * as cce_backward, plus CCE_ERR_INVALID_ARG for a negative or non-finite eps,
+ * block_eps > 0 without block_max, or an unknown dh_dtype.
  */
 cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M,
                            const int32_t *targets, const uint8_t *mask,
                            const float *lse, const float *g,
                            const float *block_max, const cce_skip *skip,
-                           float *dh, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           void *dh, int32_t dh_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Human-readable text of a status (for CCE_ERR_HIP, of the last HIP error
  * seen by this thread).  The pointer stays valid until the thread's next call. */

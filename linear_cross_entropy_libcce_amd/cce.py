@@ -25,6 +25,7 @@ TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the ski
 
 
 SB_DTYPES = {"f32": 0, "bf16": 1, "f16": 2}   # cce_sb_dtype
+DH_DTYPES = {"f32": 0, "bf16": 1}            # cce_dh_dtype
 
 
 class cce_head(ctypes.Structure):
@@ -67,7 +68,8 @@ def load(path: str = LIB_PATH):
     lib.cce_forward_ex.restype = ctypes.c_int
     lib.cce_forward_ex.argtypes = [HP, P, I64, P, P, P, P, P, P, SZ, P]
     lib.cce_backward_ex.restype = ctypes.c_int
-    lib.cce_backward_ex.argtypes = [HP, P, I64, P, P, P, P, P, ctypes.POINTER(cce_skip), P, P, SZ, P]
+    lib.cce_backward_ex.argtypes = [HP, P, I64, P, P, P, P, P, ctypes.POINTER(cce_skip), P, ctypes.c_int32, P, SZ,
+                                    P]
     lib.cce_forward_workspace_bytes.restype = SZ
     lib.cce_forward_workspace_bytes.argtypes = [HP, I64]
     lib.cce_backward_workspace_bytes.restype = SZ
@@ -168,12 +170,16 @@ def _fwd_out(M, dev, out):
     return torch.empty(M, dtype=torch.float32, device=dev), torch.empty(M, dtype=torch.float32, device=dev)
 
 
-def _bwd_in(head: Head, M, dev, lse, g, out):
+def _bwd_in(head: Head, M, dev, lse, g, out, dtype=None):
     import torch
+    dtype = torch.float32 if dtype is None else dtype
     _expect(lse, torch.float32, dev, (M,), "lse")
     if g is not None:
         _expect(g, torch.float32, dev, (M,), "g")
-    return out if out is not None else torch.empty((M, head.H), dtype=torch.float32, device=dev)
+    if out is not None:
+        _expect(out, dtype, dev, (M, head.H), "out")
+        return out
+    return torch.empty((M, head.H), dtype=dtype, device=dev)
 
 
 def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
@@ -221,19 +227,22 @@ def cce_backward(h, head: Head, targets, lse, g=None, mask=None, workspace=None,
 
 
 def cce_backward_ex(h, head: Head, targets, lse, g=None, mask=None, block_max=None, block_eps=0.0,
-                    filter_eps=0.0, workspace=None, out=None):
-    """dh with the opt-in skips (block_eps needs block_max from cce_forward_ex)."""
+                    filter_eps=0.0, workspace=None, out=None, dh_dtype="f32"):
+    """dh with the opt-in skips (block_eps needs block_max from cce_forward_ex), as
+    float32 or, with dh_dtype="bf16", bfloat16 (the fp32 result rounded once)."""
     import torch
     lib = load()
     M, dev = _tokens(h, head, targets, mask)
-    dh = _bwd_in(head, M, dev, lse, g, out)
+    if dh_dtype not in DH_DTYPES:
+        raise ValueError("dh_dtype must be one of %s" % sorted(DH_DTYPES))
+    dh = _bwd_in(head, M, dev, lse, g, out, torch.float32 if dh_dtype == "f32" else torch.bfloat16)
     if block_max is not None:
         _expect(block_max, torch.float32, dev, (M, n_blocks(head)), "block_max")
     hs = head.c_struct()
     sk = cce_skip(float(block_eps), float(filter_eps))
     ws = _workspace(lib.cce_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
     _check(lib.cce_backward_ex(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
-                               _ptr(block_max), ctypes.byref(sk), _ptr(dh), _ptr(ws),
+                               _ptr(block_max), ctypes.byref(sk), _ptr(dh), DH_DTYPES[dh_dtype], _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(dev)))
     return dh
 

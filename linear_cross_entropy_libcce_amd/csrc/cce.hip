@@ -368,17 +368,19 @@ cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const 
 cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                         const uint8_t *mask, const float *lse, const float *g, float *dh,
                         void *workspace, size_t workspace_bytes, void *stream) {
-  return cce_backward_ex(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, workspace, workspace_bytes,
-                         stream);
+  return cce_backward_ex(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, workspace,
+                         workspace_bytes, stream);
 }
 
 cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                            const uint8_t *mask, const float *lse, const float *g, const float *block_max,
-                           const cce_skip *skip, float *dh, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           const cce_skip *skip, void *dh, int32_t dh_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   cce_status s = check_common(head, h, M, targets, workspace);
   if (s != CCE_OK || M == 0) return s;
-  if (!lse || !dh || ((uintptr_t)lse & 3) || ((uintptr_t)dh & 3) || ((uintptr_t)g & 3))
+  if (dh_dtype != CCE_DH_F32 && dh_dtype != CCE_DH_BF16) return CCE_ERR_INVALID_ARG;
+  const uintptr_t dh_align = dh_dtype == CCE_DH_F32 ? 3 : 1;
+  if (!lse || !dh || ((uintptr_t)lse & 3) || ((uintptr_t)dh & dh_align) || ((uintptr_t)g & 3))
     return CCE_ERR_INVALID_ARG;
   float block_eps = 0.0f, filter_eps = 0.0f;
   if (skip) {
@@ -449,7 +451,8 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
   }
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, ws_at<const int>(workspace, p.o_inv),
-                                               ws_at<const TokRec>(workspace, p.o_tok), dh));
+                                               ws_at<const TokRec>(workspace, p.o_tok), dh,
+                                               dh_dtype == CCE_DH_BF16 ? 1 : 0));
   return hip_status();
 }
 

@@ -288,6 +288,6 @@ void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int til
                   const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
-                      float *dh);
+                      void *dh, int out_bf16);
 
 }  // namespace cce

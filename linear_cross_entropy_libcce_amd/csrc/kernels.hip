@@ -360,9 +360,10 @@ __global__ void __launch_bounds__(256) k_bmx_mask(int64_t nbv, const int *inv, f
 
 // ---------------------------------------------------------------------------
 // dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
-// zero rows for masked tokens.
+// zero rows for masked tokens; stored as fp32, or rounded once to bf16.
 template <int BITS>
-__global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, const TokRec *tok, float *dh) {
+__global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, const TokRec *tok, void *dh,
+                                                   int out_bf16) {
   const int t = blockIdx.x;
   const int d = blockIdx.y * 256 + threadIdx.x;
   const int H = a.H;
@@ -381,7 +382,10 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
       acc += rec.tval * (ld_sb(a.scales, gi, a.sbt) * q + ld_sb(a.biases, gi, a.sbt));
     }
   }
-  dh[(size_t)t * H + d] = acc;
+  if (out_bf16)
+    static_cast<uint16_t *>(dh)[(size_t)t * H + d] = (uint16_t)bf16_rne(acc);
+  else
+    static_cast<float *>(dh)[(size_t)t * H + d] = acc;
 }
 
 void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt) {
@@ -414,12 +418,12 @@ void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *
 }
 
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
-                      float *dh) {
+                      void *dh, int out_bf16) {
   const dim3 grid((unsigned)M, (unsigned)((ga.H + 255) / 256));
   if (bits == 4)
-    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh);
+    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
   else
-    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh);
+    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
 }
 
 }  // namespace cce

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 3
+    assert lib.cce_abi_version() == 4
 
 
 def head(**kw):
@@ -103,12 +103,24 @@ def test_bad_token_arguments_are_rejected(lib):
                             None) == cce.CCE_ERR_WORKSPACE
 
 
-def bwd_ex(lib, hd, block_max=None, skip=None, ws=0x100000, nbytes=None):
+def bwd_ex(lib, hd, block_max=None, skip=None, ws=0x100000, nbytes=None, dh=0x8000, dh_dtype=0):
     if nbytes is None:
         nbytes = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 4)
     sk = None if skip is None else ctypes.byref(cce.cce_skip(*skip))
-    return lib.cce_backward_ex(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, block_max, sk, 0x8000,
-                               ws, nbytes, None)
+    return lib.cce_backward_ex(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, block_max, sk, dh,
+                               dh_dtype, ws, nbytes, None)
+
+
+def test_dh_dtype_is_checked(lib):
+    hd = head()
+    need = lib.cce_backward_workspace_bytes(ctypes.byref(hd), 4)
+    for bad in (-1, 2, 7):
+        assert bwd_ex(lib, hd, dh_dtype=bad) == cce.CCE_ERR_INVALID_ARG, bad
+    # fp32 dh needs 4-byte alignment, bf16 dh 2-byte; past those checks a short
+    # workspace is the next error (nothing is launched)
+    assert bwd_ex(lib, hd, dh=0x8002, dh_dtype=cce.DH_DTYPES["f32"]) == cce.CCE_ERR_INVALID_ARG
+    assert bwd_ex(lib, hd, dh=0x8001, dh_dtype=cce.DH_DTYPES["bf16"]) == cce.CCE_ERR_INVALID_ARG
+    assert bwd_ex(lib, hd, dh=0x8002, dh_dtype=cce.DH_DTYPES["bf16"], nbytes=need - 256) == cce.CCE_ERR_WORKSPACE
 
 
 def test_bad_skip_arguments_are_rejected(lib):

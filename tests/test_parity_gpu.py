@@ -229,6 +229,28 @@ def test_repeat_runs_are_bitwise_identical(torch_cuda):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("case", ["w8_cap_mask", "w4_group32"])
+def test_bf16_dh_is_the_fp32_dh_rounded(torch_cuda, case):
+    # the bf16 output is the fp32 result rounded once (RNE, as torch rounds),
+    # so the two must agree bit for bit; masked rows are exact zeros in both
+    torch = torch_cuda
+    if case == "w8_cap_mask":
+        inp = syn.make_custom(M=300, H=512, V=3000, bits=8, seed=13, softcap=30.0, mask="random", mask_frac=0.3)
+    else:
+        inp = syn.make_custom(M=200, H=384, V=1500, bits=4, seed=14, group=32)
+    say("bf16 dh (%s): GPU backward in both output types" % case)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    g = torch.from_numpy(np.random.default_rng(3).uniform(-2, 2, size=inp["M"]).astype(np.float32)).cuda()
+    _, lse = cce.cce_forward(h, head, t, m)
+    d32 = cce.cce_backward(h, head, t, lse, g, m)
+    d16 = cce.cce_backward_ex(h, head, t, lse, g, m, dh_dtype="bf16")
+    assert d16.dtype == torch.bfloat16 and d16.shape == d32.shape
+    assert torch.equal(d16.view(torch.int16), d32.to(torch.bfloat16).view(torch.int16))
+    if m is not None:
+        assert int((d16[m == 0] != 0).sum()) == 0
+
+
 @pytest.mark.parametrize("softcap", [0.0, 30.0])
 def test_peaked_softmax(torch_cuda, softcap):
     """Target probability near 1: dh = g (1 - p_t) c'_t w_t - ..., a small
