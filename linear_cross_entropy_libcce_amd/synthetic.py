@@ -167,6 +167,20 @@ def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
                 M=M, H=w.H, V=w.V, bits=w.bits, group=w.group, softcap=float(w.softcap), sb_dtype=w.sb_dtype)
 
 
+def make_dense(M, H, V, seed, softcap=0.0, w_std=0.02, targets="uniform", zipf_a=1.1, mask="none",
+               mask_frac=0.0) -> dict:
+    """A trainable dense head and its tokens.  One default_rng(seed) stream:
+    W drawn fp32 N(0, w_std^2) [V, H] and rounded to bf16 (the usual
+    initialization scale of an LM head: logits of order 1), then h, targets
+    and mask as in make_inputs.  W and h are raw bf16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    w = bf16_bits_from_f32(rng.standard_normal((V, H), dtype=np.float32) * np.float32(w_std))
+    h = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32))
+    t = _targets(rng, M, V, targets, zipf_a)
+    m = _mask(rng, M, mask, mask_frac)
+    return dict(w=w, h=h, targets=t, mask=m, M=M, H=H, V=V, softcap=float(softcap), dense=True)
+
+
 def make_custom(M, H, V, bits, seed, softcap=0.0, scale_lo=None, scale_hi=None,
                 targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0,
                 boost_rows=0, boost=1.0, group=GROUP, sb_dtype="f32") -> dict:

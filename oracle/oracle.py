@@ -261,3 +261,75 @@ def cce_skip(inp: dict, g: Optional[np.ndarray] = None, block_eps: float = 0.0,
     lse[d["act"]] = d["lse"]
     dh[d["act"]] = dh_act
     return logp, lse, dh, dropped
+
+
+# ---------------------------------------------------------------------------
+# Trainable dense head: W a bf16 [V, H] matrix instead of a quantized one.
+# The same plain definition (page "mlx-bun 0.0.4 -> 0.0.6",
+# src/train/flash-cce.ts, header comment: log-softmax of the softcapped logits,
+# its gradient through the coefficient g * (1[v = target] - p_v) * c'(z_v)),
+# plus the weight gradient that a frozen head does not need,
+#     dW[v] = sum over supervised tokens t of coeff[t, v] * h[t],
+# i.e. dW = coeff^T . h with the target's term inside the coefficient.
+# W and h are widened exactly to fp64; numpy's fp64 matmul is the only library
+# step.  Full-vocabulary rows are formed in chunks of V only to bound memory.
+# ---------------------------------------------------------------------------
+def _widen_bf16(b) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dense_core(hd: np.ndarray, Wd: np.ndarray, tgt: np.ndarray, gt: np.ndarray, cap: float,
+               dw_rows: Optional[Sequence[int]] = None, need_dw: bool = True):
+    """The definition on fp64 arrays: hd [n, H] supervised tokens, Wd [V, H],
+    tgt [n] (outside [0, V): no target term), gt [n] cotangents.  Returns
+    (logp, lse, dh, dw) with dw [V, H], or only the rows `dw_rows`."""
+    n, V = hd.shape[0], Wd.shape[0]
+    step = 16384
+    Z = np.empty((n, V))
+    for v0 in range(0, V, step):
+        Z[:, v0:v0 + step] = hd @ Wd[v0:v0 + step].T
+    if cap > 0:
+        th = np.tanh(Z / cap)
+        Y, DC = cap * th, 1.0 - th * th
+    else:
+        Y, DC = Z, np.ones_like(Z)
+    mx = Y.max(axis=1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.exp(Y - mx).sum(axis=1))
+    rows = np.arange(n)
+    t_in = (tgt >= 0) & (tgt < V)
+    tc = np.clip(tgt, 0, V - 1)
+    logp = np.where(t_in, Y[rows, tc], 0.0) - lse
+    onehot = np.zeros_like(Y)
+    onehot[rows[t_in], tgt[t_in]] = 1.0
+    C = gt[:, None] * (onehot - np.exp(Y - lse[:, None])) * DC
+    dh = np.zeros((n, Wd.shape[1]))
+    for v0 in range(0, V, step):
+        dh += C[:, v0:v0 + step] @ Wd[v0:v0 + step]
+    dw = None
+    if need_dw:
+        dw = C.T @ hd if dw_rows is None else C[:, np.asarray(dw_rows)].T @ hd
+    return logp, lse, dh, dw
+
+
+def cce_dense(inp: dict, g: Optional[np.ndarray] = None, need_dw: bool = True,
+              dw_rows: Optional[Sequence[int]] = None, tokens: Optional[Sequence[int]] = None):
+    """(logp [M], lse [M], dh [M, H], dw) for a dict from synthetic.make_dense;
+    masked tokens get 0 and add nothing to dw.  With `tokens`, only those
+    tokens are evaluated (the others read as masked, in dw too); dw is [V, H],
+    or its rows `dw_rows`."""
+    M, H = int(inp["M"]), int(inp["H"])
+    mk = inp.get("mask")
+    sel = np.ones(M, bool) if mk is None else np.asarray(mk) != 0
+    if tokens is not None:
+        keep = np.zeros(M, bool)
+        keep[np.asarray(tokens, np.int64)] = True
+        sel &= keep
+    act = np.flatnonzero(sel)
+    hd = _widen_bf16(np.asarray(inp["h"])[act])
+    Wd = _widen_bf16(inp["w"])
+    tgt = np.asarray(inp["targets"], np.int64)[act]
+    gt = np.ones(len(act)) if g is None else np.asarray(g, np.float64)[act]
+    lp, ls, dh_a, dw = dense_core(hd, Wd, tgt, gt, float(inp["softcap"]), dw_rows, need_dw)
+    logp, lse, dh = np.zeros(M), np.zeros(M), np.zeros((M, H))
+    logp[act], lse[act], dh[act] = lp, ls, dh_a
+    return logp, lse, dh, dw
