@@ -96,6 +96,8 @@ def main():
                     help="opt-in backward skips (e.g. 1e-5,1e-5): forward with block maxima, backward skipping")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (launch-bound small M)")
+    ap.add_argument("--dense", action="store_true",
+                    help="a trainable dense bf16 head of the workload's shape (forward, dh and dW)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -128,15 +130,27 @@ def main():
         w = dataclasses.replace(w, group=args.group, name="%s, group %d" % (w.name, args.group))
     if args.sb_dtype is not None:
         w = dataclasses.replace(w, sb_dtype=args.sb_dtype, name="%s, %s scales" % (w.name, args.sb_dtype))
-    log("generating workload %d (%s)" % (args.workload, w.name))
-    inp = syn.make_inputs(w, syn.seed_for(args.workload))
+    dev = torch.device("cuda:0")
+    if args.dense:
+        if args.skip or args.group or args.sb_dtype:
+            sys.exit("--dense takes no quantization or skip options")
+        w = dataclasses.replace(w, name="%s shape, dense bf16 head" % w.name.split(" 4-bit")[0].split(" 8-bit")[0])
+        log("generating a dense head of workload %d's shape (%s)" % (args.workload, w.name))
+        inp = syn.make_dense(w.M, w.H, w.V, syn.seed_for(args.workload), softcap=w.softcap, targets=w.targets,
+                             zipf_a=w.zipf_a, mask=w.mask, mask_frac=w.mask_frac)
+        head = cce.dense_head_from_numpy(inp, dev)
+        ws_f = torch.empty(cce.dense_forward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(cce.dense_backward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
+        dw = torch.empty((inp["V"], inp["H"]), dtype=torch.float32, device=dev)
+    else:
+        log("generating workload %d (%s)" % (args.workload, w.name))
+        inp = syn.make_inputs(w, syn.seed_for(args.workload))
+        head = cce.head_from_numpy(inp, dev)
+        ws_f = torch.empty(cce.forward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(cce.backward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
     M, H, V = inp["M"], inp["H"], inp["V"]
     M_eff = M if inp["mask"] is None else int(inp["mask"].sum())
-    dev = torch.device("cuda:0")
-    head = cce.head_from_numpy(inp, dev)
     h, t, m = cce.tokens_from_numpy(inp, dev)
-    ws_f = torch.empty(cce.forward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(cce.backward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
     logp = torch.empty(M, dtype=torch.float32, device=dev)
     lse = torch.empty(M, dtype=torch.float32, device=dev)
     dh = torch.empty((M, H), dtype=torch.float32, device=dev)
@@ -146,13 +160,17 @@ def main():
     bmx = torch.empty((M, cce.n_blocks(head)), dtype=torch.float32, device=dev) if args.skip else None
 
     def fwd():
-        if args.skip:
+        if args.dense:
+            cce.cce_dense_forward(h, head, t, m, workspace=ws_f, out=(logp, lse))
+        elif args.skip:
             cce.cce_forward_ex(h, head, t, m, block_max=bmx, workspace=ws_f, out=(logp, lse))
         else:
             cce.cce_forward(h, head, t, m, workspace=ws_f, out=(logp, lse))
 
     def bwd():
-        if args.skip:
+        if args.dense:
+            cce.cce_dense_backward(h, head, t, lse, None, m, workspace=ws_b, out=dh, dw_out=dw)
+        elif args.skip:
             cce.cce_backward_ex(h, head, t, lse, None, m, block_max=bmx, block_eps=block_eps, filter_eps=filter_eps,
                                 workspace=ws_b, out=dh)
         else:
@@ -221,20 +239,25 @@ def main():
     for k, (n, tot) in sorted(per_step.items(), key=lambda kv: -kv[1][1]):
         log("  %-10s %5.1f launches/step  %8.3f ms/step" % (k, n, tot))
 
-    alg_flops = 6.0 * M_eff * V * H          # forward logits + backward recompute + dh
-    sb_size = 4 if inp.get("sb_dtype", "f32") == "f32" else 2
-    head_bytes = V * (H * inp["bits"] // 8) + 2 * sb_size * V * (H // inp["group"])  # packed codes + scales and biases
+    # forward logits + backward recompute + dh (+ dW for a dense head)
+    alg_flops = (8.0 if args.dense else 6.0) * M_eff * V * H
+    if args.dense:
+        head_bytes = 2 * V * H
+    else:
+        sb_size = 4 if inp.get("sb_dtype", "f32") == "f32" else 2
+        head_bytes = V * (H * inp["bits"] // 8) + 2 * sb_size * V * (H // inp["group"])  # codes + scales, biases
     head_gbs = 2.0 * head_bytes / (ms * 1e-3) / 1e9                   # the head is read by both passes
     tflops = alg_flops / (ms * 1e-3) / 1e12
     per_kernel_flops = {"tile_fwd": 2.0 * M_eff * V * H, "tile_bwd": 2.0 * M_eff * V * H,
-                        "dh_gemm": 2.0 * M_eff * V * H}
+                        "dh_gemm": 2.0 * M_eff * V * H, "dw_gemm": 2.0 * M_eff * V * H}
     dom = max(per_step, key=lambda k: per_step[k][1])
     n_l, t_l = per_step[dom]
     roof = None
     if dom in per_kernel_flops:
         flop_launch = per_kernel_flops[dom] / n_l
         achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
-        default_cfg = args.tokens is None and not args.skip and args.group is None and args.sb_dtype is None
+        default_cfg = (args.tokens is None and not args.skip and args.group is None and args.sb_dtype is None
+                       and not args.dense)
         tb = measured_traffic(dom) if (args.workload == 3 and default_cfg) else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
@@ -245,7 +268,7 @@ def main():
             roof["note"] = "dense-equivalent flops: skipped pairs are counted but do no work"
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.dense:
         log("cpu baseline: oracle on a token sample (~%.0f s)" % args.cpu_seconds)
         cpu = cpu_baseline(inp, args.cpu_seconds, M_eff)
 
@@ -262,14 +285,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V, "bits": inp["bits"],
-                   "group": inp["group"], "sb_dtype": inp.get("sb_dtype", "f32"), "softcap": inp["softcap"], "g": 1.0,
+        "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V,
+                   "head": "dense bf16" if args.dense else "quantized",
+                   "bits": 16 if args.dense else inp["bits"], "group": None if args.dense else inp["group"],
+                   "sb_dtype": None if args.dense else inp.get("sb_dtype", "f32"), "softcap": inp["softcap"],
+                   "g": 1.0,
                    "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps},
                    "hip_graph": bool(args.graph)},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),
         "tflops": round(tflops, 1),
-        "flops_counted": "6*M_eff*V*H" + (" (dense-equivalent: skipped pairs counted)" if args.skip else ""),
+        "flops_counted": ("8*M_eff*V*H (forward, recompute, dh, dW)" if args.dense else "6*M_eff*V*H")
+        + (" (dense-equivalent: skipped pairs counted)" if args.skip else ""),
         "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
         "head_GB_per_s": round(head_gbs, 1),
         "kernel_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 4
+#define CCE_ABI_VERSION 5
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -200,6 +200,48 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M,
                            const float *block_max, const cce_skip *skip,
                            void *dh, int32_t dh_dtype, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Trainable dense head (the original cut-cross-entropy setting, which the
+ * page's frozen quantized head specializes; same page, the note that the head
+ * is frozen so no weight gradient is formed).  Same operation as above with
+ * W a bf16 matrix, plus the weight gradient
+ *
+ *     dW_v = sum_t g_t * (1[v = target_t] - exp(y_v - lse_t)) * c'(z_v) * h_t
+ *
+ *   w        device bf16 [V][H] row-major (raw bf16 bits), 16-byte aligned;
+ *            H a multiple of 64, at most 16384;  V in [1, 2^31 - 257]
+ *   softcap  as cce_head.softcap
+ */
+typedef struct cce_dense_head {
+  const void *w;
+  int64_t V;
+  int64_t H;
+  float softcap;
+} cce_dense_head;
+
+size_t cce_dense_forward_workspace_bytes(const cce_dense_head *head, int64_t M);
+size_t cce_dense_backward_workspace_bytes(const cce_dense_head *head, int64_t M);
+
+/* Forward on a dense head: arguments, outputs and errors as cce_forward. */
+cce_status cce_dense_forward(const cce_dense_head *head, const void *h, int64_t M,
+                             const int32_t *targets, const uint8_t *mask,
+                             float *logp, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Backward on a dense head: dh as cce_backward, and
+ *   dw   device float [V][H] (4-byte aligned), fully overwritten with dW, or
+ *        NULL to skip it.  Every coefficient, the target's included, enters
+ *        dW rounded to bf16 (dh adds the target's term in fp32).  Needs
+ *        M <= 2^21; larger M with dw is CCE_ERR_UNSUPPORTED.  M = 0 enqueues
+ *        nothing and leaves dw untouched.
+ * Errors as cce_backward.
+ */
+cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t M,
+                              const int32_t *targets, const uint8_t *mask,
+                              const float *lse, const float *g, float *dh, float *dw,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable text of a status (for CCE_ERR_HIP, of the last HIP error
  * seen by this thread).  The pointer stays valid until the thread's next call. */

@@ -1,9 +1,10 @@
 """Compile libcce.so for gfx950 in-tree (hipcc, no JIT cache).
 
-Four translation units: the host API (cce.hip), the logit tile kernel
+Five translation units: the host API (cce.hip), the logit tile kernel
 (tile.hip, built with the VGPR form of MFMA because the VALU rescales its
 accumulator every quantization group), the dh contraction (dh.hip, whose
-accumulators are best left to AGPRs) and the small kernels (kernels.hip).
+accumulators are best left to AGPRs), the dense head's dW contraction
+(dw.hip) and the small kernels (kernels.hip).
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ UNITS = {
     "tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "kernels.hip": [],
     "dh.hip": [],
+    "dw.hip": [],
 }
 HEADERS = [os.path.join(CSRC, "cce_device.h"), os.path.join(ROOT, "include", "cce.h"),
            os.path.join(ROOT, "include", "cce_profile.h")]

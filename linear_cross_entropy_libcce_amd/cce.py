@@ -18,7 +18,9 @@ CCE_OK, CCE_ERR_INVALID_ARG, CCE_ERR_UNSUPPORTED, CCE_ERR_WORKSPACE, CCE_ERR_HIP
 
 EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
            "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_status_str",
-           "cce_abi_version", "cce_profile_enable", "cce_profile_read")
+           "cce_abi_version", "cce_profile_enable", "cce_profile_read",
+           "cce_dense_forward", "cce_dense_backward", "cce_dense_forward_workspace_bytes",
+           "cce_dense_backward_workspace_bytes")
 
 BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
@@ -32,6 +34,10 @@ class cce_head(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("softcap", ctypes.c_float), ("sb_dtype", ctypes.c_int32)]
+
+
+class cce_dense_head(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("softcap", ctypes.c_float)]
 
 
 class cce_skip(ctypes.Structure):
@@ -74,6 +80,15 @@ def load(path: str = LIB_PATH):
     lib.cce_forward_workspace_bytes.argtypes = [HP, I64]
     lib.cce_backward_workspace_bytes.restype = SZ
     lib.cce_backward_workspace_bytes.argtypes = [HP, I64]
+    DP = ctypes.POINTER(cce_dense_head)
+    lib.cce_dense_forward.restype = ctypes.c_int
+    lib.cce_dense_forward.argtypes = [DP, P, I64, P, P, P, P, P, SZ, P]
+    lib.cce_dense_backward.restype = ctypes.c_int
+    lib.cce_dense_backward.argtypes = [DP, P, I64, P, P, P, P, P, P, P, SZ, P]
+    lib.cce_dense_forward_workspace_bytes.restype = SZ
+    lib.cce_dense_forward_workspace_bytes.argtypes = [DP, I64]
+    lib.cce_dense_backward_workspace_bytes.restype = SZ
+    lib.cce_dense_backward_workspace_bytes.argtypes = [DP, I64]
     lib.cce_status_str.restype = ctypes.c_char_p
     lib.cce_status_str.argtypes = [ctypes.c_int]
     lib.cce_abi_version.restype = ctypes.c_int
@@ -116,6 +131,24 @@ class Head:
                         self.V, self.H, self.bits, self.group, float(self.softcap), SB_DTYPES[self.sb_dtype])
 
 
+@dataclasses.dataclass
+class DenseHead:
+    """A trainable dense head: w a contiguous bfloat16 [V, H] device tensor."""
+    w: "object"
+    softcap: float = 0.0
+
+    @property
+    def V(self) -> int:
+        return int(self.w.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.w.shape[1])
+
+    def c_struct(self) -> cce_dense_head:
+        return cce_dense_head(self.w.data_ptr(), self.V, self.H, float(self.softcap))
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -146,6 +179,14 @@ def forward_workspace_bytes(head: Head, M: int) -> int:
 
 def backward_workspace_bytes(head: Head, M: int) -> int:
     return int(load().cce_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def dense_forward_workspace_bytes(head: DenseHead, M: int) -> int:
+    return int(load().cce_dense_forward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def dense_backward_workspace_bytes(head: DenseHead, M: int) -> int:
+    return int(load().cce_dense_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
 
 
 def n_blocks(head: Head) -> int:
@@ -245,6 +286,49 @@ def cce_backward_ex(h, head: Head, targets, lse, g=None, mask=None, block_max=No
                                _ptr(block_max), ctypes.byref(sk), _ptr(dh), DH_DTYPES[dh_dtype], _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(dev)))
     return dh
+
+
+def cce_dense_forward(h, head: DenseHead, targets, mask=None, workspace=None, out=None):
+    """(logp, lse), each float32 [M], on a dense bf16 head."""
+    import torch
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    _expect(head.w, torch.bfloat16, dev, (head.V, head.H), "w")
+    logp, lse = _fwd_out(M, dev, out)
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_dense_forward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_dense_forward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse
+
+
+def cce_dense_backward(h, head: DenseHead, targets, lse, g=None, mask=None, need_dw=True, workspace=None,
+                       out=None, dw_out=None):
+    """(dh float32 [M, H], dW float32 [V, H] or None) on a dense bf16 head."""
+    import torch
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    _expect(head.w, torch.bfloat16, dev, (head.V, head.H), "w")
+    dh = _bwd_in(head, M, dev, lse, g, out)
+    dw = None
+    if need_dw:
+        if dw_out is not None:
+            _expect(dw_out, torch.float32, dev, (head.V, head.H), "dw_out")
+            dw = dw_out
+        else:
+            dw = torch.empty((head.V, head.H), dtype=torch.float32, device=dev)
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_dense_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_dense_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
+                                  _ptr(dh), _ptr(dw), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return dh, dw
+
+
+def dense_head_from_numpy(inp: dict, device="cuda") -> DenseHead:
+    """Upload the bf16 head of a synthetic.make_dense dict."""
+    import torch
+    w = torch.from_numpy(inp["w"].view("int16")).to(device).view(torch.bfloat16)
+    return DenseHead(w=w, softcap=float(inp["softcap"]))
 
 
 def head_from_numpy(inp: dict, device="cuda") -> Head:

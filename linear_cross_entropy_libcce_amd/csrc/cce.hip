@@ -92,7 +92,13 @@ struct Plan {
   // workspace offsets (bytes)
   size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, o_fl,
       fwd_bytes, bwd_bytes;
+  size_t o_hT, o_coeffT;  // dense heads: transposed h and coefficient chunk of the dW contraction
 };
+
+// A dense bf16 head runs as an internal head of 16 "bits" per element: the
+// 32-wide step path of the tile, no bias block, no scales.
+constexpr int DENSE_BITS = 16;
+constexpr int64_t MAX_DW_M_PAD = (int64_t)1 << 21;  // 32-bit buffer offsets of the dW operands
 
 cce_status check_head(const cce_head *hd) {
   if (!hd || !hd->wq || !hd->scales || !hd->biases) return CCE_ERR_INVALID_ARG;
@@ -119,13 +125,14 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.H = hd->H;
   p.bits = hd->bits;
   p.cap = hd->softcap;
+  const bool dense = hd->bits == DENSE_BITS;
   p.gs = hd->group;
   p.kw = p.gs == 32 ? 32 : KSTEP;
   p.G = (int)(p.H / p.kw);
   p.Gq = (int)(p.H / p.gs);
   p.sbt = hd->sb_dtype;
   // bias block: three columns per quantization group (fixed-point digits x S hi/lo)
-  p.Kb = (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
+  p.Kb = dense ? 0 : (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
   p.Ka = p.Kb + (int)p.H;
   p.NB = p.Kb / p.kw;
   p.wpr = (int)(p.H * p.bits / 32);
@@ -186,8 +193,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_tok = o;  o = align_up(o + sizeof(TokRec) * p.M_pad, 256);
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
-  p.o_rt = o; o = align_up(o + sizeof(float) * (size_t)(p.NB + p.G) * p.V, 256);
-  p.o_slast = o; o = align_up(o + sizeof(float) * (size_t)p.V, 256);
+  p.o_rt = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)(p.NB + p.G) * p.V), 256);
+  p.o_slast = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)p.V), 256);
   const size_t common = o;
   p.o_part = common;
   p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
@@ -197,19 +204,41 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   o = align_up(o + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
   p.o_fl = o;  // pair flags of the skips: [TT][tiles] bytes
   p.bwd_bytes = align_up(o + (size_t)p.TT * p.tiles, 256);
+  if (dense) {
+    p.o_hT = p.bwd_bytes;
+    o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
+    p.o_coeffT = o;
+    p.bwd_bytes = align_up(o + (size_t)2 * p.ld_coeff * p.M_pad, 256);
+  }
   return p;
 }
 
-cce_status check_common(const cce_head *hd, const void *h, int64_t M, const int32_t *targets,
-                        void *workspace) {
-  cce_status s = check_head(hd);
-  if (s != CCE_OK) return s;
+cce_status check_tokens(const void *h, int64_t M, const int32_t *targets, void *workspace) {
   if (M < 0) return CCE_ERR_INVALID_ARG;
   if (M > MAX_M) return CCE_ERR_UNSUPPORTED;
   if (M == 0) return CCE_OK;
   if (!h || !targets) return CCE_ERR_INVALID_ARG;
   if (((uintptr_t)h & 15) || ((uintptr_t)targets & 3)) return CCE_ERR_INVALID_ARG;
   if (workspace && ((uintptr_t)workspace & 255)) return CCE_ERR_INVALID_ARG;
+  return CCE_OK;
+}
+
+cce_status check_common(const cce_head *hd, const void *h, int64_t M, const int32_t *targets,
+                        void *workspace) {
+  const cce_status s = check_head(hd);
+  return s != CCE_OK ? s : check_tokens(h, M, targets, workspace);
+}
+
+// The internal head of a dense bf16 head.
+cce_status check_dense(const cce_dense_head *dh, cce_head &q) {
+  if (!dh || !dh->w) return CCE_ERR_INVALID_ARG;
+  if (dh->V < 1 || dh->H < 1) return CCE_ERR_INVALID_ARG;
+  if (!(dh->softcap >= 0.0f) || !std::isfinite(dh->softcap)) return CCE_ERR_INVALID_ARG;
+  if (dh->H % KSTEP != 0) return CCE_ERR_UNSUPPORTED;
+  if (dh->H > MAX_H || dh->V > (int64_t)INT32_MAX - BNT) return CCE_ERR_UNSUPPORTED;
+  if ((uintptr_t)dh->w & 15) return CCE_ERR_INVALID_ARG;
+  q = cce_head{static_cast<const uint32_t *>(dh->w), nullptr, nullptr, dh->V, dh->H, DENSE_BITS, 32,
+               dh->softcap, CCE_SB_F32};
   return CCE_OK;
 }
 
@@ -299,44 +328,10 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-int cce_abi_version(void) { return CCE_ABI_VERSION; }
-
-const char *cce_status_str(cce_status s) {
-  switch (s) {
-    case CCE_OK: return "ok";
-    case CCE_ERR_INVALID_ARG: return "invalid argument";
-    case CCE_ERR_UNSUPPORTED: return "unsupported head configuration";
-    case CCE_ERR_WORKSPACE: return "workspace missing or too small";
-    case CCE_ERR_HIP: return g_err[0] ? g_err : "HIP error";
-  }
-  return "unknown status";
-}
-
-size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M) {
-  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
-  return make_plan(head, M).fwd_bytes;
-}
-
-size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M) {
-  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
-  return make_plan(head, M).bwd_bytes;
-}
-
-cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
-                       const uint8_t *mask, float *logp, float *lse, void *workspace,
-                       size_t workspace_bytes, void *stream) {
-  return cce_forward_ex(head, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
-}
-
-cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
-                          const uint8_t *mask, float *logp, float *lse, float *block_max, void *workspace,
-                          size_t workspace_bytes, void *stream) {
-  cce_status s = check_common(head, h, M, targets, workspace);
-  if (s != CCE_OK || M == 0) return s;
+// The launches of a forward on a validated head and token set (M > 0).
+cce_status run_forward(const cce_head *head, const void *h, int64_t M, const int32_t *targets, const uint8_t *mask,
+                       float *logp, float *lse, float *block_max, void *workspace, size_t workspace_bytes,
+                       void *stream) {
   if (!logp || !lse || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3) || ((uintptr_t)block_max & 3))
     return CCE_ERR_INVALID_ARG;
   const Plan p = make_plan(head, M);
@@ -365,19 +360,12 @@ cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const 
   return hip_status();
 }
 
-cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
-                        const uint8_t *mask, const float *lse, const float *g, float *dh,
-                        void *workspace, size_t workspace_bytes, void *stream) {
-  return cce_backward_ex(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, workspace,
-                         workspace_bytes, stream);
-}
-
-cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
-                           const uint8_t *mask, const float *lse, const float *g, const float *block_max,
-                           const cce_skip *skip, void *dh, int32_t dh_dtype, void *workspace,
-                           size_t workspace_bytes, void *stream) {
-  cce_status s = check_common(head, h, M, targets, workspace);
-  if (s != CCE_OK || M == 0) return s;
+// The launches of a backward on a validated head and token set (M > 0);
+// dw (dense heads only) NULL or the [V][H] fp32 head gradient.
+cce_status run_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                        const uint8_t *mask, const float *lse, const float *g, const float *block_max,
+                        const cce_skip *skip, void *dh, int32_t dh_dtype, float *dw, void *workspace,
+                        size_t workspace_bytes, void *stream) {
   if (dh_dtype != CCE_DH_F32 && dh_dtype != CCE_DH_BF16) return CCE_ERR_INVALID_ARG;
   const uintptr_t dh_align = dh_dtype == CCE_DH_F32 ? 3 : 1;
   if (!lse || !dh || ((uintptr_t)lse & 3) || ((uintptr_t)dh & dh_align) || ((uintptr_t)g & 3))
@@ -391,6 +379,8 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
     if (block_eps > 0.0f && (!block_max || ((uintptr_t)block_max & 3))) return CCE_ERR_INVALID_ARG;
   }
   const Plan p = make_plan(head, M);
+  if (dw && ((uintptr_t)dw & 3)) return CCE_ERR_INVALID_ARG;
+  if (dw && p.M_pad > MAX_DW_M_PAD) return CCE_ERR_UNSUPPORTED;
   const bool use_fl = block_eps > 0.0f || filter_eps > 0.0f;
   if (use_fl && cdiv(p.tiles, 64) * p.TT > INT32_MAX) return CCE_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.bwd_bytes) return CCE_ERR_WORKSPACE;
@@ -436,6 +426,21 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   ga.small = a.small;
   const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
 
+  DwArgs wa{};
+  if (dw) {
+    wa.coeffT = ws_at<const uint16_t>(workspace, p.o_coeffT);
+    wa.hT = ws_at<const uint16_t>(workspace, p.o_hT);
+    wa.cnt = a.cnt;
+    wa.dw = dw;
+    wa.V = p.V;
+    wa.ks16t = p.M_pad / 16;
+    wa.H = (int)p.H;
+    wa.M_pad = (int)p.M_pad;
+    wa.HT = p.HT;
+    CCE_LAUNCH("hT", st, launch_hT(st, a.haug, p.Ka / 16, p.Kb / 8, (int)p.M_pad, (int)p.H, a.cnt,
+                                   ws_at<uint16_t>(workspace, p.o_hT)));
+  }
+
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * p.chunk_tiles;
     const int nt = std::min(p.chunk_tiles, p.tiles - t0);
@@ -449,11 +454,109 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
     ga.chunk_steps = nt * (BNT / KSTEP);
     ga.accumulate = c > 0;
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+    if (dw) {
+      CCE_LAUNCH("coeffT", st, launch_coeffT(st, a.coeff, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt, a.tok, p.V,
+                                             ga.chunk_v0, ws_at<uint16_t>(workspace, p.o_coeffT)));
+      wa.chunk_v0 = ga.chunk_v0;
+      wa.nvt = nt;
+      CCE_LAUNCH("dw_gemm", st, launch_dw(st, wa));
+    }
   }
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, ws_at<const int>(workspace, p.o_inv),
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0));
   return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int cce_abi_version(void) { return CCE_ABI_VERSION; }
+
+const char *cce_status_str(cce_status s) {
+  switch (s) {
+    case CCE_OK: return "ok";
+    case CCE_ERR_INVALID_ARG: return "invalid argument";
+    case CCE_ERR_UNSUPPORTED: return "unsupported head configuration";
+    case CCE_ERR_WORKSPACE: return "workspace missing or too small";
+    case CCE_ERR_HIP: return g_err[0] ? g_err : "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M) {
+  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(head, M).fwd_bytes;
+}
+
+size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M) {
+  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(head, M).bwd_bytes;
+}
+
+cce_status cce_forward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                       const uint8_t *mask, float *logp, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  return cce_forward_ex(head, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+cce_status cce_forward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                          const uint8_t *mask, float *logp, float *lse, float *block_max, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  cce_status s = check_common(head, h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  return run_forward(head, h, M, targets, mask, logp, lse, block_max, workspace, workspace_bytes, stream);
+}
+
+cce_status cce_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                        const uint8_t *mask, const float *lse, const float *g, float *dh,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return cce_backward_ex(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, workspace,
+                         workspace_bytes, stream);
+}
+
+cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                           const uint8_t *mask, const float *lse, const float *g, const float *block_max,
+                           const cce_skip *skip, void *dh, int32_t dh_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  cce_status s = check_common(head, h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  return run_backward(head, h, M, targets, mask, lse, g, block_max, skip, dh, dh_dtype, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t cce_dense_forward_workspace_bytes(const cce_dense_head *head, int64_t M) {
+  cce_head q;
+  if (check_dense(head, q) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(&q, M).fwd_bytes;
+}
+
+size_t cce_dense_backward_workspace_bytes(const cce_dense_head *head, int64_t M) {
+  cce_head q;
+  if (check_dense(head, q) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return make_plan(&q, M).bwd_bytes;
+}
+
+cce_status cce_dense_forward(const cce_dense_head *head, const void *h, int64_t M, const int32_t *targets,
+                             const uint8_t *mask, float *logp, float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  cce_head q;
+  cce_status s = check_dense(head, q);
+  if (s == CCE_OK) s = check_tokens(h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  return run_forward(&q, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t M, const int32_t *targets,
+                              const uint8_t *mask, const float *lse, const float *g, float *dh, float *dw,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  cce_head q;
+  cce_status s = check_dense(head, q);
+  if (s == CCE_OK) s = check_tokens(h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  return run_backward(&q, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, dw, workspace,
+                      workspace_bytes, stream);
 }
 
 int cce_profile_enable(int on) {

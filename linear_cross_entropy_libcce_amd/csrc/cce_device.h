@@ -290,4 +290,20 @@ void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16);
 
+// Head gradient of a dense head (dw.hip): dW rows [chunk_v0, chunk_v0 + 256 nvt)
+// of one coefficient chunk, all columns, over the active token tiles.
+struct DwArgs {
+  const uint16_t *coeffT;  // [local vocab row][token] fragment-major (ks16t = M_pad / 16)
+  const uint16_t *hT;      // [H][M_pad] bf16: the compacted, padded hidden states transposed
+  const int *cnt;
+  float *dw;               // [V][H] fp32
+  int64_t V, chunk_v0, ks16t;
+  int H, M_pad, HT, nvt;   // HT: 256-column tiles of H; nvt: vocabulary tiles of the chunk
+};
+void launch_hT(hipStream_t st, const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H, const int *cnt,
+               uint16_t *hT);
+void launch_coeffT(hipStream_t st, const uint16_t *coeff, int64_t ksv, int M_pad, int vrows, const int *cnt,
+                   const TokRec *tok, int64_t V, int64_t chunk_v0, uint16_t *coeffT);
+void launch_dw(hipStream_t st, const DwArgs &a);
+
 }  // namespace cce

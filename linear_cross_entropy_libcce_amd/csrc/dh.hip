@@ -1,6 +1,8 @@
 // dh.hip -- the dh contraction of libcce's backward (the second phase of the
 // page's backward: the coefficients contracted with the head, summed over
 // vocabulary blocks).
+#include <type_traits>
+
 #include "cce_device.h"
 
 namespace cce {
@@ -52,10 +54,48 @@ constexpr int SB_SLOT = 2 * 8 * KSTP;  // floats of one staged step: 2 x (up to 
 
 template <int BITS>
 struct DhRegs {
-  uint32_t w[8];  // 8-bit: 4 codes of row e; 4-bit: 4 codes in the low 16 bits
+  uint32_t w[BITS == 16 ? 16 : 8];  // 8-bit: 4 codes of row e; 4-bit: 4 codes in the low 16 bits;
+                                    // dense: 4 bf16 of row e in words 2e, 2e + 1
   uint32_t sb[2]; // raw bits of the scales or biases this thread stages (widened when staged,
                   // so the load is not waited for before the step's end)
 };
+
+// Dense bf16 head (the trainable-head variant): the same thread mapping, the
+// 8 rows x 4 columns of a thread are copied (no scales), transposed in
+// registers into one 16-byte run of v per column.
+struct DhDense {
+  int rgp, dc, wcol, tid, gq0;
+
+  __device__ __forceinline__ void load(const GemmArgs &a, int64_t vs, DhRegs<16> &p) const {
+    const int64_t rows = a.V - vs < KSTP ? a.V - vs : KSTP;
+    const rsrc_t rw = make_rsrc(a.wq + vs * a.wpr, rows * a.wpr * 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rw, (8 * rgp + e) * a.wpr * 4 + wcol, 0, 0);
+      p.w[2 * e] = x[0];
+      p.w[2 * e + 1] = x[1];
+    }
+  }
+  __device__ __forceinline__ void stage_sb(const DhRegs<16> &, float *, int) const {}
+  __device__ __forceinline__ void read_sb(const float *, float (&)[8], float (&)[8]) const {}
+
+  // Column 4*dc + k: the bf16 of rows 8*rgp .. +7, paired into words.
+  __device__ __forceinline__ void store(int k, const DhRegs<16> &p, const float (&)[8], const float (&)[8],
+                                        uint16_t *sb) const {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = p.w[2 * (2 * j) + (k >> 1)], hi = p.w[2 * (2 * j + 1) + (k >> 1)];
+      o[j] = (k & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    *(u32x4_t *)(sb + dswz(4 * dc + k, rgp)) = u32x4_t{o[0], o[1], o[2], o[3]};
+  }
+};
+
+template <int BITS, int LG, int SBW>
+struct DhProducer;
+template <int BITS, int LG, int SBW>
+using DhProd = typename std::conditional<BITS == 16, DhDense, DhProducer<BITS, LG, SBW>>::type;
 
 template <int BITS, int LG, int SBW>
 struct DhProducer {
@@ -216,7 +256,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
 
   if (nsteps > 0) {
-    DhProducer<BITS, LG, SBW> pr;
+    DhProd<BITS, LG, SBW> pr;
     pr.dc = (lane & 15) + 16 * (wave & 3);
     pr.rgp = (lane >> 4) + 4 * (wave >> 2);
     pr.wcol = (d0 + 4 * pr.dc) * BITS / 8;
@@ -352,6 +392,10 @@ static void launch_dh_bits(hipStream_t st, dim3 grid, const GemmArgs &a) {
 }
 
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
+  if (bits == 16) {  // dense bf16 head: exact path only (no skips, no small-M variant)
+    hipLaunchKernelGGL((k_dh<16, false, false, 0, 0>), grid, dim3(TW), 0, st, a);
+    return;
+  }
   if (bits == 4) launch_dh_bits<4>(st, grid, a);
   else launch_dh_bits<8>(st, grid, a);
 }

@@ -150,8 +150,9 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
   __shared__ float sRed[4];
   __shared__ float sT[HP_ROWS * HP_LD];
   const int tid = threadIdx.x;
+  constexpr bool DENSE = BITS == 16;  // bf16 head rows: no head side, no group sums
   if (blockIdx.x >= (unsigned)f.M_pad) {
-    head_prep_block((int64_t)blockIdx.x - f.M_pad, f, BITS == 8 ? 128.0f : 0.0f, sS, sT);
+    if constexpr (!DENSE) head_prep_block((int64_t)blockIdx.x - f.M_pad, f, BITS == 8 ? 128.0f : 0.0f, sS, sT);
     return;
   }
   const int r = blockIdx.x;
@@ -210,6 +211,17 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
     const u32x4_t x = (src >= 0) ? *(const u32x4_t *)(f.h + (size_t)src * H + 8 * c) : u32x4_t{0, 0, 0, 0};
     *(u32x4_t *)(f.haug + frag_slot(r, Kb / 8 + c, ks16)) = x;
     float part = 0.0f, dot = 0.0f;
+    if constexpr (DENSE) {
+      if (has_t) {
+        const u32x4_t w = *(const u32x4_t *)(wrow + 4 * c);  // 8 bf16 of the target row
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dot += bf16_to_f32(x[e] & 0xFFFFu) * bf16_to_f32(w[e] & 0xFFFFu) +
+                 bf16_to_f32(x[e] >> 16) * bf16_to_f32(w[e] >> 16);
+        zpart += dot;
+      }
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float lo = bf16_to_f32(x[e] & 0xFFFFu), hi = bf16_to_f32(x[e] >> 16);
@@ -377,9 +389,13 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     for (int k = 0; k < ksd; ++k) acc += a.dh_part[((size_t)k * act * BM + r) * H + d];
     const TokRec rec = tok[r];
     if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
-      const int64_t gi = (int64_t)rec.tgt * a.Gq + d / a.gs;
-      const float q = (float)code_at<BITS>(a.wq + (size_t)rec.tgt * a.wpr, d);
-      acc += rec.tval * (ld_sb(a.scales, gi, a.sbt) * q + ld_sb(a.biases, gi, a.sbt));
+      if constexpr (BITS == 16) {  // dense bf16 row
+        acc += rec.tval * bf16_to_f32(code_at<16>(a.wq + (size_t)rec.tgt * a.wpr, d));
+      } else {
+        const int64_t gi = (int64_t)rec.tgt * a.Gq + d / a.gs;
+        const float q = (float)code_at<BITS>(a.wq + (size_t)rec.tgt * a.wpr, d);
+        acc += rec.tval * (ld_sb(a.scales, gi, a.sbt) * q + ld_sb(a.biases, gi, a.sbt));
+      }
     }
   }
   if (out_bf16)
@@ -393,6 +409,10 @@ void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *
 }
 
 void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
+  if (bits == 16) {  // dense head: token rows only
+    hipLaunchKernelGGL(k_front<16>, dim3((unsigned)f.M_pad), dim3(256), 0, st, f);
+    return;
+  }
   const dim3 grid((unsigned)(f.M_pad + (f.V + HP_ROWS - 1) / HP_ROWS));
   if (bits == 4)
     hipLaunchKernelGGL(k_front<4>, grid, dim3(256), 0, st, f);
@@ -420,7 +440,9 @@ void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16) {
   const dim3 grid((unsigned)M, (unsigned)((ga.H + 255) / 256));
-  if (bits == 4)
+  if (bits == 16)
+    hipLaunchKernelGGL(k_dh_reduce<16>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
+  else if (bits == 4)
     hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
   else
     hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);

@@ -32,6 +32,10 @@ namespace cce {
 // first with ratio 1 in units of the row's fixed-point unit, and a scale of
 // exactly 0 is replaced by 1e-30, whose contribution is nil.
 //
+// Dense bf16 heads (BITS = 16, the trainable-head variant): the 32-wide step
+// path with the head rows copied into LDS as they are; no bias block, no
+// fold and no final scale.
+//
 // VAR_SMALL (at most 64 tokens): only the two waves of token group 0 carry
 // MFMA work and epilogues; the other six still produce the code tiles.
 //
@@ -52,7 +56,7 @@ enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
 // One step's worth of head data for one producer thread: 16 K values of each
 // of two vocabulary rows (8-bit codes and bias digits: 4 words per row; 4-bit
 // codes: the first 2 words per row) -- or, with 32-wide steps, 16 K values of
-// one row -- and the fold ratio of one row.
+// one row (dense bf16 heads: all 8 words) -- and the fold ratio of one row.
 struct ProdRegs {
   uint32_t w[8];
   float r;
@@ -75,11 +79,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // rows 32w + (l >> 2) and 32w + 16 + (l >> 2), so one load instruction covers
 // 16 rows x 64 contiguous bytes.  KW = 32: thread t loads the K half t & 1 of
 // row t >> 1 (16 values: 16 bytes of 8-bit codes or digits, 8 of 4-bit
-// codes), one load instruction covering 32 rows x 32 K.  Threads 0..255 also
-// carry row t's fold ratio.
+// codes, 32 of dense bf16 rows), one load instruction covering 32 rows x 32
+// K.  Threads 0..255 also carry row t's fold ratio (none for a dense head).
 template <int BITS, bool GS32>
 struct Producer {
+  static constexpr bool DENSE = BITS == 16;  // bf16 head rows: no codes, no scales
   static constexpr int KW = GS32 ? 32 : 64;
+  static_assert(!DENSE || GS32, "dense heads use 32-wide steps");
   int row0, q, tid;
 
   // Issue the loads of step `step` of the vocabulary tile at v0: a bias-block
@@ -93,12 +99,16 @@ struct Producer {
     const rsrc_t rw = bias ? make_rsrc(a.baug + v0 * a.Kb, rows * a.Kb)
                            : make_rsrc(a.wq + v0 * a.wpr, rows * a.wpr * 4);
     const int rowb = bias ? a.Kb : a.wpr * 4;                // bytes per row
-    const int qb = (bias || BITS == 8) ? 16 : 8;             // bytes per 16 K values
+    const int qb = DENSE ? 32 : (bias || BITS == 8) ? 16 : 8;  // bytes per 16 K values
     const int so = bias ? step * KW : g * (KW * BITS / 8);
     if (GS32) {
       // row tid >> 1, K half tid & 1
       const int voff = (tid >> 1) * rowb + (tid & 1) * qb;
-      if (bias || BITS == 8) {
+      if (DENSE) {
+        const u32x4_t x = buf_load16(rw, voff, so), y = buf_load16(rw, voff + 16, so);
+        p.w[0] = x[0]; p.w[1] = x[1]; p.w[2] = x[2]; p.w[3] = x[3];
+        p.w[4] = y[0]; p.w[5] = y[1]; p.w[6] = y[2]; p.w[7] = y[3];
+      } else if (bias || BITS == 8) {
         const u32x4_t x = buf_load16(rw, voff, so);
         p.w[0] = x[0]; p.w[1] = x[1]; p.w[2] = x[2]; p.w[3] = x[3];
       } else {
@@ -112,8 +122,10 @@ struct Producer {
         p.w[4 * i] = x[0]; p.w[4 * i + 1] = x[1]; p.w[4 * i + 2] = x[2]; p.w[4 * i + 3] = x[3];
       }
     }
-    const rsrc_t rr = make_rsrc(a.rt + (int64_t)step * a.V + v0, rows * 4);
-    p.r = buf_loadf(rr, (tid & (BNT - 1)) * 4, 0);
+    if (!DENSE) {
+      const rsrc_t rr = make_rsrc(a.rt + (int64_t)step * a.V + v0, rows * 4);
+      p.r = buf_loadf(rr, (tid & (BNT - 1)) * 4, 0);
+    }
   }
 
   // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
@@ -125,7 +137,9 @@ struct Producer {
   __device__ __forceinline__ void store(bool bias, int ks, const ProdRegs &p, uint16_t *sw) const {
     const int i = GS32 ? 0 : ks >> 1, h = ks & 1;
     uint32_t o[4];
-    if (BITS == 8 || bias) {
+    if (DENSE) {  // bf16 as stored
+      o[0] = p.w[4 * h]; o[1] = p.w[4 * h + 1]; o[2] = p.w[4 * h + 2]; o[3] = p.w[4 * h + 3];
+    } else if (BITS == 8 || bias) {
       unpack8s(p.w[4 * i + 2 * h] ^ 0x80808080u, o);
       unpack8s(p.w[4 * i + 2 * h + 1] ^ 0x80808080u, o + 2);
     } else {
@@ -136,7 +150,7 @@ struct Producer {
   }
 
   __device__ __forceinline__ void ratio(const ProdRegs &p, float *sr) const {
-    if (tid < BNT) sr[tid] = p.r;
+    if (!DENSE && tid < BNT) sr[tid] = p.r;
   }
 };
 
@@ -154,6 +168,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
   constexpr int KW = GS32 ? 32 : 64;  // K columns per step (one quantization group)
   constexpr int NKS = KW / 16;        // MFMA k-steps per step
+  constexpr bool DENSE = BITS == 16;  // bf16 head: no fold, no final scale
   constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only
@@ -259,7 +274,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[4];
-      if (live)
+      if (live && !DENSE)
 #pragma unroll
         for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
       const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
@@ -278,7 +293,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
           for (int c = 0; c < 4; ++c) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-              if (ks == 0) acc[rb][c] *= r[c];
+              if (ks == 0 && !DENSE) acc[rb][c] *= r[c];
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             }
             if (ks < NKS - 1) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KW);
@@ -302,10 +317,12 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile) * BNT;
       const bool full = v0 + BNT <= a.V;
       float xm = BWD ? 0.0f : -INFINITY;  // EXTRA: max logit (forward) or max |coefficient| (backward)
-      float sl[4];
-      const rsrc_t rl = make_rsrc(a.slast + v0, (a.V - v0 < BNT ? a.V - v0 : BNT) * 4);
+      float sl[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (!DENSE) {
+        const rsrc_t rl = make_rsrc(a.slast + v0, (a.V - v0 < BNT ? a.V - v0 : BNT) * 4);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
+        for (int c = 0; c < 4; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -490,7 +507,12 @@ void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &
       else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                      \
     }                                                                                                            \
   } while (0)
-  if (bits == 4) {
+  if (bits == 16) {  // dense bf16 head: 32-wide steps, plain variant only
+    if (mode == MODE_BWD) hipLaunchKernelGGL((k_tile<16, MODE_BWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
+    else if (mode == MODE_FWD_CAP)
+      hipLaunchKernelGGL((k_tile<16, MODE_FWD_CAP, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
+    else hipLaunchKernelGGL((k_tile<16, MODE_FWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
+  } else if (bits == 4) {
     if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(4, MODE_FWD_CAP);
     else CCE_TILE(4, MODE_FWD);

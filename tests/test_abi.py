@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 4
+    assert lib.cce_abi_version() == 5
 
 
 def head(**kw):
@@ -121,6 +121,59 @@ def test_dh_dtype_is_checked(lib):
     assert bwd_ex(lib, hd, dh=0x8002, dh_dtype=cce.DH_DTYPES["f32"]) == cce.CCE_ERR_INVALID_ARG
     assert bwd_ex(lib, hd, dh=0x8001, dh_dtype=cce.DH_DTYPES["bf16"]) == cce.CCE_ERR_INVALID_ARG
     assert bwd_ex(lib, hd, dh=0x8002, dh_dtype=cce.DH_DTYPES["bf16"], nbytes=need - 256) == cce.CCE_ERR_WORKSPACE
+
+
+def dense(**kw):
+    d = dict(w=0x1000, V=1000, H=256, softcap=0.0)
+    d.update(kw)
+    return cce.cce_dense_head(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=0), cce.CCE_ERR_INVALID_ARG),
+    (dict(w=0x1008), cce.CCE_ERR_INVALID_ARG),       # 16-byte alignment
+    (dict(V=0), cce.CCE_ERR_INVALID_ARG),
+    (dict(H=0), cce.CCE_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), cce.CCE_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), cce.CCE_ERR_INVALID_ARG),
+    (dict(H=96), cce.CCE_ERR_UNSUPPORTED),           # not a multiple of 64
+    (dict(H=16384 + 64), cce.CCE_ERR_UNSUPPORTED),
+])
+def test_bad_dense_head_is_rejected(lib, kw, status):
+    hd = dense(**kw)
+    assert lib.cce_dense_forward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x6000, 0x7000, 0x100000, 1 << 40,
+                                 None) == status
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x9000,
+                                  0x100000, 1 << 40, None) == status
+    assert lib.cce_dense_forward_workspace_bytes(ctypes.byref(hd), 4) == 0
+
+
+def test_dense_arguments_and_workspace(lib):
+    hd = dense()
+    f = lib.cce_dense_forward_workspace_bytes(ctypes.byref(hd), 300)
+    b = lib.cce_dense_backward_workspace_bytes(ctypes.byref(hd), 300)
+    # the backward also holds the transposed h and coefficient chunk of dW
+    assert 0 < f < b and b % 256 == 0
+    # M = 0 is a no-op; negative M is rejected
+    assert lib.cce_dense_forward(ctypes.byref(hd), 0, 0, 0, None, 0, 0, None, 0, None) == cce.CCE_OK
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0, -1, 0, None, 0, None, 0, 0, None, 0, None) \
+        == cce.CCE_ERR_INVALID_ARG
+    need = lib.cce_dense_backward_workspace_bytes(ctypes.byref(hd), 4)
+    # misaligned dw (fp32) is rejected; past the checks a short workspace is the next error
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x9002,
+                                  0x100000, need, None) == cce.CCE_ERR_INVALID_ARG
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, 0x9000,
+                                  0x100000, need - 256, None) == cce.CCE_ERR_WORKSPACE
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0x4000, 4, 0x5000, None, 0x7000, None, 0x8000, None,
+                                  0x100000, need - 256, None) == cce.CCE_ERR_WORKSPACE
+    # dW needs M <= 2^21
+    big = (1 << 21) + 1
+    nb = lib.cce_dense_backward_workspace_bytes(ctypes.byref(hd), big)
+    assert lib.cce_dense_backward(ctypes.byref(hd), 0x4000, big, 0x5000, None, 0x7000, None, 0x8000, 0x9000,
+                                  0x100000, nb, None) == cce.CCE_ERR_UNSUPPORTED
+    # a quantized head cannot claim 16 bits
+    q = head(bits=16)
+    assert lib.cce_forward_workspace_bytes(ctypes.byref(q), 4) == 0
 
 
 def test_bad_skip_arguments_are_rejected(lib):
