@@ -340,21 +340,33 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   }
   if (!live) return;  // rows of padding tokens only
 
-  // result lane layout: column d0 + dh*128 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j
+  // result lane layout: column d0 + dh*128 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j.
+  // Accumulating (later chunks), the 32 old values of a column block are all
+  // loaded before any of them is stored: interleaved, every load would wait
+  // for the previous store (the compiler cannot prove the rows distinct).
+  float *const slab = a.dh_part + ((size_t)ks_ * act * BM + tok0 + 4 * lh) * a.H;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d = d0 + dh * 128 + c * 32 + l32;
     if (d >= a.H) continue;
+    float old[2][16];
+    if (a.accumulate) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          old[rb][e] = slab[(size_t)(rb * 32 + 8 * (e >> 2) + (e & 3)) * a.H + d];
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) old[rb][e] = 0.0f;
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float *dst = a.dh_part + ((size_t)ks_ * act * BM + tok0 + rb * 32 + 8 * i + 4 * lh + j) * a.H + d;
-          const float v = acc[rb][c][4 * i + j];
-          *dst = a.accumulate ? (*dst + v) : v;
-        }
+      for (int e = 0; e < 16; ++e)
+        slab[(size_t)(rb * 32 + 8 * (e >> 2) + (e & 3)) * a.H + d] = old[rb][e] + acc[rb][c][e];
   }
 }
 
