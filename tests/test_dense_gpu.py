@@ -78,6 +78,7 @@ SMALL = {
     "cap30_masked": (300, 512, 3000, 30.0, "random", "uniform"),
     "nocap_ragged_zipf": (200, 256, 1000, 0.0, "none", "zipf"),
     "prefix_masked_H1536": (260, 1536, 2304, 0.0, "prefix", "uniform"),
+    "H16384_max": (70, 16384, 700, 30.0, "random", "uniform"),
 }
 
 
