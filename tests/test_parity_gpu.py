@@ -97,6 +97,18 @@ SMALL = {
     "H2560_V300_8bit_cap_f16": dict(M=200, H=2560, V=300, bits=8, softcap=30.0, sb_dtype="f16"),
     "M40_H512_V900_8bit_group32": dict(M=40, H=512, V=900, bits=8, group=32),
     "M50_H640_V333_4bit_group128_bf16": dict(M=50, H=640, V=333, bits=4, group=128, sb_dtype="bf16"),
+    # at most 33 tokens (the small-M tile: every group size, both widths, narrow
+    # scales, softcap, masks, vocabularies that end inside a tile)
+    "M1_H256_V1000_4bit": dict(M=1, H=256, V=1000, bits=4),
+    "M7_H512_V777_8bit_cap_zipf": dict(M=7, H=512, V=777, bits=8, softcap=30.0, targets="zipf"),
+    "M16_H1536_V4097_4bit_group32_bf16": dict(M=16, H=1536, V=4097, bits=4, group=32, sb_dtype="bf16"),
+    "M24_H1024_V2049_8bit_group128_f16_randmask": dict(M=24, H=1024, V=2049, bits=8, group=128, sb_dtype="f16",
+                                                       mask="random", mask_frac=0.3),
+    "M31_H2560_V3001_8bit_cap_group32": dict(M=31, H=2560, V=3001, bits=8, softcap=30.0, group=32),
+    "M32_H768_V515_4bit_cap_group128_prefixmask": dict(M=32, H=768, V=515, bits=4, softcap=30.0, group=128,
+                                                       mask="prefix", mask_frac=0.5),
+    "M32_H640_V64_8bit_f16": dict(M=32, H=640, V=64, bits=8, sb_dtype="f16"),
+    "M33_H512_V900_8bit": dict(M=33, H=512, V=900, bits=8),
 }
 
 
@@ -267,11 +279,11 @@ def test_peaked_softmax(torch_cuda, softcap):
     check(inp, gpu, orc, np.arange(64), "peaked")
 
 
-@pytest.mark.parametrize("M", [40, 64, 65])
+@pytest.mark.parametrize("M", [1, 16, 32, 40, 64, 65])
 def test_small_m_on_the_full_head(torch_cuda, M):
-    # the small-M launch (M <= 64: only the first token group multiplies, many
-    # dh splits) and its neighbour M = 65, on workload 3's full head; every
-    # token against the oracle
+    # the small-M launch on workload 3's full head (M <= 64: only the first
+    # token group of the tile multiplies, many dh splits) and its neighbour
+    # M = 65; every token against the oracle
     w = syn.WORKLOADS[3]
     say("small M=%d on workload 3's head: generating inputs" % M)
     inp = syn.make_inputs(w, syn.seed_for(3), M=M)
