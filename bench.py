@@ -29,14 +29,24 @@ COPY_BYTES = 1 << 30        # calibration copy: reads and writes exactly this ma
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_M8192_H2560_V262144_8bit.txt")
 
 
+def _code_only(text):
+    """C/C++ source without comments and blank lines (string literals in these
+    sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources; a traffic measurement is valid only for them."""
+    """Hash of the code of the HIP sources (comments excluded); a traffic
+    measurement is valid only for the kernels it was taken on."""
     import hashlib
     d = os.path.join(ROOT, "linear_cross_entropy_libcce_amd", "csrc")
     hsh = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         hsh.update(f.encode())
-        hsh.update(open(os.path.join(d, f), "rb").read())
+        hsh.update(_code_only(open(os.path.join(d, f)).read()).encode())
     return hsh.hexdigest()[:16]
 
 

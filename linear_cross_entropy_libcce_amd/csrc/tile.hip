@@ -11,7 +11,8 @@ namespace cce {
 // rows [128(w%2), +128) of the tile as 2 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16 (rows = tokens, columns = vocabulary rows).
 //
-// Per K step (one quantization group of 64):
+// Per K step (one quantization group: 64 columns, 32 for group 32; a group of
+// 128 takes two steps, the second with ratio 1):
 //  * the code tile of the step is in LDS as bf16 (double buffered) and shared
 //    by the eight waves;
 //  * the token operand comes straight from the fragment-major augmented rows

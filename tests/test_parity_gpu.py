@@ -87,7 +87,7 @@ SMALL = {
     "wide_H256_V700_4bit": dict(M=4200, H=256, V=700, bits=4),
     "wide_H512_V389_8bit_cap_randmask": dict(M=4500, H=512, V=389, bits=8, softcap=30.0, mask="random",
                                              mask_frac=0.4),
-    # quantization groups of 32 (two folds per K step) and 128, bf16 / fp16 scales and biases
+    # quantization groups of 32 (32-wide K steps) and 128, bf16 / fp16 scales and biases
     "H512_V900_8bit_group32": dict(M=300, H=512, V=900, bits=8, group=32),
     "H768_V700_4bit_cap_group32_bf16_randmask": dict(M=400, H=768, V=700, bits=4, softcap=30.0, group=32,
                                                      sb_dtype="bf16", mask="random", mask_frac=0.3),
