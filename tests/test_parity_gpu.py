@@ -209,6 +209,26 @@ def test_all_masked_and_out_of_range_targets(torch_cuda):
     assert np.allclose(gpu[0][:4], -gpu[1][:4], atol=1e-6)
 
 
+def test_empty_token_batch(torch_cuda):
+    # M = 0 through the binding: a successful no-op with empty outputs, for the
+    # quantized and the dense head (no workspace is needed)
+    torch = torch_cuda
+    inp = syn.make_custom(M=0, H=128, V=500, bits=8, seed=4, softcap=30.0)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    logp, lse = cce.cce_forward(h, head, t, m)
+    dh = cce.cce_backward(h, head, t, lse, None, m)
+    torch.cuda.synchronize()
+    assert logp.shape == (0,) and lse.shape == (0,) and dh.shape == (0, 128)
+    d = syn.make_dense(M=0, H=128, V=300, seed=4)
+    dhead = cce.dense_head_from_numpy(d)
+    h2, t2, _ = cce.tokens_from_numpy(d)
+    logp2, lse2 = cce.cce_dense_forward(h2, dhead, t2)
+    dh2, dw2 = cce.cce_dense_backward(h2, dhead, t2, lse2)
+    torch.cuda.synchronize()
+    assert logp2.shape == (0,) and dh2.shape == (0, 128) and dw2.shape == (300, 128)
+
+
 def test_workspace_reuse_across_sizes(torch_cuda):
     # one caller-owned workspace (sized for the larger call) serves calls of
     # different M back to back, forward and backward, with results equal to
