@@ -70,13 +70,38 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 //   group.
 // * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
 //   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
-// One workgroup per 64 rows, three flat passes: (1) |b'| of every (row,
-// group) with a shared-memory max per row; (2) the digits, lanes over
-// consecutive (row, group) pairs so that the loads and the byte stores of a
-// wave are contiguous; (3) the ratio table, whose layout is [step][V] (read
-// that way by the tile): the scales of 64 groups at a time are staged in LDS
-// with contiguous loads, then written with lanes over rows.
+// One workgroup per 64 rows.  Digits: when a row's group count is a multiple
+// of 4 (and the scales and biases are aligned for it), four threads share a
+// row, each taking 4 consecutive groups at a time with one vector load per
+// operand: the row's max |b'| is a shuffle reduction over the four, and
+// each set of 4 digits is one 32-bit store per part.  Otherwise two flat
+// passes: |b'| of every (row, group) with a shared-memory max per row, then
+// the digits with lanes over consecutive (row, group) pairs and byte stores.
+// Then the ratio table, whose layout is [step][V] (read that way by the
+// tile): the scales of 64 groups at a time are staged in LDS with contiguous
+// loads, then written with lanes over rows.
 constexpr int HP_ROWS = 64, HP_COLS = 64, HP_LD = HP_COLS + 1;
+
+// 4 consecutive scale or bias values from element i (i % 4 == 0, base aligned
+// to 4 elements), widened to fp32.
+__device__ __forceinline__ void ld_sb4(const void *base, int64_t i, int sbt, float *o) {
+  if (sbt == SB_F32) {
+    const f32x4_t x = *(const f32x4_t *)(static_cast<const float *>(base) + i);
+    o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
+  } else {
+    const uint2 w = *(const uint2 *)(static_cast<const uint16_t *>(base) + i);
+    o[0] = sb_widen(w.x & 0xFFFFu, sbt); o[1] = sb_widen(w.x >> 16, sbt);
+    o[2] = sb_widen(w.y & 0xFFFFu, sbt); o[3] = sb_widen(w.y >> 16, sbt);
+  }
+}
+
+// The two digit bytes (offset by 128) of b' in units of u = max|b'| / 32639.
+__device__ __forceinline__ void bias_digits(float bp, float inv, uint32_t &d1b, uint32_t &d0b) {
+  const int q = (int)fminf(fmaxf(rintf(bp * inv), -32639.0f), 32639.0f);
+  const int d1 = (q + 128) >> 8;  // floor((q + 128) / 256), in [-127, 127]
+  d1b = (uint32_t)(d1 + 128);
+  d0b = (uint32_t)(q - 256 * d1 + 128);
+}
 
 __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, float *su, float *sT) {
   const int64_t V = f.V;
@@ -86,29 +111,69 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
   const int rows = (int)(V - v0 < HP_ROWS ? V - v0 : HP_ROWS);
   unsigned *smax = reinterpret_cast<unsigned *>(su);
   float *sprev = su + HP_ROWS;
-  if (tid < HP_ROWS) smax[tid] = 0u;
-  __syncthreads();
   const int64_t e0 = v0 * Gq;  // first (row, group) element of the block
-  const int n = rows * Gq;
-  for (int i = tid; i < n; i += 256) {
-    const float bp = fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt));
-    atomicMax(&smax[i / Gq], __float_as_uint(fabsf(bp)));  // |b'| >= 0: integer order is float order
+  const uintptr_t al = sbt == SB_F32 ? 15 : 7;
+  if ((Gq & 3) == 0 && (((uintptr_t)f.scales | (uintptr_t)f.biases) & al) == 0) {
+    const int r = tid >> 2, qd = tid & 3, G4 = Gq >> 2;
+    const int64_t er = e0 + (int64_t)r * Gq;  // first element of row r
+    float m = 0.0f;
+    if (r < rows)
+      for (int j = qd; j < G4; j += 4) {
+        float sc[4], bi[4];
+        ld_sb4(f.scales, er + 4 * j, sbt, sc);
+        ld_sb4(f.biases, er + 4 * j, sbt, bi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(fmaf(shift, sc[k], bi[k])));
+      }
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    if (r < rows) {
+      if (qd == 0) smax[r] = __float_as_uint(m);
+      const float u = m / 32639.0f;
+      const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+      uint8_t *row = f.baug + (v0 + r) * Kb;
+      for (int j = qd; j < G4; j += 4) {
+        float sc[4], bi[4];
+        ld_sb4(f.scales, er + 4 * j, sbt, sc);
+        ld_sb4(f.biases, er + 4 * j, sbt, bi);
+        uint32_t w1 = 0, w0 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t d1b, d0b;
+          bias_digits(fmaf(shift, sc[k], bi[k]), inv, d1b, d0b);
+          w1 |= d1b << (8 * k);
+          w0 |= d0b << (8 * k);
+        }
+        *(uint32_t *)(row + 4 * j) = w1;
+        *(uint32_t *)(row + Gq + 4 * j) = w1;
+        *(uint32_t *)(row + 2 * Gq + 4 * j) = w0;
+      }
+      for (int o = 3 * Gq + 4 * qd; o < Kb; o += 16) *(uint32_t *)(row + o) = 0x80808080u;
+    }
+    __syncthreads();
+  } else {
+    if (tid < HP_ROWS) smax[tid] = 0u;
+    __syncthreads();
+    const int n = rows * Gq;
+    for (int i = tid; i < n; i += 256) {
+      const float bp = fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt));
+      atomicMax(&smax[i / Gq], __float_as_uint(fabsf(bp)));  // |b'| >= 0: integer order is float order
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const int r = i / Gq, gi = i - r * Gq;
+      const float u = __uint_as_float(smax[r]) / 32639.0f;
+      const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+      uint32_t d1b, d0b;
+      bias_digits(fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt)), inv, d1b, d0b);
+      uint8_t *row = f.baug + (v0 + r) * Kb;
+      row[gi] = (uint8_t)d1b;
+      row[Gq + gi] = (uint8_t)d1b;
+      row[2 * Gq + gi] = (uint8_t)d0b;
+    }
+    const int pad = Kb - 3 * Gq;
+    for (int i = tid; i < rows * pad; i += 256) f.baug[(v0 + i / pad) * Kb + 3 * Gq + i % pad] = (uint8_t)128;
   }
-  __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    const int r = i / Gq, gi = i - r * Gq;
-    const float u = __uint_as_float(smax[r]) / 32639.0f;
-    const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
-    const float bp = fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt));
-    const int q = (int)fminf(fmaxf(rintf(bp * inv), -32639.0f), 32639.0f);
-    const int d1 = (q + 128) >> 8;  // floor((q + 128) / 256), in [-127, 127]
-    uint8_t *row = f.baug + (v0 + r) * Kb;
-    row[gi] = (uint8_t)(d1 + 128);
-    row[Gq + gi] = (uint8_t)(d1 + 128);
-    row[2 * Gq + gi] = (uint8_t)(q - 256 * d1 + 128);
-  }
-  const int pad = Kb - 3 * Gq;
-  for (int i = tid; i < rows * pad; i += 256) f.baug[(v0 + i / pad) * Kb + 3 * Gq + i % pad] = (uint8_t)128;
   const int64_t v = v0 + lane;
   if (wave == 0 && lane < rows) {
     sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
