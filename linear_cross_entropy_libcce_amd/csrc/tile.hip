@@ -37,8 +37,11 @@ namespace cce {
 // path with the head rows copied into LDS as they are; no bias block, no
 // fold and no final scale.
 //
-// VAR_SMALL (at most 64 tokens): only the two waves of token group 0 carry
-// MFMA work and epilogues; the other six still produce the code tiles.
+// VAR_SMALL (at most 64 tokens, one token group): every wave multiplies the
+// 64 tokens by its own 32 vocabulary rows of the tile (one column block), so
+// all eight waves share the MFMA work and the epilogues; the forward
+// combines the waves' softmax partials into the two halves' partials at the
+// end.
 //
 // VAR_EXTRA (a second instantiation, so the plain passes carry none of it):
 //  * forward: the largest logit of every (token, vocabulary tile), written to
@@ -182,8 +185,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int tile_end = min(tile_begin + tpw, a.range_tiles);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int tg = wave >> 1, vh = wave & 1;  // the two waves of a token group sit on two SIMDs
-  const bool live = SMALL ? tg == 0 : true;  // this wave's tokens can be supervised
+  // the two waves of a token group sit on two SIMDs; small M: one token group
+  // and 32 vocabulary rows per wave
+  const int tg = SMALL ? 0 : wave >> 1, vh = SMALL ? wave >> 2 : wave & 1;
+  constexpr bool live = true;
+  constexpr int NC = SMALL ? 1 : 4;  // 32-row column blocks per wave
   const int l32 = lane & 31, lh = lane >> 5;
   const int steps = a.NB + a.G;
 
@@ -193,7 +199,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   __shared__ float sX[2][BM];  // EXTRA: per-wave tile maxima, read after the step's barrier
 
   const int tok0 = tt * BM + tg * 64;
-  const int vcol0 = vh * 128;  // this wave's first vocabulary row within the tile
+  const int vcol0 = SMALL ? wave * 32 : vh * 128;  // this wave's first vocabulary row within the tile
   // fragment-major h rows of the workgroup's 256 tokens: one 1 KiB block per
   // (32 tokens, 16 K); this wave's two token blocks start at hv0, hv0 + hstride.
   const rsrc_t rh = make_rsrc(a.haug + (size_t)(tt * BM >> 5) * a.ks16 * 512, (int64_t)8 * a.ks16 * 1024);
@@ -239,7 +245,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     int boff[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) boff[ks] = swz<KW>(vcol0 + l32, 2 * ks + lh);
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][NC];
     bf16x8_t hA[2][NKS];
 
     // step `n` (<= steps) steps after (tile, st)
@@ -274,24 +280,24 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       const bool sbias = sn < a.NB;
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
-      float r[4];
+      float r[NC];
       if (live && !DENSE)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+        for (int c = 0; c < NC; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
       const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
       // B operand of column block c for k-step ks + 1 is read as soon as its
       // two MFMAs of k-step ks are issued; a scheduling barrier after each
       // k-step keeps this order (left free, the compiler hoists every LDS read
       // and unpack and runs out of registers).
-      bf16x8_t bq[4];
+      bf16x8_t bq[NC];
       if (live)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KW);
+        for (int c = 0; c < NC; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KW);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (live) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               if (ks == 0 && !DENSE) acc[rb][c] *= r[c];
@@ -318,14 +324,16 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       const int64_t v0 = (int64_t)(a.range_tile0 + tile) * BNT;
       const bool full = v0 + BNT <= a.V;
       float xm = BWD ? 0.0f : -INFINITY;  // EXTRA: max logit (forward) or max |coefficient| (backward)
-      float sl[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      float sl[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sl[c] = 1.0f;
       if (!DENSE) {
         const rsrc_t rl = make_rsrc(a.slast + v0, (a.V - v0 < BNT ? a.V - v0 : BNT) * 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
+        for (int c = 0; c < NC; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -460,7 +468,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
@@ -484,10 +492,34 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     if (idx < total) do_step(idx, tile, st, P1, P0);
   }
 
-  if (!BWD && live) {
-    float *dst = a.part + ((size_t)(2 * wr + vh) * a.M_pad + tok0 + lane) * 2;
-    dst[0] = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
-    dst[1] = run_s;
+  if (!BWD) {
+    const float m_out = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
+    if (SMALL) {
+      // the four waves of each vocabulary half combine their partials
+      float *sp = &sZ[0][0];  // 8 x 64 x (max, sum); the epilogues are done
+      __syncthreads();
+      sp[(wave * 64 + lane) * 2] = m_out;
+      sp[(wave * 64 + lane) * 2 + 1] = run_s;
+      __syncthreads();
+      if (wave < 2) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m = fmaxf(m, sp[((4 * wave + w) * 64 + lane) * 2]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = sp[((4 * wave + w) * 64 + lane) * 2], sw = sp[((4 * wave + w) * 64 + lane) * 2 + 1];
+          sum += (mw == -INFINITY) ? 0.0f : sw * __builtin_amdgcn_exp2f((mw - m) * LOG2E);
+        }
+        float *dst = a.part + ((size_t)(2 * wr + wave) * a.M_pad + tok0 + lane) * 2;
+        dst[0] = m;
+        dst[1] = sum;
+      }
+    } else {
+      float *dst = a.part + ((size_t)(2 * wr + vh) * a.M_pad + tok0 + lane) * 2;
+      dst[0] = m_out;
+      dst[1] = run_s;
+    }
   }
 }
 
