@@ -26,7 +26,8 @@ namespace cce {
 // Reads are raw buffer loads (rows past V read as zeros), so the step has no
 // per-lane predicate.  Each split owns its fp32 slab: no atomics, and a
 // repeated call gives identical bits.
-// SMALL (at most 64 tokens): only the two waves of token group 0 multiply.
+// SMALL (at most 64 tokens, one token group): every wave multiplies the 64
+// tokens by its own 32 of the workgroup's 256 dh columns.
 // SKIP (second instantiation): the split contracts only the vocabulary tiles
 // of its range whose pair flag is set for its token tile; their K steps are
 // listed in LDS first, in order.
@@ -196,8 +197,12 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   int nsteps = min(steps_per, a.chunk_steps - step0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tg = wave >> 1, dh = wave & 1;  // the two waves of a token group sit on two SIMDs
-  const bool live = SMALL ? tg == 0 : true;  // at most 64 tokens: token group 0 only
+  // the two waves of a token group sit on two SIMDs; small M: one token group,
+  // 32 columns per wave
+  const int tg = SMALL ? 0 : wave >> 1, dh = wave & 1;
+  constexpr bool live = true;
+  constexpr int NC = SMALL ? 1 : 4;                 // 32-column blocks per wave
+  const int col0 = SMALL ? wave * 32 : dh * 128;   // this wave's first column within the tile
   const int l32 = lane & 31, lh = lane >> 5;
 
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][DTW * KSTP];
@@ -247,11 +252,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int cv0 = ((tg * 2) * (int)a.ksv * 64 + lane) * 16;
   const int cstride = (int)a.ksv * 1024;
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[2][NC];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
 
@@ -263,11 +268,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.tid = tid;
     pr.gq0 = d0 / a.gs;
     DhRegs<BITS> P0, P1;
-    // this lane's B-operand chunk offsets (row dh*128 + l32 + 32c, chunk 2ks + lh);
+    // this lane's B-operand chunk offsets (row col0 + l32 + 32c, chunk 2ks + lh);
     // the swizzle key of row d + 32c equals that of row d
     int boff[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) boff[ks] = dswz(dh * 128 + l32, 2 * ks + lh);
+    for (int ks = 0; ks < 4; ++ks) boff[ks] = dswz(col0 + l32, 2 * ks + lh);
     bf16x8_t cA[2][4];
     float sc[8], bi[8];
     // chunk K step of step i of this split (past the end: the last one)
@@ -306,15 +311,15 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       pr.read_sb(sSB[cb ^ 1], sc, bi);
       const uint16_t *sw = sB[cb];
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
-      bf16x8_t bq[4];
+      bf16x8_t bq[NC];
       if (live)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
+        for (int c = 0; c < NC; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         if (live) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
@@ -338,16 +343,15 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   } else if (a.accumulate) {
     return;
   }
-  if (!live) return;  // rows of padding tokens only
 
-  // result lane layout: column d0 + dh*128 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j.
+  // result lane layout: column d0 + col0 + c*32 + l32, rows tok0 + rb*32 + 8i + 4*lh + j.
   // Accumulating (later chunks), the 32 old values of a column block are all
   // loaded before any of them is stored: interleaved, every load would wait
   // for the previous store (the compiler cannot prove the rows distinct).
   float *const slab = a.dh_part + ((size_t)ks_ * act * BM + tok0 + 4 * lh) * a.H;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int d = d0 + dh * 128 + c * 32 + l32;
+  for (int c = 0; c < NC; ++c) {
+    const int d = d0 + col0 + c * 32 + l32;
     if (d >= a.H) continue;
     float old[2][16];
     if (a.accumulate) {
