@@ -301,9 +301,10 @@ def test_peaked_softmax(torch_cuda, softcap):
 
 @pytest.mark.parametrize("M", [1, 16, 32, 40, 64, 65])
 def test_small_m_on_the_full_head(torch_cuda, M):
-    # the small-M launch on workload 3's full head (M <= 64: only the first
-    # token group of the tile multiplies, many dh splits) and its neighbour
-    # M = 65; every token against the oracle
+    # the small-M launch on workload 3's full head (M <= 64: every wave of the
+    # tile and of the dh contraction multiplies all the tokens by its own 32
+    # rows or columns, many dh splits) and its neighbour M = 65; every token
+    # against the oracle
     w = syn.WORKLOADS[3]
     say("small M=%d on workload 3's head: generating inputs" % M)
     inp = syn.make_inputs(w, syn.seed_for(3), M=M)
