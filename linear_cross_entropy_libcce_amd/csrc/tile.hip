@@ -217,7 +217,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     tgt_t = rec.tgt;
   }
   const float c1 = -2.0f * LOG2E * a.inv_cap;  // t = exp2(|z| * c1)
-  const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 * u / (1 + t))
+  const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 / (1 + exp2(c3 z)))
+  const float c3 = 2.0f * LOG2E * a.inv_cap;
   const float capl2 = LOG2E * a.cap;           // c(z) * log2(e) = capl2 * tanh(z / cap)
   const float ng = -g_t, ng4 = -4.0f * g_t;    // backward coefficient factors
 
@@ -355,13 +356,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
           const int64_t vb = v0 + vcol0 + c * 32 + k0;
           const int nv = full ? 16 : (int)(a.V - vb < 0 ? 0 : (a.V - vb < 16 ? a.V - vb : 16));
           if (MODE == MODE_FWD_CAP) {
-            // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum.
+            // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum.  With
+            // c(z) - cap = -2 cap / (1 + e^{2z/cap}): e^{2z/cap} overflowing
+            // gives exp(0) = 1 and underflowing e^{-2 cap}, the two limits.
             float ssum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-              const float t = __builtin_amdgcn_exp2f(fabsf(z[k]) * c1);
-              const float u = z[k] >= 0.0f ? t : 1.0f;
-              const float e = __builtin_amdgcn_exp2f(c2 * u * __builtin_amdgcn_rcpf(1.0f + t));
+              const float tp = __builtin_amdgcn_exp2f(z[k] * c3);
+              const float e = __builtin_amdgcn_exp2f(c2 * __builtin_amdgcn_rcpf(1.0f + tp));
               ssum += (k < nv) ? e : 0.0f;
               if (EXTRA) xm = fmaxf(xm, (k < nv) ? z[k] : -INFINITY);
             }
