@@ -221,6 +221,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const float c3 = 2.0f * LOG2E * a.inv_cap;
   const float capl2 = LOG2E * a.cap;           // c(z) * log2(e) = capl2 * tanh(z / cap)
   const float ng = -g_t, ng4 = -4.0f * g_t;    // backward coefficient factors
+  const float m2capl2 = -2.0f * capl2, capl2_lse2 = capl2 - lse2;  // c(z) log2(e) - lse2 = fma(m2capl2, r, capl2_lse2)
 
   // EXTRA backward: walk the flagged tiles of the range only
   const uint8_t *fl_row = (BWD && EXTRA) ? a.fl + (int64_t)tt * a.fl_ld + a.range_tile0 : nullptr;
@@ -392,14 +393,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             const int tk = (dtk >= 0 && dtk < 16) ? (int)dtk : -1;
             float cv[16];
             if (a.cap > 0.0f) {
-              // with t = e^{-2|z|/cap} and r = 1/(1+t): tanh(|z|/cap) = 2r - 1 and
-              // c'(z) = 1 - tanh^2 = 4 t r^2 (no cancellation for large |z|)
+              // with r = 1/(1 + e^{2z/cap}): tanh(z/cap) = 1 - 2r and
+              // c'(z) = 1 - tanh^2 = 4 r (1 - r).  e^{2z/cap} overflowing gives
+              // r = 0 (tanh = 1, c' = 0); for z far below zero r rounds to 1
+              // and c' to 0 where it is below ~1e-7, its absolute error.
 #pragma unroll
               for (int k = 0; k < 16; ++k) {
-                const float t = __builtin_amdgcn_exp2f(fabsf(z[k]) * c1);
-                const float r = __builtin_amdgcn_rcpf(1.0f + t);
-                const float arg = fmaf(copysignf(capl2, z[k]), fmaf(2.0f, r, -1.0f), -lse2);
-                cv[k] = __builtin_amdgcn_exp2f(arg) * (t * r) * (r * ng4);
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
+                const float arg = fmaf(m2capl2, r, capl2_lse2);
+                cv[k] = __builtin_amdgcn_exp2f(arg) * fmaf(-r, r, r) * ng4;
               }
             } else {
 #pragma unroll
