@@ -357,7 +357,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
           const int64_t vb = v0 + vcol0 + c * 32 + k0;
           const int nv = full ? 16 : (int)(a.V - vb < 0 ? 0 : (a.V - vb < 16 ? a.V - vb : 16));
           if (MODE == MODE_FWD_CAP) {
-            // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum.  With
+            // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum (cap <= 40,
+            // so that even e^{-2 cap} is a normal fp32; see launch_tile).  With
             // c(z) - cap = -2 cap / (1 + e^{2z/cap}): e^{2z/cap} overflowing
             // gives exp(0) = 1 and underflowing e^{-2 cap}, the two limits.
             float ssum = 0.0f;
@@ -376,7 +377,18 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               z[k] = (k < nv) ? z[k] : -INFINITY;
               tmax = fmaxf(tmax, z[k]);
             }
-            if (EXTRA) xm = fmaxf(xm, tmax);
+            if (EXTRA) xm = fmaxf(xm, tmax);  // raw logits: the softcap is applied to the maximum later
+            if (a.cap > 0.0f) {
+              // a softcap too large for the fixed reference of MODE_FWD_CAP:
+              // c(z) = cap (1 - 2 / (1 + e^{2z/cap})) under a running maximum
+              tmax = -INFINITY;
+#pragma unroll
+              for (int k = 0; k < 16; ++k) {
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
+                z[k] = (k < nv) ? a.cap * fmaf(-2.0f, r, 1.0f) : -INFINITY;
+                tmax = fmaxf(tmax, z[k]);
+              }
+            }
             const float mnew = fmaxf(run_m, tmax);
             if (mnew != -INFINITY) {
               const float mb = mnew * LOG2E;
@@ -527,8 +539,13 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   }
 }
 
+// The forward's fixed reference e^{c(z) - cap} keeps every term <= 1, but the
+// largest term of a token can be as small as e^{-2 cap}: it stays a normal
+// fp32 for cap <= 40.  Larger softcaps take the running-maximum forward.
+constexpr float CAP_FIXED_REF_MAX = 40.0f;
+
 void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
-  const int mode = bwd ? MODE_BWD : (a.cap > 0.0f ? MODE_FWD_CAP : MODE_FWD);
+  const int mode = bwd ? MODE_BWD : ((a.cap > 0.0f && a.cap <= CAP_FIXED_REF_MAX) ? MODE_FWD_CAP : MODE_FWD);
   const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
   const bool gs32 = a.kw == 32;
   // group 32 has no small-M instantiation (the plain one is correct there)

@@ -314,6 +314,22 @@ def test_small_m_on_the_full_head(torch_cuda, M):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "smallM%d" % M)
 
 
+@pytest.mark.parametrize("cap", [40.0, 50.0, 100.0, 1000.0])
+def test_large_softcaps(torch_cuda, cap):
+    # every logit far below the cap: e^{c(z) - cap} of the largest logit is
+    # below fp32's smallest normal once 2 cap exceeds ~87, so such caps need a
+    # running maximum; against the oracle, several vocabulary tiles and splits,
+    # a ragged tail and masked tokens, 4- and 8-bit heads
+    for bits, H, V in ((8, 512, 2300), (4, 768, 1500)):
+        inp = syn.make_custom(M=150, H=H, V=V, bits=bits, seed=int(cap) + bits, softcap=cap,
+                              mask="random", mask_frac=0.2)
+        g = np.random.default_rng(7).uniform(-1.5, 1.5, size=150)
+        say("softcap %g, %d-bit: GPU" % (cap, bits))
+        gpu = run_gpu(torch_cuda, inp, g=g)
+        assert np.all(np.isfinite(gpu[0])) and np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))
+        check(inp, gpu, oracle.cce(inp, g=g), np.arange(150), "cap%g_%dbit" % (cap, bits))
+
+
 def test_hip_graph_capture_and_replay(torch_cuda):
     # the calls enqueue kernels only (no allocation, no host synchronization,
     # no memset), so a forward + backward can be captured in a HIP graph; every
