@@ -330,6 +330,30 @@ def test_large_softcaps(torch_cuda, cap):
         check(inp, gpu, oracle.cce(inp, g=g), np.arange(150), "cap%g_%dbit" % (cap, bits))
 
 
+@pytest.mark.parametrize("bits,cap", [(8, 30.0), (4, 0.0)])
+def test_zero_and_tiny_scales(torch_cuda, bits, cap):
+    # the fold divides consecutive group scales (a zero scale stands in as
+    # 1e-30): groups of scale exactly 0 first, in the middle (two in a row)
+    # and last, rows whose every scale is 0 (constant per group: the bias
+    # alone), and rows of scales near 1e-20, against the oracle, which uses
+    # the stored values as they are
+    M, H, V = 120, 512, 1300
+    inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=91 + bits, softcap=cap, mask="random", mask_frac=0.2)
+    sc = inp["scales"]
+    sc[0:100, 0] = 0.0
+    sc[100:200, 3:5] = 0.0
+    sc[200:210, :] = 0.0
+    sc[300:320, -1] = 0.0
+    sc[400:420, :] *= np.float32(1e-20)
+    sc[500:520, 1::2] = 0.0
+    inp["targets"][:20] = np.arange(200, 220)  # some targets on the all-zero-scale rows
+    g = np.random.default_rng(3).uniform(-1.5, 1.5, size=M)
+    say("zero and tiny scales, %d-bit, cap %g: GPU" % (bits, cap))
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    assert all(np.all(np.isfinite(x)) for x in gpu)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "zeroscale%d" % bits)
+
+
 def test_hip_graph_capture_and_replay(torch_cuda):
     # the calls enqueue kernels only (no allocation, no host synchronization,
     # no memset), so a forward + backward can be captured in a HIP graph; every
