@@ -79,6 +79,7 @@ SMALL = {
     "nocap_ragged_zipf": (200, 256, 1000, 0.0, "none", "zipf"),
     "prefix_masked_H1536": (260, 1536, 2304, 0.0, "prefix", "uniform"),
     "H16384_max": (70, 16384, 700, 30.0, "random", "uniform"),
+    "cap100_randmask": (250, 512, 1500, 100.0, "random", "uniform"),
 }
 
 

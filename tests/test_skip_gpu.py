@@ -71,9 +71,13 @@ def gpu_run(torch, inp, g, block_eps, filter_eps):
     return bmx.cpu().numpy().astype(np.float64), dh.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name", list(CASES))
+# block maxima also under a softcap above 40 (the forward's running-maximum path)
+BMX_CASES = dict(CASES, H512_V1100_4bit_cap100_randmask=(700, 512, 1100, 4, 73, "random", 100.0))
+
+
+@pytest.mark.parametrize("name", list(BMX_CASES))
 def test_block_max_matches_oracle(torch_cuda, name):
-    inp = flat_blocks(*CASES[name])
+    inp = flat_blocks(*BMX_CASES[name])
     say("%s: block_max" % name)
     head = cce.head_from_numpy(inp)
     h, t, m = cce.tokens_from_numpy(inp)
