@@ -354,6 +354,25 @@ def test_zero_and_tiny_scales(torch_cuda, bits, cap):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "zeroscale%d" % bits)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_outlier_group_biases(torch_cuda, bits):
+    # the bias block holds each row's b' (b, plus 128 s for 8-bit codes) in
+    # 16-bit fixed point relative to the row's largest |b'|: one group per row
+    # with b' = 1 (20-40x the others) loosens it for the whole row and must
+    # still meet the tolerance
+    M, H, V = 64, 2560, 2000
+    inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=5, softcap=0.0)
+    s, b = inp["scales"], inp["biases"]
+    rows = np.arange(V)
+    grp = rows % s.shape[1]
+    shift = np.float32(128.0 if bits == 8 else 0.0)
+    b[rows, grp] = np.float32(1.0) - shift * s[rows, grp]
+    g = np.random.default_rng(4).uniform(-1.5, 1.5, size=M)
+    say("outlier group biases, %d-bit: GPU" % bits)
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "outlier_b%d" % bits)
+
+
 def test_hip_graph_capture_and_replay(torch_cuda):
     # the calls enqueue kernels only (no allocation, no host synchronization,
     # no memset), so a forward + backward can be captured in a HIP graph; every
