@@ -373,6 +373,25 @@ def test_outlier_group_biases(torch_cuda, bits):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "outlier_b%d" % bits)
 
 
+def test_large_token_count(torch_cuda):
+    # 300000 tokens (1172 token tiles after compaction; the mask compacted by
+    # its own launch): sampled tokens, the first and last supervised ones
+    # among them, against the oracle, and properties of every token
+    M = 300000
+    inp = syn.make_custom(M=M, H=256, V=700, bits=8, seed=17, softcap=30.0, mask="random", mask_frac=0.25)
+    g = np.random.default_rng(8).uniform(-1.5, 1.5, size=M)
+    say("M=%d: GPU" % M)
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    rows = sample_rows(inp, 40, 17)
+    rows = np.unique(np.concatenate([rows, np.arange(M - 40, M)]))
+    say("M=%d: oracle on %d tokens" % (M, len(rows)))
+    check(inp, gpu, oracle.cce(inp, g=g, tokens=rows), rows, "largeM")
+    glogp, glse, gdh = gpu
+    act = inp["mask"] != 0
+    assert np.all(glogp[act] <= 1e-6) and np.all(np.isfinite(glse)) and np.all(np.isfinite(gdh))
+    assert not np.any(glogp[~act]) and not np.any(glse[~act]) and not np.any(gdh[~act])
+
+
 def test_hip_graph_capture_and_replay(torch_cuda):
     # the calls enqueue kernels only (no allocation, no host synchronization,
     # no memset), so a forward + backward can be captured in a HIP graph; every
