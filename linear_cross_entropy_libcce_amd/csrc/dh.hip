@@ -200,7 +200,6 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   // the two waves of a token group sit on two SIMDs; small M: one token group,
   // 32 columns per wave
   const int tg = SMALL ? 0 : wave >> 1, dh = wave & 1;
-  constexpr bool live = true;
   constexpr int NC = SMALL ? 1 : 4;                 // 32-column blocks per wave
   const int col0 = SMALL ? wave * 32 : dh * 128;   // this wave's first column within the tile
   const int l32 = lane & 31, lh = lane >> 5;
@@ -312,12 +311,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
       const uint16_t *sw = sB[cb];
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
       bf16x8_t bq[NC];
-      if (live)
 #pragma unroll
         for (int c = 0; c < NC; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        if (live) {
+        {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll

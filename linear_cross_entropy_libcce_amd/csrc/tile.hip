@@ -188,7 +188,6 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   // the two waves of a token group sit on two SIMDs; small M: one token group
   // and 32 vocabulary rows per wave
   const int tg = SMALL ? 0 : wave >> 1, vh = SMALL ? wave >> 2 : wave & 1;
-  constexpr bool live = true;
   constexpr int NC = SMALL ? 1 : 4;  // 32-row column blocks per wave
   const int l32 = lane & 31, lh = lane >> 5;
   const int steps = a.NB + a.G;
@@ -283,7 +282,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[NC];
-      if (live && !DENSE)
+      if (!DENSE)
 #pragma unroll
         for (int c = 0; c < NC; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
       const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
@@ -292,12 +291,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       // k-step keeps this order (left free, the compiler hoists every LDS read
       // and unpack and runs out of registers).
       bf16x8_t bq[NC];
-      if (live)
 #pragma unroll
         for (int c = 0; c < NC; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KW);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        if (live) {
+        {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -489,7 +487,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
       mfma_step(idx & 1, sn, vnn, snn, cur, nxt);
-      if (live && st == steps - 1) epilogue(tile);
+      if (st == steps - 1) epilogue(tile);
       __syncthreads();
       if (EXTRA && st == steps - 1) tile_extra(tile);
     };
