@@ -441,32 +441,56 @@ __global__ void __launch_bounds__(256) k_bmx_mask(int64_t nbv, const int *inv, f
 template <int BITS>
 __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, const TokRec *tok, void *dh,
                                                    int out_bf16) {
+  // four consecutive columns per thread (H % 64 == 0): 16-byte slab loads,
+  // one code word, scale and bias for the four, one vector store
   const int t = blockIdx.x;
-  const int d = blockIdx.y * 256 + threadIdx.x;
+  const int d = (blockIdx.y * 256 + threadIdx.x) * 4;
   const int H = a.H;
   if (d >= H) return;
   const int r = inv[t];
-  float acc = 0.0f;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (r >= 0) {
     const int act = active_tiles(a.cnt);
     int ksd, steps_per;
     dh_split(a, act, ksd, steps_per);
-    for (int k = 0; k < ksd; ++k) acc += a.dh_part[((size_t)k * act * BM + r) * H + d];
+    for (int k = 0; k < ksd; ++k) acc += *(const f32x4_t *)(a.dh_part + ((size_t)k * act * BM + r) * H + d);
     const TokRec rec = tok[r];
     if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
+      const uint32_t *row = a.wq + (size_t)rec.tgt * a.wpr;
+      float w[4];
       if constexpr (BITS == 16) {  // dense bf16 row
-        acc += rec.tval * bf16_to_f32(code_at<16>(a.wq + (size_t)rec.tgt * a.wpr, d));
+        const uint32_t x0 = row[d / 2], x1 = row[d / 2 + 1];
+        w[0] = bf16_to_f32(x0 & 0xFFFFu); w[1] = bf16_to_f32(x0 >> 16);
+        w[2] = bf16_to_f32(x1 & 0xFFFFu); w[3] = bf16_to_f32(x1 >> 16);
       } else {
-        const int64_t gi = (int64_t)rec.tgt * a.Gq + d / a.gs;
-        const float q = (float)code_at<BITS>(a.wq + (size_t)rec.tgt * a.wpr, d);
-        acc += rec.tval * (ld_sb(a.scales, gi, a.sbt) * q + ld_sb(a.biases, gi, a.sbt));
+        const int64_t gi = (int64_t)rec.tgt * a.Gq + d / a.gs;  // the four share a group (group >= 32)
+        const float sc = ld_sb(a.scales, gi, a.sbt), bi = ld_sb(a.biases, gi, a.sbt);
+        const uint32_t word = row[d * BITS / 32] >> ((d * BITS) % 32);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = sc * (float)((word >> (BITS * e)) & ((1u << BITS) - 1u)) + bi;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += rec.tval * w[e];
     }
   }
-  if (out_bf16)
-    static_cast<uint16_t *>(dh)[(size_t)t * H + d] = (uint16_t)bf16_rne(acc);
-  else
-    static_cast<float *>(dh)[(size_t)t * H + d] = acc;
+  // the ABI asks dh for element alignment only: vector stores when the base allows
+  if (out_bf16) {
+    uint16_t *o = static_cast<uint16_t *>(dh) + (size_t)t * H + d;
+    if (((uintptr_t)dh & 7) == 0) {
+      *(uint2 *)o = uint2{bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16), bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (uint16_t)bf16_rne(acc[e]);
+    }
+  } else {
+    float *o = static_cast<float *>(dh) + (size_t)t * H + d;
+    if (((uintptr_t)dh & 15) == 0) {
+      *(f32x4_t *)o = acc;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[e];
+    }
+  }
 }
 
 void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt) {
@@ -504,7 +528,7 @@ void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *
 
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16) {
-  const dim3 grid((unsigned)M, (unsigned)((ga.H + 255) / 256));
+  const dim3 grid((unsigned)M, (unsigned)((ga.H + 1023) / 1024));
   if (bits == 16)
     hipLaunchKernelGGL(k_dh_reduce<16>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
   else if (bits == 4)

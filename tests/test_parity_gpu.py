@@ -392,6 +392,26 @@ def test_large_token_count(torch_cuda):
     assert not np.any(glogp[~act]) and not np.any(glse[~act]) and not np.any(gdh[~act])
 
 
+def test_dh_output_with_element_alignment_only(torch_cuda):
+    # the ABI asks dh for element alignment only: an output one element into a
+    # larger buffer (fp32 4-byte, bf16 2-byte aligned) gets the same bits as an
+    # aligned one
+    import torch
+    inp = syn.make_custom(M=90, H=512, V=800, bits=8, seed=61, softcap=30.0, mask="random", mask_frac=0.2)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    M, H = inp["M"], inp["H"]
+    _, lse = cce.cce_forward(h, head, t, m)
+    for dtype, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        ref = cce.cce_backward_ex(h, head, t, lse, None, m, dh_dtype=name)
+        buf = torch.full((M * H + 1,), 7.0, dtype=dtype, device="cuda")
+        out = buf[1:].view(M, H)
+        assert out.data_ptr() % 16 != 0
+        cce.cce_backward_ex(h, head, t, lse, None, m, out=out, dh_dtype=name)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and buf[0].item() == 7.0
+
+
 def test_hip_graph_capture_and_replay(torch_cuda):
     # the calls enqueue kernels only (no allocation, no host synchronization,
     # no memset), so a forward + backward can be captured in a HIP graph; every
