@@ -314,12 +314,13 @@ def test_small_m_on_the_full_head(torch_cuda, M):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "smallM%d" % M)
 
 
-@pytest.mark.parametrize("cap", [40.0, 50.0, 100.0, 1000.0])
-def test_large_softcaps(torch_cuda, cap):
-    # every logit far below the cap: e^{c(z) - cap} of the largest logit is
-    # below fp32's smallest normal once 2 cap exceeds ~87, so such caps need a
-    # running maximum; against the oracle, several vocabulary tiles and splits,
-    # a ragged tail and masked tokens, 4- and 8-bit heads
+@pytest.mark.parametrize("cap", [0.5, 40.0, 50.0, 100.0, 1000.0])
+def test_softcap_range(torch_cuda, cap):
+    # every logit far below a large cap: e^{c(z) - cap} of the largest logit
+    # is below fp32's smallest normal once 2 cap exceeds ~87, so such caps
+    # need a running maximum; a cap of 0.5 saturates nearly every logit.
+    # Against the oracle, several vocabulary tiles and splits, a ragged tail
+    # and masked tokens, 4- and 8-bit heads
     for bits, H, V in ((8, 512, 2300), (4, 768, 1500)):
         inp = syn.make_custom(M=150, H=H, V=V, bits=bits, seed=int(cap) + bits, softcap=cap,
                               mask="random", mask_frac=0.2)
