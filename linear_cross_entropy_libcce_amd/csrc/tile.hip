@@ -112,12 +112,11 @@ struct Producer {
         const u32x4_t x = buf_load16(rw, voff, so), y = buf_load16(rw, voff + 16, so);
         p.w[0] = x[0]; p.w[1] = x[1]; p.w[2] = x[2]; p.w[3] = x[3];
         p.w[4] = y[0]; p.w[5] = y[1]; p.w[6] = y[2]; p.w[7] = y[3];
-      } else if (bias || BITS == 8) {
+      } else {
+        // 16 bytes for digits and codes alike (a 4-bit code step uses the
+        // first 8): one load instruction for both kinds of step
         const u32x4_t x = buf_load16(rw, voff, so);
         p.w[0] = x[0]; p.w[1] = x[1]; p.w[2] = x[2]; p.w[3] = x[3];
-      } else {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rw, voff, so, 0);
-        p.w[0] = x[0]; p.w[1] = x[1];
       }
     } else {
 #pragma unroll
@@ -143,11 +142,20 @@ struct Producer {
     uint32_t o[4];
     if (DENSE) {  // bf16 as stored
       o[0] = p.w[4 * h]; o[1] = p.w[4 * h + 1]; o[2] = p.w[4 * h + 2]; o[3] = p.w[4 * h + 3];
-    } else if (BITS == 8 || bias) {
+    } else if (BITS == 8) {
       unpack8s(p.w[4 * i + 2 * h] ^ 0x80808080u, o);
       unpack8s(p.w[4 * i + 2 * h + 1] ^ 0x80808080u, o + 2);
     } else {
-      unpack4(p.w[4 * i + h], o);
+      // 4-bit head: the eight nibbles of the code word are spread to bytes
+      // (codes 0 1 2 3 | 4 5 6 7) and a uniform select takes them or the two
+      // digit words, so both kinds of step share one straight-line unpack.
+      const uint32_t w = p.w[4 * i + h];
+      const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+      const uint32_t c0 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // ev.b0 od.b0 ev.b1 od.b1
+      const uint32_t c1 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // ev.b2 od.b2 ev.b3 od.b3
+      const uint32_t flip = bias ? 0x80808080u : 0u;
+      unpack8s((bias ? p.w[4 * i + 2 * h] : c0) ^ flip, o);
+      unpack8s((bias ? p.w[4 * i + 2 * h + 1] : c1) ^ flip, o + 2);
     }
     const int off = GS32 ? swz<KW>(tid >> 1, 2 * (tid & 1) + h) : swz<KW>(row0 + 16 * i, 2 * q + h);
     *(u32x4_t *)(sw + off) = u32x4_t{o[0], o[1], o[2], o[3]};
