@@ -320,15 +320,16 @@ def test_softcap_range(torch_cuda, cap):
     # is below fp32's smallest normal once 2 cap exceeds ~87, so such caps
     # need a running maximum; a cap of 0.5 saturates nearly every logit.
     # Against the oracle, several vocabulary tiles and splits, a ragged tail
-    # and masked tokens, 4- and 8-bit heads
-    for bits, H, V in ((8, 512, 2300), (4, 768, 1500)):
-        inp = syn.make_custom(M=150, H=H, V=V, bits=bits, seed=int(cap) + bits, softcap=cap,
-                              mask="random", mask_frac=0.2)
-        g = np.random.default_rng(7).uniform(-1.5, 1.5, size=150)
-        say("softcap %g, %d-bit: GPU" % (cap, bits))
+    # and masked tokens, 4- and 8-bit heads, groups of 32 and the small-M launch
+    for bits, H, V, M, group in ((8, 512, 2300, 150, 64), (4, 768, 1500, 150, 64), (4, 512, 900, 150, 32),
+                                 (8, 512, 1100, 20, 64)):
+        inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=int(cap) + bits + group + M, softcap=cap,
+                              mask="random", mask_frac=0.2, group=group)
+        g = np.random.default_rng(7).uniform(-1.5, 1.5, size=M)
+        say("softcap %g, %d-bit, group %d, M=%d: GPU" % (cap, bits, group, M))
         gpu = run_gpu(torch_cuda, inp, g=g)
         assert np.all(np.isfinite(gpu[0])) and np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))
-        check(inp, gpu, oracle.cce(inp, g=g), np.arange(150), "cap%g_%dbit" % (cap, bits))
+        check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "cap%g_%dbit_g%d_M%d" % (cap, bits, group, M))
 
 
 @pytest.mark.parametrize("bits,cap", [(8, 30.0), (4, 0.0)])
