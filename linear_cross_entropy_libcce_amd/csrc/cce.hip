@@ -90,7 +90,7 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_part, o_coeff, o_dhp, o_fl,
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_bnz, o_part, o_coeff, o_dhp, o_fl,
       fwd_bytes, bwd_bytes;
   size_t o_hT, o_coeffT;  // dense heads: transposed h and coefficient chunk of the dW contraction
 };
@@ -195,6 +195,7 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
   p.o_rt = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)(p.NB + p.G) * p.V), 256);
   p.o_slast = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)p.V), 256);
+  p.o_bnz = o; o = align_up(o + (dense ? 0 : sizeof(int) * (size_t)cdiv(p.V, 64)), 256);
   const size_t common = o;
   p.o_part = common;
   p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
@@ -290,6 +291,7 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   f.Gq = p.Gq;
   f.sbt = p.sbt;
   f.slast = ws_at<float>(ws, p.o_slast);
+  f.bnz = ws_at<int>(ws, p.o_bnz);
   f.V = p.V;
   f.H = (int)p.H;
   f.G = p.G;
@@ -309,6 +311,8 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
   a.rt = ws_at<const float>(ws, p.o_rt);
   a.slast = ws_at<const float>(ws, p.o_slast);
+  a.bnz = ws_at<const int>(ws, p.o_bnz);
+  a.nbnz = (int)cdiv(p.V, 64);
   a.wq = hd->wq;
   a.cnt = ws_at<const int>(ws, p.o_cnt);
   a.tok = ws_at<const TokRec>(ws, p.o_tok);

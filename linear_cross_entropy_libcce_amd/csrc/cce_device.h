@@ -112,6 +112,8 @@ struct TileArgs {
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
   const float *rt;       // [NB + G][V] fold ratio of every step (before its first K column)
   const float *slast;    // [V] effective scale of the last group
+  const int *bnz;        // [nbnz] nonzero-bias-block flags of the head's 64-row blocks
+  int nbnz;
   const uint32_t *wq;
   const int *cnt;
   const TokRec *tok;
@@ -154,6 +156,7 @@ struct FrontArgs {
   uint16_t *haug;
   uint8_t *baug;           // head side: bias-block digits, fold ratios, last scale
   float *rt, *slast;
+  int *bnz;                // [ceil(V / 64)]: 1 where a block of 64 rows has a nonzero bias digit
   int64_t V;
   int H, G, Kb, Ka, NB, wpr, M_pad;  // NB, G: tile K steps of the bias block and of h
   int gs, Gq, sbt;         // quantization group, groups per row, scale/bias dtype

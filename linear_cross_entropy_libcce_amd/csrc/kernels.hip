@@ -175,6 +175,10 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
     for (int i = tid; i < rows * pad; i += 256) f.baug[(v0 + i / pad) * Kb + 3 * Gq + i % pad] = (uint8_t)128;
   }
   const int64_t v = v0 + lane;
+  if (wave == 0) {  // every digit of the block's rows is zero iff their largest |b'| is 0
+    const unsigned long long nz = __ballot(lane < rows && smax[lane] != 0u);
+    if (lane == 0) f.bnz[blk] = nz != 0ull;
+  }
   if (wave == 0 && lane < rows) {
     sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
     for (int s2 = 0; s2 < NB; ++s2) f.rt[s2 * V + v] = 1.0f;

@@ -198,7 +198,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int tg = SMALL ? 0 : wave >> 1, vh = SMALL ? wave >> 2 : wave & 1;
   constexpr int NC = SMALL ? 1 : 4;  // 32-row column blocks per wave
   const int l32 = lane & 31, lh = lane >> 5;
-  const int steps = a.NB + a.G;
+  // A head whose bias block is all zero digits (every b' = 0: symmetric 8-bit
+  // quantization, b = -128 s) starts at the first code step; the bias steps
+  // would add exact zeros to an accumulator that starts at zero.
+  int bnz = 0;
+  if (!DENSE)
+    for (int i = tid; i < a.nbnz; i += TW) bnz |= a.bnz[i];
+  // (the pipeline looks two steps ahead: at least two steps per tile)
+  const int s0 = __builtin_amdgcn_readfirstlane((DENSE || a.G < 2 || __syncthreads_or(bnz)) ? 0 : a.NB);
+  const int steps = a.NB + a.G - s0;
 
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KW];
   __shared__ __attribute__((aligned(16))) float sR[2][BNT];
@@ -262,22 +270,22 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       int s2 = st + n, t2 = tile;
       if (s2 >= steps) { s2 -= steps; t2 = next_tile(tile); }
       v0 = (int64_t)(a.range_tile0 + t2) * BNT;
-      step = s2;
+      step = s0 + s2;
     };
     const int first_tile = next_tile(tile_begin - 1);
     {
       const int64_t v0 = (int64_t)(a.range_tile0 + first_tile) * BNT;
       int64_t v1; int s1;
       coords(first_tile, 0, 1, v1, s1);
-      pr.load(a, v0, 0, P0);
+      pr.load(a, v0, s0, P0);
       pr.load(a, v1, s1, P1);
 #pragma unroll
-      for (int part = 0; part < NKS; ++part) pr.store(true, part, P0, sW[0]);
+      for (int part = 0; part < NKS; ++part) pr.store(s0 < a.NB, part, P0, sW[0]);
       pr.ratio(P0, sR[0]);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, 0));
-        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, 0));
+        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, s0 * NKS * 1024));
+        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, s0 * NKS * 1024));
       }
       __syncthreads();
     }

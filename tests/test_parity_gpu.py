@@ -356,6 +356,27 @@ def test_zero_and_tiny_scales(torch_cuda, bits, cap):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "zeroscale%d" % bits)
 
 
+@pytest.mark.parametrize("where,H", [("none", 512), ("first", 512), ("middle", 512), ("last", 512),
+                                     ("none", 64)])
+def test_zero_bias_block_start(torch_cuda, where, H):
+    # a symmetric 8-bit head (b = -128 s: every b' is 0) starts each tile at
+    # its first code step; one row with b' != 0 in the first, a middle or the
+    # last 64-row block must bring the bias steps back for every tile.  Ten
+    # tokens target that row, whose logit moves by the sum of h.  H = 64 has a
+    # single code step and keeps the bias steps.
+    M, V = 150, 1333
+    inp = syn.make_custom(M=M, H=H, V=V, bits=8, seed=23 + H, softcap=30.0, mask="random", mask_frac=0.2)
+    s, b = inp["scales"], inp["biases"]
+    row = {"none": None, "first": 3, "middle": 700, "last": V - 1}[where]
+    if row is not None:
+        b[row, :] = np.float32(1.0) - np.float32(128.0) * s[row, :]
+        inp["targets"][:10] = row
+    g = np.random.default_rng(9).uniform(-1.5, 1.5, size=M)
+    say("zero bias block, nonzero row %s, H=%d: GPU" % (where, H))
+    gpu = run_gpu(torch_cuda, inp, g=g)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "biasstart_%s_%d" % (where, H))
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 def test_outlier_group_biases(torch_cuda, bits):
     # the bias block holds each row's b' (b, plus 128 s for 8-bit codes) in
