@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 //
 // * Head side of the bias block.  The block carries sum_g b'[v][g] * S[t][g]
 //   (S the group sum of h) with b' = b + 128 s for 8-bit heads, whose codes
-//   the tile uses as q - 128, and b' = b for 4-bit heads.  Row v's b' is
+//   the tile uses as q - 128, and b' = b + 8 s for 4-bit heads (codes used
+//   as q - 8): symmetric heads have b' = 0.  Row v's b' is
 //   written in 16-bit fixed point, b' ~= u_v * n, u_v = max_g |b'| / 32639,
 //   n = 256 d1 + d0 with signed digits d1, d0 in [-128, 127] (exact in bf16),
 //   stored as bytes offset by 128.  Column kk of the block (part = kk / G,
@@ -221,7 +222,7 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
   const int tid = threadIdx.x;
   constexpr bool DENSE = BITS == 16;  // bf16 head rows: no head side, no group sums
   if (blockIdx.x >= (unsigned)f.M_pad) {
-    if constexpr (!DENSE) head_prep_block((int64_t)blockIdx.x - f.M_pad, f, BITS == 8 ? 128.0f : 0.0f, sS, sT);
+    if constexpr (!DENSE) head_prep_block((int64_t)blockIdx.x - f.M_pad, f, BITS == 8 ? 128.0f : 8.0f, sS, sT);
     return;
   }
   const int r = blockIdx.x;

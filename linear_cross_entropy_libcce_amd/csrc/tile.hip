@@ -134,8 +134,8 @@ struct Producer {
   // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
   // Bytes are stored offset by 128 (8-bit codes as they come, bias digits
   // written so); flipping the top bit gives the signed value q - 128 (resp.
-  // the digit), one sign-extending convert per byte.  4-bit codes stay
-  // unsigned.
+  // the digit), one sign-extending convert per byte.  4-bit codes are used
+  // as q - 8.
   // KW = 32: slice ks (0, 1) is K chunk 2 (tid & 1) + ks of row tid >> 1.
   __device__ __forceinline__ void store(bool bias, int ks, const ProdRegs &p, uint16_t *sw) const {
     const int i = GS32 ? 0 : ks >> 1, h = ks & 1;
@@ -147,15 +147,17 @@ struct Producer {
       unpack8s(p.w[4 * i + 2 * h + 1] ^ 0x80808080u, o + 2);
     } else {
       // 4-bit head: the eight nibbles of the code word are spread to bytes
-      // (codes 0 1 2 3 | 4 5 6 7) and a uniform select takes them or the two
-      // digit words, so both kinds of step share one straight-line unpack.
+      // (codes 0 1 2 3 | 4 5 6 7) as 128 + q, less 8 per byte (no borrow
+      // between bytes): 120 + q, which the shared flip of the top bit turns
+      // into the signed code q - 8, as it turns a stored digit byte into the
+      // digit.  A uniform select takes the codes or the two digit words, so
+      // both kinds of step share one straight-line unpack.
       const uint32_t w = p.w[4 * i + h];
-      const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-      const uint32_t c0 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // ev.b0 od.b0 ev.b1 od.b1
-      const uint32_t c1 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // ev.b2 od.b2 ev.b3 od.b3
-      const uint32_t flip = bias ? 0x80808080u : 0u;
-      unpack8s((bias ? p.w[4 * i + 2 * h] : c0) ^ flip, o);
-      unpack8s((bias ? p.w[4 * i + 2 * h + 1] : c1) ^ flip, o + 2);
+      const uint32_t ev = (w & 0x0F0F0F0Fu) | 0x80808080u, od = ((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u;
+      const uint32_t c0 = __builtin_amdgcn_perm(od, ev, 0x05010400u) - 0x08080808u;  // ev.b0 od.b0 ev.b1 od.b1
+      const uint32_t c1 = __builtin_amdgcn_perm(od, ev, 0x07030602u) - 0x08080808u;  // ev.b2 od.b2 ev.b3 od.b3
+      unpack8s((bias ? p.w[4 * i + 2 * h] : c0) ^ 0x80808080u, o);
+      unpack8s((bias ? p.w[4 * i + 2 * h + 1] : c1) ^ 0x80808080u, o + 2);
     }
     const int off = GS32 ? swz<KW>(tid >> 1, 2 * (tid & 1) + h) : swz<KW>(row0 + 16 * i, 2 * q + h);
     *(u32x4_t *)(sw + off) = u32x4_t{o[0], o[1], o[2], o[3]};

@@ -379,7 +379,7 @@ def test_zero_bias_block_start(torch_cuda, where, H):
 
 @pytest.mark.parametrize("bits", [8, 4])
 def test_outlier_group_biases(torch_cuda, bits):
-    # the bias block holds each row's b' (b, plus 128 s for 8-bit codes) in
+    # the bias block holds each row's b' (b plus 128 s for 8-bit codes, 8 s for 4-bit) in
     # 16-bit fixed point relative to the row's largest |b'|: one group per row
     # with b' = 1 (20-40x the others) loosens it for the whole row and must
     # still meet the tolerance
@@ -388,7 +388,7 @@ def test_outlier_group_biases(torch_cuda, bits):
     s, b = inp["scales"], inp["biases"]
     rows = np.arange(V)
     grp = rows % s.shape[1]
-    shift = np.float32(128.0 if bits == 8 else 0.0)
+    shift = np.float32(128.0 if bits == 8 else 8.0)
     b[rows, grp] = np.float32(1.0) - shift * s[rows, grp]
     g = np.random.default_rng(4).uniform(-1.5, 1.5, size=M)
     say("outlier group biases, %d-bit: GPU" % bits)
