@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of libcce's flash cut-cross-entropy head, forward + backward.
 
-One step = cce_forward + cce_backward (g = 1) over one batch of the synthetic
+One step = forward + backward (g = 1) over one batch of the synthetic
 workload M=8192 tokens, H=2560, V=262144, 8-bit affine head (group 64),
 softcap 30 -- the largest single-GPU workload at H=2560, V=262144.  Inputs are
-resident in HBM and workspaces preallocated before the timed region.
+resident in HBM and workspaces preallocated before the timed region.  Under a
+softcap of at most 40 the step is the single pass cce_forward_backward (the
+logits computed once); otherwise, and always in the `two_calls` field, it is
+cce_forward + cce_backward (the backward recomputes the logits).  Each step
+is timed between its own pair of HIP events; the median is reported.
 
 Prints one JSON line.  `value` is supervised tokens per second of fwd+bwd.
 `roofline` is for the kernel family with the most time per step, timed live
@@ -86,7 +90,16 @@ def cpu_baseline(inp, seconds, M_eff):
     t0 = time.perf_counter()
     oracle.cce(inp, tokens=toks)
     dt = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": model,
             "sample": "fwd+bwd of %d random supervised tokens of the full workload (%.1f s)" % (n, dt)}
 
 
@@ -102,8 +115,14 @@ def main():
     ap.add_argument("--group", type=int, default=None, help="override the quantization group (32, 64, 128)")
     ap.add_argument("--sb-dtype", type=str, default=None, choices=["f32", "bf16", "f16"],
                     help="override the storage of scales and biases")
+    ap.add_argument("--bias", type=str, default=None, choices=["symmetric", "affine"],
+                    help="head kind: symmetric (bias = -zero_point*scale, the workload's own) or affine "
+                         "(a float head min/max-quantized, bias = group minimum: every row has b' != 0)")
     ap.add_argument("--skip", type=str, default=None, metavar="BLOCK_EPS,FILTER_EPS",
                     help="opt-in backward skips (e.g. 1e-5,1e-5): forward with block maxima, backward skipping")
+    ap.add_argument("--path", type=str, default="auto", choices=["auto", "calls"],
+                    help="auto: the single pass cce_forward_backward where the head allows it (softcap in (0, 40]), "
+                         "else cce_forward + cce_backward; calls: always the two calls")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (launch-bound small M)")
     ap.add_argument("--dense", action="store_true",
@@ -140,6 +159,8 @@ def main():
         w = dataclasses.replace(w, group=args.group, name="%s, group %d" % (w.name, args.group))
     if args.sb_dtype is not None:
         w = dataclasses.replace(w, sb_dtype=args.sb_dtype, name="%s, %s scales" % (w.name, args.sb_dtype))
+    if args.bias is not None and args.bias != w.bias:
+        w = dataclasses.replace(w, bias=args.bias, name="%s, %s head" % (w.name, args.bias))
     dev = torch.device("cuda:0")
     if args.dense:
         if args.skip or args.group or args.sb_dtype:
@@ -186,55 +207,74 @@ def main():
         else:
             cce.cce_backward(h, head, t, lse, None, m, workspace=ws_b, out=dh)
 
-    def step():
+    def calls():
         fwd()
         bwd()
+
+    # the single pass (cce_forward_backward) where the head allows it: a
+    # quantized head with 0 < softcap <= 40, no skips; else the two calls
+    fused = (not args.dense and not args.skip and args.path != "calls" and 0.0 < inp["softcap"] <= 40.0)
+    if fused:
+        ws_fb = torch.empty(cce.forward_backward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
+
+    def fused_step():
+        cce.cce_forward_backward(h, head, t, None, m, workspace=ws_fb, out=(logp, lse, dh))
+
+    step = fused_step if fused else calls
+    log("step: %s" % ("cce_forward_backward (single pass)" if fused else "cce_forward + cce_backward"))
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
+        if fused:
+            calls()
     torch.cuda.synchronize()
-    timed_step = step
-    if args.graph:
+
+    def replayable(fn):
+        if not args.graph:
+            return fn
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            step()
+            fn()
         torch.cuda.current_stream().wait_stream(s)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            fn()
         torch.cuda.synchronize()
-        timed_step = graph.replay
         log("captured one step in a HIP graph")
+        return graph.replay
+
+    def timed(fn):
+        """Per-step milliseconds, each step between its own pair of events."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(args.steps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
     log("timing %d steps" % args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        timed_step()
-    e1.record()
-    torch.cuda.synchronize()
+    per = timed(replayable(step))
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
-    log("%.3f ms/step (wall %.3f ms/step)" % (ms, 1e3 * wall / args.steps))
+    ms = float(np.median(per))
+    ms_mean = float(np.mean(per))
+    log("%.3f ms/step median, %.3f mean (wall %.3f ms/step)" % (ms, ms_mean, 1e3 * wall / args.steps))
 
-    # forward and backward alone (same inputs), for the split the step hides
-    def timed(fn):
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a0.record()
-        for _ in range(args.steps):
-            fn()
-        a1.record()
-        torch.cuda.synchronize()
-        return a0.elapsed_time(a1) / args.steps
-
-    ms_fwd = timed(fwd)
-    ms_bwd = timed(bwd)
-    log("forward %.3f ms, backward %.3f ms" % (ms_fwd, ms_bwd))
+    # the forward and the backward alone (same inputs), and the two calls as
+    # a step when the single pass is the one timed above
+    ms_fwd = float(np.median(timed(fwd)))
+    ms_bwd = float(np.median(timed(bwd)))
+    log("forward %.3f ms, backward %.3f ms (median)" % (ms_fwd, ms_bwd))
+    two_calls = None
+    if fused:
+        ms_calls = float(np.median(timed(replayable(calls))))
+        two_calls = {"ms_per_step": round(ms_calls, 4), "tokens_per_s": round(M_eff / (ms_calls * 1e-3), 1),
+                     "tflops": round(6.0 * M_eff * V * H / (ms_calls * 1e-3) / 1e12, 1)}
+        log("cce_forward + cce_backward: %.3f ms/step (median)" % ms_calls)
 
     # per-kernel timing pass (same steps, events around every launch)
     log("per-kernel timing pass")
@@ -249,16 +289,19 @@ def main():
     for k, (n, tot) in sorted(per_step.items(), key=lambda kv: -kv[1][1]):
         log("  %-10s %5.1f launches/step  %8.3f ms/step" % (k, n, tot))
 
-    # forward logits + backward recompute + dh (+ dW for a dense head)
-    alg_flops = (8.0 if args.dense else 6.0) * M_eff * V * H
+    # MFMA work per step: forward logits and dh always, the backward's logit
+    # recompute unless the single pass ran (and dW for a dense head)
+    gemms = 4.0 if args.dense else (2.0 if fused else 3.0)
+    exec_flops = 2.0 * gemms * M_eff * V * H
     if args.dense:
         head_bytes = 2 * V * H
     else:
         sb_size = 4 if inp.get("sb_dtype", "f32") == "f32" else 2
         head_bytes = V * (H * inp["bits"] // 8) + 2 * sb_size * V * (H // inp["group"])  # codes + scales, biases
     head_gbs = 2.0 * head_bytes / (ms * 1e-3) / 1e9                   # the head is read by both passes
-    tflops = alg_flops / (ms * 1e-3) / 1e12
+    tflops = exec_flops / (ms * 1e-3) / 1e12
     per_kernel_flops = {"tile_fwd": 2.0 * M_eff * V * H, "tile_bwd": 2.0 * M_eff * V * H,
+                        "tile_fused": 2.0 * M_eff * V * H,
                         "dh_gemm": 2.0 * M_eff * V * H, "dw_gemm": 2.0 * M_eff * V * H}
     dom = max(per_step, key=lambda k: per_step[k][1])
     n_l, t_l = per_step[dom]
@@ -267,7 +310,7 @@ def main():
         flop_launch = per_kernel_flops[dom] / n_l
         achieved = flop_launch / (t_l / n_l * 1e-3) / 1e12
         default_cfg = (args.tokens is None and not args.skip and args.group is None and args.sb_dtype is None
-                       and not args.dense)
+                       and not args.dense and args.bias in (None, "symmetric"))
         tb = measured_traffic(dom) if (args.workload == 3 and default_cfg) else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
@@ -290,6 +333,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -298,16 +342,21 @@ def main():
         "config": {"workload": w.name, "M": M, "M_supervised": M_eff, "H": H, "V": V,
                    "head": "dense bf16" if args.dense else "quantized",
                    "bits": 16 if args.dense else inp["bits"], "group": None if args.dense else inp["group"],
-                   "sb_dtype": None if args.dense else inp.get("sb_dtype", "f32"), "softcap": inp["softcap"],
+                   "sb_dtype": None if args.dense else inp.get("sb_dtype", "f32"),
+                   "bias": None if args.dense else w.bias, "softcap": inp["softcap"],
                    "g": 1.0,
                    "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps},
-                   "hip_graph": bool(args.graph)},
+                   "hip_graph": bool(args.graph),
+                   "step": "cce_forward_backward" if fused else "cce_forward+cce_backward"},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),
+        "two_calls": two_calls,
         "tflops": round(tflops, 1),
-        "flops_counted": ("8*M_eff*V*H (forward, recompute, dh, dW)" if args.dense else "6*M_eff*V*H")
+        "flops_counted": ("8*M_eff*V*H (forward, recompute, dh, dW)" if args.dense else
+                          ("4*M_eff*V*H (logits once, dh)" if fused else "6*M_eff*V*H (logits, recompute, dh)"))
         + (" (dense-equivalent: skipped pairs counted)" if args.skip else ""),
         "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
+        "tflops_6mvh": round(6.0 * M_eff * V * H / (ms * 1e-3) / 1e12, 1),
         "head_GB_per_s": round(head_gbs, 1),
         "kernel_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
         "roofline": roof,

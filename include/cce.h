@@ -14,7 +14,10 @@
  *     dh_t = g_t * d logp_t / d h_t
  *          = g_t * sum_v (1[v = target_t] - exp(y_v - lse_t)) * c'(z_v) * W_v
  *
- * without ever writing the [M, V] logits or a dequantized head to memory.
+ * The [M, V] logits and a dequantized head are never written to memory.  The
+ * coefficients g * (1[v = target] - exp(y - lse)) * c' are: the backward stages
+ * them in bf16 in the caller's workspace one vocabulary chunk at a time (at
+ * most 1 GiB per chunk; 4 chunks of 8192 x 65536 at M = 8192, V = 262144).
  *
  * Conventions shared by every call:
  *  - Pointers named "device" are HIP device (or managed) memory on the current
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 5
+#define CCE_ABI_VERSION 6
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -200,6 +203,30 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M,
                            const float *block_max, const cce_skip *skip,
                            void *dh, int32_t dh_dtype, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Forward and backward in one call, for a caller that has g before the
+ * forward (a loss linear in logp, e.g. g = -1/N for the mean cross entropy),
+ * or that wants d logp_t / d h_t itself (g = NULL) and scales it by its g
+ * later: dh is linear in g, row by row.  Same operation as cce_forward
+ * followed by cce_backward (page "mlx-bun 0.0.4 -> 0.0.6",
+ * src/train/flash-cce.ts, flashCceForward and flashCceBackward), outputs as
+ * there: logp, lse [M] and dh [M][H] of dh_dtype.
+ *
+ * With a softcap in (0, 40] the logits are computed once: the forward sums
+ * e^{y - cap} against the fixed reference cap (every term <= 1, the largest
+ * one >= e^{-2 cap}), and the same epilogue writes every coefficient up to
+ * the token's factor g e^{cap - lse}, which the split reduce applies once
+ * lse is known.  Other heads run the forward, then the backward, in this call.
+ *   workspace  device, 256-byte aligned, >= cce_forward_backward_workspace_bytes
+ * Errors as cce_forward and cce_backward_ex.
+ */
+size_t cce_forward_backward_workspace_bytes(const cce_head *head, int64_t M);
+cce_status cce_forward_backward(const cce_head *head, const void *h, int64_t M,
+                                const int32_t *targets, const uint8_t *mask,
+                                const float *g, float *logp, float *lse,
+                                void *dh, int32_t dh_dtype, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Trainable dense head (the original cut-cross-entropy setting, which the

@@ -20,7 +20,7 @@ EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
            "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_status_str",
            "cce_abi_version", "cce_profile_enable", "cce_profile_read",
            "cce_dense_forward", "cce_dense_backward", "cce_dense_forward_workspace_bytes",
-           "cce_dense_backward_workspace_bytes")
+           "cce_dense_backward_workspace_bytes", "cce_forward_backward", "cce_forward_backward_workspace_bytes")
 
 BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
@@ -80,6 +80,10 @@ def load(path: str = LIB_PATH):
     lib.cce_forward_workspace_bytes.argtypes = [HP, I64]
     lib.cce_backward_workspace_bytes.restype = SZ
     lib.cce_backward_workspace_bytes.argtypes = [HP, I64]
+    lib.cce_forward_backward.restype = ctypes.c_int
+    lib.cce_forward_backward.argtypes = [HP, P, I64, P, P, P, P, P, P, ctypes.c_int32, P, SZ, P]
+    lib.cce_forward_backward_workspace_bytes.restype = SZ
+    lib.cce_forward_backward_workspace_bytes.argtypes = [HP, I64]
     DP = ctypes.POINTER(cce_dense_head)
     lib.cce_dense_forward.restype = ctypes.c_int
     lib.cce_dense_forward.argtypes = [DP, P, I64, P, P, P, P, P, SZ, P]
@@ -179,6 +183,10 @@ def forward_workspace_bytes(head: Head, M: int) -> int:
 
 def backward_workspace_bytes(head: Head, M: int) -> int:
     return int(load().cce_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def forward_backward_workspace_bytes(head: Head, M: int) -> int:
+    return int(load().cce_forward_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
 
 
 def dense_forward_workspace_bytes(head: DenseHead, M: int) -> int:
@@ -286,6 +294,29 @@ def cce_backward_ex(h, head: Head, targets, lse, g=None, mask=None, block_max=No
                                _ptr(block_max), ctypes.byref(sk), _ptr(dh), DH_DTYPES[dh_dtype], _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(dev)))
     return dh
+
+
+def cce_forward_backward(h, head: Head, targets, g=None, mask=None, workspace=None, out=None, dh_dtype="f32"):
+    """(logp, lse, dh) in one call for a g known up front (None: all ones, so
+    dh = d logp / d h, which the caller may scale row by row later)."""
+    import torch
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    if dh_dtype not in DH_DTYPES:
+        raise ValueError("dh_dtype must be one of %s" % sorted(DH_DTYPES))
+    if out is not None:
+        logp, lse, dh = out
+        _expect(logp, torch.float32, dev, (M,), "logp")
+    else:
+        logp, lse = _fwd_out(M, dev, None)
+        dh = None
+    dh = _bwd_in(head, M, dev, lse, g, dh, torch.float32 if dh_dtype == "f32" else torch.bfloat16)
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_forward_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_forward_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(g), _ptr(logp),
+                                    _ptr(lse), _ptr(dh), DH_DTYPES[dh_dtype], _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse, dh
 
 
 def cce_dense_forward(h, head: DenseHead, targets, mask=None, workspace=None, out=None):

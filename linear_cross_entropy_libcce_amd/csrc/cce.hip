@@ -81,6 +81,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
   int64_t M, M_pad, V, H;
   int G, Kb, Ka, NB, bits, wpr, TT, tiles;  // NB, G: tile K steps (kw columns) of the bias block and of h
+  int P, NBr;                               // columns of each half of the bias block; steps of its first half
   int kw;                                   // 64, or 32 for quantization group 32 (one group per step)
   int gs, Gq, sbt;                           // quantization group, groups per row, scale/bias dtype
   float cap;
@@ -90,9 +91,14 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_bnz, o_part, o_coeff, o_dhp, o_fl,
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_bmx, o_sabs, o_part, o_coeff, o_dhp, o_fl,
       fwd_bytes, bwd_bytes;
   size_t o_hT, o_coeffT;  // dense heads: transposed h and coefficient chunk of the dW contraction
+  // fused pass (softcap in (0, CAP_FIXED_REF_MAX], quantized head): launched
+  // work ids per chunk, split capacity per chunk, partials and target c'
+  bool fused;
+  int fus_blocks, fus_max_splits, mass_ld;
+  size_t o_fpart, o_tdc, o_smass, fus_bytes;
 };
 
 // A dense bf16 head runs as an internal head of 16 "bits" per element: the
@@ -131,10 +137,14 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.G = (int)(p.H / p.kw);
   p.Gq = (int)(p.H / p.gs);
   p.sbt = hd->sb_dtype;
-  // bias block: three columns per quantization group (fixed-point digits x S hi/lo)
-  p.Kb = dense ? 0 : (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
+  // bias block: two halves (refinement, coarse) of three columns per
+  // quantization group (fixed-point digit x piece of S), each half padded to
+  // whole 64-wide steps
+  p.P = dense ? 0 : (int)(cdiv(3 * p.Gq, KSTEP) * KSTEP);
+  p.Kb = 2 * p.P;
   p.Ka = p.Kb + (int)p.H;
   p.NB = p.Kb / p.kw;
+  p.NBr = p.P / p.kw;
   p.wpr = (int)(p.H * p.bits / 32);
   p.TT = (int)(p.M_pad / BM);
   p.tiles = (int)cdiv(p.V, BNT);
@@ -195,7 +205,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
   p.o_rt = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)(p.NB + p.G) * p.V), 256);
   p.o_slast = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)p.V), 256);
-  p.o_bnz = o; o = align_up(o + (dense ? 0 : sizeof(int) * (size_t)cdiv(p.V, 64)), 256);
+  p.o_bmx = o; o = align_up(o + (dense ? 0 : sizeof(unsigned) * (size_t)cdiv(p.V, 64)), 256);
+  p.o_sabs = o; o = align_up(o + sizeof(float) * p.M_pad, 256);
   const size_t common = o;
   p.o_part = common;
   p.fwd_bytes = align_up(common + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
@@ -204,7 +215,28 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_dhp = o;
   o = align_up(o + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
   p.o_fl = o;  // pair flags of the skips: [TT][tiles] bytes
-  p.bwd_bytes = align_up(o + (size_t)p.TT * p.tiles, 256);
+  o = align_up(o + (size_t)p.TT * p.tiles, 256);
+  // The tile launches of the backward and the fused pass: every coefficient
+  // chunk with the same grid and split plan (so that the splits of all chunks
+  // are numbered in one sequence), at most 64 MiB of per-split partials.
+  p.fused = !dense && p.cap > 0.0f && p.cap <= CAP_FIXED_REF_MAX;
+  {
+    const int64_t nwr = cdiv(p.chunk_tiles, p.bwd_tpw);
+    p.fus_blocks = (int)(p.TT * nwr);
+    p.fus_max_splits = (int)std::max<int64_t>(
+        nwr, std::min<int64_t>(std::min<int64_t>(p.chunk_tiles, p.fus_blocks),
+                               ((int64_t)64 << 20) / 16 / p.M_pad / p.nchunks));
+    p.mass_ld = 2 * p.fus_max_splits * p.nchunks;
+  }
+  // the target's c' and (fused pass) non-target sum per compacted row, then
+  // the partials: the fused pass's [slot][M_pad] (max, sum) pairs, or the
+  // backward's [M_pad][mass_ld] non-target mass
+  p.o_tdc = o;
+  o = align_up(o + sizeof(float) * p.M_pad, 256);
+  p.o_smass = o;
+  o = align_up(o + sizeof(float) * p.M_pad, 256);
+  p.o_fpart = o;
+  p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
   if (dense) {
     p.o_hT = p.bwd_bytes;
     o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
@@ -291,7 +323,9 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   f.Gq = p.Gq;
   f.sbt = p.sbt;
   f.slast = ws_at<float>(ws, p.o_slast);
-  f.bnz = ws_at<int>(ws, p.o_bnz);
+  f.bmxb = ws_at<unsigned>(ws, p.o_bmx);
+  f.sabs = ws_at<float>(ws, p.o_sabs);
+  f.P = p.P;
   f.V = p.V;
   f.H = (int)p.H;
   f.G = p.G;
@@ -306,21 +340,24 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
 }
 
 TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
+  const bool dense = hd->bits == DENSE_BITS;
   TileArgs a{};
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
   a.baug = ws_at<const uint8_t>(ws, p.o_baug);
   a.rt = ws_at<const float>(ws, p.o_rt);
   a.slast = ws_at<const float>(ws, p.o_slast);
-  a.bnz = ws_at<const int>(ws, p.o_bnz);
-  a.nbnz = (int)cdiv(p.V, 64);
+  a.bmxb = ws_at<const unsigned>(ws, p.o_bmx);
+  a.nbmx = dense ? 0 : (int)cdiv(p.V, 64);
+  a.sabs = ws_at<const float>(ws, p.o_sabs);
   a.wq = hd->wq;
   a.cnt = ws_at<const int>(ws, p.o_cnt);
-  a.tok = ws_at<const TokRec>(ws, p.o_tok);
+  a.tok = ws_at<TokRec>(ws, p.o_tok);
   a.V = p.V;
   a.G = p.G;
   a.Ka = p.Ka;
   a.Kb = p.Kb;
   a.NB = p.NB;
+  a.NBr = p.NBr;
   a.kw = p.kw;
   a.wpr = p.wpr;
   a.M_pad = (int)p.M_pad;
@@ -349,16 +386,18 @@ cce_status run_forward(const cce_head *head, const void *h, int64_t M, const int
   a.part = ws_at<float>(workspace, p.o_part);
   a.range_tile0 = 0;
   a.range_tiles = p.tiles;
+  a.chunk = 0;
+  a.full_tiles = p.tiles;
   a.nblocks = p.fwd_blocks;
   a.max_splits = p.max_splits;
   a.bmx = block_max;
   a.idx = ws_at<const int>(workspace, p.o_idx);
   a.nbv = p.tiles;
   const dim3 grid((unsigned)(cdiv(a.nblocks, 8) * 8));
-  CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, false, grid, a));
-  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.tiles, p.max_splits, (int)p.M_pad,
+  CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, PASS_FWD, grid, a));
+  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.tiles, p.tiles, p.max_splits, (int)p.M_pad,
                                        ws_at<const int>(workspace, p.o_inv), a.cnt,
-                                       ws_at<const TokRec>(workspace, p.o_tok), logp, lse));
+                                       ws_at<const TokRec>(workspace, p.o_tok), 0.0f, nullptr, logp, lse));
   if (block_max && mask)
     CCE_LAUNCH("bmx_mask", st, launch_bmx_mask(st, (int)M, p.tiles, ws_at<const int>(workspace, p.o_inv), block_max));
   return hip_status();
@@ -404,6 +443,18 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
   a.fl = fl;
   a.fl_ld = p.tiles;
   a.filter_eps = filter_eps;
+  // 1 - p_t from the non-target mass, except under the skips (the target's
+  // term is then -expm1(y_t - lse), as the skips' model keeps it) and for a
+  // dense head (its dW takes the whole coefficient chunk by chunk; dh is the
+  // same with or without dW)
+  a.tmass = (fl == nullptr && head->bits != DENSE_BITS) ? 1 : 0;
+  a.tdc = ws_at<float>(workspace, p.o_tdc);
+  a.mass = ws_at<float>(workspace, p.o_fpart);
+  a.mass_ld = p.mass_ld;
+  a.full_tiles = p.chunk_tiles;
+  a.nblocks = p.fus_blocks;
+  a.max_splits = p.fus_max_splits;
+  const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
 
   GemmArgs ga{};
   ga.coeff = a.coeff;
@@ -450,9 +501,8 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
     const int nt = std::min(p.chunk_tiles, p.tiles - t0);
     a.range_tile0 = t0;
     a.range_tiles = nt;
-    a.nblocks = p.TT * (int)cdiv(nt, p.bwd_tpw);
-    const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
-    CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, true, g1, a));
+    a.chunk = c;
+    CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, PASS_BWD, g1, a));
     ga.chunk_v0 = (int64_t)t0 * BNT;
     ga.chunk_tile0 = t0;
     ga.chunk_steps = nt * (BNT / KSTEP);
@@ -468,9 +518,80 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
   }
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, ws_at<const int>(workspace, p.o_inv),
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
-                                               dh_dtype == CCE_DH_BF16 ? 1 : 0));
+                                               dh_dtype == CCE_DH_BF16 ? 1 : 0,
+                                               ReduceTarget{a.tmass, a.mass, a.mass_ld, a.nblocks, a.full_tiles,
+                                                            p.tiles, a.max_splits, nullptr, 0.0f, a.tdc}));
   return hip_status();
 }
+
+// The single pass (PASS_FUSED) for a quantized head with 0 < softcap <=
+// CAP_FIXED_REF_MAX and a known g: per coefficient chunk, the logit tile
+// writes its forward partials and the unnormalized coefficients, and the dh
+// contraction consumes the chunk; then the merge (lse, logp) and the split
+// reduce, which scales the slabs by g e^{cap - lse} and adds the target's
+// term.  No logit is computed twice.
+cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                     const uint8_t *mask, const float *g, float *logp, float *lse, void *dh, int32_t dh_dtype,
+                     void *workspace, hipStream_t st) {
+  enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false);
+  TileArgs a = tile_args(p, head, workspace);
+  a.part = ws_at<float>(workspace, p.o_fpart);
+  a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
+  a.ld_coeff = p.ld_coeff;
+  a.tdc = ws_at<float>(workspace, p.o_tdc);
+  a.full_tiles = p.chunk_tiles;
+  a.nblocks = p.fus_blocks;
+  a.max_splits = p.fus_max_splits;
+  const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
+
+  GemmArgs ga{};
+  ga.coeff = a.coeff;
+  ga.ksv = p.ld_coeff / 16;
+  ga.wq = head->wq;
+  ga.scales = head->scales;
+  ga.biases = head->biases;
+  ga.cnt = a.cnt;
+  ga.dh_part = ws_at<float>(workspace, p.o_dhp);
+  ga.V = p.V;
+  ga.H = (int)p.H;
+  ga.gs = p.gs;
+  ga.Gq = p.Gq;
+  ga.sbt = p.sbt;
+  ga.wpr = p.wpr;
+  ga.M_pad = (int)p.M_pad;
+  ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);
+  ga.TT = p.TT;
+  ga.HT = p.HT;
+  ga.ksplit = p.ksplit;
+  ga.nblocks = p.TT * p.HT * p.ksplit;
+  ga.small = a.small;
+  const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
+
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+    a.range_tile0 = t0;
+    a.range_tiles = nt;
+    a.chunk = c;
+    CCE_LAUNCH("tile_fused", st, launch_tile(st, p.bits, PASS_FUSED, g1, a));
+    ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_tile0 = t0;
+    ga.chunk_steps = nt * (BNT / KSTEP);
+    ga.accumulate = c > 0;
+    CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+  }
+  const int *inv = ws_at<const int>(workspace, p.o_inv);
+  const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
+  float *smass = ws_at<float>(workspace, p.o_smass);
+  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits,
+                                       (int)p.M_pad, inv, a.cnt, tok, p.cap, smass, logp, lse));
+  const ReduceTarget rt{2, nullptr, 0, 0, 0, 0, 0, smass, p.cap, a.tdc};
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, dh_dtype == CCE_DH_BF16 ? 1 : 0,
+                                               rt));
+  return hip_status();
+}
+
+size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : std::max(p.fwd_bytes, p.bwd_bytes); }
 
 }  // namespace
 
@@ -527,6 +648,32 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   cce_status s = check_common(head, h, M, targets, workspace);
   if (s != CCE_OK || M == 0) return s;
   return run_backward(head, h, M, targets, mask, lse, g, block_max, skip, dh, dh_dtype, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t cce_forward_backward_workspace_bytes(const cce_head *head, int64_t M) {
+  if (check_head(head) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  return fwdbwd_bytes(make_plan(head, M));
+}
+
+cce_status cce_forward_backward(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                                const uint8_t *mask, const float *g, float *logp, float *lse, void *dh,
+                                int32_t dh_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  cce_status s = check_common(head, h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  if (!logp || !lse || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3)) return CCE_ERR_INVALID_ARG;
+  if (dh_dtype != CCE_DH_F32 && dh_dtype != CCE_DH_BF16) return CCE_ERR_INVALID_ARG;
+  if (!dh || ((uintptr_t)dh & (dh_dtype == CCE_DH_F32 ? 3 : 1)) || ((uintptr_t)g & 3)) return CCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(head, M);
+  if (!workspace || workspace_bytes < fwdbwd_bytes(p)) return CCE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (p.fused) return run_fused(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
+  // other heads: the forward, then the backward on the lse it wrote (the
+  // backward's front rewrites the shared part of the workspace after it)
+  s = run_forward(head, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
+  if (s != CCE_OK) return s;
+  return run_backward(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, dh_dtype, nullptr, workspace,
                       workspace_bytes, stream);
 }
 

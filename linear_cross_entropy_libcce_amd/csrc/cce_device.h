@@ -11,14 +11,18 @@
 //    group the MFMA yields A_g = sum_d h_d q_d in fp32 and the tile folds it as
 //    acc += s[v,g] * A_g (the qdot factoring of the page's scalar forward
 //    kernel, lifted onto the matrix cores).  The bias term sum_g b[v,g]*S[t,g]
-//    (S = per-group sum of h) rides along as extra K columns: hi/lo bf16
-//    splits S_hi*b_hi + S_lo*b_hi + S_hi*b_lo, accumulated directly.
+//    (S = per-group sum of h) rides along as extra K columns: b' in per-row
+//    fixed point as three signed byte digits, S split into three bf16
+//    pieces, and the digit x piece products that matter as MFMA columns
+//    (a 16-bit block, and a refinement block to 24 bits, see kernels.hip).
 //  * The backward contracts bf16 coefficients -g*p*c' with a bf16-dequantized
 //    head tile (s*q + b rounded once, in LDS), fp32 accumulation.  The target
 //    column's whole term g*(1 - p_t)*c'_t*w_t is kept out of that path and
 //    added in fp32, with 1 - p_t = -expm1(y_t - lse): exact for a flat softmax
 //    (where that term dominates) and for a peaked one (where it is a small
-//    difference of large numbers).
+//    difference of large numbers).  The target logit y_t is taken from the
+//    tile that owns the target's column, so it carries the same arithmetic as
+//    the lse it is compared with.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 lane layout (verified on gfx950): operand
 // lane l holds row l%32, K elements 8*(l/32)..+8; result lane l holds column
@@ -45,9 +49,22 @@ constexpr int MAX_GQ = 512;    // quantization groups per row (group >= 32)
 struct TokRec {
   float lse;   // backward: lse of the token (0 for padding rows)
   float g;     // backward: cotangent (0 for padding rows)
-  float tval;  // forward: softcapped target logit; backward: target coefficient
-  int tgt;     // target id, -1 for padding rows
+  float tval;  // forward: softcapped target logit; backward: target coefficient.
+               // 0 from the front; the tile workgroup whose vocabulary tile
+               // holds the target overwrites it (one writer per token)
+  int tgt;     // target id in [0, V), or -1 (padding row, out-of-range target)
 };
+
+// Bias block precision.  Bound on the error one logit takes from the 16-bit
+// (coarse) bias block: 2^-15 * B * T, with B the head's largest |b'| and T the
+// token's sum over groups of |S_g|; the refinement block (24 bits) brings it
+// to 2^-22 * B * T.  A token tile takes the refinement when the coarse bound
+// of any of its tokens exceeds this (absolute logit error).
+constexpr float BIAS_COARSE_TOL = 1e-4f;
+constexpr float BIAS_COARSE_BOUND = 1.0f / 32768.0f;  // 2^-15
+// Fixed-point range of b' in units u_v = max_g |b'| / BIAS_NMAX: three
+// balanced signed digits, n = 65536 d2 + 256 d1 + d0, |d| <= 127 at the top.
+constexpr float BIAS_NMAX = 8355711.0f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -112,22 +129,38 @@ struct TileArgs {
   const uint8_t *baug;   // [V][Kb] fixed-point digits (offset by 128): head side of the bias block
   const float *rt;       // [NB + G][V] fold ratio of every step (before its first K column)
   const float *slast;    // [V] effective scale of the last group
-  const int *bnz;        // [nbnz] nonzero-bias-block flags of the head's 64-row blocks
-  int nbnz;
+  const unsigned *bmxb;  // [nbmx] largest |b'| (fp32 bits) of each 64-row block of the head
+  int nbmx;
+  const float *sabs;     // [M_pad] sum over groups of |S_g| of each compacted row (0: padding)
   const uint32_t *wq;
   const int *cnt;
-  const TokRec *tok;
+  TokRec *tok;           // read: lse, g, tgt; written: tval of the tokens whose target is in the tile
   float *part;           // forward: [nwr][M_pad] x (max, sumexp)
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
   int64_t V;
   int G, Ka, Kb, NB, wpr, M_pad;  // NB, G: K steps of the bias block and of h (kw columns each)
+  int NBr;               // K steps of the bias block's refinement half (its first half)
   int kw;                // K columns per step: 64, or 32 for quantization group 32
   int64_t ks16;          // Ka / 16 (fragment-major h rows)
   int64_t ksv;           // ld_coeff / 16 (fragment-major coefficient chunk)
   int range_tile0, range_tiles;
   int nblocks;           // launched work ids (the split per active token tile is derived on the device)
-  int max_splits;        // forward: capacity of the partial buffer in splits per token
+  int max_splits;        // forward: capacity of the partial buffer in splits per token and chunk
+  // The range is chunk `chunk` of a vocabulary cut into chunks of full_tiles
+  // tiles (one chunk covering the range: chunk 0, full_tiles = range_tiles);
+  // the split size follows the full chunk, so the partials of every chunk
+  // are numbered on from the previous chunk's (see vsplit).
+  int chunk, full_tiles;
+  float *tdc;            // coefficient passes: c'(z) of each compacted row's target, next to its tval
+  // backward: 1 = write each split's non-target probability mass to `mass`
+  // and the target's logit and c' (tval, tdc), the reduce forming the target's
+  // term from them; 0 = tval is the target's whole coefficient, with
+  // 1 - p_t = -expm1(y_t - lse) (the skips, and a dense head, whose dW takes
+  // the coefficient chunk by chunk)
+  int tmass;
+  float *mass;           // backward with tmass: [M_pad][mass_ld] non-target mass of each split
+  int mass_ld;
   float cap, inv_cap;
   // forward, optional: block_max[idx[r]][tile] = largest softcapped logit of
   // vocabulary tile `tile` for compacted row r (nbv = tiles per row)
@@ -156,9 +189,11 @@ struct FrontArgs {
   uint16_t *haug;
   uint8_t *baug;           // head side: bias-block digits, fold ratios, last scale
   float *rt, *slast;
-  int *bnz;                // [ceil(V / 64)]: 1 where a block of 64 rows has a nonzero bias digit
+  unsigned *bmxb;          // [ceil(V / 64)]: largest |b'| (fp32 bits) of each block of 64 rows
+  float *sabs;             // [M_pad]: sum over groups of |S_g| of each compacted row
   int64_t V;
   int H, G, Kb, Ka, NB, wpr, M_pad;  // NB, G: tile K steps of the bias block and of h
+  int P;                   // columns of each half of the bias block (Kb = 2 P)
   int gs, Gq, sbt;         // quantization group, groups per row, scale/bias dtype
   float cap;
   int bwd;
@@ -223,6 +258,30 @@ __device__ __forceinline__ int splits_for(int nblocks, int act, int units, int c
   return (units + per - 1) / per;
 }
 
+// Vocabulary splits of a tile launch over chunk `chunk` (range_tiles tiles)
+// of a vocabulary cut into chunks of full_tiles tiles: nwr_full splits of tpw
+// tiles per active token tile for a full chunk, nwr of them for this one,
+// whose partials start at split slot0 = chunk * nwr_full.  `nblocks` is the
+// work ids of a full chunk's launch (every chunk is launched alike).
+struct VSplit {
+  int nwr_full, tpw, nwr, slot0;
+};
+__device__ __forceinline__ VSplit vsplit(int nblocks, int act, int full_tiles, int range_tiles, int chunk, int cap) {
+  VSplit v;
+  v.nwr_full = splits_for(nblocks, act, full_tiles, cap);
+  v.tpw = (full_tiles + v.nwr_full - 1) / v.nwr_full;
+  v.nwr = (range_tiles + v.tpw - 1) / v.tpw;
+  v.slot0 = chunk * v.nwr_full;
+  return v;
+}
+// Splits (partials per token, in pairs of vocabulary halves) over all `tiles`
+// tiles of the vocabulary cut into chunks of full_tiles.
+__device__ __forceinline__ int vsplit_total(int nblocks, int act, int full_tiles, int tiles, int cap) {
+  const int nch = (tiles + full_tiles - 1) / full_tiles;
+  const VSplit v = vsplit(nblocks, act, full_tiles, tiles - (nch - 1) * full_tiles, nch - 1, cap);
+  return v.slot0 + v.nwr;
+}
+
 // K splits of the dh contraction for act active token tiles: as many as the
 // launched workgroups allow, bounded by the slab capacity (ks * act <=
 // ksplit * TT, the slabs being laid out over the active rows only).
@@ -283,15 +342,38 @@ __device__ __forceinline__ float softcap_d(float z, float cap, float inv_cap, fl
 // Launch entry points of the kernel translation units (host side).
 void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt);
 void launch_front(hipStream_t st, int bits, const FrontArgs &f);
-void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a);
+// Passes of the logit tile: forward partials, backward coefficients, or both
+// at once (the fused pass, softcap in (0, CAP_FIXED_REF_MAX]; quantized heads).
+enum { PASS_FWD = 0, PASS_BWD = 1, PASS_FUSED = 2 };
+constexpr float CAP_FIXED_REF_MAX = 40.0f;
+void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &a);
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
                  const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl);
 void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *bmx);
-void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
-                  const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
+// fused_cap > 0: the fused pass's partials leave the target's column out;
+// the merge adds its e^{y_t - cap} and writes their sum S to smass[r]
+void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float fused_cap, float *smass,
+                  float *logp, float *lse);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
+// How the split reduce forms the target's term g (1 - p_t) c'_t w_t.
+//  mode 0: tval is the whole coefficient (the tile used -expm1(y_t - lse));
+//  mode 1: 1 - p_t = S, the backward's non-target probability mass summed
+//          over the partial slots in a fixed order; tval = y_t, tdc = c'_t;
+//  mode 2: the fused pass: S sums e^{y - cap} over the non-target columns,
+//          e_t = e^{y_t - cap}, the slabs (sums of -e c' w) are scaled by
+//          g / (S + e_t) and 1 - p_t = S / (S + e_t).
+struct ReduceTarget {
+  int mode;
+  const float *mass;   // mode 1: [M_pad][mass_ld] the backward splits' non-target mass
+  int mass_ld;
+  int nblocks, full_tiles, tiles, max_splits;  // mode 1: the tile launches' split plan (vsplit_total)
+  const float *smass;  // mode 2: [M_pad] S, written by the merge
+  float cap;
+  const float *tdc;    // [M_pad] c' of the target
+};
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
-                      void *dh, int out_bf16);
+                      void *dh, int out_bf16, const ReduceTarget &rt);
 
 // Head gradient of a dense head (dw.hip): dW rows [chunk_v0, chunk_v0 + 256 nvt)
 // of one coefficient chunk, all columns, over the active token tiles.

@@ -1,5 +1,5 @@
-// kernels.hip -- the small kernels of libcce (compaction, prep, target logit,
-// merge, split reduce).
+// kernels.hip -- the small kernels of libcce (compaction, front: token rows
+// and head preparation, merge, pair flags of the skips, split reduce).
 #include "cce_device.h"
 
 namespace cce {
@@ -44,38 +44,41 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 // The front of every call, one launch (after the compaction):
 //
 // Workgroups [0, M_pad): compacted row r.  Gather h, write the augmented row
-// [bias block | h] in fragment-major layout and the token record, and the
-// target logit in fp32 straight from the packed target row,
-// z = sum_g (s * sum_{d in g} h_d q_d + b * S_g): forward tval = c(z),
-// backward tval = g * (1 - exp(c(z) - lse)) * c'(z), the target column's
-// coefficient.  Bias block column kk (part = kk / G, gi = kk % G): part 0 ->
-// 256 S_hi[gi], 1 -> 256 S_lo[gi], 2 -> S_hi[gi], else 0, with S = per-group
-// sum of h split into bf16 hi + lo (the head side holds the matching
-// fixed-point digits of the biases).  h rows are 16-byte aligned.
+// [bias block | h] in fragment-major layout, the row's sum over groups of
+// |S_g| and its token record (target id, or -1 when the target is outside
+// [0, V); tval 0 -- the tile that owns the target's column fills it in).
+//
+// The bias block carries sum_g b'[v][g] * S[t][g] (S = per-group sum of h)
+// with b' = b + 128 s for 8-bit heads, whose codes the tile uses as q - 128,
+// and b' = b + 8 s for 4-bit heads (codes used as q - 8): symmetric heads have
+// b' = 0.  Row v holds b' in fixed point, b' ~= u_v * n with
+// u_v = max_g |b'| / BIAS_NMAX and n = 65536 d2 + 256 d1 + d0 (balanced signed
+// digits, exact in bf16, stored as bytes offset by 128); the token side holds
+// S = S1 + S2 + S3 (three bf16 pieces, each the rounding of what the
+// previous ones leave).  The products that matter are MFMA columns, in two
+// halves of P columns each (part = column / Gq within the half, group gi =
+// column % Gq, zero past 3 Gq):
+//
+//   half 0, refinement:  d2 * 65536 S3 | d1 * 256 S2 | d0 * S1
+//   half 1, coarse:      d2 * 65536 S1 | d2 * 65536 S2 | d1 * 256 S1
+//
+// Half 1 alone is b' to 16 bits (per-logit error <= 2^-15 max|b'| sum_g |S_g|);
+// both halves to 24 bits (<= 2^-22 of the same); the tile chooses per token
+// tile (see BIAS_COARSE_TOL) and starts at half 1 when half 0 is not needed.
 //
 // Workgroups [M_pad, M_pad + ceil(V / 64)): the head side, 64 rows each.
 // Per-call head preparation (the head is frozen, so this depends on the head
 // only):
 //
-// * Head side of the bias block.  The block carries sum_g b'[v][g] * S[t][g]
-//   (S the group sum of h) with b' = b + 128 s for 8-bit heads, whose codes
-//   the tile uses as q - 128, and b' = b + 8 s for 4-bit heads (codes used
-//   as q - 8): symmetric heads have b' = 0.  Row v's b' is
-//   written in 16-bit fixed point, b' ~= u_v * n, u_v = max_g |b'| / 32639,
-//   n = 256 d1 + d0 with signed digits d1, d0 in [-128, 127] (exact in bf16),
-//   stored as bytes offset by 128.  Column kk of the block (part = kk / G,
-//   gi = kk % G) holds d1 for parts 0 and 1 and d0 for part 2, zero past 3G;
-//   the token side holds [256 S_hi, 256 S_lo, S_hi] (S split into bf16 hi +
-//   lo), so the block sums u_v^-1 * sum_g b' S up to the dropped d0 * S_lo
-//   term and the fixed-point rounding, both below 2^-16 of max|b'| * |S| per
-//   group.
+// * The digits of the bias block and, per block of 64 rows, the largest |b'|
+//   (fp32 bits; zero for a symmetric head, whose bias block is then skipped).
 // * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
 //   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
 // One workgroup per 64 rows.  Digits: when a row's group count is a multiple
 // of 4 (and the scales and biases are aligned for it), four threads share a
 // row, each taking 4 consecutive groups at a time with one vector load per
 // operand: the row's max |b'| is a shuffle reduction over the four, and
-// each set of 4 digits is one 32-bit store per part.  Otherwise two flat
+// each set of 4 digits is one 32-bit store per column part.  Otherwise two flat
 // passes: |b'| of every (row, group) with a shared-memory max per row, then
 // the digits with lanes over consecutive (row, group) pairs and byte stores.
 // Then the ratio table, whose layout is [step][V] (read that way by the
@@ -96,17 +99,28 @@ __device__ __forceinline__ void ld_sb4(const void *base, int64_t i, int sbt, flo
   }
 }
 
-// The two digit bytes (offset by 128) of b' in units of u = max|b'| / 32639.
-__device__ __forceinline__ void bias_digits(float bp, float inv, uint32_t &d1b, uint32_t &d0b) {
-  const int q = (int)fminf(fmaxf(rintf(bp * inv), -32639.0f), 32639.0f);
-  const int d1 = (q + 128) >> 8;  // floor((q + 128) / 256), in [-127, 127]
+// Unit of a row whose largest |b'| is m (0 below the range where the digits
+// could matter: such a row gets zero digits, an error below 1e-23 |S|).
+__device__ __forceinline__ float bias_unit(float m) {
+  const float u = m / BIAS_NMAX;
+  return u >= 1e-30f ? u : 0.0f;
+}
+
+// The three digit bytes (offset by 128) of b' in units u (inv = 1/u, or 0).
+__device__ __forceinline__ void bias_digits(float bp, float inv, uint32_t &d2b, uint32_t &d1b, uint32_t &d0b) {
+  const int n = (int)fminf(fmaxf(rintf(bp * inv), -BIAS_NMAX), BIAS_NMAX);
+  const int d0 = ((n + 128) & 255) - 128;  // n - d0 is a multiple of 256
+  const int n1 = (n - d0) >> 8;           // |n1| <= 32639
+  const int d1 = ((n1 + 128) & 255) - 128;
+  const int d2 = (n1 - d1) >> 8;          // |d2| <= 127
+  d2b = (uint32_t)(d2 + 128);
   d1b = (uint32_t)(d1 + 128);
-  d0b = (uint32_t)(q - 256 * d1 + 128);
+  d0b = (uint32_t)(d0 + 128);
 }
 
 __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, float *su, float *sT) {
   const int64_t V = f.V;
-  const int Gq = f.Gq, Kb = f.Kb, NB = f.NB, sbt = f.sbt;
+  const int Gq = f.Gq, Kb = f.Kb, NB = f.NB, P = f.P, sbt = f.sbt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t v0 = blk * HP_ROWS;
   const int rows = (int)(V - v0 < HP_ROWS ? V - v0 : HP_ROWS);
@@ -130,26 +144,33 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
     m = fmaxf(m, __shfl_xor(m, 2, 64));
     if (r < rows) {
       if (qd == 0) smax[r] = __float_as_uint(m);
-      const float u = m / 32639.0f;
+      const float u = bias_unit(m);
       const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
       uint8_t *row = f.baug + (v0 + r) * Kb;
       for (int j = qd; j < G4; j += 4) {
         float sc[4], bi[4];
         ld_sb4(f.scales, er + 4 * j, sbt, sc);
         ld_sb4(f.biases, er + 4 * j, sbt, bi);
-        uint32_t w1 = 0, w0 = 0;
+        uint32_t w2 = 0, w1 = 0, w0 = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          uint32_t d1b, d0b;
-          bias_digits(fmaf(shift, sc[k], bi[k]), inv, d1b, d0b);
+          uint32_t d2b, d1b, d0b;
+          bias_digits(fmaf(shift, sc[k], bi[k]), inv, d2b, d1b, d0b);
+          w2 |= d2b << (8 * k);
           w1 |= d1b << (8 * k);
           w0 |= d0b << (8 * k);
         }
-        *(uint32_t *)(row + 4 * j) = w1;
-        *(uint32_t *)(row + Gq + 4 * j) = w1;
-        *(uint32_t *)(row + 2 * Gq + 4 * j) = w0;
+        *(uint32_t *)(row + 4 * j) = w2;               // refinement: d2 x 65536 S3
+        *(uint32_t *)(row + Gq + 4 * j) = w1;          //             d1 x 256 S2
+        *(uint32_t *)(row + 2 * Gq + 4 * j) = w0;      //             d0 x S1
+        *(uint32_t *)(row + P + 4 * j) = w2;           // coarse:     d2 x 65536 S1
+        *(uint32_t *)(row + P + Gq + 4 * j) = w2;      //             d2 x 65536 S2
+        *(uint32_t *)(row + P + 2 * Gq + 4 * j) = w1;  //             d1 x 256 S1
       }
-      for (int o = 3 * Gq + 4 * qd; o < Kb; o += 16) *(uint32_t *)(row + o) = 0x80808080u;
+      for (int o = 3 * Gq + 4 * qd; o < P; o += 16) {
+        *(uint32_t *)(row + o) = 0x80808080u;
+        *(uint32_t *)(row + P + o) = 0x80808080u;
+      }
     }
     __syncthreads();
   } else {
@@ -163,25 +184,34 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
     __syncthreads();
     for (int i = tid; i < n; i += 256) {
       const int r = i / Gq, gi = i - r * Gq;
-      const float u = __uint_as_float(smax[r]) / 32639.0f;
+      const float u = bias_unit(__uint_as_float(smax[r]));
       const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
-      uint32_t d1b, d0b;
-      bias_digits(fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt)), inv, d1b, d0b);
+      uint32_t d2b, d1b, d0b;
+      bias_digits(fmaf(shift, ld_sb(f.scales, e0 + i, sbt), ld_sb(f.biases, e0 + i, sbt)), inv, d2b, d1b, d0b);
       uint8_t *row = f.baug + (v0 + r) * Kb;
-      row[gi] = (uint8_t)d1b;
+      row[gi] = (uint8_t)d2b;
       row[Gq + gi] = (uint8_t)d1b;
       row[2 * Gq + gi] = (uint8_t)d0b;
+      row[P + gi] = (uint8_t)d2b;
+      row[P + Gq + gi] = (uint8_t)d2b;
+      row[P + 2 * Gq + gi] = (uint8_t)d1b;
     }
-    const int pad = Kb - 3 * Gq;
-    for (int i = tid; i < rows * pad; i += 256) f.baug[(v0 + i / pad) * Kb + 3 * Gq + i % pad] = (uint8_t)128;
+    const int pad = P - 3 * Gq;
+    for (int i = tid; i < rows * pad; i += 256) {
+      uint8_t *row = f.baug + (v0 + i / pad) * Kb + 3 * Gq + i % pad;
+      row[0] = (uint8_t)128;
+      row[P] = (uint8_t)128;
+    }
   }
   const int64_t v = v0 + lane;
-  if (wave == 0) {  // every digit of the block's rows is zero iff their largest |b'| is 0
-    const unsigned long long nz = __ballot(lane < rows && smax[lane] != 0u);
-    if (lane == 0) f.bnz[blk] = nz != 0ull;
+  if (wave == 0) {  // the block's largest |b'| (0: every digit of its rows is zero)
+    unsigned mb = lane < rows ? smax[lane] : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (unsigned)__shfl_xor((int)mb, o, 64));
+    if (lane == 0) f.bmxb[blk] = mb;
   }
   if (wave == 0 && lane < rows) {
-    sprev[lane] = __uint_as_float(smax[lane]) / 32639.0f;  // the bias block's unit precedes group 0
+    sprev[lane] = bias_unit(__uint_as_float(smax[lane]));  // the bias block's unit precedes group 0
     for (int s2 = 0; s2 < NB; ++s2) f.rt[s2 * V + v] = 1.0f;
   }
   // group g's entry ratio s_{g-1} / s_g goes to the K step where g starts:
@@ -212,6 +242,24 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
     if (tid < rows) sprev[tid] = sT[tid * HP_LD + cw - 1];
   }
   if (tid < rows) f.slast[v0 + tid] = scale_eff(sprev[tid]);
+}
+
+// Token-side value of bias-block column kk (see the layout above), from the
+// row's group sums: S = p1 + p2 + p3, each piece the bf16 rounding of what
+// the previous ones leave (the differences are exact in fp32).
+__device__ __forceinline__ uint32_t bias_col(const float *sS, int kk, int P, int Gq) {
+  const int half = kk >= P ? 1 : 0, kl = kk - half * P;
+  const int part = kl / Gq, gi = kl - part * Gq;
+  if (part >= 3) return 0u;
+  const float S = sS[gi];
+  const float p1 = bf16_to_f32(bf16_rne(S));
+  const float r1 = S - p1;
+  const float p2 = bf16_to_f32(bf16_rne(r1));
+  const float p3 = bf16_to_f32(bf16_rne(r1 - p2));
+  float x;
+  if (half == 1) x = part == 0 ? 65536.0f * p1 : (part == 1 ? 65536.0f * p2 : 256.0f * p1);  // coarse
+  else x = part == 0 ? 65536.0f * p3 : (part == 1 ? 256.0f * p2 : p1);                       // refinement
+  return bf16_rne(x);  // exact: a bf16 piece times a power of two
 }
 
 template <int BITS>
@@ -273,82 +321,42 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
   const int64_t ks16 = f.Ka / 16;
   const int nch = H / 8;     // 16-byte chunks of the h part
   const int cpg = f.gs / 8;  // chunks per quantization group (4, 8 or 16)
-  const int tgt = (src >= 0) ? f.targets[src] : -1;
-  const bool has_t = src >= 0 && tgt >= 0 && (int64_t)tgt < f.V;
-  const uint32_t *wrow = f.wq + (size_t)(has_t ? tgt : 0) * f.wpr;
-  float zpart = 0.0f;
+  float sab = 0.0f;          // sum over groups of |S_g| (this thread's groups)
   for (int c = tid; c < nch; c += 256) {
     const u32x4_t x = (src >= 0) ? *(const u32x4_t *)(f.h + (size_t)src * H + 8 * c) : u32x4_t{0, 0, 0, 0};
     *(u32x4_t *)(f.haug + frag_slot(r, Kb / 8 + c, ks16)) = x;
-    float part = 0.0f, dot = 0.0f;
-    if constexpr (DENSE) {
-      if (has_t) {
-        const u32x4_t w = *(const u32x4_t *)(wrow + 4 * c);  // 8 bf16 of the target row
+    if constexpr (DENSE) continue;
+    float part = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dot += bf16_to_f32(x[e] & 0xFFFFu) * bf16_to_f32(w[e] & 0xFFFFu) +
-                 bf16_to_f32(x[e] >> 16) * bf16_to_f32(w[e] >> 16);
-        zpart += dot;
-      }
-      continue;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf16_to_f32(x[e] & 0xFFFFu), hi = bf16_to_f32(x[e] >> 16);
-      part += lo + hi;
-      if (has_t) dot += lo * (float)code_at<BITS>(wrow, 8 * c + 2 * e) + hi * (float)code_at<BITS>(wrow, 8 * c + 2 * e + 1);
-    }
-    if (has_t) {
-      const int64_t gi = (int64_t)tgt * Gq + c / cpg;
-      zpart += ld_sb(f.scales, gi, f.sbt) * dot + ld_sb(f.biases, gi, f.sbt) * part;
-    }
+    for (int e = 0; e < 4; ++e) part += bf16_to_f32(x[e] & 0xFFFFu) + bf16_to_f32(x[e] >> 16);
     // the chunks of one group sit in cpg consecutive lanes
     for (int o = 1; o < cpg; o <<= 1) part += __shfl_xor(part, o, 16);
-    if (c % cpg == 0) sS[c / cpg] = part;
+    if (c % cpg == 0) {
+      sS[c / cpg] = part;
+      sab += fabsf(part);
+    }
   }
-  zpart = wave_sum(zpart);
-  if ((tid & 63) == 0) sRed[tid >> 6] = zpart;
+  if constexpr (!DENSE) {
+    sab = wave_sum(sab);
+    if ((tid & 63) == 0) sRed[tid >> 6] = sab;
+  }
   __syncthreads();
   for (int c = tid; c < Kb / 8; c += 256) {
     uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t pr2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kk = 8 * c + 2 * e + u;
-        const int part = kk / Gq, gi = kk - part * Gq;
-        uint32_t val = 0;
-        if (part < 3) {
-          const float S = sS[gi];
-          const uint32_t hi = bf16_rne(S);
-          const float x = (part == 1) ? 256.0f * (S - bf16_to_f32(hi)) : bf16_to_f32(hi) * (part == 0 ? 256.0f : 1.0f);
-          val = bf16_rne(x);
-        }
-        pr2[u] = val;
-      }
-      o[e] = pr2[0] | (pr2[1] << 16);
-    }
+    for (int e = 0; e < 4; ++e)
+      o[e] = bias_col(sS, 8 * c + 2 * e, f.P, Gq) | (bias_col(sS, 8 * c + 2 * e + 1, f.P, Gq) << 16);
     *(u32x4_t *)(f.haug + frag_slot(r, c, ks16)) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
   if (tid == 0) {
+    const int tgt = (src >= 0) ? f.targets[src] : -1;
     TokRec rec;
     rec.lse = (src >= 0 && f.lse) ? f.lse[src] : 0.0f;
     rec.g = (src >= 0) ? (f.g ? f.g[src] : 1.0f) : 0.0f;
-    rec.tgt = tgt;
-    float out = 0.0f;
-    if (has_t) {
-      const float z = sRed[0] + sRed[1] + sRed[2] + sRed[3];
-      float y = z, dc = 1.0f;
-      if (f.cap > 0.0f) {
-        const float th = tanhf(z / f.cap);
-        y = f.cap * th;
-        dc = 1.0f - th * th;
-      }
-      out = f.bwd ? rec.g * -expm1f(y - rec.lse) * dc : y;
-    }
-    rec.tval = out;
+    rec.tgt = (src >= 0 && tgt >= 0 && (int64_t)tgt < f.V) ? tgt : -1;
+    rec.tval = 0.0f;
     f.tok[r] = rec;
+    if (!DENSE) f.sabs[r] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
   }
 }
 
@@ -359,11 +367,13 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
 // most 64) reads the token's partials in parallel and reduces with shuffles;
 // one token per thread when there are few splits, a wave per token when a
 // few supervised tokens carry hundreds of splits.
-__global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int tiles, int max_splits,
-                                               int M_pad, const int *inv, const int *cnt, const TokRec *tok,
-                                               int M, float *logp, float *lse) {
-  // two partials (vocabulary halves of the tile) per split of the forward
-  const int nsplit = 2 * splits_for(nblocks, active_tiles(cnt), tiles, max_splits);
+__global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int full_tiles, int tiles,
+                                               int max_splits, int M_pad, const int *inv, const int *cnt,
+                                               const TokRec *tok, float fused_cap, float *smass, int M,
+                                               float *logp, float *lse) {
+  // two partials (vocabulary halves of the tile) per split, over every chunk
+  // of the vocabulary the forward's launches covered
+  const int nsplit = 2 * vsplit_total(nblocks, active_tiles(cnt), full_tiles, tiles, max_splits);
   int L = 1;
   while (L < nsplit && L < 64) L <<= 1;
   const int per_block = 256 / L;
@@ -388,9 +398,15 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, i
     lse[t] = 0.0f;
     return;
   }
+  const TokRec rec = tok[r];
+  // the fused pass's partials leave the target's column out (mx = cap there)
+  if (fused_cap > 0.0f) {
+    smass[r] = se;
+    if (rec.tgt >= 0) se += expf(rec.tval - mx);
+  }
   const float l = mx + logf(se);
   lse[t] = l;
-  logp[t] = tok[r].tval - l;
+  logp[t] = rec.tval - l;
 }
 
 // ---------------------------------------------------------------------------
@@ -442,24 +458,51 @@ __global__ void __launch_bounds__(256) k_bmx_mask(int64_t nbv, const int *inv, f
 
 // ---------------------------------------------------------------------------
 // dh[t][:] = sum_k dh_part[k][r][:] + tval * w[target][:] (fp32 dequant),
-// zero rows for masked tokens; stored as fp32, or rounded once to bf16.
+// zero rows for masked tokens; stored as fp32, or rounded once to bf16.  The
+// target's coefficient is tval itself or formed here from the splits'
+// non-target mass (ReduceTarget); in the fused pass the slab sum is first
+// scaled to the true coefficients.
 template <int BITS>
 __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, const TokRec *tok, void *dh,
-                                                   int out_bf16) {
+                                                   int out_bf16, ReduceTarget tg) {
   // four consecutive columns per thread (H % 64 == 0): 16-byte slab loads,
   // one code word, scale and bias for the four, one vector store
   const int t = blockIdx.x;
   const int d = (blockIdx.y * 256 + threadIdx.x) * 4;
   const int H = a.H;
-  if (d >= H) return;
   const int r = inv[t];
+  const int act = active_tiles(a.cnt);
+  // mode 1: the token's non-target mass, its splits' contiguous run summed
+  // by the workgroup in a fixed order (every thread takes part)
+  float S = 0.0f;
+  if (tg.mode == 1 && r >= 0) {
+    __shared__ float sS[4];
+    const int ns = 2 * vsplit_total(tg.nblocks, act, tg.full_tiles, tg.tiles, tg.max_splits);
+    float x = 0.0f;
+    for (int k = threadIdx.x; k < ns; k += 256) x += tg.mass[(size_t)r * tg.mass_ld + k];
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) sS[threadIdx.x >> 6] = x;
+    __syncthreads();
+    S = (sS[0] + sS[1]) + (sS[2] + sS[3]);
+  }
+  if (d >= H) return;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (r >= 0) {
-    const int act = active_tiles(a.cnt);
     int ksd, steps_per;
     dh_split(a, act, ksd, steps_per);
     for (int k = 0; k < ksd; ++k) acc += *(const f32x4_t *)(a.dh_part + ((size_t)k * act * BM + r) * H + d);
-    const TokRec rec = tok[r];
+    TokRec rec = tok[r];
+    const bool ht = rec.tgt >= 0;
+    if (tg.mode == 1) {
+      rec.tval = ht ? rec.g * S * tg.tdc[r] : 0.0f;
+    } else if (tg.mode == 2) {
+      // fused: p_v = e_v / (S + e_t), the slabs sum -e c' w
+      S = tg.smass[r];
+      const float et = ht ? expf(rec.tval - tg.cap) : 0.0f;
+      const float inv_tot = 1.0f / (S + et);
+      acc *= rec.g * inv_tot;
+      rec.tval = ht ? rec.g * (S * inv_tot) * tg.tdc[r] : 0.0f;
+    }
     if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
       const uint32_t *row = a.wq + (size_t)rec.tgt * a.wpr;
       float w[4];
@@ -514,10 +557,11 @@ void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
     hipLaunchKernelGGL(k_front<8>, grid, dim3(256), 0, st, f);
 }
 
-void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int tiles, int max_splits, int M_pad,
-                  const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, part, nblocks, tiles, max_splits,
-                     M_pad, inv, cnt, tok, M, logp, lse);
+void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float fused_cap, float *smass,
+                  float *logp, float *lse) {
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, part, nblocks, full_tiles, tiles,
+                     max_splits, M_pad, inv, cnt, tok, fused_cap, smass, M, logp, lse);
 }
 
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
@@ -532,14 +576,14 @@ void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *
 }
 
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
-                      void *dh, int out_bf16) {
+                      void *dh, int out_bf16, const ReduceTarget &tg) {
   const dim3 grid((unsigned)M, (unsigned)((ga.H + 1023) / 1024));
   if (bits == 16)
-    hipLaunchKernelGGL(k_dh_reduce<16>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
+    hipLaunchKernelGGL(k_dh_reduce<16>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16, tg);
   else if (bits == 4)
-    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
+    hipLaunchKernelGGL(k_dh_reduce<4>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16, tg);
   else
-    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16);
+    hipLaunchKernelGGL(k_dh_reduce<8>, grid, dim3(256), 0, st, ga, inv, tok, dh, out_bf16, tg);
 }
 
 }  // namespace cce

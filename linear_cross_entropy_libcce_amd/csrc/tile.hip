@@ -54,7 +54,11 @@ namespace cce {
 constexpr int ZROW = 36;  // padded fp32 row stride of the per-wave transpose scratch (32 columns)
 constexpr float LOG2E = 1.4426950408889634f;
 
-enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2 };
+// MODE_FUSED (softcap <= 40): the forward's fixed reference e^{c(z) - cap}
+// also gives every coefficient up to a per-token factor, so one pass writes
+// both the partial sums and the unnormalized coefficients -e^{c(z) - cap} c'(z)
+// (the split reduce scales them by g e^{cap - lse} once the merge has lse).
+enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2, MODE_FUSED = 3 };
 enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
 
 // One step's worth of head data for one producer thread: 16 K values of each
@@ -180,17 +184,23 @@ __device__ __forceinline__ float cap_d(float z, float c1, float cap, float &dc) 
 template <int BITS, int MODE, int VAR, bool GS32>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
+  constexpr bool FUSED = MODE == MODE_FUSED;
+  constexpr bool COEF = BWD || FUSED;  // writes coefficients
   constexpr int KW = GS32 ? 32 : 64;  // K columns per step (one quantization group)
   constexpr int NKS = KW / 16;        // MFMA k-steps per step
   constexpr bool DENSE = BITS == 16;  // bf16 head: no fold, no final scale
   constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
+  // epilogue columns per chunk: the fused pass keeps three values per column
+  // live (logit, coefficient, probability term) next to the next step's
+  // prefetched operands and takes 8 at a time (with 16 its step loop spilled)
+  constexpr int EW = FUSED ? 8 : 16;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only
   const int act = active_tiles(a.cnt);
-  const int nwr = splits_for(a.nblocks, act, a.range_tiles, a.max_splits);
-  const int tpw = (a.range_tiles + nwr - 1) / nwr;
-  if (bid >= act * nwr) return;
-  const int tt = bid / nwr, wr = bid % nwr;
+  const VSplit vs = vsplit(a.nblocks, act, a.full_tiles, a.range_tiles, a.chunk, a.max_splits);
+  const int tpw = vs.tpw;
+  if (bid >= act * vs.nwr_full || bid % vs.nwr_full >= vs.nwr) return;
+  const int tt = bid / vs.nwr_full, wr = bid % vs.nwr_full;
   const int tile_begin = wr * tpw;
   const int tile_end = min(tile_begin + tpw, a.range_tiles);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -200,20 +210,49 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int tg = SMALL ? 0 : wave >> 1, vh = SMALL ? wave >> 2 : wave & 1;
   constexpr int NC = SMALL ? 1 : 4;  // 32-row column blocks per wave
   const int l32 = lane & 31, lh = lane >> 5;
-  // A head whose bias block is all zero digits (every b' = 0: symmetric 8-bit
-  // quantization, b = -128 s) starts at the first code step; the bias steps
-  // would add exact zeros to an accumulator that starts at zero.
-  int bnz = 0;
-  if (!DENSE)
-    for (int i = tid; i < a.nbnz; i += TW) bnz |= a.bnz[i];
-  // (the pipeline looks two steps ahead: at least two steps per tile)
-  const int s0 = __builtin_amdgcn_readfirstlane((DENSE || a.G < 2 || __syncthreads_or(bnz)) ? 0 : a.NB);
+  // First K step.  A head whose bias block is all zero digits (every b' = 0:
+  // symmetric quantization, b = -128 s or -8 s) starts at the first code
+  // step; the bias steps would add exact zeros to an accumulator that starts
+  // at zero.  Otherwise the token tile takes the bias block's refinement
+  // half only when the coarse half's error bound, 2^-15 B T with B the
+  // head's largest |b'| and T the tile's largest sum of |S_g|, exceeds
+  // BIAS_COARSE_TOL.  Forward and backward decide alike on the same inputs.
+  // (The pipeline looks two steps ahead: at least two steps per tile.)
+  __shared__ unsigned sDec[2][8];
+  int s0 = 0;
+  if (!DENSE) {
+    unsigned bm = 0u, tm = 0u;  // fp32 bits of values >= 0: integer order is float order
+    for (int i = tid; i < a.nbmx; i += TW) bm = max(bm, a.bmxb[i]);
+    if (tid < BM) tm = __float_as_uint(a.sabs[tt * BM + tid]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      bm = max(bm, (unsigned)__shfl_xor((int)bm, o, 64));
+      tm = max(tm, (unsigned)__shfl_xor((int)tm, o, 64));
+    }
+    if (lane == 0) {
+      sDec[0][wave] = bm;
+      sDec[1][wave] = tm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      bm = max(bm, sDec[0][w]);
+      tm = max(tm, sDec[1][w]);
+    }
+    const float B = __uint_as_float(bm), T = __uint_as_float(tm);
+    s0 = (a.G < 2) ? 0 : (B == 0.0f ? a.NB : (BIAS_COARSE_BOUND * B * T > BIAS_COARSE_TOL ? 0 : a.NBr));
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+  }
   const int steps = a.NB + a.G - s0;
 
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][BNT * KW];
   __shared__ __attribute__((aligned(16))) float sR[2][BNT];
   __shared__ __attribute__((aligned(16))) float sZ[8][64 * ZROW];
   __shared__ float sX[2][BM];  // EXTRA: per-wave tile maxima, read after the step's barrier
+  // coefficient passes: each lane's running non-target sum (kept in LDS, not
+  // in a register the whole step loop would carry)
+  __shared__ float sRun[COEF ? 8 : 1][64];
+  if (COEF) sRun[wave][lane] = 0.0f;
 
   const int tok0 = tt * BM + tg * 64;
   const int vcol0 = SMALL ? wave * 32 : vh * 128;  // this wave's first vocabulary row within the tile
@@ -225,20 +264,28 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   float *zs = sZ[wave];
 
   float run_m = -INFINITY, run_s = 0.0f;
-  float lse2 = 0.0f, g_t = 0.0f;
-  int tgt_t = -1;
-  if (BWD) {
+  // Backward: two per-token values carried through the step loop (the tile
+  // sits at the register limit): the exponent offset and the coefficient
+  // factor of the one epilogue form the softcap selects.
+  //   cap > 0: p = exp2(fma(-2 cap log2 e, r, kofs)), kofs = cap log2 e - lse log2 e;
+  //            coefficient p (r - r^2) kfac, kfac = -4 g
+  //   no cap:  p = exp2(fma(z, log2 e, -kofs)), kofs = lse log2 e; kfac = -g
+  float kofs = 0.0f, kfac = 0.0f;
+  int tgt_t;
+  {
     const TokRec rec = a.tok[tok0 + lane];
-    lse2 = rec.lse * LOG2E;
-    g_t = rec.g;
-    tgt_t = rec.tgt;
+    tgt_t = rec.tgt;  // in [0, V), or -1
+    if (BWD) {
+      const float lse2 = rec.lse * LOG2E;
+      kofs = a.cap > 0.0f ? LOG2E * a.cap - lse2 : lse2;
+      kfac = a.cap > 0.0f ? -4.0f * rec.g : -rec.g;
+    }
   }
   const float c1 = -2.0f * LOG2E * a.inv_cap;  // t = exp2(|z| * c1)
   const float c2 = -2.0f * LOG2E * a.cap;      // e^{c(z) - cap} = exp2(c2 / (1 + exp2(c3 z)))
   const float c3 = 2.0f * LOG2E * a.inv_cap;
   const float capl2 = LOG2E * a.cap;           // c(z) * log2(e) = capl2 * tanh(z / cap)
-  const float ng = -g_t, ng4 = -4.0f * g_t;    // backward coefficient factors
-  const float m2capl2 = -2.0f * capl2, capl2_lse2 = capl2 - lse2;  // c(z) log2(e) - lse2 = fma(m2capl2, r, capl2_lse2)
+  const float m2capl2 = -2.0f * capl2;         // c(z) log2(e) = fma(m2capl2, r, capl2)
 
   // EXTRA backward: walk the flagged tiles of the range only
   const uint8_t *fl_row = (BWD && EXTRA) ? a.fl + (int64_t)tt * a.fl_ld + a.range_tile0 : nullptr;
@@ -363,15 +410,47 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll 1
-        for (int k0 = 0; k0 < 32; k0 += 16) {
-          float z[16];
+        for (int k0 = 0; k0 < 32; k0 += EW) {
+          float z[EW];
 #pragma unroll
-          for (int k = 0; k < 16; k += 4) {
+          for (int k = 0; k < EW; k += 4) {
             const f32x4_t x = *(const f32x4_t *)(zs + lane * ZROW + k0 + k);
             z[k] = x[0]; z[k + 1] = x[1]; z[k + 2] = x[2]; z[k + 3] = x[3];
           }
           const int64_t vb = v0 + vcol0 + c * 32 + k0;
-          const int nv = full ? 16 : (int)(a.V - vb < 0 ? 0 : (a.V - vb < 16 ? a.V - vb : 16));
+          const int nv = full ? EW : (int)(a.V - vb < 0 ? 0 : (a.V - vb < EW ? a.V - vb : EW));
+          // the target's position among these EW columns, or -1 (targets are
+          // in [0, V), so a position found is below nv)
+          const int64_t dtk = (int64_t)tgt_t - vb;
+          const int tk = (tgt_t >= 0 && dtk >= 0 && dtk < EW) ? (int)dtk : -1;
+          // The lane whose target falls here writes the target's logit (and,
+          // for the coefficient passes, its c') from this tile's own
+          // arithmetic -- the rare chunk: a uniform branch; the coefficient
+          // passes take it with their masking pass below.
+          auto capture = [&]() {
+            float zt = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EW; ++k) zt = (k == tk) ? z[k] : zt;
+            if (tk >= 0) {
+              float yt = zt, dct = 1.0f;
+              if (a.cap > 0.0f) {  // as the epilogues below: r = 1/(1 + e^{2z/cap})
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(zt * c3));
+                yt = a.cap * fmaf(-2.0f, r, 1.0f);
+                dct = 4.0f * fmaf(-r, r, r);
+              }
+              if (BWD && !a.tmass) {
+                // the target's whole coefficient g (1 - p_t) c'_t with
+                // 1 - p_t = -expm1(y_t - lse) (g and lse as given, reloaded
+                // here: not worth registers for the whole tile)
+                const TokRec rec = a.tok[tok0 + lane];
+                a.tok[tok0 + lane].tval = rec.g * -expm1f(yt - rec.lse) * dct;
+              } else {
+                a.tok[tok0 + lane].tval = yt;
+                if (COEF) a.tdc[tok0 + lane] = dct;  // the reduce forms the target's term
+              }
+            }
+          };
+          if (!COEF && __builtin_amdgcn_ballot_w64(tk >= 0) != 0) capture();
           if (MODE == MODE_FWD_CAP) {
             // |c(z)| <= cap: e^{c(z) - cap} needs no running maximum (cap <= 40,
             // so that even e^{-2 cap} is a normal fp32; see launch_tile).  With
@@ -379,7 +458,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             // gives exp(0) = 1 and underflowing e^{-2 cap}, the two limits.
             float ssum = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 0; k < EW; ++k) {
               const float tp = __builtin_amdgcn_exp2f(z[k] * c3);
               const float e = __builtin_amdgcn_exp2f(c2 * __builtin_amdgcn_rcpf(1.0f + tp));
               ssum += (k < nv) ? e : 0.0f;
@@ -389,7 +468,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
           } else if (MODE == MODE_FWD) {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 0; k < EW; ++k) {
               z[k] = (k < nv) ? z[k] : -INFINITY;
               tmax = fmaxf(tmax, z[k]);
             }
@@ -399,7 +478,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               // c(z) = cap (1 - 2 / (1 + e^{2z/cap})) under a running maximum
               tmax = -INFINITY;
 #pragma unroll
-              for (int k = 0; k < 16; ++k) {
+              for (int k = 0; k < EW; ++k) {
                 const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
                 z[k] = (k < nv) ? a.cap * fmaf(-2.0f, r, 1.0f) : -INFINITY;
                 tmax = fmaxf(tmax, z[k]);
@@ -410,48 +489,74 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               const float mb = mnew * LOG2E;
               float ssum = 0.0f;
 #pragma unroll
-              for (int k = 0; k < 16; ++k) ssum += __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -mb));
+              for (int k = 0; k < EW; ++k) ssum += __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -mb));
               run_s = run_s * __builtin_amdgcn_exp2f((run_m - mnew) * LOG2E) + ssum;
               run_m = mnew;
             }
           } else {
-            // -g * softmax * c'; the target column is left out here and its
-            // whole term g * (1 - p) * c' * w is added in fp32 by k_dh_reduce.
-            const int64_t dtk = (int64_t)tgt_t - vb;  // target's position in this chunk, or -1
-            const int tk = (dtk >= 0 && dtk < 16) ? (int)dtk : -1;
-            float cv[16];
-            if (a.cap > 0.0f) {
+            // Coefficients -g p c' (backward) or -e c' (fused: e = e^{c(z) -
+            // cap}, the token's factor g e^{cap - lse} applied by the reduce),
+            // and pv = p or e summed over the non-target columns: the mass
+            // 1 - p_t of the target's term is that sum (backward), or S / (S +
+            // e_t) (fused), formed from the same terms as the coefficients.
+            // The target column is left out here; its whole term is added in
+            // fp32 by k_dh_reduce.
+            float cv[EW], pv[EW];
+            if (FUSED) {
+              // c' = 4 r (1 - r)
+#pragma unroll
+              for (int k = 0; k < EW; ++k) {
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
+                pv[k] = __builtin_amdgcn_exp2f(c2 * r);
+                cv[k] = -4.0f * pv[k] * fmaf(-r, r, r);
+              }
+            } else if (a.cap > 0.0f) {
               // with r = 1/(1 + e^{2z/cap}): tanh(z/cap) = 1 - 2r and
               // c'(z) = 1 - tanh^2 = 4 r (1 - r).  e^{2z/cap} overflowing gives
               // r = 0 (tanh = 1, c' = 0); for z far below zero r rounds to 1
               // and c' to 0 where it is below ~1e-7, its absolute error.
 #pragma unroll
-              for (int k = 0; k < 16; ++k) {
+              for (int k = 0; k < EW; ++k) {
                 const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
-                const float arg = fmaf(m2capl2, r, capl2_lse2);
-                cv[k] = __builtin_amdgcn_exp2f(arg) * fmaf(-r, r, r) * ng4;
+                pv[k] = __builtin_amdgcn_exp2f(fmaf(m2capl2, r, kofs));
+                cv[k] = pv[k] * fmaf(-r, r, r) * kfac;
               }
             } else {
 #pragma unroll
-              for (int k = 0; k < 16; ++k) cv[k] = __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -lse2)) * ng;
+              for (int k = 0; k < EW; ++k) {
+                pv[k] = __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -kofs));
+                cv[k] = pv[k] * kfac;
+              }
             }
             // a ragged chunk, or a lane whose target falls in it: the whole
             // wave takes the masking pass (the common case skips it)
-            if (EXTRA || nv < 16 || __builtin_amdgcn_ballot_w64(tk >= 0) != 0) {
+            if (EXTRA || nv < EW || __builtin_amdgcn_ballot_w64(tk >= 0) != 0) {
+              capture();
 #pragma unroll
-              for (int k = 0; k < 16; ++k) cv[k] = (k < nv && k != tk) ? cv[k] : 0.0f;
+              for (int k = 0; k < EW; ++k) {
+                cv[k] = (k < nv && k != tk) ? cv[k] : 0.0f;
+                pv[k] = (k < nv && k != tk) ? pv[k] : 0.0f;
+              }
             }
-            uint32_t pk[8];
+            if (!EXTRA) {
+              float ps = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 16; k += 2) {
+              for (int k = 0; k < EW; ++k) ps += pv[k];
+              sRun[wave][lane] += ps;  // the wave's own slot: in order, no barrier
+            }
+            uint32_t pk[EW / 2];
+#pragma unroll
+            for (int k = 0; k < EW; k += 2) {
               if (EXTRA) xm = fmaxf(xm, fmaxf(fabsf(cv[k]), fabsf(cv[k + 1])));
               pk[k / 2] = pack_rne(cv[k], cv[k + 1]);
             }
-            // fragment-major chunk: these 16 vocab rows are K chunks 2m, 2m+1
+            // fragment-major chunk: these EW vocab rows are K chunk(s) cm (cm + 1)
             const int64_t vloc = (int64_t)tile * BNT + vcol0 + c * 32 + k0;
             const int cm = (int)(vloc >> 3);
-            *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm, a.ksv)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-            *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + 1, a.ksv)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+#pragma unroll
+            for (int q = 0; q < EW / 8; ++q)
+              *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
+                  u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -524,8 +629,22 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     if (idx < total) do_step(idx, tile, st, P1, P0);
   }
 
-  if (!BWD) {
-    const float m_out = (MODE == MODE_FWD_CAP && total > 0) ? a.cap : run_m;
+  // partials: (max, sum-exp) of the forward passes, [slot][M_pad] pairs; the
+  // backward's non-target probability mass, [M_pad][mass_ld] (token-major:
+  // the split reduce sums each token's run), when it forms the target's term
+  if (!BWD || (!EXTRA && a.tmass)) {
+    if (COEF) run_s = sRun[wave][lane];
+    const float m_out = BWD ? 0.0f : (((MODE == MODE_FWD_CAP || FUSED) && total > 0) ? a.cap : run_m);
+    auto put = [&](int half, float m, float sum) {
+      const int slot = 2 * (vs.slot0 + wr) + half;
+      if (BWD) {
+        a.mass[(size_t)(tok0 + lane) * a.mass_ld + slot] = sum;
+      } else {
+        float *dst = a.part + ((size_t)slot * a.M_pad + tok0 + lane) * 2;
+        dst[0] = m;
+        dst[1] = sum;
+      }
+    };
     if (SMALL) {
       // the four waves of each vocabulary half combine their partials
       float *sp = &sZ[0][0];  // 8 x 64 x (max, sum); the epilogues are done
@@ -543,26 +662,25 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
           const float mw = sp[((4 * wave + w) * 64 + lane) * 2], sw = sp[((4 * wave + w) * 64 + lane) * 2 + 1];
           sum += (mw == -INFINITY) ? 0.0f : sw * __builtin_amdgcn_exp2f((mw - m) * LOG2E);
         }
-        float *dst = a.part + ((size_t)(2 * wr + wave) * a.M_pad + tok0 + lane) * 2;
-        dst[0] = m;
-        dst[1] = sum;
+        put(wave, m, sum);
       }
     } else {
-      float *dst = a.part + ((size_t)(2 * wr + vh) * a.M_pad + tok0 + lane) * 2;
-      dst[0] = m_out;
-      dst[1] = run_s;
+      put(vh, m_out, run_s);
     }
   }
 }
 
 // The forward's fixed reference e^{c(z) - cap} keeps every term <= 1, but the
 // largest term of a token can be as small as e^{-2 cap}: it stays a normal
-// fp32 for cap <= 40.  Larger softcaps take the running-maximum forward.
-constexpr float CAP_FIXED_REF_MAX = 40.0f;
+// fp32 for cap <= CAP_FIXED_REF_MAX (40).  Larger softcaps take the
+// running-maximum forward (and no fused pass).
 
-void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &a) {
-  const int mode = bwd ? MODE_BWD : ((a.cap > 0.0f && a.cap <= CAP_FIXED_REF_MAX) ? MODE_FWD_CAP : MODE_FWD);
-  const bool extra = bwd ? a.fl != nullptr : a.bmx != nullptr;
+void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &a) {
+  const bool bwd = pass == PASS_BWD;
+  const int mode = pass == PASS_FUSED ? MODE_FUSED
+                                      : (bwd ? MODE_BWD
+                                             : ((a.cap > 0.0f && a.cap <= CAP_FIXED_REF_MAX) ? MODE_FWD_CAP : MODE_FWD));
+  const bool extra = pass == PASS_FUSED ? false : (bwd ? a.fl != nullptr : a.bmx != nullptr);
   const bool gs32 = a.kw == 32;
   // group 32 has no small-M instantiation (the plain one is correct there)
   const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? VAR_SMALL : VAR_PLAIN);
@@ -577,21 +695,31 @@ void launch_tile(hipStream_t st, int bits, bool bwd, dim3 grid, const TileArgs &
       else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                      \
     }                                                                                                            \
   } while (0)
+  // the fused pass: no EXTRA variant (no skips, no block maxima)
+#define CCE_TILE_FUSED(B)                                                                                        \
+  do {                                                                                                           \
+    if (gs32) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);            \
+    else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_SMALL, false>), grid, dim3(TW), 0, st, a); \
+    else hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                \
+  } while (0)
   if (bits == 16) {  // dense bf16 head: 32-wide steps, plain variant only
     if (mode == MODE_BWD) hipLaunchKernelGGL((k_tile<16, MODE_BWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
     else if (mode == MODE_FWD_CAP)
       hipLaunchKernelGGL((k_tile<16, MODE_FWD_CAP, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
     else hipLaunchKernelGGL((k_tile<16, MODE_FWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
   } else if (bits == 4) {
-    if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
+    if (mode == MODE_FUSED) CCE_TILE_FUSED(4);
+    else if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(4, MODE_FWD_CAP);
     else CCE_TILE(4, MODE_FWD);
   } else {
-    if (mode == MODE_BWD) CCE_TILE(8, MODE_BWD);
+    if (mode == MODE_FUSED) CCE_TILE_FUSED(8);
+    else if (mode == MODE_BWD) CCE_TILE(8, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(8, MODE_FWD_CAP);
     else CCE_TILE(8, MODE_FWD);
   }
 #undef CCE_TILE
+#undef CCE_TILE_FUSED
 }
 
 }  // namespace cce

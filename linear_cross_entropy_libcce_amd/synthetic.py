@@ -22,6 +22,17 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
 5. mask uint8 [M] (1 = supervised token) or None: a contiguous masked prefix,
    or exactly round(frac*M) masked positions chosen by a seeded permutation.
 
+Affine heads (``bias="affine"``) replace steps 1-2 by the quantization of a
+float head, the way an asymmetric min/max quantizer (MLX's affine mode) makes
+one: row means mu_v ~ N(0, row_mean_std^2) are drawn first, then the float
+rows w_v = mu_v + N(0, w_std^2) [V, H] in row chunks; per group the bias is
+the group minimum and the scale (max - min) / (2**bits - 1), both rounded to
+the storage type, and each code is round((w - bias) / scale) clipped to
+[0, 2**bits).  Codes are then bell-shaped rather than uniform, every group
+holds a 0 and (nearly always) a top code, and the bias is not a multiple of
+the scale, so the zero point is arbitrary -- the head every real quantized
+LM head is.
+
 A peaked workload multiplies the scales (and so the biases) of the first
 ``boost_rows`` vocabulary rows by ``boost`` after step 2.  Their logits then
 dominate every token's softmax, as the frequent tokens of a trained model's
@@ -62,6 +73,9 @@ class Workload:
     boost: float = 1.0
     group: int = GROUP            # quantization group: 32, 64 or 128
     sb_dtype: str = "f32"         # storage of scales and biases: "f32" | "bf16" | "f16"
+    bias: str = "symmetric"       # "symmetric" (b = -zero_point*s) | "affine" (min/max quantized float head)
+    w_std: float = 0.02           # affine: spread of a float row around its mean
+    row_mean_std: float = 0.02    # affine: spread of the row means
 
     @property
     def G(self) -> int:
@@ -142,10 +156,61 @@ def _mask(rng, M, kind, frac) -> Optional[np.ndarray]:
     return m
 
 
+def _round_sb(x: np.ndarray, sb_dtype: str) -> np.ndarray:
+    """fp32 values rounded to the storage type (nearest, ties to even), as fp32."""
+    if sb_dtype == "bf16":
+        return f32_from_bf16_bits(bf16_bits_from_f32(x))
+    if sb_dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    return np.asarray(x, np.float32)
+
+
+def _store_sb(x: np.ndarray, sb_dtype: str) -> np.ndarray:
+    """fp32 values exact in the storage type -> the stored array."""
+    if sb_dtype == "bf16":
+        return bf16_bits_from_f32(x)
+    if sb_dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return np.asarray(x, np.float32)
+
+
+def _affine_head(rng, w: Workload, chunk_rows: int = 4096):
+    """Min/max (asymmetric) quantization of a float head drawn row chunk by
+    row chunk: returns packed words, scales and biases (stored types)."""
+    V, H, G, bits = w.V, w.H, w.G, w.bits
+    top = (1 << bits) - 1
+    per = 32 // bits
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    mu = (rng.standard_normal(V, dtype=np.float32) * np.float32(w.row_mean_std)).astype(np.float32)
+    wq = np.empty((V, w.words_per_row), np.uint32)
+    scales = np.empty((V, G), np.float32)
+    biases = np.empty((V, G), np.float32)
+    for v0 in range(0, V, chunk_rows):
+        v1 = min(V, v0 + chunk_rows)
+        x = rng.standard_normal((v1 - v0, H), dtype=np.float32) * np.float32(w.w_std) + mu[v0:v1, None]
+        xg = x.reshape(v1 - v0, G, w.group)
+        lo = xg.min(axis=2)
+        hi = xg.max(axis=2)
+        s = _round_sb(((hi - lo) / np.float32(top)).astype(np.float32), w.sb_dtype)
+        b = _round_sb(lo, w.sb_dtype)
+        safe = np.where(s > 0, s, np.float32(1.0))
+        q = np.rint((xg - b[:, :, None]) / safe[:, :, None])
+        q = np.clip(q, 0, top).astype(np.uint32).reshape(v1 - v0, w.words_per_row, per)
+        wq[v0:v1] = np.bitwise_or.reduce(q << shifts, axis=2)
+        scales[v0:v1] = s
+        biases[v0:v1] = b
+    return wq, _store_sb(scales, w.sb_dtype), _store_sb(biases, w.sb_dtype)
+
+
 def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
     """All arrays of one workload (M may be overridden for reduced cases)."""
     M = w.M if M is None else M
     rng = np.random.default_rng(seed)
+    if w.bias == "affine":
+        wq, scales, biases = _affine_head(rng, w)
+        return _tokens(rng, w, M, wq, scales, biases)
+    if w.bias != "symmetric":
+        raise ValueError(w.bias)
     wq = rng.integers(0, 2**32, size=(w.V, w.words_per_row), dtype=np.uint32)
     scales = rng.uniform(w.scale_lo, w.scale_hi, size=(w.V, w.G)).astype(np.float32)
     if w.boost_rows > 0:
@@ -160,6 +225,11 @@ def make_inputs(w: Workload, seed: int, M: Optional[int] = None) -> dict:
         scales, biases = bf16_bits_from_f32(scales), bf16_bits_from_f32(biases)
     elif w.sb_dtype == "f16":
         scales, biases = scales.astype(np.float16).view(np.uint16), biases.astype(np.float16).view(np.uint16)
+    return _tokens(rng, w, M, wq, scales, biases)
+
+
+def _tokens(rng, w: Workload, M: int, wq, scales, biases) -> dict:
+    """Steps 3-5 of the recipe (hidden states, targets, mask) on the same stream."""
     h = bf16_bits_from_f32(rng.standard_normal((M, w.H), dtype=np.float32))
     targets = _targets(rng, M, w.V, w.targets, w.zipf_a)
     mask = _mask(rng, M, w.mask, w.mask_frac)
@@ -183,13 +253,15 @@ def make_dense(M, H, V, seed, softcap=0.0, w_std=0.02, targets="uniform", zipf_a
 
 def make_custom(M, H, V, bits, seed, softcap=0.0, scale_lo=None, scale_hi=None,
                 targets="uniform", mask="none", mask_frac=0.0, h_scale=1.0,
-                boost_rows=0, boost=1.0, group=GROUP, sb_dtype="f32") -> dict:
+                boost_rows=0, boost=1.0, group=GROUP, sb_dtype="f32", bias="symmetric",
+                w_std=0.02, row_mean_std=0.02) -> dict:
     """A reduced/edge-case workload with the same value distributions."""
     if scale_lo is None:
         scale_lo, scale_hi = (0.005, 0.02) if bits == 4 else (0.0005, 0.002)
     w = Workload("custom", M, H, V, bits, scale_lo, scale_hi, softcap=softcap,
                  targets=targets, mask=mask, mask_frac=mask_frac,
-                 boost_rows=boost_rows, boost=boost, group=group, sb_dtype=sb_dtype)
+                 boost_rows=boost_rows, boost=boost, group=group, sb_dtype=sb_dtype,
+                 bias=bias, w_std=w_std, row_mean_std=row_mean_std)
     d = make_inputs(w, seed)
     if h_scale != 1.0:
         d["h"] = bf16_bits_from_f32(f32_from_bf16_bits(d["h"]) * np.float32(h_scale))

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 5
+    assert lib.cce_abi_version() == 6
 
 
 def head(**kw):
@@ -200,3 +200,32 @@ def test_profile_api_without_launches(lib):
 def test_status_strings(lib):
     for s in range(5):
         assert lib.cce_status_str(s)
+
+
+def fwdbwd(lib, hd, M=4, logp=0x6000, lse=0x7000, dh=0x8000, dh_dtype=0, g=None, ws=0x100000, nbytes=1 << 40):
+    return lib.cce_forward_backward(ctypes.byref(hd), 0x4000, M, 0x5000, None, g, logp, lse, dh, dh_dtype, ws,
+                                    nbytes, None)
+
+
+def test_forward_backward_arguments(lib):
+    # the one-call forward + backward checks like its two halves, before any launch
+    hd = head(softcap=30.0)
+    n = lib.cce_forward_backward_workspace_bytes(ctypes.byref(hd), 1000)
+    # the single pass (softcap <= 40) keeps the forward partials of every
+    # chunk next to the backward's buffers; other heads reuse one workspace
+    assert n >= lib.cce_backward_workspace_bytes(ctypes.byref(hd), 1000) and n % 256 == 0
+    plain = head(softcap=0.0)
+    assert lib.cce_forward_backward_workspace_bytes(ctypes.byref(plain), 1000) == max(
+        lib.cce_forward_workspace_bytes(ctypes.byref(plain), 1000),
+        lib.cce_backward_workspace_bytes(ctypes.byref(plain), 1000))
+    assert lib.cce_forward_backward_workspace_bytes(ctypes.byref(head(bits=3)), 16) == 0
+    assert fwdbwd(lib, head(bits=5)) == cce.CCE_ERR_UNSUPPORTED
+    assert fwdbwd(lib, hd, M=-1) == cce.CCE_ERR_INVALID_ARG
+    assert fwdbwd(lib, hd, M=0) == cce.CCE_OK
+    assert fwdbwd(lib, hd, logp=None) == cce.CCE_ERR_INVALID_ARG
+    assert fwdbwd(lib, hd, dh=None) == cce.CCE_ERR_INVALID_ARG
+    assert fwdbwd(lib, hd, dh=0x8002) == cce.CCE_ERR_INVALID_ARG        # fp32 dh: 4-byte aligned
+    assert fwdbwd(lib, hd, dh_dtype=2) == cce.CCE_ERR_INVALID_ARG
+    assert fwdbwd(lib, hd, g=0x9002) == cce.CCE_ERR_INVALID_ARG
+    assert fwdbwd(lib, hd, ws=None) == cce.CCE_ERR_WORKSPACE
+    assert fwdbwd(lib, hd, nbytes=n - 1, M=1000) == cce.CCE_ERR_WORKSPACE

@@ -1,0 +1,171 @@
+"""cce_forward_backward on the GPU, through the C ABI, against the fp64 oracle.
+
+With a softcap in (0, 40] the call is a single pass over the head: the
+forward's fixed reference e^{y - cap} gives every coefficient up to the
+token's factor g e^{cap - lse}, which the split reduce applies after the
+merge (no logit is computed twice).  Other heads run the forward and the
+backward in sequence, which must equal the two separate calls bit for bit.
+Tolerances as in test_parity_gpu.py (|dlogp|, |dlse| <= 5e-3, dh relative L2
+<= 1e-2, worst row <= 5e-2).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_cross_entropy_libcce_amd import cce
+from linear_cross_entropy_libcce_amd import synthetic as syn
+from test_parity_gpu import check, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print("[fused] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cce.load()
+    return torch
+
+
+def run_fused(torch, inp, g=None, dh_dtype="f32"):
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    gg = None if g is None else torch.from_numpy(np.asarray(g, np.float32)).cuda()
+    logp, lse, dh = cce.cce_forward_backward(h, head, t, gg, m, dh_dtype=dh_dtype)
+    torch.cuda.synchronize()
+    return (logp.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            dh.float().cpu().numpy().astype(np.float64))
+
+
+CASES = {
+    "H512_V1000_8bit_cap30": dict(M=600, H=512, V=1000, bits=8, softcap=30.0),
+    "H1536_V777_4bit_cap30_zipf_randmask": dict(M=300, H=1536, V=777, bits=4, softcap=30.0, targets="zipf",
+                                               mask="random", mask_frac=0.3),
+    "H2560_V400_8bit_cap40_prefixmask": dict(M=520, H=2560, V=400, bits=8, softcap=40.0, mask="prefix",
+                                            mask_frac=0.5),
+    "H512_V900_8bit_cap30_group32": dict(M=300, H=512, V=900, bits=8, softcap=30.0, group=32),
+    "H768_V700_4bit_cap30_group32_bf16": dict(M=400, H=768, V=700, bits=4, softcap=30.0, group=32,
+                                             sb_dtype="bf16"),
+    "H1024_V600_8bit_cap10_group128_f16": dict(M=270, H=1024, V=600, bits=8, softcap=10.0, group=128,
+                                               sb_dtype="f16"),
+    "H256_V700_4bit_cap0.5_wide": dict(M=4200, H=256, V=700, bits=4, softcap=0.5),
+    # small M (the small-M tile) and a vocabulary in two coefficient chunks
+    "M1_H256_V1000_8bit_cap30": dict(M=1, H=256, V=1000, bits=8, softcap=30.0),
+    "M16_H1536_V4097_4bit_cap30": dict(M=16, H=1536, V=4097, bits=4, softcap=30.0),
+    "M64_H512_V3000_8bit_cap30_randmask": dict(M=64, H=512, V=3000, bits=8, softcap=30.0, mask="random",
+                                               mask_frac=0.3),
+    "M20_H64_V600000_8bit_cap20_two_chunks": dict(M=20, H=64, V=600000, bits=8, softcap=20.0),
+    "M300_H64_V600000_4bit_cap30_two_chunks": dict(M=300, H=64, V=600000, bits=4, softcap=30.0),
+}
+
+
+@pytest.mark.parametrize("bias", ["sym", "affine"])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fused_against_oracle(torch_cuda, name, bias):
+    kw = CASES[name]
+    inp = syn.make_custom(seed=zlib.crc32(name.encode()) % 1000, bias="symmetric" if bias == "sym" else "affine",
+                          **kw)
+    g = np.random.default_rng(3).uniform(-2, 2, size=kw["M"])
+    say("%s (%s head): fused forward + backward" % (name, bias))
+    gpu = run_fused(torch_cuda, inp, g=g)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(kw["M"]), "fused_%s_%s" % (name, bias))
+
+
+@pytest.mark.parametrize("cap", [0.0, 50.0])
+def test_other_heads_equal_the_two_calls(torch_cuda, cap):
+    # no softcap or one above 40: the call runs the forward and the backward,
+    # bit for bit what cce_forward followed by cce_backward give
+    torch = torch_cuda
+    inp = syn.make_custom(M=300, H=512, V=1300, bits=8, seed=81, softcap=cap, mask="random", mask_frac=0.2,
+                          bias="affine")
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    g = torch.from_numpy(np.random.default_rng(5).uniform(-1, 1, size=300).astype(np.float32)).cuda()
+    logp, lse, dh = cce.cce_forward_backward(h, head, t, g, m)
+    logp0, lse0 = cce.cce_forward(h, head, t, m)
+    dh0 = cce.cce_backward(h, head, t, lse0, g, m)
+    torch.cuda.synchronize()
+    assert torch.equal(logp, logp0) and torch.equal(lse, lse0) and torch.equal(dh, dh0)
+
+
+def test_fused_matches_the_two_calls(torch_cuda):
+    # under a softcap the single pass and the two calls compute the same
+    # quantities in different orders: within rounding of each other
+    torch = torch_cuda
+    inp = syn.make_custom(M=700, H=1024, V=3000, bits=8, seed=82, softcap=30.0, mask="random", mask_frac=0.2,
+                          bias="affine")
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    logp, lse, dh = cce.cce_forward_backward(h, head, t, None, m)
+    logp0, lse0 = cce.cce_forward(h, head, t, m)
+    dh0 = cce.cce_backward(h, head, t, lse0, None, m)
+    torch.cuda.synchronize()
+    dl = (logp - logp0).abs().max().item()
+    ds = (lse - lse0).abs().max().item()
+    rel = ((dh - dh0).norm() / dh0.norm()).item()
+    say("fused vs two calls: max|dlogp| %.3g max|dlse| %.3g dh rel %.3g" % (dl, ds, rel))
+    assert dl <= 1e-4 and ds <= 1e-4 and rel <= 5e-3
+
+
+def test_fused_is_linear_in_g(torch_cuda):
+    # dh(g) = g * dh(1) row by row (the caller may scale d logp / d h later)
+    torch = torch_cuda
+    inp = syn.make_custom(M=300, H=512, V=2000, bits=4, seed=83, softcap=30.0, bias="affine")
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    gn = np.random.default_rng(6).uniform(-3, 3, size=300).astype(np.float32)
+    g = torch.from_numpy(gn).cuda()
+    _, _, dh1 = cce.cce_forward_backward(h, head, t, None, m)
+    _, _, dhg = cce.cce_forward_backward(h, head, t, g, m)
+    torch.cuda.synchronize()
+    ref = dh1 * g[:, None]
+    rel = ((dhg - ref).norm() / ref.norm()).item()
+    say("linearity in g: rel %.3g" % rel)
+    assert rel <= 1e-6
+
+
+def test_fused_bf16_dh_is_the_fp32_dh_rounded(torch_cuda):
+    torch = torch_cuda
+    inp = syn.make_custom(M=300, H=512, V=3000, bits=8, seed=84, softcap=30.0, mask="random", mask_frac=0.3)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    _, _, d32 = cce.cce_forward_backward(h, head, t, None, m)
+    _, _, d16 = cce.cce_forward_backward(h, head, t, None, m, dh_dtype="bf16")
+    torch.cuda.synchronize()
+    assert d16.dtype == torch.bfloat16
+    assert torch.equal(d16.view(torch.int16), d32.to(torch.bfloat16).view(torch.int16))
+
+
+def test_fused_repeat_runs_are_bitwise_identical(torch_cuda):
+    inp = syn.make_custom(M=300, H=512, V=3000, bits=8, seed=85, softcap=30.0, bias="affine")
+    a = run_fused(torch_cuda, inp)
+    b = run_fused(torch_cuda, inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,bias", [(3, "sym"), (3, "affine"), (2, "sym")])
+def test_fused_full_size_workload_sampled(torch_cuda, cfg, bias):
+    # the softcapped workloads at full size (the launch bench.py times), one
+    # supervised token per token tile and the first and last against the oracle
+    import dataclasses
+    w = dataclasses.replace(syn.WORKLOADS[cfg], bias="symmetric" if bias == "sym" else "affine")
+    say("workload %d (%s head): generating inputs" % (cfg, bias))
+    inp = syn.make_inputs(w, syn.seed_for(cfg))
+    say("workload %d: fused forward + backward at full size" % cfg)
+    gpu = run_fused(torch_cuda, inp)
+    rows = sample_rows(inp, 4, cfg + 10, every=8 if cfg == 2 else None)
+    say("workload %d: oracle on %d sampled tokens" % (cfg, len(rows)))
+    check(inp, gpu, oracle.cce(inp, tokens=rows), rows, "fused_workload%d_%s" % (cfg, bias))
+    act = np.ones(inp["M"], bool) if inp["mask"] is None else inp["mask"] != 0
+    assert np.all(gpu[0][act] <= 1e-6) and np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))

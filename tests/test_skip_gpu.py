@@ -36,14 +36,15 @@ def torch_cuda():
     return torch
 
 
-def flat_blocks(M, H, V, bits, seed, mask, cap=0.0):
+def flat_blocks(M, H, V, bits, seed, mask, cap=0.0, bias="symmetric", group=64):
     """Vocabulary blocks 1.. made of one repeated row each, targets mostly in
     block 0 (every 97th token's in block 2): the probability spreads evenly
     over the repeated rows (each below 0.01, the blocks holding ~30% of it), so
     the pairs of blocks 1.. go cold for whole token tiles while carrying enough
     mass that dropping them moves dh by ~35%.  The per-pair maxima sit far from
     the eps values used (warm pairs >= 0.08, cold <= 0.014)."""
-    inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=seed, mask=mask, mask_frac=0.3, softcap=cap)
+    inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=seed, mask=mask, mask_frac=0.3, softcap=cap, bias=bias,
+                          group=group)
     for k in ("wq", "scales", "biases"):
         a = inp[k]
         for b in range(1, (V + 255) // 256):
@@ -58,6 +59,9 @@ def flat_blocks(M, H, V, bits, seed, mask, cap=0.0):
 CASES = {
     "H256_V1000_8bit_randmask": (600, 256, 1000, 8, 71, "random"),
     "H512_V1100_4bit_cap": (700, 512, 1100, 4, 72, "none", 30.0),
+    # affine heads (b' != 0 on every row: the bias block runs), 64- and 32-wide steps
+    "H512_V1100_8bit_cap_randmask_affine": (700, 512, 1100, 8, 75, "random", 30.0, "affine"),
+    "H512_V1000_4bit_group32_affine": (600, 512, 1000, 4, 76, "none", 0.0, "affine", 32),
 }
 
 
