@@ -270,6 +270,26 @@ cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t
                               const float *lse, const float *g, float *dh, float *dw,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The library's own buffer of CCE_STATIC_SCRATCH_BYTES per
+ * device (a file-scope device array, held by every device the library runs
+ * on until the process ends) serves as the workspace; the caller still passes
+ * inputs and outputs, as for cce_forward.  Every call on one device shares
+ * that device's buffer: calls that overlap on one device (other streams,
+ * other threads) race, and must be ordered by the caller.  The buffer keeps
+ * the last call's contents; nothing in it needs to start at zero.
+ * Arguments, results and errors are those of cce_forward, plus
+ * CCE_ERR_WORKSPACE when cce_forward_workspace_bytes(head, M) exceeds
+ * CCE_STATIC_SCRATCH_BYTES and CCE_ERR_HIP when the buffer's device address
+ * cannot be found.
+ */
+#define CCE_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+cce_status cce_forward_static(const cce_head *head, const void *h, int64_t M,
+                              const int32_t *targets, const uint8_t *mask,
+                              float *logp, float *lse, void *stream);
+
 /* Human-readable text of a status (for CCE_ERR_HIP, of the last HIP error
  * seen by this thread).  The pointer stays valid until the thread's next call. */
 const char *cce_status_str(cce_status status);

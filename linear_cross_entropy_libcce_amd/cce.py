@@ -20,7 +20,8 @@ EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
            "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_status_str",
            "cce_abi_version", "cce_profile_enable", "cce_profile_read",
            "cce_dense_forward", "cce_dense_backward", "cce_dense_forward_workspace_bytes",
-           "cce_dense_backward_workspace_bytes", "cce_forward_backward", "cce_forward_backward_workspace_bytes")
+           "cce_dense_backward_workspace_bytes", "cce_forward_backward", "cce_forward_backward_workspace_bytes",
+           "cce_forward_static")
 
 BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.cce_forward_backward.argtypes = [HP, P, I64, P, P, P, P, P, P, ctypes.c_int32, P, SZ, P]
     lib.cce_forward_backward_workspace_bytes.restype = SZ
     lib.cce_forward_backward_workspace_bytes.argtypes = [HP, I64]
+    lib.cce_forward_static.restype = ctypes.c_int
+    lib.cce_forward_static.argtypes = [HP, P, I64, P, P, P, P, P]
     DP = ctypes.POINTER(cce_dense_head)
     lib.cce_dense_forward.restype = ctypes.c_int
     lib.cce_dense_forward.argtypes = [DP, P, I64, P, P, P, P, P, SZ, P]
@@ -240,6 +243,21 @@ def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
     ws = _workspace(lib.cce_forward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
     _check(lib.cce_forward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse
+
+
+STATIC_SCRATCH_BYTES = 128 << 20   # CCE_STATIC_SCRATCH_BYTES
+
+
+def cce_forward_static(h, head: Head, targets, mask=None, out=None):
+    """(logp, lse) like cce_forward, with the library's own device scratch as
+    the workspace (no workspace argument, nothing allocated by the library)."""
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    logp, lse = _fwd_out(M, dev, out)
+    hs = head.c_struct()
+    _check(lib.cce_forward_static(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(logp), _ptr(lse),
+                                  _stream(dev)))
     return logp, lse
 
 

@@ -15,6 +15,12 @@
 #include "cce_device.h"
 #include "cce_profile.h"
 
+// The workspace of cce_forward_static: one array per device, which the
+// loader allocates with the code object.  Host code never passes its name to
+// a kernel (on the host it names a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[CCE_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace cce;
@@ -591,6 +597,26 @@ cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t
   return hip_status();
 }
 
+// Device address of this device's `scratch`, looked up with the device
+// current the first time a call runs on it (nullptr if the lookup fails).
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+void *scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hip_status();  // keep the HIP error text for cce_status_str
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : std::max(p.fwd_bytes, p.bwd_bytes); }
 
 }  // namespace
@@ -649,6 +675,19 @@ cce_status cce_backward_ex(const cce_head *head, const void *h, int64_t M, const
   if (s != CCE_OK || M == 0) return s;
   return run_backward(head, h, M, targets, mask, lse, g, block_max, skip, dh, dh_dtype, nullptr, workspace,
                       workspace_bytes, stream);
+}
+
+cce_status cce_forward_static(const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                              const uint8_t *mask, float *logp, float *lse, void *stream) {
+  cce_status s = check_common(head, h, M, targets, nullptr);
+  if (s != CCE_OK || M == 0) return s;
+  if (make_plan(head, M).fwd_bytes > CCE_STATIC_SCRATCH_BYTES) return CCE_ERR_WORKSPACE;
+  void *ws = scratch_ptr();
+  if (!ws) {
+    if (!g_err[0]) std::snprintf(g_err, sizeof g_err, "HIP error: no device address for the static scratch");
+    return CCE_ERR_HIP;
+  }
+  return run_forward(head, h, M, targets, mask, logp, lse, nullptr, ws, CCE_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t cce_forward_backward_workspace_bytes(const cce_head *head, int64_t M) {

@@ -229,3 +229,15 @@ def test_forward_backward_arguments(lib):
     assert fwdbwd(lib, hd, g=0x9002) == cce.CCE_ERR_INVALID_ARG
     assert fwdbwd(lib, hd, ws=None) == cce.CCE_ERR_WORKSPACE
     assert fwdbwd(lib, hd, nbytes=n - 1, M=1000) == cce.CCE_ERR_WORKSPACE
+
+
+def test_static_forward_size_limit(lib):
+    # the no-allocation forward rejects a plan larger than its device scratch
+    # before any HIP call (so this runs without a GPU)
+    big = head(V=400000, H=4096, bits=8)
+    assert lib.cce_forward_workspace_bytes(ctypes.byref(big), 8) > cce.STATIC_SCRATCH_BYTES
+    assert lib.cce_forward_static(ctypes.byref(big), 0x4000, 8, 0x5000, None, 0x6000, 0x7000, None) == \
+        cce.CCE_ERR_WORKSPACE
+    assert lib.cce_forward_static(ctypes.byref(head(bits=5)), 0x4000, 8, 0x5000, None, 0x6000, 0x7000, None) == \
+        cce.CCE_ERR_UNSUPPORTED
+    assert lib.cce_forward_static(ctypes.byref(head()), 0x4000, 0, 0x5000, None, 0x6000, 0x7000, None) == cce.CCE_OK
