@@ -4,11 +4,13 @@
 One step = forward + backward (g = 1) over one batch of the synthetic
 workload M=8192 tokens, H=2560, V=262144, 8-bit affine head (group 64),
 softcap 30 -- the largest single-GPU workload at H=2560, V=262144.  Inputs are
-resident in HBM and workspaces preallocated before the timed region.  Under a
-softcap of at most 40 the step is the single pass cce_forward_backward (the
-logits computed once); otherwise, and always in the `two_calls` field, it is
-cce_forward + cce_backward (the backward recomputes the logits).  Each step
-is timed between its own pair of HIP events; the median is reported.
+resident in HBM and workspaces preallocated before the timed region.  The
+step is one call of cce_forward_backward: under a softcap of at most 40 its
+single pass (the logits computed once), otherwise its forward and backward
+passes after one front.  The `two_calls` field times cce_forward +
+cce_backward (the backward recomputes the logits) on the same inputs; the
+skips and the dense head always take their calls.  Each step is timed
+between its own pair of HIP events; the median is reported.
 
 Prints one JSON line.  `value` is supervised tokens per second of fwd+bwd.
 `roofline` is for the kernel family with the most time per step, timed live
@@ -84,11 +86,15 @@ def cpu_baseline(inp, seconds, M_eff):
     rng = np.random.default_rng(0)
     t0 = time.perf_counter()
     oracle.cce(inp, tokens=act[:1])
-    per_tok = time.perf_counter() - t0
-    n = int(max(1, min(64, seconds / max(per_tok, 1e-3))))
+    per_tok = max(time.perf_counter() - t0, 1e-6)
+    # a random sample of the supervised tokens (all of them when there are
+    # few), repeated until the sample has taken about `seconds`
+    n = int(max(1, min(64, len(act), seconds / per_tok)))
+    reps = int(max(1, min(10000, seconds / (n * per_tok))))
     toks = rng.choice(act, size=n, replace=False)
     t0 = time.perf_counter()
-    oracle.cce(inp, tokens=toks)
+    for _ in range(reps):
+        oracle.cce(inp, tokens=toks)
     dt = time.perf_counter() - t0
     model = None
     try:
@@ -98,9 +104,10 @@ def cpu_baseline(inp, seconds, M_eff):
                 break
     except OSError:
         pass
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": n * reps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "nproc": os.cpu_count(), "cpu_model": model,
-            "sample": "fwd+bwd of %d random supervised tokens of the full workload (%.1f s)" % (n, dt)}
+            "sample": "fwd+bwd of %d random supervised tokens of the full workload%s (%.1f s)"
+                      % (n, "" if reps == 1 else ", %d times" % reps, dt)}
 
 
 def main():
@@ -211,22 +218,25 @@ def main():
         fwd()
         bwd()
 
-    # the single pass (cce_forward_backward) where the head allows it: a
-    # quantized head with 0 < softcap <= 40, no skips; else the two calls
-    fused = (not args.dense and not args.skip and args.path != "calls" and 0.0 < inp["softcap"] <= 40.0)
-    if fused:
+    # one call (cce_forward_backward) for a quantized head without skips: the
+    # single pass where the head allows it (0 < softcap <= 40), else its two
+    # passes after one front; the skips and the dense head take the two calls
+    combined = not args.dense and not args.skip and args.path != "calls"
+    fused = combined and 0.0 < inp["softcap"] <= 40.0
+    if combined:
         ws_fb = torch.empty(cce.forward_backward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
 
     def fused_step():
         cce.cce_forward_backward(h, head, t, None, m, workspace=ws_fb, out=(logp, lse, dh))
 
-    step = fused_step if fused else calls
-    log("step: %s" % ("cce_forward_backward (single pass)" if fused else "cce_forward + cce_backward"))
+    step = fused_step if combined else calls
+    log("step: %s" % (("cce_forward_backward (%s)" % ("single pass" if fused else "two passes, one front"))
+                      if combined else "cce_forward + cce_backward"))
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
-        if fused:
+        if combined:
             calls()
     torch.cuda.synchronize()
 
@@ -270,7 +280,7 @@ def main():
     ms_bwd = float(np.median(timed(bwd)))
     log("forward %.3f ms, backward %.3f ms (median)" % (ms_fwd, ms_bwd))
     two_calls = None
-    if fused:
+    if combined:
         ms_calls = float(np.median(timed(replayable(calls))))
         two_calls = {"ms_per_step": round(ms_calls, 4), "tokens_per_s": round(M_eff / (ms_calls * 1e-3), 1),
                      "tflops": round(6.0 * M_eff * V * H / (ms_calls * 1e-3) / 1e12, 1)}
@@ -347,7 +357,8 @@ def main():
                    "g": 1.0,
                    "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps},
                    "hip_graph": bool(args.graph),
-                   "step": "cce_forward_backward" if fused else "cce_forward+cce_backward"},
+                   "step": ("cce_forward_backward (single pass)" if fused else
+                            ("cce_forward_backward (two passes)" if combined else "cce_forward+cce_backward"))},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),
         "two_calls": two_calls,

@@ -105,6 +105,9 @@ struct Plan {
   bool fused;
   int fus_blocks, fus_max_splits, mass_ld;
   size_t o_fpart, o_tdc, o_smass, fus_bytes;
+  // cce_forward_backward without the single pass: the forward's partials
+  // after the backward's buffers (the backward tile merges them itself)
+  size_t o_ppart, twopass_bytes;
 };
 
 // A dense bf16 head runs as an internal head of 16 "bits" per element: the
@@ -243,6 +246,8 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   o = align_up(o + sizeof(float) * p.M_pad, 256);
   p.o_fpart = o;
   p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
+  p.o_ppart = p.bwd_bytes;
+  p.twopass_bytes = align_up(p.o_ppart + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
   if (dense) {
     p.o_hT = p.bwd_bytes;
     o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
@@ -296,7 +301,7 @@ T *ws_at(void *ws, size_t off) {
 // compaction, augmented rows and token records, target logits
 void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32_t *targets,
                    const uint8_t *mask, const float *lse, const float *g, void *ws, hipStream_t st,
-                   bool bwd) {
+                   bool bwd, float *out_logp = nullptr, float *out_lse = nullptr) {
   int *cnt = ws_at<int>(ws, p.o_cnt);
   int *idx = ws_at<int>(ws, p.o_idx);
   int *inv = ws_at<int>(ws, p.o_inv);
@@ -305,8 +310,11 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   // up to this many tokens the front's row blocks compact the mask themselves
   // (each scans all M mask bytes), one launch fewer
   const bool fuse = p.M <= FUSED_COMPACT_MAX_M;
-  if (!fuse) CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt));
+  if (!fuse)
+    CCE_LAUNCH("compact", st, launch_compact(st, mask, (int)p.M, (int)p.M_pad, idx, inv, cnt, out_logp, out_lse));
   FrontArgs f{};
+  f.out_logp = out_logp;
+  f.out_lse = out_lse;
   f.compact = fuse ? 1 : 0;
   f.M = (int)p.M;
   f.mask = mask;
@@ -597,6 +605,88 @@ cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t
   return hip_status();
 }
 
+// cce_forward_backward on a head without the single pass (no softcap, or one
+// above CAP_FIXED_REF_MAX): one front (with g), the forward tile, then the
+// backward chunks, whose tiles form each token's lse from the forward's
+// partials themselves (no merge launch; the workgroup of split 0 of chunk 0
+// writes logp and lse), the dh contraction and the split reduce.
+cce_status run_twopass(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                       const uint8_t *mask, const float *g, float *logp, float *lse, void *dh, int32_t dh_dtype,
+                       void *workspace, hipStream_t st) {
+  enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false, logp, lse);
+  TileArgs a = tile_args(p, head, workspace);
+  float *ppart = ws_at<float>(workspace, p.o_ppart);
+  a.part = ppart;
+  a.range_tile0 = 0;
+  a.range_tiles = p.tiles;
+  a.chunk = 0;
+  a.full_tiles = p.tiles;
+  a.nblocks = p.fwd_blocks;
+  a.max_splits = p.max_splits;
+  CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, PASS_FWD, dim3((unsigned)(cdiv(a.nblocks, 8) * 8)), a));
+
+  TileArgs b = tile_args(p, head, workspace);
+  b.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
+  b.ld_coeff = p.ld_coeff;
+  b.tmass = 1;
+  b.tdc = ws_at<float>(workspace, p.o_tdc);
+  b.mass = ws_at<float>(workspace, p.o_fpart);
+  b.mass_ld = p.mass_ld;
+  b.full_tiles = p.chunk_tiles;
+  b.nblocks = p.fus_blocks;
+  b.max_splits = p.fus_max_splits;
+  b.fpart = ppart;
+  b.f_nblocks = p.fwd_blocks;
+  b.f_tiles = p.tiles;
+  b.f_max_splits = p.max_splits;
+  b.idx = ws_at<const int>(workspace, p.o_idx);
+  b.out_logp = logp;
+  b.out_lse = lse;
+  const dim3 g1((unsigned)(cdiv(b.nblocks, 8) * 8));
+
+  GemmArgs ga{};
+  ga.coeff = b.coeff;
+  ga.ksv = p.ld_coeff / 16;
+  ga.wq = head->wq;
+  ga.scales = head->scales;
+  ga.biases = head->biases;
+  ga.cnt = b.cnt;
+  ga.dh_part = ws_at<float>(workspace, p.o_dhp);
+  ga.V = p.V;
+  ga.H = (int)p.H;
+  ga.gs = p.gs;
+  ga.Gq = p.Gq;
+  ga.sbt = p.sbt;
+  ga.wpr = p.wpr;
+  ga.M_pad = (int)p.M_pad;
+  ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);
+  ga.TT = p.TT;
+  ga.HT = p.HT;
+  ga.ksplit = p.ksplit;
+  ga.nblocks = p.TT * p.HT * p.ksplit;
+  ga.small = b.small;
+  const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+    b.range_tile0 = t0;
+    b.range_tiles = nt;
+    b.chunk = c;
+    CCE_LAUNCH("tile_bwd", st, launch_tile(st, p.bits, PASS_BWD, g1, b));
+    ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_tile0 = t0;
+    ga.chunk_steps = nt * (BNT / KSTEP);
+    ga.accumulate = c > 0;
+    CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+  }
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, ws_at<const int>(workspace, p.o_inv),
+                                               ws_at<const TokRec>(workspace, p.o_tok), dh,
+                                               dh_dtype == CCE_DH_BF16 ? 1 : 0,
+                                               ReduceTarget{1, b.mass, b.mass_ld, b.nblocks, b.full_tiles, p.tiles,
+                                                            b.max_splits, nullptr, 0.0f, b.tdc}));
+  return hip_status();
+}
+
 // Device address of this device's `scratch`, looked up with the device
 // current the first time a call runs on it (nullptr if the lookup fails).
 std::mutex g_scratch_mu;
@@ -617,7 +707,7 @@ void *scratch_ptr() {
   return g_scratch_ptr[dev];
 }
 
-size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : std::max(p.fwd_bytes, p.bwd_bytes); }
+size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : p.twopass_bytes; }
 
 }  // namespace
 
@@ -708,12 +798,7 @@ cce_status cce_forward_backward(const cce_head *head, const void *h, int64_t M, 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   if (p.fused) return run_fused(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
-  // other heads: the forward, then the backward on the lse it wrote (the
-  // backward's front rewrites the shared part of the workspace after it)
-  s = run_forward(head, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
-  if (s != CCE_OK) return s;
-  return run_backward(head, h, M, targets, mask, lse, g, nullptr, nullptr, dh, dh_dtype, nullptr, workspace,
-                      workspace_bytes, stream);
+  return run_twopass(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
 }
 
 size_t cce_dense_forward_workspace_bytes(const cce_dense_head *head, int64_t M) {

@@ -161,6 +161,13 @@ struct TileArgs {
   int tmass;
   float *mass;           // backward with tmass: [M_pad][mass_ld] non-target mass of each split
   int mass_ld;
+  // backward of cce_forward_backward without a softcap reference: each lane
+  // forms its token's lse from the forward's partials (fpart, the forward
+  // launch's split plan f_*) instead of a merge launch, and the workgroup of
+  // split 0 of chunk 0 (vocabulary half 0) writes logp and lse of its tokens
+  const float *fpart;
+  int f_nblocks, f_tiles, f_max_splits;
+  float *out_logp, *out_lse;
   float cap, inv_cap;
   // forward, optional: block_max[idx[r]][tile] = largest softcapped logit of
   // vocabulary tile `tile` for compacted row r (nbv = tiles per row)
@@ -202,6 +209,8 @@ struct FrontArgs {
   int compact, M;
   const uint8_t *mask;
   int *idx_out, *inv, *cnt;
+  // non-NULL: logp and lse of masked tokens are written (0) here
+  float *out_logp, *out_lse;
 };
 
 struct GemmArgs {
@@ -340,7 +349,9 @@ __device__ __forceinline__ float softcap_d(float z, float cap, float inv_cap, fl
 
 
 // Launch entry points of the kernel translation units (host side).
-void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt);
+// out_logp, out_lse: NULL, or outputs whose masked tokens get 0
+void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt,
+                    float *out_logp, float *out_lse);
 void launch_front(hipStream_t st, int bits, const FrontArgs &f);
 // Passes of the logit tile: forward partials, backward coefficients, or both
 // at once (the fused pass, softcap in (0, CAP_FIXED_REF_MAX]; quantized heads).

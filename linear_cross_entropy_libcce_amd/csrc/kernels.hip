@@ -8,7 +8,8 @@ namespace cce {
 // Token compaction: idx[r] = t of the r-th supervised token, inv[t] = r or -1.
 // One workgroup of 1024 threads scans the mask in order (ballot + popcount).
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, int M_pad,
-                                                   int *idx, int *inv, int *cnt) {
+                                                   int *idx, int *inv, int *cnt, float *out_logp,
+                                                   float *out_lse) {
   __shared__ int wsum[16];
   __shared__ int base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -30,6 +31,10 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
     if (t < M) {
       inv[t] = f ? r : -1;
       if (f) idx[r] = t;
+      if (!f && out_logp) {
+        out_logp[t] = 0.0f;
+        out_lse[t] = 0.0f;
+      }
     }
     __syncthreads();
     if (tid == 0) base += total;
@@ -308,7 +313,12 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
     if (r < M && r >= t0 && r < t1) {  // rank of token r
       int k = excl;
       for (int t = t0; t < r; ++t) k += f.mask ? (f.mask[t] != 0) : 1;
-      f.inv[r] = (!f.mask || f.mask[r] != 0) ? k : -1;
+      const bool sup = !f.mask || f.mask[r] != 0;
+      f.inv[r] = sup ? k : -1;
+      if (!sup && f.out_logp) {
+        f.out_logp[r] = 0.0f;
+        f.out_lse[r] = 0.0f;
+      }
     }
     if (r == 0 && tid == 0) f.cnt[0] = sC[0] + sC[1] + sC[2] + sC[3];
     __syncthreads();
@@ -541,8 +551,9 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
   }
 }
 
-void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt) {
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, M, M_pad, idx, inv, cnt);
+void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *idx, int *inv, int *cnt,
+                    float *out_logp, float *out_lse) {
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, M, M_pad, idx, inv, cnt, out_logp, out_lse);
 }
 
 void launch_front(hipStream_t st, int bits, const FrontArgs &f) {

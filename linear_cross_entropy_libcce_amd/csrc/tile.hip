@@ -276,7 +276,37 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     const TokRec rec = a.tok[tok0 + lane];
     tgt_t = rec.tgt;  // in [0, V), or -1
     if (BWD) {
-      const float lse2 = rec.lse * LOG2E;
+      float lse_t = rec.lse;
+      if (a.fpart) {
+        // the forward's partials of this token, merged as the merge launch
+        // would: lse = m* + log sum_s s_s e^{m_s - m*}
+        // (one pass with a running maximum, eight partials loaded at a time)
+        const int r = tok0 + lane;
+        const int ns = 2 * vsplit_total(a.f_nblocks, act, a.f_tiles, a.f_tiles, a.f_max_splits);
+        const float2 *fp = reinterpret_cast<const float2 *>(a.fpart) + r;
+        float mx = -INFINITY, se = 0.0f;
+        for (int k0 = 0; k0 < ns; k0 += 8) {
+          float2 x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            x[j] = (k0 + j < ns) ? fp[(size_t)(k0 + j) * a.M_pad] : float2{-INFINITY, 0.0f};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float mn = fmaxf(mx, x[j].x);
+            if (mn != -INFINITY) {
+              se = se * __expf(mx - mn) + x[j].y * __expf(x[j].x - mn);
+              mx = mn;
+            }
+          }
+        }
+        lse_t = mx + logf(se);
+        if (a.chunk == 0 && wr == 0 && vh == 0 && (!SMALL || wave == 0) && r < a.cnt[0]) {
+          const int t = a.idx[r];
+          a.out_lse[t] = lse_t;
+          a.out_logp[t] = rec.tval - lse_t;  // the forward's capture of the target logit
+        }
+      }
+      const float lse2 = lse_t * LOG2E;
       kofs = a.cap > 0.0f ? LOG2E * a.cap - lse2 : lse2;
       kfac = a.cap > 0.0f ? -4.0f * rec.g : -rec.g;
     }

@@ -212,12 +212,12 @@ def test_forward_backward_arguments(lib):
     hd = head(softcap=30.0)
     n = lib.cce_forward_backward_workspace_bytes(ctypes.byref(hd), 1000)
     # the single pass (softcap <= 40) keeps the forward partials of every
-    # chunk next to the backward's buffers; other heads reuse one workspace
+    # chunk next to the backward's buffers; other heads keep the forward's
+    # partials after the backward's buffers (their backward tiles merge them)
     assert n >= lib.cce_backward_workspace_bytes(ctypes.byref(hd), 1000) and n % 256 == 0
     plain = head(softcap=0.0)
-    assert lib.cce_forward_backward_workspace_bytes(ctypes.byref(plain), 1000) == max(
-        lib.cce_forward_workspace_bytes(ctypes.byref(plain), 1000),
-        lib.cce_backward_workspace_bytes(ctypes.byref(plain), 1000))
+    assert lib.cce_forward_backward_workspace_bytes(ctypes.byref(plain), 1000) > \
+        lib.cce_backward_workspace_bytes(ctypes.byref(plain), 1000)
     assert lib.cce_forward_backward_workspace_bytes(ctypes.byref(head(bits=3)), 16) == 0
     assert fwdbwd(lib, head(bits=5)) == cce.CCE_ERR_UNSUPPORTED
     assert fwdbwd(lib, hd, M=-1) == cce.CCE_ERR_INVALID_ARG

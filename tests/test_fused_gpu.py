@@ -3,8 +3,10 @@
 With a softcap in (0, 40] the call is a single pass over the head: the
 forward's fixed reference e^{y - cap} gives every coefficient up to the
 token's factor g e^{cap - lse}, which the split reduce applies after the
-merge (no logit is computed twice).  Other heads run the forward and the
-backward in sequence, which must equal the two separate calls bit for bit.
+merge (no logit is computed twice).  Other heads run a forward and a
+backward pass after one front; the backward tiles merge the forward's
+partials themselves, so the results match the two separate calls to
+rounding.
 Tolerances as in test_parity_gpu.py (|dlogp|, |dlse| <= 5e-3, dh relative L2
 <= 1e-2, worst row <= 5e-2).
 """
@@ -65,6 +67,13 @@ CASES = {
                                                mask_frac=0.3),
     "M20_H64_V600000_8bit_cap20_two_chunks": dict(M=20, H=64, V=600000, bits=8, softcap=20.0),
     "M300_H64_V600000_4bit_cap30_two_chunks": dict(M=300, H=64, V=600000, bits=4, softcap=30.0),
+    # no softcap or one above 40: the call's two passes (the backward tiles
+    # merge the forward's partials themselves; no merge launch, one front)
+    "M16_H256_V4096_4bit_nocap": dict(M=16, H=256, V=4096, bits=4),
+    "H512_V1000_8bit_nocap_randmask": dict(M=600, H=512, V=1000, bits=8, mask="random", mask_frac=0.3),
+    "H768_V700_4bit_cap50_group32_bf16": dict(M=400, H=768, V=700, bits=4, softcap=50.0, group=32, sb_dtype="bf16"),
+    "M2100_H256_V900_8bit_nocap_randmask": dict(M=2100, H=256, V=900, bits=8, mask="random", mask_frac=0.4),
+    "M20_H64_V600000_8bit_nocap_two_chunks": dict(M=20, H=64, V=600000, bits=8),
 }
 
 
@@ -81,9 +90,10 @@ def test_fused_against_oracle(torch_cuda, name, bias):
 
 
 @pytest.mark.parametrize("cap", [0.0, 50.0])
-def test_other_heads_equal_the_two_calls(torch_cuda, cap):
-    # no softcap or one above 40: the call runs the forward and the backward,
-    # bit for bit what cce_forward followed by cce_backward give
+def test_other_heads_match_the_two_calls(torch_cuda, cap):
+    # no softcap or one above 40: the call runs a forward and a backward pass,
+    # the backward tiles merging the forward's partials themselves: the same
+    # quantities as cce_forward followed by cce_backward, in another order
     torch = torch_cuda
     inp = syn.make_custom(M=300, H=512, V=1300, bits=8, seed=81, softcap=cap, mask="random", mask_frac=0.2,
                           bias="affine")
@@ -94,7 +104,13 @@ def test_other_heads_equal_the_two_calls(torch_cuda, cap):
     logp0, lse0 = cce.cce_forward(h, head, t, m)
     dh0 = cce.cce_backward(h, head, t, lse0, g, m)
     torch.cuda.synchronize()
-    assert torch.equal(logp, logp0) and torch.equal(lse, lse0) and torch.equal(dh, dh0)
+    dl = (logp - logp0).abs().max().item()
+    ds = (lse - lse0).abs().max().item()
+    rel = ((dh - dh0).norm() / dh0.norm()).item()
+    say("two passes vs two calls (cap %g): max|dlogp| %.3g max|dlse| %.3g dh rel %.3g" % (cap, dl, ds, rel))
+    assert dl <= 1e-5 and ds <= 1e-5 and rel <= 1e-5
+    mk = m == 0
+    assert int((logp[mk] != 0).sum()) == 0 and int((lse[mk] != 0).sum()) == 0 and int((dh[mk] != 0).sum()) == 0
 
 
 def test_fused_matches_the_two_calls(torch_cuda):
