@@ -104,7 +104,7 @@ struct Plan {
   // work ids per chunk, split capacity per chunk, partials and target c'
   bool fused;
   int fus_blocks, fus_max_splits, mass_ld;
-  size_t o_fpart, o_tdc, o_smass, fus_bytes;
+  size_t o_fpart, o_tdc, fus_bytes;
   // cce_forward_backward without the single pass: the forward's partials
   // after the backward's buffers (the backward tile merges them itself)
   size_t o_ppart, twopass_bytes;
@@ -237,12 +237,10 @@ Plan make_plan(const cce_head *hd, int64_t M) {
                                ((int64_t)64 << 20) / 16 / p.M_pad / p.nchunks));
     p.mass_ld = 2 * p.fus_max_splits * p.nchunks;
   }
-  // the target's c' and (fused pass) non-target sum per compacted row, then
-  // the partials: the fused pass's [slot][M_pad] (max, sum) pairs, or the
-  // backward's [M_pad][mass_ld] non-target mass
+  // the target's c' per compacted row, then the partials: the fused pass's
+  // [slot][M_pad] (max, sum) pairs, or the backward's [M_pad][mass_ld]
+  // non-target mass
   p.o_tdc = o;
-  o = align_up(o + sizeof(float) * p.M_pad, 256);
-  p.o_smass = o;
   o = align_up(o + sizeof(float) * p.M_pad, 256);
   p.o_fpart = o;
   p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
@@ -411,7 +409,7 @@ cce_status run_forward(const cce_head *head, const void *h, int64_t M, const int
   CCE_LAUNCH("tile_fwd", st, launch_tile(st, p.bits, PASS_FWD, grid, a));
   CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.tiles, p.tiles, p.max_splits, (int)p.M_pad,
                                        ws_at<const int>(workspace, p.o_inv), a.cnt,
-                                       ws_at<const TokRec>(workspace, p.o_tok), 0.0f, nullptr, logp, lse));
+                                       ws_at<const TokRec>(workspace, p.o_tok), logp, lse));
   if (block_max && mask)
     CCE_LAUNCH("bmx_mask", st, launch_bmx_mask(st, (int)M, p.tiles, ws_at<const int>(workspace, p.o_inv), block_max));
   return hip_status();
@@ -534,16 +532,18 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                ReduceTarget{a.tmass, a.mass, a.mass_ld, a.nblocks, a.full_tiles,
-                                                            p.tiles, a.max_splits, nullptr, 0.0f, a.tdc}));
+                                                            p.tiles, a.max_splits, nullptr, 0, 0.0f, a.tdc,
+                                                            nullptr, nullptr}));
   return hip_status();
 }
 
 // The single pass (PASS_FUSED) for a quantized head with 0 < softcap <=
 // CAP_FIXED_REF_MAX and a known g: per coefficient chunk, the logit tile
 // writes its forward partials and the unnormalized coefficients, and the dh
-// contraction consumes the chunk; then the merge (lse, logp) and the split
-// reduce, which scales the slabs by g e^{cap - lse} and adds the target's
-// term.  No logit is computed twice.
+// contraction consumes the chunk; then the split reduce, which also takes
+// the place of the merge: it sums each token's split sums into lse and logp,
+// scales the slabs by g e^{cap - lse} and adds the target's term.  No logit
+// is computed twice.
 cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                      const uint8_t *mask, const float *g, float *logp, float *lse, void *dh, int32_t dh_dtype,
                      void *workspace, hipStream_t st) {
@@ -596,10 +596,8 @@ cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t
   }
   const int *inv = ws_at<const int>(workspace, p.o_inv);
   const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
-  float *smass = ws_at<float>(workspace, p.o_smass);
-  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits,
-                                       (int)p.M_pad, inv, a.cnt, tok, p.cap, smass, logp, lse));
-  const ReduceTarget rt{2, nullptr, 0, 0, 0, 0, 0, smass, p.cap, a.tdc};
+  const ReduceTarget rt{2, nullptr, 0, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, a.part, (int)p.M_pad,
+                        p.cap, a.tdc, logp, lse};
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                rt));
   return hip_status();
@@ -683,7 +681,7 @@ cce_status run_twopass(const Plan &p, const cce_head *head, const void *h, int64
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                ReduceTarget{1, b.mass, b.mass_ld, b.nblocks, b.full_tiles, p.tiles,
-                                                            b.max_splits, nullptr, 0.0f, b.tdc}));
+                                                            b.max_splits, nullptr, 0, 0.0f, b.tdc, nullptr, nullptr}));
   return hip_status();
 }
 

@@ -361,11 +361,8 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
                  const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl);
 void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *bmx);
-// fused_cap > 0: the fused pass's partials leave the target's column out;
-// the merge adds its e^{y_t - cap} and writes their sum S to smass[r]
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
-                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float fused_cap, float *smass,
-                  float *logp, float *lse);
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 // How the split reduce forms the target's term g (1 - p_t) c'_t w_t.
 //  mode 0: tval is the whole coefficient (the tile used -expm1(y_t - lse));
@@ -378,10 +375,12 @@ struct ReduceTarget {
   int mode;
   const float *mass;   // mode 1: [M_pad][mass_ld] the backward splits' non-target mass
   int mass_ld;
-  int nblocks, full_tiles, tiles, max_splits;  // mode 1: the tile launches' split plan (vsplit_total)
-  const float *smass;  // mode 2: [M_pad] S, written by the merge
+  int nblocks, full_tiles, tiles, max_splits;  // modes 1, 2: the tile launches' split plan (vsplit_total)
+  const float *part;   // mode 2: the single pass's partials [split][M_pad][2]: (cap, sum of e over the split)
+  int M_pad;
   float cap;
   const float *tdc;    // [M_pad] c' of the target
+  float *logp, *lse;   // mode 2: the outputs of the forward (the single pass has no merge launch)
 };
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16, const ReduceTarget &rt);

@@ -123,6 +123,122 @@ __device__ __forceinline__ void bias_digits(float bp, float inv, uint32_t &d2b, 
   d0b = (uint32_t)(d0 + 128);
 }
 
+// The digits of groups 4j .. 4j + 3 of one row, b' taken from bp(k), into
+// the row's six columns parts (three per half of the bias block).
+template <typename BP>
+__device__ __forceinline__ void put_digits4(uint8_t *row, int j, int Gq, int P, float inv, BP bp) {
+  uint32_t w2 = 0, w1 = 0, w0 = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t d2b, d1b, d0b;
+    bias_digits(bp(k), inv, d2b, d1b, d0b);
+    w2 |= d2b << (8 * k);
+    w1 |= d1b << (8 * k);
+    w0 |= d0b << (8 * k);
+  }
+  *(uint32_t *)(row + 4 * j) = w2;               // refinement: d2 x 65536 S3
+  *(uint32_t *)(row + Gq + 4 * j) = w1;          //             d1 x 256 S2
+  *(uint32_t *)(row + 2 * Gq + 4 * j) = w0;      //             d0 x S1
+  *(uint32_t *)(row + P + 4 * j) = w2;           // coarse:     d2 x 65536 S1
+  *(uint32_t *)(row + P + Gq + 4 * j) = w2;      //             d2 x 65536 S2
+  *(uint32_t *)(row + P + 2 * Gq + 4 * j) = w1;  //             d1 x 256 S1
+}
+
+// Rows of at most HP_COLS groups, a multiple of 4 (and operands aligned for
+// 4-element loads): the block's scales and biases are loaded once, all loads
+// issued together (the block's elements are contiguous), into registers.  b'
+// is staged in LDS for the row maxima and the digits, then the scales for
+// the ratio table: one memory round trip instead of one per pass.
+__device__ void head_prep_staged(int64_t blk, const FrontArgs &f, float shift, float *su, float *sT) {
+  const int64_t V = f.V;
+  const int Gq = f.Gq, Kb = f.Kb, NB = f.NB, P = f.P, sbt = f.sbt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t v0 = blk * HP_ROWS;
+  const int rows = (int)(V - v0 < HP_ROWS ? V - v0 : HP_ROWS);
+  unsigned *smax = reinterpret_cast<unsigned *>(su);
+  const int64_t e0 = v0 * Gq;
+  const int n = rows * Gq;  // a multiple of 4
+  constexpr int IT = HP_ROWS * HP_COLS / 1024;  // 4-element slots per thread
+  float sc[IT][4], bp[IT][4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = 4 * (tid + 256 * it);
+    if (i < n) {
+      float bi[4];
+      ld_sb4(f.scales, e0 + i, sbt, sc[it]);
+      ld_sb4(f.biases, e0 + i, sbt, bi);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bp[it][k] = fmaf(shift, sc[it][k], bi[k]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = 4 * (tid + 256 * it);
+    if (i < n) {
+      const int r = i / Gq, gi = i - r * Gq;  // the four share a row (Gq % 4 == 0)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sT[r * HP_LD + gi + k] = bp[it][k];
+    }
+  }
+  __syncthreads();
+  {
+    // four threads per row: its max |b'| (a shuffle reduction), then its
+    // digits, 4 groups at a time
+    const int r = tid >> 2, qd = tid & 3, G4 = Gq >> 2;
+    float m = 0.0f;
+    if (r < rows)
+      for (int gi = qd; gi < Gq; gi += 4) m = fmaxf(m, fabsf(sT[r * HP_LD + gi]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    if (r < rows) {
+      if (qd == 0) smax[r] = __float_as_uint(m);
+      const float u = bias_unit(m);
+      const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
+      uint8_t *row = f.baug + (v0 + r) * Kb;
+      const float *br = sT + r * HP_LD;
+      for (int j = qd; j < G4; j += 4) put_digits4(row, j, Gq, P, inv, [&](int k) { return br[4 * j + k]; });
+      for (int o = 3 * Gq + 4 * qd; o < P; o += 16) {
+        *(uint32_t *)(row + o) = 0x80808080u;
+        *(uint32_t *)(row + P + o) = 0x80808080u;
+      }
+    }
+  }
+  __syncthreads();  // b' reads done, smax written
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = 4 * (tid + 256 * it);
+    if (i < n) {
+      const int r = i / Gq, gi = i - r * Gq;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sT[r * HP_LD + gi + k] = sc[it][k];
+    }
+  }
+  __syncthreads();
+  const int64_t v = v0 + lane;
+  if (wave == 0) {  // the block's largest |b'| (0: every digit of its rows is zero)
+    unsigned mb = lane < rows ? smax[lane] : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (unsigned)__shfl_xor((int)mb, o, 64));
+    if (lane == 0) f.bmxb[blk] = mb;
+  }
+  if (lane < rows) {
+    if (wave == 0)
+      for (int s2 = 0; s2 < NB; ++s2) f.rt[s2 * V + v] = 1.0f;
+    // group g's entry ratio s_{g-1} / s_g (the bias block's unit before group 0)
+    for (int g = wave; g < Gq; g += 4) {
+      const float prev = g > 0 ? sT[lane * HP_LD + g - 1] : bias_unit(__uint_as_float(smax[lane]));
+      const float e = scale_eff(prev) / scale_eff(sT[lane * HP_LD + g]);
+      if (f.gs == 128) {
+        f.rt[(int64_t)(NB + 2 * g) * V + v] = e;
+        f.rt[(int64_t)(NB + 2 * g + 1) * V + v] = 1.0f;
+      } else {
+        f.rt[(int64_t)(NB + g) * V + v] = e;
+      }
+    }
+    if (wave == 1) f.slast[v] = scale_eff(sT[lane * HP_LD + Gq - 1]);
+  }
+}
+
 __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, float *su, float *sT) {
   const int64_t V = f.V;
   const int Gq = f.Gq, Kb = f.Kb, NB = f.NB, P = f.P, sbt = f.sbt;
@@ -133,6 +249,10 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
   float *sprev = su + HP_ROWS;
   const int64_t e0 = v0 * Gq;  // first (row, group) element of the block
   const uintptr_t al = sbt == SB_F32 ? 15 : 7;
+  if ((Gq & 3) == 0 && (((uintptr_t)f.scales | (uintptr_t)f.biases) & al) == 0 && Gq <= HP_COLS) {
+    head_prep_staged(blk, f, shift, su, sT);
+    return;
+  }
   if ((Gq & 3) == 0 && (((uintptr_t)f.scales | (uintptr_t)f.biases) & al) == 0) {
     const int r = tid >> 2, qd = tid & 3, G4 = Gq >> 2;
     const int64_t er = e0 + (int64_t)r * Gq;  // first element of row r
@@ -156,21 +276,7 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
         float sc[4], bi[4];
         ld_sb4(f.scales, er + 4 * j, sbt, sc);
         ld_sb4(f.biases, er + 4 * j, sbt, bi);
-        uint32_t w2 = 0, w1 = 0, w0 = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t d2b, d1b, d0b;
-          bias_digits(fmaf(shift, sc[k], bi[k]), inv, d2b, d1b, d0b);
-          w2 |= d2b << (8 * k);
-          w1 |= d1b << (8 * k);
-          w0 |= d0b << (8 * k);
-        }
-        *(uint32_t *)(row + 4 * j) = w2;               // refinement: d2 x 65536 S3
-        *(uint32_t *)(row + Gq + 4 * j) = w1;          //             d1 x 256 S2
-        *(uint32_t *)(row + 2 * Gq + 4 * j) = w0;      //             d0 x S1
-        *(uint32_t *)(row + P + 4 * j) = w2;           // coarse:     d2 x 65536 S1
-        *(uint32_t *)(row + P + Gq + 4 * j) = w2;      //             d2 x 65536 S2
-        *(uint32_t *)(row + P + 2 * Gq + 4 * j) = w1;  //             d1 x 256 S1
+        put_digits4(row, j, Gq, P, inv, [&](int k) { return fmaf(shift, sc[k], bi[k]); });
       }
       for (int o = 3 * Gq + 4 * qd; o < P; o += 16) {
         *(uint32_t *)(row + o) = 0x80808080u;
@@ -379,8 +485,7 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
 // few supervised tokens carry hundreds of splits.
 __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int full_tiles, int tiles,
                                                int max_splits, int M_pad, const int *inv, const int *cnt,
-                                               const TokRec *tok, float fused_cap, float *smass, int M,
-                                               float *logp, float *lse) {
+                                               const TokRec *tok, int M, float *logp, float *lse) {
   // two partials (vocabulary halves of the tile) per split, over every chunk
   // of the vocabulary the forward's launches covered
   const int nsplit = 2 * vsplit_total(nblocks, active_tiles(cnt), full_tiles, tiles, max_splits);
@@ -409,11 +514,6 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, i
     return;
   }
   const TokRec rec = tok[r];
-  // the fused pass's partials leave the target's column out (mx = cap there)
-  if (fused_cap > 0.0f) {
-    smass[r] = se;
-    if (rec.tgt >= 0) se += expf(rec.tval - mx);
-  }
   const float l = mx + logf(se);
   lse[t] = l;
   logp[t] = rec.tval - l;
@@ -482,18 +582,36 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
   const int H = a.H;
   const int r = inv[t];
   const int act = active_tiles(a.cnt);
-  // mode 1: the token's non-target mass, its splits' contiguous run summed
-  // by the workgroup in a fixed order (every thread takes part)
+  // mode 1: the token's non-target mass over the backward's splits; mode 2:
+  // S, the sum of e = e^{y - cap} over the non-target columns, from the
+  // single pass's split sums.  Summed by the workgroup in a fixed order
+  // (every thread takes part).
   float S = 0.0f;
-  if (tg.mode == 1 && r >= 0) {
+  if (tg.mode != 0 && r >= 0) {
     __shared__ float sS[4];
     const int ns = 2 * vsplit_total(tg.nblocks, act, tg.full_tiles, tg.tiles, tg.max_splits);
     float x = 0.0f;
-    for (int k = threadIdx.x; k < ns; k += 256) x += tg.mass[(size_t)r * tg.mass_ld + k];
+    if (tg.mode == 1)
+      for (int k = threadIdx.x; k < ns; k += 256) x += tg.mass[(size_t)r * tg.mass_ld + k];
+    else
+      for (int k = threadIdx.x; k < ns; k += 256) x += tg.part[((size_t)k * tg.M_pad + r) * 2 + 1];
     x = wave_sum(x);
     if ((threadIdx.x & 63) == 0) sS[threadIdx.x >> 6] = x;
     __syncthreads();
     S = (sS[0] + sS[1]) + (sS[2] + sS[3]);
+  }
+  // mode 2 also finishes the forward, in place of a merge launch: with the
+  // fixed reference, lse = cap + log(S + e_t) and logp = y_t - lse (the
+  // target's e_t from the logit its tile captured); masked tokens get zeros
+  if (tg.mode == 2 && blockIdx.y == 0 && threadIdx.x == 0) {
+    float l = 0.0f, lp = 0.0f;
+    if (r >= 0) {
+      const TokRec rec = tok[r];
+      l = tg.cap + logf(S + (rec.tgt >= 0 ? expf(rec.tval - tg.cap) : 0.0f));
+      lp = rec.tval - l;
+    }
+    tg.lse[t] = l;
+    tg.logp[t] = lp;
   }
   if (d >= H) return;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -506,8 +624,7 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     if (tg.mode == 1) {
       rec.tval = ht ? rec.g * S * tg.tdc[r] : 0.0f;
     } else if (tg.mode == 2) {
-      // fused: p_v = e_v / (S + e_t), the slabs sum -e c' w
-      S = tg.smass[r];
+      // single pass: p_v = e_v / (S + e_t), the slabs sum -e c' w
       const float et = ht ? expf(rec.tval - tg.cap) : 0.0f;
       const float inv_tot = 1.0f / (S + et);
       acc *= rec.g * inv_tot;
@@ -569,10 +686,9 @@ void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
 }
 
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
-                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float fused_cap, float *smass,
-                  float *logp, float *lse) {
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, part, nblocks, full_tiles, tiles,
-                     max_splits, M_pad, inv, cnt, tok, fused_cap, smass, M, logp, lse);
+                     max_splits, M_pad, inv, cnt, tok, M, logp, lse);
 }
 
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,

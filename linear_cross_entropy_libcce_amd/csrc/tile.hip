@@ -400,6 +400,17 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             }
             if (ks < NKS - 1) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KW);
           }
+          // Left free, the compiler hoists the whole fold (128 multiplies)
+          // above the first MFMA, and the matrix pipe idles while both waves
+          // of a SIMD fold.  Pinned here: column block c's fold, then its two
+          // MFMAs (measured 0.5-1.6% faster, except the capped forward).
+          if (ks == 0 && !DENSE && MODE != MODE_FWD_CAP) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // VALU: the fold of acc[0..1][c]
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            }
+          }
           hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
           hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
         }
