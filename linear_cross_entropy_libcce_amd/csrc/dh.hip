@@ -208,6 +208,12 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float sSB[2][SB_SLOT];
   __shared__ uint16_t sList[SKIP ? MAX_LIST : 1];
   __shared__ int sCount[SKIP ? 9 : 1];
+  // small M: the eight waves multiply the same coefficient rows, so the
+  // step's coefficient operand (2 row blocks x 4 k-steps = 8 fragments of 1
+  // KiB) is loaded once per workgroup, one fragment per wave, and shared
+  // through LDS (double buffered like the head tile) instead of eight times
+  // from L1.
+  __shared__ __attribute__((aligned(16))) u32x4_t sCA[SMALL ? 2 : 1][SMALL ? 8 * 64 : 1];
 
   if (SKIP) {
     // flagged tiles of [step0 / 4, (step0 + nsteps) / 4), compacted in order:
@@ -290,10 +296,14 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.load(a, vrow(1), P1);
     pr.stage_sb(P0, sSB[0], a.sbt);
     pr.stage_sb(P1, sSB[1], a.sbt);
+    if (SMALL) {
+      sCA[0][wave * 64 + lane] = buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, koff(0));
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, koff(0)));
-      cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, koff(0)));
+      for (int ks = 0; ks < 4; ++ks) {
+        cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, koff(0)));
+        cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, koff(0)));
+      }
     }
     __syncthreads();
     pr.read_sb(sSB[0], sc, bi);
@@ -306,10 +316,22 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     // load step st + 2 into `nxt` and stage its scales in slot st & 1.
     auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &nxt) {
       const int cb = st & 1;
+      const int knext = koff(st + 1 < nsteps ? st + 1 : st);
+      // small M: this wave's coefficient fragment of the next step is loaded
+      // before the head loads, so that waiting for it (at the step's end) does
+      // not wait for them too (loads complete in issue order for s_waitcnt)
+      u32x4_t cfrag;
+      if (SMALL) cfrag = buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, knext);
       pr.load(a, vrow(st + 2), nxt);  // past the split: valid rows or zeros, never used
       pr.read_sb(sSB[cb ^ 1], sc, bi);
       const uint16_t *sw = sB[cb];
-      const int knext = koff(st + 1 < nsteps ? st + 1 : st);
+      if (SMALL) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          cA[0][ks] = __builtin_bit_cast(bf16x8_t, sCA[cb][ks * 64 + lane]);
+          cA[1][ks] = __builtin_bit_cast(bf16x8_t, sCA[cb][(4 + ks) * 64 + lane]);
+        }
+      }
       bf16x8_t bq[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) bq[c] = *(const bf16x8_t *)(sw + boff[0] + c * 32 * KSTP);
@@ -323,13 +345,16 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTP);
           }
-          cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
-          cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));
+          if (!SMALL) {
+            cA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + ks * 1024, knext));
+            cA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rc, cv0 + cstride + ks * 1024, knext));
+          }
         }
         pr.store(ks, cur, sc, bi, sB[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.stage_sb(nxt, sSB[cb], a.sbt);
+      if (SMALL) sCA[cb ^ 1][wave * 64 + lane] = cfrag;  // read after the barrier
       __syncthreads();
     };
     int st = 0;

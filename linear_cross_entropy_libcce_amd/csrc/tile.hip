@@ -253,6 +253,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   // in a register the whole step loop would carry)
   __shared__ float sRun[COEF ? 8 : 1][64];
   if (COEF) sRun[wave][lane] = 0.0f;
+  // small M: the eight waves multiply the same token rows, so the step's
+  // token operand (2 row blocks x 4 k-steps = 8 fragments of 1 KiB) is loaded
+  // once per workgroup, one fragment per wave, and shared through LDS (double
+  // buffered like the code tile) instead of eight times from L1.
+  __shared__ __attribute__((aligned(16))) u32x4_t sH[SMALL ? 2 : 1][SMALL ? 8 * 64 : 1];
 
   const int tok0 = tt * BM + tg * 64;
   const int vcol0 = SMALL ? wave * 32 : vh * 128;  // this wave's first vocabulary row within the tile
@@ -361,10 +366,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
       for (int part = 0; part < NKS; ++part) pr.store(s0 < a.NB, part, P0, sW[0]);
       pr.ratio(P0, sR[0]);
+      if (SMALL) {
+        sH[0][wave * 64 + lane] = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s0 * NKS * 1024);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, s0 * NKS * 1024));
-        hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, s0 * NKS * 1024));
+        for (int ks = 0; ks < NKS; ++ks) {
+          hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, s0 * NKS * 1024));
+          hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, s0 * NKS * 1024));
+        }
       }
       __syncthreads();
     }
@@ -374,13 +383,25 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     // the step after next (into `nxt`) issued first.
     auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt) {
       const bool sbias = sn < a.NB;
+      const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
+      // small M: this wave's token fragment of the next step is loaded before
+      // the head loads, so that waiting for it (at the step's end) does not
+      // wait for them too (loads complete in issue order for s_waitcnt)
+      u32x4_t hfrag;
+      if (SMALL) hfrag = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, hnext);
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[NC];
       if (!DENSE)
 #pragma unroll
         for (int c = 0; c < NC; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
-      const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
+      if (SMALL) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          hA[0][ks] = __builtin_bit_cast(bf16x8_t, sH[cb][ks * 64 + lane]);
+          hA[1][ks] = __builtin_bit_cast(bf16x8_t, sH[cb][(4 + ks) * 64 + lane]);
+        }
+      }
       // B operand of column block c for k-step ks + 1 is read as soon as its
       // two MFMAs of k-step ks are issued; a scheduling barrier after each
       // k-step keeps this order (left free, the compiler hoists every LDS read
@@ -411,13 +432,16 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
             }
           }
-          hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
-          hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
+          if (!SMALL) {
+            hA[0][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + ks * 1024, hnext));
+            hA[1][ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, hv0 + hstride + ks * 1024, hnext));
+          }
         }
         pr.store(sbias, ks, cur, sW[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.ratio(cur, sR[cb ^ 1]);
+      if (SMALL) sH[cb ^ 1][wave * 64 + lane] = hfrag;  // read after the step's barrier
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
