@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.wcol = (d0 + 4 * pr.dc) * BITS / 8;
     pr.tid = tid;
     pr.gq0 = d0 / a.gs;
-    DhRegs<BITS> P0, P1;
+    DhRegs<BITS> P0, P1, P2;
     // this lane's B-operand chunk offsets (row col0 + l32 + 32c, chunk 2ks + lh);
     // the swizzle key of row d + 32c equals that of row d
     int boff[4];
@@ -292,12 +292,20 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     // K offset (bytes) of step i in the fragment-major chunk
     auto koff = [&](int i) { return cstep(i) * 4 * 1024; };
 
+    // the coefficient fragment this wave stages for step i (small M)
+    auto cfrag_load = [&](int i) {
+      return buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, koff(i < nsteps ? i : nsteps - 1));
+    };
+    u32x4_t C0, C1, C2;  // small M: staged fragments of three steps, as P0..P2
     pr.load(a, vrow(0), P0);
     pr.load(a, vrow(1), P1);
+    if (SMALL) pr.load(a, vrow(2), P2);
     pr.stage_sb(P0, sSB[0], a.sbt);
     pr.stage_sb(P1, sSB[1], a.sbt);
     if (SMALL) {
-      sCA[0][wave * 64 + lane] = buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, koff(0));
+      sCA[0][wave * 64 + lane] = cfrag_load(0);
+      C1 = cfrag_load(1);
+      C2 = cfrag_load(2);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -313,16 +321,18 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 
     // Step st: MFMAs on buffer st & 1; dequantize step st + 1 (words in `cur`,
     // scales in LDS slot (st + 1) & 1) into the other buffer between them;
-    // load step st + 2 into `nxt` and stage its scales in slot st & 1.
-    auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &nxt) {
+    // load step st + LA into `nxt` and stage the scales of step st + 2 (`mid`
+    // for small M, else `nxt`) in slot st & 1.  Small M loads its head words
+    // three steps ahead (LA = 3, register sets P0..P2 in turn) and its
+    // coefficient fragments likewise: a step is short there, and one step of
+    // cover left both loads waited for.  The fragment is loaded before the
+    // head words (loads complete in issue order for s_waitcnt).
+    auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &mid, DhRegs<BITS> &nxt, u32x4_t &cfc,
+                       u32x4_t &cfn) {
       const int cb = st & 1;
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
-      // small M: this wave's coefficient fragment of the next step is loaded
-      // before the head loads, so that waiting for it (at the step's end) does
-      // not wait for them too (loads complete in issue order for s_waitcnt)
-      u32x4_t cfrag;
-      if (SMALL) cfrag = buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, knext);
-      pr.load(a, vrow(st + 2), nxt);  // past the split: valid rows or zeros, never used
+      if (SMALL) cfn = cfrag_load(st + 3);
+      pr.load(a, vrow(st + (SMALL ? 3 : 2)), nxt);  // past the split: valid rows or zeros, never used
       pr.read_sb(sSB[cb ^ 1], sc, bi);
       const uint16_t *sw = sB[cb];
       if (SMALL) {
@@ -353,16 +363,26 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
         pr.store(ks, cur, sc, bi, sB[cb ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pr.stage_sb(nxt, sSB[cb], a.sbt);
-      if (SMALL) sCA[cb ^ 1][wave * 64 + lane] = cfrag;  // read after the barrier
+      pr.stage_sb(SMALL ? mid : nxt, sSB[cb], a.sbt);
+      if (SMALL) sCA[cb ^ 1][wave * 64 + lane] = cfc;  // step st + 1's: read after the barrier
       __syncthreads();
     };
     int st = 0;
-    for (; st + 1 < nsteps; st += 2) {
-      do_step(st, P1, P0);
-      do_step(st + 1, P0, P1);
+    if constexpr (SMALL) {
+      for (; st + 2 < nsteps; st += 3) {
+        do_step(st, P1, P2, P0, C1, C0);
+        do_step(st + 1, P2, P0, P1, C2, C1);
+        do_step(st + 2, P0, P1, P2, C0, C2);
+      }
+      if (st < nsteps) do_step(st, P1, P2, P0, C1, C0);
+      if (st + 1 < nsteps) do_step(st + 1, P2, P0, P1, C2, C1);
+    } else {
+      for (; st + 1 < nsteps; st += 2) {
+        do_step(st, P1, P0, P0, C0, C0);
+        do_step(st + 1, P0, P1, P1, C0, C0);
+      }
+      if (st < nsteps) do_step(st, P1, P0, P0, C0, C0);
     }
-    if (st < nsteps) do_step(st, P1, P0);
   } else if (a.accumulate) {
     return;
   }

@@ -341,7 +341,13 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     pr.row0 = wave * 32 + (lane >> 2);
     pr.q = lane & 3;
     pr.tid = tid;
-    ProdRegs P0, P1;
+    // Head words are loaded LA steps ahead into register sets used in turn:
+    // two steps (P0, P1), or three for small M (P2 too), whose steps are
+    // short enough that one step of cover left the loads waited for; small M
+    // stages its token fragments three steps ahead alike (H0..H2).
+    constexpr int LA = SMALL ? 3 : 2;
+    ProdRegs P0, P1, P2;
+    u32x4_t H0, H1, H2;
     // this lane's B-operand chunk offsets (row vcol0 + l32 + 32c, chunk 2ks + lh)
     int boff[NKS];
 #pragma unroll
@@ -349,10 +355,10 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     f32x16_t acc[2][NC];
     bf16x8_t hA[2][NKS];
 
-    // step `n` (<= steps) steps after (tile, st)
+    // step `n` steps after (tile, st)
     auto coords = [&](int tile, int st, int n, int64_t &v0, int &step) {
       int s2 = st + n, t2 = tile;
-      if (s2 >= steps) { s2 -= steps; t2 = next_tile(tile); }
+      while (s2 >= steps) { s2 -= steps; t2 = next_tile(t2); }
       v0 = (int64_t)(a.range_tile0 + t2) * BNT;
       step = s0 + s2;
     };
@@ -363,6 +369,13 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       coords(first_tile, 0, 1, v1, s1);
       pr.load(a, v0, s0, P0);
       pr.load(a, v1, s1, P1);
+      if (SMALL) {
+        int64_t v2; int s2;
+        coords(first_tile, 0, 2, v2, s2);
+        pr.load(a, v2, s2, P2);
+        H1 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s1 * NKS * 1024);
+        H2 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s2 * NKS * 1024);
+      }
 #pragma unroll
       for (int part = 0; part < NKS; ++part) pr.store(s0 < a.NB, part, P0, sW[0]);
       pr.ratio(P0, sR[0]);
@@ -381,14 +394,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     // The MFMA work of one step on LDS buffer cb, with the producer slices of
     // the next step (words in `cur`) placed between the MFMAs and the loads of
     // the step after next (into `nxt`) issued first.
-    auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt) {
+    auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt, u32x4_t &hcur,
+                         u32x4_t &hnxt) {
       const bool sbias = sn < a.NB;
       const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
-      // small M: this wave's token fragment of the next step is loaded before
-      // the head loads, so that waiting for it (at the step's end) does not
-      // wait for them too (loads complete in issue order for s_waitcnt)
-      u32x4_t hfrag;
-      if (SMALL) hfrag = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, hnext);
+      // small M: this wave's token fragment of step + LA is loaded before the
+      // head words, so that waiting for it does not wait for them too (loads
+      // complete in issue order for s_waitcnt)
+      if (SMALL) hnxt = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, snn * NKS * 1024);
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[NC];
@@ -441,7 +454,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.ratio(cur, sR[cb ^ 1]);
-      if (SMALL) sH[cb ^ 1][wave * 64 + lane] = hfrag;  // read after the step's barrier
+      if (SMALL) sH[cb ^ 1][wave * 64 + lane] = hcur;  // step + 1's: read after the step's barrier
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
@@ -661,11 +674,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 
     // One step: MFMAs on buffer idx & 1, then the tile's epilogue after its
     // last step.
-    auto do_step = [&](int idx, int tile, int st, ProdRegs &cur, ProdRegs &nxt) {
+    auto do_step = [&](int idx, int tile, int st, ProdRegs &cur, ProdRegs &nxt, u32x4_t &hcur, u32x4_t &hnxt) {
       int64_t vn, vnn;
       int sn, snn;
-      coords(tile, st, 1, vn, sn);    // next step: unpacked now
-      coords(tile, st, 2, vnn, snn);  // step after next: loaded now
+      coords(tile, st, 1, vn, sn);     // next step: unpacked now
+      coords(tile, st, LA, vnn, snn);  // loaded now
       if (st == 0) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -674,7 +687,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
-      mfma_step(idx & 1, sn, vnn, snn, cur, nxt);
+      mfma_step(idx & 1, sn, vnn, snn, cur, nxt, hcur, hnxt);
       if (st == steps - 1) epilogue(tile);
       __syncthreads();
       if (EXTRA && st == steps - 1) tile_extra(tile);
@@ -685,13 +698,30 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       if (++st == steps) { st = 0; tile = next_tile(tile); }
     };
     int idx = 0;
-    for (; idx + 1 < total; idx += 2) {
-      do_step(idx, tile, st, P1, P0);
-      advance();
-      do_step(idx + 1, tile, st, P0, P1);
-      advance();
+    if constexpr (SMALL) {
+      // step i unpacks set (i + 1) % 3 and loads step i + 3 into set i % 3
+      for (; idx + 2 < total; idx += 3) {
+        do_step(idx, tile, st, P1, P0, H1, H0);
+        advance();
+        do_step(idx + 1, tile, st, P2, P1, H2, H1);
+        advance();
+        do_step(idx + 2, tile, st, P0, P2, H0, H2);
+        advance();
+      }
+      if (idx < total) do_step(idx, tile, st, P1, P0, H1, H0);
+      if (idx + 1 < total) {
+        advance();
+        do_step(idx + 1, tile, st, P2, P1, H2, H1);
+      }
+    } else {
+      for (; idx + 1 < total; idx += 2) {
+        do_step(idx, tile, st, P1, P0, H0, H0);
+        advance();
+        do_step(idx + 1, tile, st, P0, P1, H0, H0);
+        advance();
+      }
+      if (idx < total) do_step(idx, tile, st, P1, P0, H0, H0);
     }
-    if (idx < total) do_step(idx, tile, st, P1, P0);
   }
 
   // partials: (max, sum-exp) of the forward passes, [slot][M_pad] pairs; the
