@@ -237,13 +237,12 @@ Plan make_plan(const cce_head *hd, int64_t M) {
                                ((int64_t)64 << 20) / 16 / p.M_pad / p.nchunks));
     p.mass_ld = 2 * p.fus_max_splits * p.nchunks;
   }
-  // the target's c' per compacted row, then the partials: the fused pass's
-  // [slot][M_pad] (max, sum) pairs, or the backward's [M_pad][mass_ld]
-  // non-target mass
+  // the target's c' per compacted row, then the [M_pad][mass_ld] split sums:
+  // the backward's non-target mass or the single pass's non-target sum of e
   p.o_tdc = o;
   o = align_up(o + sizeof(float) * p.M_pad, 256);
   p.o_fpart = o;
-  p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
+  p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * (size_t)p.mass_ld * p.M_pad, 256);
   p.o_ppart = p.bwd_bytes;
   p.twopass_bytes = align_up(p.o_ppart + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
   if (dense) {
@@ -532,8 +531,7 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                ReduceTarget{a.tmass, a.mass, a.mass_ld, a.nblocks, a.full_tiles,
-                                                            p.tiles, a.max_splits, nullptr, 0, 0.0f, a.tdc,
-                                                            nullptr, nullptr}));
+                                                            p.tiles, a.max_splits, 0.0f, a.tdc, nullptr, nullptr}));
   return hip_status();
 }
 
@@ -549,7 +547,8 @@ cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t
                      void *workspace, hipStream_t st) {
   enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false);
   TileArgs a = tile_args(p, head, workspace);
-  a.part = ws_at<float>(workspace, p.o_fpart);
+  a.mass = ws_at<float>(workspace, p.o_fpart);
+  a.mass_ld = p.mass_ld;
   a.coeff = ws_at<uint16_t>(workspace, p.o_coeff);
   a.ld_coeff = p.ld_coeff;
   a.tdc = ws_at<float>(workspace, p.o_tdc);
@@ -596,8 +595,8 @@ cce_status run_fused(const Plan &p, const cce_head *head, const void *h, int64_t
   }
   const int *inv = ws_at<const int>(workspace, p.o_inv);
   const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
-  const ReduceTarget rt{2, nullptr, 0, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, a.part, (int)p.M_pad,
-                        p.cap, a.tdc, logp, lse};
+  const ReduceTarget rt{2, a.mass, a.mass_ld, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, p.cap, a.tdc,
+                        logp, lse};
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                rt));
   return hip_status();
@@ -681,7 +680,7 @@ cce_status run_twopass(const Plan &p, const cce_head *head, const void *h, int64
                                                ws_at<const TokRec>(workspace, p.o_tok), dh,
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                ReduceTarget{1, b.mass, b.mass_ld, b.nblocks, b.full_tiles, p.tiles,
-                                                            b.max_splits, nullptr, 0, 0.0f, b.tdc, nullptr, nullptr}));
+                                                            b.max_splits, 0.0f, b.tdc, nullptr, nullptr}));
   return hip_status();
 }
 

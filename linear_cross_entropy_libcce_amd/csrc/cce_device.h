@@ -159,7 +159,7 @@ struct TileArgs {
   // 1 - p_t = -expm1(y_t - lse) (the skips, and a dense head, whose dW takes
   // the coefficient chunk by chunk)
   int tmass;
-  float *mass;           // backward with tmass: [M_pad][mass_ld] non-target mass of each split
+  float *mass;           // backward with tmass, single pass: [M_pad][mass_ld] non-target mass (sum) of each split
   int mass_ld;
   // backward of cce_forward_backward without a softcap reference: each lane
   // forms its token's lse from the forward's partials (fpart, the forward
@@ -373,11 +373,12 @@ void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 //          g / (S + e_t) and 1 - p_t = S / (S + e_t).
 struct ReduceTarget {
   int mode;
-  const float *mass;   // mode 1: [M_pad][mass_ld] the backward splits' non-target mass
+  // [M_pad][mass_ld], per split of the tile launches: mode 1 the backward's
+  // non-target mass, mode 2 the single pass's sum of e = e^{y - cap} over the
+  // non-target columns
+  const float *mass;
   int mass_ld;
-  int nblocks, full_tiles, tiles, max_splits;  // modes 1, 2: the tile launches' split plan (vsplit_total)
-  const float *part;   // mode 2: the single pass's partials [split][M_pad][2]: (cap, sum of e over the split)
-  int M_pad;
+  int nblocks, full_tiles, tiles, max_splits;  // the tile launches' split plan (vsplit_total)
   float cap;
   const float *tdc;    // [M_pad] c' of the target
   float *logp, *lse;   // mode 2: the outputs of the forward (the single pass has no merge launch)

@@ -584,17 +584,14 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
   const int act = active_tiles(a.cnt);
   // mode 1: the token's non-target mass over the backward's splits; mode 2:
   // S, the sum of e = e^{y - cap} over the non-target columns, from the
-  // single pass's split sums.  Summed by the workgroup in a fixed order
-  // (every thread takes part).
+  // single pass's split sums.  The token's contiguous run, summed by the
+  // workgroup in a fixed order (every thread takes part).
   float S = 0.0f;
   if (tg.mode != 0 && r >= 0) {
     __shared__ float sS[4];
     const int ns = 2 * vsplit_total(tg.nblocks, act, tg.full_tiles, tg.tiles, tg.max_splits);
     float x = 0.0f;
-    if (tg.mode == 1)
-      for (int k = threadIdx.x; k < ns; k += 256) x += tg.mass[(size_t)r * tg.mass_ld + k];
-    else
-      for (int k = threadIdx.x; k < ns; k += 256) x += tg.part[((size_t)k * tg.M_pad + r) * 2 + 1];
+    for (int k = threadIdx.x; k < ns; k += 256) x += tg.mass[(size_t)r * tg.mass_ld + k];
     x = wave_sum(x);
     if ((threadIdx.x & 63) == 0) sS[threadIdx.x >> 6] = x;
     __syncthreads();

@@ -725,14 +725,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   }
 
   // partials: (max, sum-exp) of the forward passes, [slot][M_pad] pairs; the
-  // backward's non-target probability mass, [M_pad][mass_ld] (token-major:
-  // the split reduce sums each token's run), when it forms the target's term
+  // backward's non-target probability mass, or the single pass's sum of e
+  // over the non-target columns (its reference is cap), [M_pad][mass_ld]
+  // (token-major: the split reduce sums each token's run)
   if (!BWD || (!EXTRA && a.tmass)) {
     if (COEF) run_s = sRun[wave][lane];
     const float m_out = BWD ? 0.0f : (((MODE == MODE_FWD_CAP || FUSED) && total > 0) ? a.cap : run_m);
     auto put = [&](int half, float m, float sum) {
       const int slot = 2 * (vs.slot0 + wr) + half;
-      if (BWD) {
+      if (COEF) {
         a.mass[(size_t)(tok0 + lane) * a.mass_ld + slot] = sum;
       } else {
         float *dst = a.part + ((size_t)slot * a.M_pad + tok0 + lane) * 2;
