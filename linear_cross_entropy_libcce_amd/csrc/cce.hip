@@ -178,6 +178,9 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.nchunks = (int)cdiv(p.tiles, p.chunk_tiles);
   p.ld_coeff = (int64_t)p.chunk_tiles * BNT;
   p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(4, (int64_t)p.TT * p.chunk_tiles / (2 * cus)));
+  // small M: the tile's small variant is resident once per CU (its LDS), so
+  // one round of workgroups, each one unbroken pipeline over its tiles
+  if (p.M <= 64) p.bwd_tpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)p.chunk_tiles / cus));
   p.HT = (int)cdiv(p.H, 256);
   // Vocabulary splits of the dh contraction: the fewest that fill whole rounds
   // of resident workgroups (one per CU) to >= 97%, else the best fill of up
@@ -238,7 +241,7 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     p.mass_ld = 2 * p.fus_max_splits * p.nchunks;
   }
   // the target's c' per compacted row, then the [M_pad][mass_ld] split sums:
-  // the backward's non-target mass or the single pass's non-target sum of e
+  // the backward's non-target mass or the single pass's non-target sum of 4 e
   p.o_tdc = o;
   o = align_up(o + sizeof(float) * p.M_pad, 256);
   p.o_fpart = o;

@@ -374,8 +374,8 @@ void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 struct ReduceTarget {
   int mode;
   // [M_pad][mass_ld], per split of the tile launches: mode 1 the backward's
-  // non-target mass, mode 2 the single pass's sum of e = e^{y - cap} over the
-  // non-target columns
+  // non-target mass, mode 2 the single pass's sum of 4 e (e = e^{y - cap})
+  // over the non-target columns
   const float *mass;
   int mass_ld;
   int nblocks, full_tiles, tiles, max_splits;  // the tile launches' split plan (vsplit_total)

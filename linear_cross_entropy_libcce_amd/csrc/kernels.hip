@@ -596,6 +596,7 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     if ((threadIdx.x & 63) == 0) sS[threadIdx.x >> 6] = x;
     __syncthreads();
     S = (sS[0] + sS[1]) + (sS[2] + sS[3]);
+    if (tg.mode == 2) S *= 0.25f;  // the single pass's tiles sum 4 e (exact)
   }
   // mode 2 also finishes the forward, in place of a merge launch: with the
   // fixed reference, lse = cap + log(S + e_t) and logp = y_t - lse (the

@@ -194,6 +194,10 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   // live (logit, coefficient, probability term) next to the next step's
   // prefetched operands and takes 8 at a time (with 16 its step loop spilled)
   constexpr int EW = FUSED ? 8 : 16;
+  // the single pass reads the logit only as 2 z / cap (the capped forward
+  // keeps z: its block-maximum variant needs the raw logit, and the two give
+  // bit-identical lse)
+  constexpr bool ZPRE = FUSED;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only
   const int act = active_tiles(a.cnt);
@@ -475,6 +479,12 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) sl[c] = buf_loadf(rl, (vcol0 + c * 32 + l32) * 4, 0);
       }
+      // ZPRE: the epilogue only ever needs z through 2 z / cap (in log2 units),
+      // so the transpose scratch holds acc * (s_last * c3): one multiply per
+      // column instead of one per logit
+      if (ZPRE)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sl[c] *= c3;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -512,7 +522,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             if (tk >= 0) {
               float yt = zt, dct = 1.0f;
               if (a.cap > 0.0f) {  // as the epilogues below: r = 1/(1 + e^{2z/cap})
-                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(zt * c3));
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ZPRE ? zt : zt * c3));
                 yt = a.cap * fmaf(-2.0f, r, 1.0f);
                 dct = 4.0f * fmaf(-r, r, r);
               }
@@ -581,12 +591,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             // fp32 by k_dh_reduce.
             float cv[EW], pv[EW];
             if (FUSED) {
-              // c' = 4 r (1 - r)
+              // c' = 4 r (1 - r); the term is taken as 4 e = exp2(c2 r + 2), so
+              // the coefficient -e c' is -(4 e)(r - r^2) and the split sums
+              // carry 4 S (the reduce takes the factor 4 back out, exactly)
 #pragma unroll
               for (int k = 0; k < EW; ++k) {
-                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k] * c3));
-                pv[k] = __builtin_amdgcn_exp2f(c2 * r);
-                cv[k] = -4.0f * pv[k] * fmaf(-r, r, r);
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[k]));
+                pv[k] = __builtin_amdgcn_exp2f(fmaf(c2, r, 2.0f));
+                cv[k] = -pv[k] * fmaf(-r, r, r);
               }
             } else if (a.cap > 0.0f) {
               // with r = 1/(1 + e^{2z/cap}): tanh(z/cap) = 1 - 2r and
@@ -725,7 +737,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   }
 
   // partials: (max, sum-exp) of the forward passes, [slot][M_pad] pairs; the
-  // backward's non-target probability mass, or the single pass's sum of e
+  // backward's non-target probability mass, or the single pass's sum of 4 e
   // over the non-target columns (its reference is cap), [M_pad][mass_ld]
   // (token-major: the split reduce sums each token's run)
   if (!BWD || (!EXTRA && a.tmass)) {
