@@ -2,11 +2,11 @@
 
 With a softcap in (0, 40] the call is a single pass over the head: the
 forward's fixed reference e^{y - cap} gives every coefficient up to the
-token's factor g e^{cap - lse}, which the split reduce applies after the
-merge (no logit is computed twice).  Other heads run a forward and a
-backward pass after one front; the backward tiles merge the forward's
-partials themselves, so the results match the two separate calls to
-rounding.
+token's factor g e^{cap - lse}, which the split reduce applies once it has
+summed the token's split sums into lse (no logit is computed twice, no merge
+launch).  Other heads run a forward and a backward pass after one front; the
+backward tiles merge the forward's partials themselves, so the results match
+the two separate calls to rounding.
 Tolerances as in test_parity_gpu.py (|dlogp|, |dlse| <= 5e-3, dh relative L2
 <= 1e-2, worst row <= 5e-2).
 """
@@ -185,3 +185,73 @@ def test_fused_full_size_workload_sampled(torch_cuda, cfg, bias):
     check(inp, gpu, oracle.cce(inp, tokens=rows), rows, "fused_workload%d_%s" % (cfg, bias))
     act = np.ones(inp["M"], bool) if inp["mask"] is None else inp["mask"] != 0
     assert np.all(gpu[0][act] <= 1e-6) and np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))
+
+
+GRAPH_CASES = {
+    "single_pass_cap30": dict(M=300, H=512, V=2000, bits=8, softcap=30.0, mask="random", mask_frac=0.2, seed=41),
+    "two_passes_nocap": dict(M=300, H=512, V=2000, bits=4, mask="random", mask_frac=0.2, seed=42),
+    "small_M20_cap30": dict(M=20, H=256, V=3000, bits=8, softcap=30.0, seed=43),
+}
+
+
+def _replays_match(torch, step, outs):
+    """Warm up on a side stream, capture one step in a HIP graph, then replay
+    it three times with eager work and synchronizations between the replays;
+    every replay must reproduce the eager outputs bit for bit."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(1000, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        say("graph: replay %d" % rep)
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r)
+    del junk
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_combined_call_replays_from_a_hip_graph(torch_cuda, name):
+    # the combined call enqueues kernels only (no allocation, no host
+    # synchronization, no memset), in every form: the single pass, the two
+    # passes without a softcap, the small-M variants
+    torch = torch_cuda
+    kw = dict(GRAPH_CASES[name])
+    seed = kw.pop("seed")
+    inp = syn.make_custom(seed=seed, **kw)
+    say("%s: capture cce_forward_backward" % name)
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    M, H = inp["M"], inp["H"]
+    ws = torch.empty(cce.forward_backward_workspace_bytes(head, M), dtype=torch.uint8, device="cuda")
+    g = torch.from_numpy(np.random.default_rng(seed).uniform(-2, 2, M).astype(np.float32)).cuda()
+    logp = torch.empty(M, dtype=torch.float32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    dh = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    _replays_match(torch, lambda: cce.cce_forward_backward(h, head, t, g, m, workspace=ws, out=(logp, lse, dh)),
+                   [logp, lse, dh])
+
+
+def test_static_forward_replays_from_a_hip_graph(torch_cuda):
+    # the forward on the library's own device scratch, which exists for
+    # callers such as graph capture that cannot allocate
+    torch = torch_cuda
+    inp = syn.make_custom(M=64, H=256, V=3000, bits=8, seed=44, softcap=30.0, mask="random", mask_frac=0.25)
+    say("static forward: capture")
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    M = inp["M"]
+    logp = torch.empty(M, dtype=torch.float32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    _replays_match(torch, lambda: cce.cce_forward_static(h, head, t, m, out=(logp, lse)), [logp, lse])
