@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 // and b' = b + 8 s for 4-bit heads (codes used as q - 8): symmetric heads have
 // b' = 0.  Row v holds b' in fixed point, b' ~= u_v * n with
 // u_v = max_g |b'| / BIAS_NMAX and n = 65536 d2 + 256 d1 + d0 (balanced signed
-// digits, exact in bf16, stored as bytes offset by 128); the token side holds
+// digits, exact in bf16, stored as two's-complement bytes); the token side holds
 // S = S1 + S2 + S3 (three bf16 pieces, each the rounding of what the
 // previous ones leave).  The products that matter are MFMA columns, in two
 // halves of P columns each (part = column / Gq within the half, group gi =
@@ -77,6 +77,10 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t *mask, int M, in
 //
 // * The digits of the bias block and, per block of 64 rows, the largest |b'|
 //   (fp32 bits; zero for a symmetric head, whose bias block is then skipped).
+//   A block whose largest |b'| is 0 writes no digits: the tile reads such a
+//   block's bias steps through an empty buffer resource, i.e. as zero bytes,
+//   which are its digits (all zero).  A symmetric head's front so writes no
+//   bias block at all.
 // * Fold ratios of every step, rt[step][v]: 1 for the bias steps, then
 //   u_v / s_0, s_0 / s_1, ... with effective scales, and s_last[v] = s_{G-1}.
 // One workgroup per 64 rows.  Digits: when a row's group count is a multiple
@@ -111,16 +115,16 @@ __device__ __forceinline__ float bias_unit(float m) {
   return u >= 1e-30f ? u : 0.0f;
 }
 
-// The three digit bytes (offset by 128) of b' in units u (inv = 1/u, or 0).
+// The three digit bytes (two's complement) of b' in units u (inv = 1/u, or 0).
 __device__ __forceinline__ void bias_digits(float bp, float inv, uint32_t &d2b, uint32_t &d1b, uint32_t &d0b) {
   const int n = (int)fminf(fmaxf(rintf(bp * inv), -BIAS_NMAX), BIAS_NMAX);
   const int d0 = ((n + 128) & 255) - 128;  // n - d0 is a multiple of 256
   const int n1 = (n - d0) >> 8;           // |n1| <= 32639
   const int d1 = ((n1 + 128) & 255) - 128;
   const int d2 = (n1 - d1) >> 8;          // |d2| <= 127
-  d2b = (uint32_t)(d2 + 128);
-  d1b = (uint32_t)(d1 + 128);
-  d0b = (uint32_t)(d0 + 128);
+  d2b = (uint32_t)d2 & 0xFFu;
+  d1b = (uint32_t)d1 & 0xFFu;
+  d0b = (uint32_t)d0 & 0xFFu;
 }
 
 // The digits of groups 4j .. 4j + 3 of one row, b' taken from bp(k), into
@@ -190,16 +194,19 @@ __device__ void head_prep_staged(int64_t blk, const FrontArgs &f, float shift, f
       for (int gi = qd; gi < Gq; gi += 4) m = fmaxf(m, fabsf(sT[r * HP_LD + gi]));
     m = fmaxf(m, __shfl_xor(m, 1, 64));
     m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const bool any = __syncthreads_or(r < rows && m > 0.0f);  // the block carries digits
     if (r < rows) {
       if (qd == 0) smax[r] = __float_as_uint(m);
+    }
+    if (any && r < rows) {
       const float u = bias_unit(m);
       const float inv = (u > 0.0f) ? 1.0f / u : 0.0f;
       uint8_t *row = f.baug + (v0 + r) * Kb;
       const float *br = sT + r * HP_LD;
       for (int j = qd; j < G4; j += 4) put_digits4(row, j, Gq, P, inv, [&](int k) { return br[4 * j + k]; });
       for (int o = 3 * Gq + 4 * qd; o < P; o += 16) {
-        *(uint32_t *)(row + o) = 0x80808080u;
-        *(uint32_t *)(row + P + o) = 0x80808080u;
+        *(uint32_t *)(row + o) = 0u;
+        *(uint32_t *)(row + P + o) = 0u;
       }
     }
   }
@@ -279,8 +286,8 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
         put_digits4(row, j, Gq, P, inv, [&](int k) { return fmaf(shift, sc[k], bi[k]); });
       }
       for (int o = 3 * Gq + 4 * qd; o < P; o += 16) {
-        *(uint32_t *)(row + o) = 0x80808080u;
-        *(uint32_t *)(row + P + o) = 0x80808080u;
+        *(uint32_t *)(row + o) = 0u;
+        *(uint32_t *)(row + P + o) = 0u;
       }
     }
     __syncthreads();
@@ -310,8 +317,8 @@ __device__ void head_prep_block(int64_t blk, const FrontArgs &f, float shift, fl
     const int pad = P - 3 * Gq;
     for (int i = tid; i < rows * pad; i += 256) {
       uint8_t *row = f.baug + (v0 + i / pad) * Kb + 3 * Gq + i % pad;
-      row[0] = (uint8_t)128;
-      row[P] = (uint8_t)128;
+      row[0] = 0;
+      row[P] = 0;
     }
   }
   const int64_t v = v0 + lane;

@@ -104,7 +104,15 @@ struct Producer {
     const int64_t rows = a.V - v0 < BNT ? a.V - v0 : BNT;
     const bool bias = step < a.NB;
     const int g = step - a.NB;
-    const rsrc_t rw = bias ? make_rsrc(a.baug + v0 * a.Kb, rows * a.Kb)
+    // a bias step reads the digits of this wave's 32 rows, which lie in one
+    // 64-row block; a block whose largest |b'| is 0 has no digits stored (the
+    // front skips it), and an empty resource reads its zero digits as zeros
+    int64_t brows = rows;
+    if (!DENSE && bias) {  // wave-uniform: only bias steps look the block up
+      const int64_t blk = (v0 >> 6) + __builtin_amdgcn_readfirstlane(tid >> 7);
+      if (a.bmxb[blk < a.nbmx ? blk : a.nbmx - 1] == 0u) brows = 0;
+    }
+    const rsrc_t rw = bias ? make_rsrc(a.baug + v0 * a.Kb, brows * a.Kb)
                            : make_rsrc(a.wq + v0 * a.wpr, rows * a.wpr * 4);
     const int rowb = bias ? a.Kb : a.wpr * 4;                // bytes per row
     const int qb = DENSE ? 32 : (bias || BITS == 8) ? 16 : 8;  // bytes per 16 K values
@@ -136,10 +144,10 @@ struct Producer {
   }
 
   // Slice ks: row row0 + 16 * (ks >> 1), K chunk 2q + (ks & 1) (8 values).
-  // Bytes are stored offset by 128 (8-bit codes as they come, bias digits
-  // written so); flipping the top bit gives the signed value q - 128 (resp.
-  // the digit), one sign-extending convert per byte.  4-bit codes are used
-  // as q - 8.
+  // 8-bit codes come as unsigned bytes; flipping the top bit gives the signed
+  // value q - 128, one sign-extending convert per byte.  Bias digits are
+  // stored as signed bytes and pass unflipped.  4-bit codes are used as
+  // q - 8.
   // KW = 32: slice ks (0, 1) is K chunk 2 (tid & 1) + ks of row tid >> 1.
   __device__ __forceinline__ void store(bool bias, int ks, const ProdRegs &p, uint16_t *sw) const {
     const int i = GS32 ? 0 : ks >> 1, h = ks & 1;
@@ -147,21 +155,21 @@ struct Producer {
     if (DENSE) {  // bf16 as stored
       o[0] = p.w[4 * h]; o[1] = p.w[4 * h + 1]; o[2] = p.w[4 * h + 2]; o[3] = p.w[4 * h + 3];
     } else if (BITS == 8) {
-      unpack8s(p.w[4 * i + 2 * h] ^ 0x80808080u, o);
-      unpack8s(p.w[4 * i + 2 * h + 1] ^ 0x80808080u, o + 2);
+      const uint32_t flip = bias ? 0u : 0x80808080u;  // wave-uniform
+      unpack8s(p.w[4 * i + 2 * h] ^ flip, o);
+      unpack8s(p.w[4 * i + 2 * h + 1] ^ flip, o + 2);
     } else {
       // 4-bit head: the eight nibbles of the code word are spread to bytes
-      // (codes 0 1 2 3 | 4 5 6 7) as 128 + q, less 8 per byte (no borrow
-      // between bytes): 120 + q, which the shared flip of the top bit turns
-      // into the signed code q - 8, as it turns a stored digit byte into the
-      // digit.  A uniform select takes the codes or the two digit words, so
-      // both kinds of step share one straight-line unpack.
+      // (codes 0 1 2 3 | 4 5 6 7) as q | 0x80, less 8 per byte (no borrow
+      // between bytes): 120 + q, whose flipped top bit is the signed code
+      // q - 8.  A uniform select takes those or the two digit words, so both
+      // kinds of step share one straight-line unpack.
       const uint32_t w = p.w[4 * i + h];
       const uint32_t ev = (w & 0x0F0F0F0Fu) | 0x80808080u, od = ((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u;
       const uint32_t c0 = __builtin_amdgcn_perm(od, ev, 0x05010400u) - 0x08080808u;  // ev.b0 od.b0 ev.b1 od.b1
       const uint32_t c1 = __builtin_amdgcn_perm(od, ev, 0x07030602u) - 0x08080808u;  // ev.b2 od.b2 ev.b3 od.b3
-      unpack8s((bias ? p.w[4 * i + 2 * h] : c0) ^ 0x80808080u, o);
-      unpack8s((bias ? p.w[4 * i + 2 * h + 1] : c1) ^ 0x80808080u, o + 2);
+      unpack8s(bias ? p.w[4 * i + 2 * h] : c0 ^ 0x80808080u, o);
+      unpack8s(bias ? p.w[4 * i + 2 * h + 1] : c1 ^ 0x80808080u, o + 2);
     }
     const int off = GS32 ? swz<KW>(tid >> 1, 2 * (tid & 1) + h) : swz<KW>(row0 + 16 * i, 2 * q + h);
     *(u32x4_t *)(sw + off) = u32x4_t{o[0], o[1], o[2], o[3]};
