@@ -623,7 +623,20 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
   if (r >= 0) {
     int ksd, steps_per;
     dh_split(a, act, ksd, steps_per);
-    for (int k = 0; k < ksd; ++k) acc += *(const f32x4_t *)(a.dh_part + ((size_t)k * act * BM + r) * H + d);
+    // the slabs summed in order, eight loads issued before their adds (few
+    // tokens have tens of splits, and a load waited for before the next one
+    // is issued made the sum a chain of memory latencies)
+    const float *sp = a.dh_part + (size_t)r * H + d;
+    const size_t sstride = (size_t)act * BM * H;
+    int k = 0;
+    for (; k + 8 <= ksd; k += 8) {
+      f32x4_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = *(const f32x4_t *)(sp + (size_t)(k + j) * sstride);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += x[j];
+    }
+    for (; k < ksd; ++k) acc += *(const f32x4_t *)(sp + (size_t)k * sstride);
     TokRec rec = tok[r];
     const bool ht = rec.tgt >= 0;
     if (tg.mode == 1) {
