@@ -235,6 +235,10 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   {
     const int64_t nwr = cdiv(p.chunk_tiles, p.bwd_tpw);
     p.fus_blocks = (int)(p.TT * nwr);
+    // few token tiles (M <= 1024): one round of workgroups (the tile is
+    // resident once per CU, and the device gives fewer active tiles more
+    // splits, which would otherwise make a second, shorter-pipelined round)
+    if (p.TT <= 4) p.fus_blocks = (int)std::min<int64_t>(p.fus_blocks, cus);
     p.fus_max_splits = (int)std::max<int64_t>(
         nwr, std::min<int64_t>(std::min<int64_t>(p.chunk_tiles, p.fus_blocks),
                                ((int64_t)64 << 20) / 16 / p.M_pad / p.nchunks));
