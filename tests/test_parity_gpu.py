@@ -404,25 +404,42 @@ def test_zero_and_tiny_scales(torch_cuda, bits, cap):
     check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "zeroscale%d" % bits)
 
 
-@pytest.mark.parametrize("where,H", [("none", 512), ("first", 512), ("middle", 512), ("last", 512),
-                                     ("none", 64)])
-def test_zero_bias_block_start(torch_cuda, where, H):
-    # a symmetric 8-bit head (b = -128 s: every b' is 0) starts each tile at
-    # its first code step; one row with b' != 0 in the first, a middle or the
-    # last 64-row block must bring the bias steps back for every tile.  Ten
-    # tokens target that row, whose logit moves by the sum of h.  H = 64 has a
-    # single code step and keeps the bias steps.
-    M, V = 150, 1333
-    inp = syn.make_custom(M=M, H=H, V=V, bits=8, seed=23 + H, softcap=30.0, mask="random", mask_frac=0.2)
+@pytest.mark.parametrize("where,H,bits,M,group", [
+    ("none", 512, 8, 150, 64), ("first", 512, 8, 150, 64), ("middle", 512, 8, 150, 64),
+    ("last", 512, 8, 150, 64), ("none", 64, 8, 150, 64), ("middle", 512, 4, 150, 64),
+    ("middle", 512, 8, 40, 64), ("last", 768, 4, 40, 64), ("middle", 512, 8, 150, 32),
+    ("first", 512, 4, 40, 128)])
+def test_zero_bias_block_start(torch_cuda, where, H, bits, M, group):
+    # a symmetric head (b = -128 s or -8 s: every b' is 0) starts each tile at
+    # its first code step, and its front stores no bias digits; one row with
+    # b' != 0 in the first, a middle or the last 64-row block must bring the
+    # bias steps back for every tile, the other blocks' zero digits then read
+    # through an empty buffer resource.  Ten tokens target that row, whose
+    # logit moves by the sum of h.  H = 64 has a single code step and keeps
+    # the bias steps.  M = 40 takes the small-M tile, group 32 the 32-wide step.
+    V = 1333
+    inp = syn.make_custom(M=M, H=H, V=V, bits=bits, seed=23 + H + bits + M + group, softcap=30.0, mask="random",
+                          mask_frac=0.2, group=group)
     s, b = inp["scales"], inp["biases"]
+    shift = np.float32(128.0 if bits == 8 else 8.0)
     row = {"none": None, "first": 3, "middle": 700, "last": V - 1}[where]
     if row is not None:
-        b[row, :] = np.float32(1.0) - np.float32(128.0) * s[row, :]
+        b[row, :] = np.float32(1.0) - shift * s[row, :]
         inp["targets"][:10] = row
     g = np.random.default_rng(9).uniform(-1.5, 1.5, size=M)
-    say("zero bias block, nonzero row %s, H=%d: GPU" % (where, H))
+    say("zero bias block, nonzero row %s, H=%d, %d-bit, M=%d, group %d: GPU" % (where, H, bits, M, group))
     gpu = run_gpu(torch_cuda, inp, g=g)
-    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "biasstart_%s_%d" % (where, H))
+    orc = oracle.cce(inp, g=g)
+    name = "biasstart_%s_%d_%d_%d_%d" % (where, H, bits, M, group)
+    check(inp, gpu, orc, np.arange(M), name)
+    # the single pass (softcap 30) reads the same bias block
+    torch = torch_cuda
+    head = cce.head_from_numpy(inp)
+    h, t, m = cce.tokens_from_numpy(inp)
+    lp, ls, dh = cce.cce_forward_backward(h, head, t, torch.from_numpy(g.astype(np.float32)).cuda(), m)
+    torch.cuda.synchronize()
+    one = tuple(x.cpu().numpy().astype(np.float64) for x in (lp, ls, dh))
+    check(inp, one, orc, np.arange(M), name + "_single_pass")
 
 
 @pytest.mark.parametrize("bits", [8, 4])
