@@ -383,7 +383,7 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   a.ksv = p.ld_coeff / 16;
   a.cap = p.cap;
   a.inv_cap = p.cap > 0.0f ? 1.0f / p.cap : 0.0f;
-  a.small = p.M <= 64 ? 1 : 0;
+  a.small = p.M <= 32 ? 2 : (p.M <= 64 ? 1 : 0);  // 2: one 32-row token block
   return a;
 }
 

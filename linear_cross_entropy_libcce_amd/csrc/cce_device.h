@@ -181,7 +181,7 @@ struct TileArgs {
   uint8_t *fl;
   int64_t fl_ld;
   float filter_eps;
-  int small;             // at most 64 tokens: only token group 0 of the tile multiplies
+  int small;             // 1: at most 64 tokens (token group 0 of the tile multiplies); 2: at most 32
 };
 
 // Arguments of the front launch (token rows, target logit, head side).

@@ -26,8 +26,10 @@ namespace cce {
 // Reads are raw buffer loads (rows past V read as zeros), so the step has no
 // per-lane predicate.  Each split owns its fp32 slab: no atomics, and a
 // repeated call gives identical bits.
-// SMALL (at most 64 tokens, one token group): every wave multiplies the 64
-// tokens by its own 32 of the workgroup's 256 dh columns.
+// SMALL (1: at most 64 tokens, one token group): every wave multiplies the 64
+// tokens by its own 32 of the workgroup's 256 dh columns; SMALL = 2 (at most
+// 32 tokens) keeps one 32-row token block (half the MFMAs, coefficient
+// fragments and slab rows).
 // SKIP (second instantiation): the split contracts only the vocabulary tiles
 // of its range whose pair flag is set for its token tile; their K steps are
 // listed in LDS first, in order.
@@ -180,7 +182,7 @@ struct DhProducer {
 
 constexpr int MAX_LIST = 2048;  // vocabulary tiles per split (a chunk holds at most 2048)
 
-template <int BITS, bool SKIP, bool SMALL, int LG, int SBW>
+template <int BITS, bool SKIP, int SMALL, int LG, int SBW>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   // the launched work ids are spread over the active token tiles only;
@@ -200,6 +202,10 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   // the two waves of a token group sit on two SIMDs; small M: one token group,
   // 32 columns per wave
   const int tg = SMALL ? 0 : wave >> 1, dh = wave & 1;
+  constexpr int NRB = SMALL == 2 ? 1 : 2;  // 32-row token blocks per wave
+  // small M: wave w stages coefficient fragment (row block w / 4, k-step w % 4)
+  // of each step; with one row block only waves 0..3 have one
+  const bool cload = NRB == 2 || wave < 4;
   constexpr int NC = SMALL ? 1 : 4;                 // 32-column blocks per wave
   const int col0 = SMALL ? wave * 32 : dh * 128;   // this wave's first column within the tile
   const int l32 = lane & 31, lh = lane >> 5;
@@ -303,9 +309,11 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.stage_sb(P0, sSB[0], a.sbt);
     pr.stage_sb(P1, sSB[1], a.sbt);
     if (SMALL) {
-      sCA[0][wave * 64 + lane] = cfrag_load(0);
-      C1 = cfrag_load(1);
-      C2 = cfrag_load(2);
+      if (cload) {
+        sCA[0][wave * 64 + lane] = cfrag_load(0);
+        C1 = cfrag_load(1);
+        C2 = cfrag_load(2);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -331,7 +339,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
                        u32x4_t &cfn) {
       const int cb = st & 1;
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
-      if (SMALL) cfn = cfrag_load(st + 3);
+      if (SMALL && cload) cfn = cfrag_load(st + 3);
       pr.load(a, vrow(st + (SMALL ? 3 : 2)), nxt);  // past the split: valid rows or zeros, never used
       pr.read_sb(sSB[cb ^ 1], sc, bi);
       const uint16_t *sw = sB[cb];
@@ -339,7 +347,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           cA[0][ks] = __builtin_bit_cast(bf16x8_t, sCA[cb][ks * 64 + lane]);
-          cA[1][ks] = __builtin_bit_cast(bf16x8_t, sCA[cb][(4 + ks) * 64 + lane]);
+          if (NRB == 2) cA[1][ks] = __builtin_bit_cast(bf16x8_t, sCA[cb][(4 + ks) * 64 + lane]);
         }
       }
       bf16x8_t bq[NC];
@@ -351,7 +359,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < NRB; ++rb)
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             if (ks < 3) bq[c] = *(const bf16x8_t *)(sw + boff[ks + 1] + c * 32 * KSTP);
           }
@@ -364,7 +372,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.stage_sb(SMALL ? mid : nxt, sSB[cb], a.sbt);
-      if (SMALL) sCA[cb ^ 1][wave * 64 + lane] = cfc;  // step st + 1's: read after the barrier
+      if (SMALL && cload) sCA[cb ^ 1][wave * 64 + lane] = cfc;  // step st + 1's: read after the barrier
       __syncthreads();
     };
     int st = 0;
@@ -399,18 +407,18 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     float old[2][16];
     if (a.accumulate) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           old[rb][e] = slab[(size_t)(rb * 32 + 8 * (e >> 2) + (e & 3)) * a.H + d];
     } else {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) old[rb][e] = 0.0f;
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         slab[(size_t)(rb * 32 + 8 * (e >> 2) + (e & 3)) * a.H + d] = old[rb][e] + acc[rb][c][e];
@@ -418,18 +426,22 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
 }
 
 template <int B, int LG, int SBW>
-static void launch_dh_variant(hipStream_t st, dim3 grid, const GemmArgs &a, bool skip, bool small) {
+static void launch_dh_variant(hipStream_t st, dim3 grid, const GemmArgs &a, bool skip, int small) {
   if (skip) {
-    hipLaunchKernelGGL((k_dh<B, true, false, LG, SBW>), grid, dim3(TW), 0, st, a);
+    hipLaunchKernelGGL((k_dh<B, true, 0, LG, SBW>), grid, dim3(TW), 0, st, a);
     return;
   }
   if constexpr (LG == 2 && SBW == 4) {
-    if (small) {
-      hipLaunchKernelGGL((k_dh<B, false, true, LG, SBW>), grid, dim3(TW), 0, st, a);
+    if (small == 2) {
+      hipLaunchKernelGGL((k_dh<B, false, 2, LG, SBW>), grid, dim3(TW), 0, st, a);
+      return;
+    }
+    if (small == 1) {
+      hipLaunchKernelGGL((k_dh<B, false, 1, LG, SBW>), grid, dim3(TW), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((k_dh<B, false, false, LG, SBW>), grid, dim3(TW), 0, st, a);
+  hipLaunchKernelGGL((k_dh<B, false, 0, LG, SBW>), grid, dim3(TW), 0, st, a);
 }
 
 template <int B>
@@ -437,22 +449,22 @@ static void launch_dh_bits(hipStream_t st, dim3 grid, const GemmArgs &a) {
   const bool skip = a.fl != nullptr;
   const bool wide = a.sbt == SB_F32;
   // the small-M instantiation exists for the default storage only (group 64, fp32)
-  const bool small = !skip && a.small && a.gs == KSTEP && wide;
+  const int small = (!skip && a.gs == KSTEP && wide) ? a.small : 0;
   if (a.gs == 64) {
     if (wide) launch_dh_variant<B, 2, 4>(st, grid, a, skip, small);
-    else launch_dh_variant<B, 2, 2>(st, grid, a, skip, false);
+    else launch_dh_variant<B, 2, 2>(st, grid, a, skip, 0);
   } else if (a.gs == 32) {
-    if (wide) launch_dh_variant<B, 3, 4>(st, grid, a, skip, false);
-    else launch_dh_variant<B, 3, 2>(st, grid, a, skip, false);
+    if (wide) launch_dh_variant<B, 3, 4>(st, grid, a, skip, 0);
+    else launch_dh_variant<B, 3, 2>(st, grid, a, skip, 0);
   } else {
-    if (wide) launch_dh_variant<B, 1, 4>(st, grid, a, skip, false);
-    else launch_dh_variant<B, 1, 2>(st, grid, a, skip, false);
+    if (wide) launch_dh_variant<B, 1, 4>(st, grid, a, skip, 0);
+    else launch_dh_variant<B, 1, 2>(st, grid, a, skip, 0);
   }
 }
 
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a) {
   if (bits == 16) {  // dense bf16 head: exact path only (no skips, no small-M variant)
-    hipLaunchKernelGGL((k_dh<16, false, false, 0, 0>), grid, dim3(TW), 0, st, a);
+    hipLaunchKernelGGL((k_dh<16, false, 0, 0, 0>), grid, dim3(TW), 0, st, a);
     return;
   }
   if (bits == 4) launch_dh_bits<4>(st, grid, a);

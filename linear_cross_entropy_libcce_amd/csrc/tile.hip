@@ -41,7 +41,9 @@ namespace cce {
 // 64 tokens by its own 32 vocabulary rows of the tile (one column block), so
 // all eight waves share the MFMA work and the epilogues; the forward
 // combines the waves' softmax partials into the two halves' partials at the
-// end.
+// end.  VAR_SMALL32 (at most 32 tokens): the same with one 32-row token block,
+// so half the MFMAs, folds, token fragments and coefficient stores; the
+// epilogue's lanes 32..63 (padding tokens) compute on zeros and store nothing.
 //
 // VAR_EXTRA (a second instantiation, so the plain passes carry none of it):
 //  * forward: the largest logit of every (token, vocabulary tile), written to
@@ -59,7 +61,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 // both the partial sums and the unnormalized coefficients -e^{c(z) - cap} c'(z)
 // (the split reduce scales them by g e^{cap - lse} once the merge has lse).
 enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2, MODE_FUSED = 3 };
-enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2 };
+enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2, VAR_SMALL32 = 3 };
 
 // One step's worth of head data for one producer thread: 16 K values of each
 // of two vocabulary rows (8-bit codes and bias digits: 4 words per row; 4-bit
@@ -197,7 +199,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr int KW = GS32 ? 32 : 64;  // K columns per step (one quantization group)
   constexpr int NKS = KW / 16;        // MFMA k-steps per step
   constexpr bool DENSE = BITS == 16;  // bf16 head: no fold, no final scale
-  constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL;
+  constexpr bool EXTRA = VAR == VAR_EXTRA, SMALL = VAR == VAR_SMALL || VAR == VAR_SMALL32;
+  constexpr int NRB = VAR == VAR_SMALL32 ? 1 : 2;  // 32-row token blocks per wave
   // epilogue columns per chunk: the fused pass keeps three values per column
   // live (logit, coefficient, probability term) next to the next step's
   // prefetched operands and takes 8 at a time (with 16 its step loop spilled)
@@ -279,6 +282,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   const int hv0 = ((tg * 2) * (int)a.ks16 * 64 + lane) * 16;
   const int hstride = (int)a.ks16 * 1024;
   float *zs = sZ[wave];
+  // small M: wave w stages token fragment (row block w / 4, k-step w % 4) of
+  // each step; with one row block only waves 0..3 have one
+  const bool hload = NRB == 2 || wave < 4;
+  if (NRB == 1)  // padding token rows of the transpose scratch, never written by a tile
+    for (int i = lane; i < 32 * ZROW; i += 64) zs[32 * ZROW + i] = 0.0f;
 
   float run_m = -INFINITY, run_s = 0.0f;
   // Backward: two per-token values carried through the step loop (the tile
@@ -366,6 +374,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     for (int ks = 0; ks < NKS; ++ks) boff[ks] = swz<KW>(vcol0 + l32, 2 * ks + lh);
     f32x16_t acc[2][NC];
     bf16x8_t hA[2][NKS];
+    // small M starts each tile by folding with ratio 0 (see mfma_step): the
+    // accumulator must hold finite values before the first tile
+    if (SMALL)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
 
     // step `n` steps after (tile, st)
     auto coords = [&](int tile, int st, int n, int64_t &v0, int &step) {
@@ -385,14 +402,17 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         int64_t v2; int s2;
         coords(first_tile, 0, 2, v2, s2);
         pr.load(a, v2, s2, P2);
-        H1 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s1 * NKS * 1024);
-        H2 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s2 * NKS * 1024);
+        if (hload) {
+          H1 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s1 * NKS * 1024);
+          H2 = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s2 * NKS * 1024);
+        }
       }
 #pragma unroll
       for (int part = 0; part < NKS; ++part) pr.store(s0 < a.NB, part, P0, sW[0]);
       pr.ratio(P0, sR[0]);
       if (SMALL) {
-        sH[0][wave * 64 + lane] = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s0 * NKS * 1024);
+        if (hload)
+          sH[0][wave * 64 + lane] = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, s0 * NKS * 1024);
       } else {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -406,25 +426,32 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     // The MFMA work of one step on LDS buffer cb, with the producer slices of
     // the next step (words in `cur`) placed between the MFMAs and the loads of
     // the step after next (into `nxt`) issued first.
-    auto mfma_step = [&](int cb, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt, u32x4_t &hcur,
-                         u32x4_t &hnxt) {
+    auto mfma_step = [&](int cb, bool first, int sn, int64_t vnn, int snn, ProdRegs &cur, ProdRegs &nxt,
+                         u32x4_t &hcur, u32x4_t &hnxt) {
       const bool sbias = sn < a.NB;
       const int hnext = sn * NKS * 1024;  // fragment-major: 1 KiB per 16 K of a 32-row block
       // small M: this wave's token fragment of step + LA is loaded before the
       // head words, so that waiting for it does not wait for them too (loads
       // complete in issue order for s_waitcnt)
-      if (SMALL) hnxt = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, snn * NKS * 1024);
+      if (SMALL && hload) hnxt = buf_load16(rh, hv0 + (wave >> 2) * hstride + (wave & 3) * 1024, snn * NKS * 1024);
       pr.load(a, vnn, snn, nxt);
       const uint16_t *sw = sW[cb];
       float r[NC];
       if (!DENSE)
 #pragma unroll
         for (int c = 0; c < NC; ++c) r[c] = sR[cb][vcol0 + c * 32 + l32];
+      // small M: a tile's first step clears the accumulator through its fold
+      // (ratio 0; the accumulator is finite), one select per column block in
+      // place of a select per accumulator element, which the compiler made of
+      // the clearing in this three-step loop
+      if (SMALL)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) r[c] = first ? 0.0f : r[c];
       if (SMALL) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           hA[0][ks] = __builtin_bit_cast(bf16x8_t, sH[cb][ks * 64 + lane]);
-          hA[1][ks] = __builtin_bit_cast(bf16x8_t, sH[cb][(4 + ks) * 64 + lane]);
+          if (NRB == 2) hA[1][ks] = __builtin_bit_cast(bf16x8_t, sH[cb][(4 + ks) * 64 + lane]);
         }
       }
       // B operand of column block c for k-step ks + 1 is read as soon as its
@@ -440,7 +467,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < NRB; ++rb) {
               if (ks == 0 && !DENSE) acc[rb][c] *= r[c];
               acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA[rb][ks], bq[c], acc[rb][c], 0, 0, 0);
             }
@@ -466,7 +493,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.ratio(cur, sR[cb ^ 1]);
-      if (SMALL) sH[cb ^ 1][wave * 64 + lane] = hcur;  // step + 1's: read after the step's barrier
+      if (SMALL && hload) sH[cb ^ 1][wave * 64 + lane] = hcur;  // step + 1's: read after the step's barrier
     };
 
     // ---- epilogue of vocabulary tile `tile`.  acc[rb][c][4i+j] is the logit
@@ -496,7 +523,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -651,10 +678,11 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             // fragment-major chunk: these EW vocab rows are K chunk(s) cm (cm + 1)
             const int64_t vloc = (int64_t)tile * BNT + vcol0 + c * 32 + k0;
             const int cm = (int)(vloc >> 3);
+            if (NRB == 2 || lane < 32)
 #pragma unroll
-            for (int q = 0; q < EW / 8; ++q)
-              *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
-                  u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+              for (int q = 0; q < EW / 8; ++q)
+                *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
+                    u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -699,7 +727,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
       int sn, snn;
       coords(tile, st, 1, vn, sn);     // next step: unpacked now
       coords(tile, st, LA, vnn, snn);  // loaded now
-      if (st == 0) {
+      if (!SMALL && st == 0) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -707,7 +735,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][c][e] = 0.0f;
       }
-      mfma_step(idx & 1, sn, vnn, snn, cur, nxt, hcur, hnxt);
+      mfma_step(idx & 1, st == 0, sn, vnn, snn, cur, nxt, hcur, hnxt);
       if (st == steps - 1) epilogue(tile);
       __syncthreads();
       if (EXTRA && st == steps - 1) tile_extra(tile);
@@ -799,7 +827,7 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
   const bool extra = pass == PASS_FUSED ? false : (bwd ? a.fl != nullptr : a.bmx != nullptr);
   const bool gs32 = a.kw == 32;
   // group 32 has no small-M instantiation (the plain one is correct there)
-  const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? VAR_SMALL : VAR_PLAIN);
+  const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? (a.small == 2 ? VAR_SMALL32 : VAR_SMALL) : VAR_PLAIN);
 #define CCE_TILE(B, MD)                                                                                          \
   do {                                                                                                           \
     if (gs32) {                                                                                                  \
@@ -808,6 +836,8 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
     } else {                                                                                                     \
       if (var == VAR_EXTRA) hipLaunchKernelGGL((k_tile<B, MD, VAR_EXTRA, false>), grid, dim3(TW), 0, st, a);     \
       else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL, false>), grid, dim3(TW), 0, st, a); \
+      else if (var == VAR_SMALL32)                                                                               \
+        hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL32, false>), grid, dim3(TW), 0, st, a);                       \
       else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                      \
     }                                                                                                            \
   } while (0)
@@ -816,6 +846,8 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
   do {                                                                                                           \
     if (gs32) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);            \
     else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_SMALL, false>), grid, dim3(TW), 0, st, a); \
+    else if (var == VAR_SMALL32)                                                                                 \
+      hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_SMALL32, false>), grid, dim3(TW), 0, st, a);                 \
     else hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                \
   } while (0)
   if (bits == 16) {  // dense bf16 head: 32-wide steps, plain variant only
