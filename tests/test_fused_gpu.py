@@ -187,6 +187,22 @@ def test_fused_full_size_workload_sampled(torch_cuda, cfg, bias):
     assert np.all(gpu[0][act] <= 1e-6) and np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,bias", [(1, "sym"), (16, "sym"), (32, "affine"), (33, "sym"), (64, "affine")])
+def test_fused_small_m_on_the_full_head(torch_cuda, M, bias):
+    # the single pass at small M on workload 3's full head: one 32-row token
+    # block (M <= 32) and two (33..64) in the tile and the dh contraction,
+    # with and without the bias block; every token against the oracle
+    import dataclasses
+    w = dataclasses.replace(syn.WORKLOADS[3], bias="symmetric" if bias == "sym" else "affine")
+    say("small M=%d on workload 3's head (%s): generating inputs" % (M, bias))
+    inp = syn.make_inputs(w, syn.seed_for(3), M=M)
+    g = np.random.default_rng(M + 7).uniform(-1.5, 1.5, size=M)
+    gpu = run_fused(torch_cuda, inp, g=g)
+    say("small M=%d: oracle on all tokens" % M)
+    check(inp, gpu, oracle.cce(inp, g=g), np.arange(M), "fused_smallM%d_%s" % (M, bias))
+
+
 GRAPH_CASES = {
     "single_pass_cap30": dict(M=300, H=512, V=2000, bits=8, softcap=30.0, mask="random", mask_frac=0.2, seed=41),
     "two_passes_nocap": dict(M=300, H=512, V=2000, bits=4, mask="random", mask_frac=0.2, seed=42),
