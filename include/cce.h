@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 6
+#define CCE_ABI_VERSION 7
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -99,13 +99,42 @@ typedef struct cce_head {
   int32_t group;
   float softcap;
   int32_t sb_dtype;
+  /* Optional: the head's preparation, or NULL.  Every call first derives
+   * per-row data from the scales and biases (the fold ratios s_{g-1} / s_g,
+   * the last scale, the fixed-point digits of b + z s and their block
+   * maxima).  A frozen head can have that written once by cce_head_prepare
+   * into a device buffer of prep_bytes (256-byte aligned); a call given it
+   * skips that work and needs a smaller workspace.  The caller keeps it in
+   * step with wq, scales and biases (the library cannot tell). */
+  const void *prep;
+  size_t prep_bytes;
 } cce_head;
+
+/*
+ * The head is frozen while the caller trains (page "mlx-bun 0.0.4 -> 0.0.6",
+ * src/train/flash-cce.ts, the FlashCceHead interface), so its preparation can
+ * be made once for many calls.  Bytes of the prepared buffer for this head
+ * (its prep fields ignored), 0 when the head is invalid.  Depends on V, H,
+ * bits and group only.
+ */
+size_t cce_head_prepare_bytes(const cce_head *head);
+
+/*
+ * Writes the head's preparation into `prep` (device, 256-byte aligned, at
+ * least cce_head_prepare_bytes), asynchronously on `stream`; the head's own
+ * prep fields are ignored.  Set head->prep / prep_bytes to it for later calls.
+ * Errors: those of the head (CCE_ERR_INVALID_ARG, CCE_ERR_UNSUPPORTED),
+ * CCE_ERR_INVALID_ARG for a NULL or misaligned prep, CCE_ERR_WORKSPACE when
+ * prep_bytes is too small, CCE_ERR_HIP after a failed launch.
+ */
+cce_status cce_head_prepare(const cce_head *head, void *prep, size_t prep_bytes, void *stream);
 
 /*
  * Bytes of device workspace that cce_forward / cce_backward need for this head
  * and M tokens.  Returns 0 when the head or M is invalid (cce_forward then
- * reports why).  The value depends only on (V, H, bits, M) and the compute
- * unit count of the current device (the launch plan fills whole rounds).
+ * reports why).  The value depends only on (V, H, bits, group, M, whether
+ * head->prep is set) and the compute unit count of the current device (the
+ * launch plan fills whole rounds).
  */
 size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M);
 size_t cce_backward_workspace_bytes(const cce_head *head, int64_t M);

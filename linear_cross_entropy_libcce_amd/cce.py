@@ -21,7 +21,7 @@ EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
            "cce_abi_version", "cce_profile_enable", "cce_profile_read",
            "cce_dense_forward", "cce_dense_backward", "cce_dense_forward_workspace_bytes",
            "cce_dense_backward_workspace_bytes", "cce_forward_backward", "cce_forward_backward_workspace_bytes",
-           "cce_forward_static")
+           "cce_forward_static", "cce_head_prepare", "cce_head_prepare_bytes")
 
 BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
@@ -34,7 +34,8 @@ DH_DTYPES = {"f32": 0, "bf16": 1}            # cce_dh_dtype
 class cce_head(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("V", ctypes.c_int64), ("H", ctypes.c_int64), ("bits", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("softcap", ctypes.c_float), ("sb_dtype", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("softcap", ctypes.c_float), ("sb_dtype", ctypes.c_int32),
+                ("prep", ctypes.c_void_p), ("prep_bytes", ctypes.c_size_t)]
 
 
 class cce_dense_head(ctypes.Structure):
@@ -87,6 +88,10 @@ def load(path: str = LIB_PATH):
     lib.cce_forward_backward_workspace_bytes.argtypes = [HP, I64]
     lib.cce_forward_static.restype = ctypes.c_int
     lib.cce_forward_static.argtypes = [HP, P, I64, P, P, P, P, P]
+    lib.cce_head_prepare_bytes.restype = SZ
+    lib.cce_head_prepare_bytes.argtypes = [HP]
+    lib.cce_head_prepare.restype = ctypes.c_int
+    lib.cce_head_prepare.argtypes = [HP, P, SZ, P]
     DP = ctypes.POINTER(cce_dense_head)
     lib.cce_dense_forward.restype = ctypes.c_int
     lib.cce_dense_forward.argtypes = [DP, P, I64, P, P, P, P, P, SZ, P]
@@ -124,6 +129,7 @@ class Head:
     softcap: float = 0.0
     group: int = 64
     sb_dtype: str = "f32"
+    prep: "object" = None   # uint8 device tensor written by cce_head_prepare, or None
 
     @property
     def V(self) -> int:
@@ -135,7 +141,8 @@ class Head:
 
     def c_struct(self) -> cce_head:
         return cce_head(self.wq.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
-                        self.V, self.H, self.bits, self.group, float(self.softcap), SB_DTYPES[self.sb_dtype])
+                        self.V, self.H, self.bits, self.group, float(self.softcap), SB_DTYPES[self.sb_dtype],
+                        _ptr(self.prep), 0 if self.prep is None else self.prep.numel())
 
 
 @dataclasses.dataclass
@@ -247,6 +254,33 @@ def cce_forward(h, head: Head, targets, mask=None, workspace=None, out=None):
 
 
 STATIC_SCRATCH_BYTES = 128 << 20   # CCE_STATIC_SCRATCH_BYTES
+
+
+def cce_head_prepare_bytes(head: Head) -> int:
+    """Bytes of the head's prepared buffer (0 for an invalid head)."""
+    hs = head.c_struct()
+    hs.prep, hs.prep_bytes = None, 0
+    return int(load().cce_head_prepare_bytes(ctypes.byref(hs)))
+
+
+def cce_head_prepare(head: Head, prep=None):
+    """Write the head's preparation (into `prep`, a uint8 device tensor, or a
+    new one) on the current stream and attach it to `head`: later calls skip
+    the per-call preparation.  Returns the buffer.  Call again after changing
+    wq, scales or biases (or set head.prep = None)."""
+    import torch
+    lib = load()
+    dev = head.scales.device
+    nb = cce_head_prepare_bytes(head)
+    if nb == 0:
+        raise CceError(CCE_ERR_INVALID_ARG, "invalid head")
+    if prep is None:
+        prep = torch.empty(nb, dtype=torch.uint8, device=dev)
+    hs = head.c_struct()
+    hs.prep, hs.prep_bytes = None, 0
+    _check(lib.cce_head_prepare(ctypes.byref(hs), _ptr(prep), prep.numel(), _stream(dev)))
+    head.prep = prep
+    return prep
 
 
 def cce_forward_static(h, head: Head, targets, mask=None, out=None):

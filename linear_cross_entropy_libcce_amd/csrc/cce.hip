@@ -97,8 +97,12 @@ struct Plan {
   int chunk_tiles, nchunks, ksplit, k_tiles, HT, bwd_tpw;  // k_tiles: vocabulary tiles per dh split
   int64_t ld_coeff;
   // workspace offsets (bytes)
-  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_baug, o_rt, o_slast, o_bmx, o_sabs, o_part, o_coeff, o_dhp, o_fl,
-      fwd_bytes, bwd_bytes;
+  size_t o_cnt, o_idx, o_inv, o_tok, o_haug, o_sabs, o_part, o_coeff, o_dhp, o_fl, fwd_bytes, bwd_bytes;
+  // the head side (bias-block digits, fold ratios, last scales, digit block
+  // maxima): offsets within its region, which is the caller's prepared buffer
+  // (head->prep) or lies in the workspace at o_hs
+  bool prep;
+  size_t o_hs, h_baug, h_rt, h_slast, h_bmx, hs_bytes;
   size_t o_hT, o_coeffT;  // dense heads: transposed h and coefficient chunk of the dW contraction
   // fused pass (softcap in (0, CAP_FIXED_REF_MAX], quantized head): launched
   // work ids per chunk, split capacity per chunk, partials and target c'
@@ -115,7 +119,28 @@ struct Plan {
 constexpr int DENSE_BITS = 16;
 constexpr int64_t MAX_DW_M_PAD = (int64_t)1 << 21;  // 32-bit buffer offsets of the dW operands
 
-cce_status check_head(const cce_head *hd) {
+// Layout of the head side (depends on V, H, bits and group only).
+struct HeadSide {
+  size_t baug, rt, slast, bmx, bytes;
+};
+HeadSide head_side(const cce_head *hd) {
+  const bool dense = hd->bits == DENSE_BITS;
+  const int64_t kw = hd->group == 32 ? 32 : KSTEP;
+  const int64_t G = hd->H / kw, Gq = hd->H / hd->group;
+  const int64_t P = dense ? 0 : cdiv(3 * Gq, KSTEP) * KSTEP;
+  const int64_t Kb = 2 * P, NB = Kb / kw;
+  HeadSide r{};
+  size_t o = 0;
+  r.baug = o;  o = align_up(o + (size_t)hd->V * Kb, 256);
+  r.rt = o;    o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)(NB + G) * hd->V), 256);
+  r.slast = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)hd->V), 256);
+  r.bmx = o;   o = align_up(o + (dense ? 0 : sizeof(unsigned) * (size_t)cdiv(hd->V, 64)), 256);
+  r.bytes = o;
+  return r;
+}
+
+// The head's own fields, without a prepared head side.
+cce_status check_head_fields(const cce_head *hd) {
   if (!hd || !hd->wq || !hd->scales || !hd->biases) return CCE_ERR_INVALID_ARG;
   if (hd->V < 1 || hd->H < 1) return CCE_ERR_INVALID_ARG;
   if (!(hd->softcap >= 0.0f) || !std::isfinite(hd->softcap)) return CCE_ERR_INVALID_ARG;
@@ -130,6 +155,13 @@ cce_status check_head(const cce_head *hd) {
   if (((uintptr_t)hd->wq & 15) || ((uintptr_t)hd->scales & sal) || ((uintptr_t)hd->biases & sal))
     return CCE_ERR_INVALID_ARG;
   return CCE_OK;
+}
+
+cce_status check_head(const cce_head *hd) {
+  const cce_status s = check_head_fields(hd);
+  if (s != CCE_OK || !hd->prep) return s;
+  if ((uintptr_t)hd->prep & 255) return CCE_ERR_INVALID_ARG;
+  return hd->prep_bytes < head_side(hd).bytes ? CCE_ERR_WORKSPACE : CCE_OK;
 }
 
 Plan make_plan(const cce_head *hd, int64_t M) {
@@ -214,10 +246,17 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.o_inv = o;  o = align_up(o + sizeof(int) * std::max<int64_t>(M, 1), 256);
   p.o_tok = o;  o = align_up(o + sizeof(TokRec) * p.M_pad, 256);
   p.o_haug = o; o = align_up(o + (size_t)2 * p.M_pad * p.Ka, 256);
-  p.o_baug = o; o = align_up(o + (size_t)p.V * p.Kb, 256);
-  p.o_rt = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)(p.NB + p.G) * p.V), 256);
-  p.o_slast = o; o = align_up(o + (dense ? 0 : sizeof(float) * (size_t)p.V), 256);
-  p.o_bmx = o; o = align_up(o + (dense ? 0 : sizeof(unsigned) * (size_t)cdiv(p.V, 64)), 256);
+  {
+    const HeadSide hs = head_side(hd);
+    p.prep = hd->prep != nullptr;
+    p.h_baug = hs.baug;
+    p.h_rt = hs.rt;
+    p.h_slast = hs.slast;
+    p.h_bmx = hs.bmx;
+    p.hs_bytes = hs.bytes;
+    p.o_hs = o;
+    if (!p.prep) o = align_up(o + hs.bytes, 256);
+  }
   p.o_sabs = o; o = align_up(o + sizeof(float) * p.M_pad, 256);
   const size_t common = o;
   p.o_part = common;
@@ -302,6 +341,13 @@ T *ws_at(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+// an array of the head side: in the prepared buffer, or in the workspace
+template <typename T>
+T *hs_at(const Plan &p, const cce_head *hd, void *ws, size_t off) {
+  char *base = p.prep ? static_cast<char *>(const_cast<void *>(hd->prep)) : static_cast<char *>(ws) + p.o_hs;
+  return reinterpret_cast<T *>(base + off);
+}
+
 // compaction, augmented rows and token records, target logits
 void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32_t *targets,
                    const uint8_t *mask, const float *lse, const float *g, void *ws, hipStream_t st,
@@ -335,13 +381,14 @@ void enqueue_front(const Plan &p, const cce_head *hd, const void *h, const int32
   f.biases = hd->biases;
   f.tok = tok;
   f.haug = haug;
-  f.baug = ws_at<uint8_t>(ws, p.o_baug);
-  f.rt = ws_at<float>(ws, p.o_rt);
+  f.baug = hs_at<uint8_t>(p, hd, ws, p.h_baug);
+  f.rt = hs_at<float>(p, hd, ws, p.h_rt);
   f.gs = p.gs;
   f.Gq = p.Gq;
   f.sbt = p.sbt;
-  f.slast = ws_at<float>(ws, p.o_slast);
-  f.bmxb = ws_at<unsigned>(ws, p.o_bmx);
+  f.slast = hs_at<float>(p, hd, ws, p.h_slast);
+  f.bmxb = hs_at<unsigned>(p, hd, ws, p.h_bmx);
+  f.head = p.prep ? 0 : 1;  // a prepared head: token rows only
   f.sabs = ws_at<float>(ws, p.o_sabs);
   f.P = p.P;
   f.V = p.V;
@@ -361,10 +408,10 @@ TileArgs tile_args(const Plan &p, const cce_head *hd, void *ws) {
   const bool dense = hd->bits == DENSE_BITS;
   TileArgs a{};
   a.haug = ws_at<const uint16_t>(ws, p.o_haug);
-  a.baug = ws_at<const uint8_t>(ws, p.o_baug);
-  a.rt = ws_at<const float>(ws, p.o_rt);
-  a.slast = ws_at<const float>(ws, p.o_slast);
-  a.bmxb = ws_at<const unsigned>(ws, p.o_bmx);
+  a.baug = hs_at<const uint8_t>(p, hd, ws, p.h_baug);
+  a.rt = hs_at<const float>(p, hd, ws, p.h_rt);
+  a.slast = hs_at<const float>(p, hd, ws, p.h_slast);
+  a.bmxb = hs_at<const unsigned>(p, hd, ws, p.h_bmx);
   a.nbmx = dense ? 0 : (int)cdiv(p.V, 64);
   a.sabs = ws_at<const float>(ws, p.o_sabs);
   a.wq = hd->wq;
@@ -728,6 +775,48 @@ const char *cce_status_str(cce_status s) {
     case CCE_ERR_HIP: return g_err[0] ? g_err : "HIP error";
   }
   return "unknown status";
+}
+
+size_t cce_head_prepare_bytes(const cce_head *head) {
+  if (check_head_fields(head) != CCE_OK) return 0;
+  return head_side(head).bytes;
+}
+
+cce_status cce_head_prepare(const cce_head *head, void *prep, size_t prep_bytes, void *stream) {
+  const cce_status s = check_head_fields(head);
+  if (s != CCE_OK) return s;
+  if (!prep || ((uintptr_t)prep & 255)) return CCE_ERR_INVALID_ARG;
+  const HeadSide hs = head_side(head);
+  if (prep_bytes < hs.bytes) return CCE_ERR_WORKSPACE;
+  // the front's head blocks alone (no token rows), into the caller's buffer
+  const Plan p = make_plan(head, 0);
+  char *b = static_cast<char *>(prep);
+  FrontArgs f{};
+  f.wq = head->wq;
+  f.scales = head->scales;
+  f.biases = head->biases;
+  f.baug = reinterpret_cast<uint8_t *>(b + hs.baug);
+  f.rt = reinterpret_cast<float *>(b + hs.rt);
+  f.slast = reinterpret_cast<float *>(b + hs.slast);
+  f.bmxb = reinterpret_cast<unsigned *>(b + hs.bmx);
+  f.gs = p.gs;
+  f.Gq = p.Gq;
+  f.sbt = p.sbt;
+  f.P = p.P;
+  f.V = p.V;
+  f.H = (int)p.H;
+  f.G = p.G;
+  f.Kb = p.Kb;
+  f.Ka = p.Ka;
+  f.NB = p.NB;
+  f.wpr = p.wpr;
+  f.M_pad = 0;
+  f.cap = p.cap;
+  f.head = 1;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  CCE_LAUNCH("front", st, launch_front(st, p.bits, f));
+  return hip_status();
 }
 
 size_t cce_forward_workspace_bytes(const cce_head *head, int64_t M) {

@@ -204,6 +204,7 @@ struct FrontArgs {
   int gs, Gq, sbt;         // quantization group, groups per row, scale/bias dtype
   float cap;
   int bwd;
+  int head;                // 1: the head blocks run (the head side is not prepared)
   // compact != 0: the row blocks compact the mask themselves (small M) and
   // write idx_out, inv and cnt; otherwise idx comes from the compaction launch
   int compact, M;

@@ -696,7 +696,9 @@ void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
     hipLaunchKernelGGL(k_front<16>, dim3((unsigned)f.M_pad), dim3(256), 0, st, f);
     return;
   }
-  const dim3 grid((unsigned)(f.M_pad + (f.V + HP_ROWS - 1) / HP_ROWS));
+  // token rows [0, M_pad), then the head blocks of HP_ROWS vocabulary rows
+  const dim3 grid((unsigned)(f.M_pad + (f.head ? (f.V + HP_ROWS - 1) / HP_ROWS : 0)));
+  if (grid.x == 0) return;
   if (bits == 4)
     hipLaunchKernelGGL(k_front<4>, grid, dim3(256), 0, st, f);
   else

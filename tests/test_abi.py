@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 6
+    assert lib.cce_abi_version() == 7
 
 
 def head(**kw):
@@ -45,6 +45,35 @@ def fwd(lib, hd, M=4, h=0x4000, targets=0x5000, logp=0x6000, lse=0x7000, ws=None
     if ws is None:
         ws, nbytes = 0x100000, 1 << 40
     return lib.cce_forward(ctypes.byref(hd), h, M, targets, None, logp, lse, ws, nbytes, None)
+
+
+def test_head_prepare_sizes_and_errors(lib):
+    # the prepared head side: its size depends on the head's shape only, and a
+    # head that carries it needs less workspace; the checks return before any
+    # launch (no GPU needed)
+    hd = head()
+    nb = lib.cce_head_prepare_bytes(ctypes.byref(hd))
+    assert nb > 0 and nb % 256 == 0
+    assert lib.cce_head_prepare_bytes(ctypes.byref(head(V=100000))) > nb
+    assert lib.cce_head_prepare_bytes(ctypes.byref(head(bits=3))) == 0
+    assert lib.cce_head_prepare_bytes(ctypes.byref(head(prep=0x9000, prep_bytes=1))) == nb  # prep fields ignored
+    for M in (16, 100000):
+        plain = lib.cce_forward_workspace_bytes(ctypes.byref(hd), M)
+        prepd = lib.cce_forward_workspace_bytes(ctypes.byref(head(prep=0x900000, prep_bytes=nb)), M)
+        assert 0 < prepd < plain and plain - prepd >= nb - 256
+        plain = lib.cce_forward_backward_workspace_bytes(ctypes.byref(hd), M)
+        prepd = lib.cce_forward_backward_workspace_bytes(ctypes.byref(head(prep=0x900000, prep_bytes=nb)), M)
+        assert 0 < prepd < plain
+    # a prepared buffer too small, or misaligned: no workspace size, and calls refuse
+    assert lib.cce_forward_workspace_bytes(ctypes.byref(head(prep=0x900000, prep_bytes=nb - 256)), 16) == 0
+    assert fwd(lib, head(prep=0x900000, prep_bytes=nb - 256)) == cce.CCE_ERR_WORKSPACE
+    assert fwd(lib, head(prep=0x900010, prep_bytes=nb)) == cce.CCE_ERR_INVALID_ARG
+    # cce_head_prepare's own checks
+    assert lib.cce_head_prepare(ctypes.byref(hd), None, nb, None) == cce.CCE_ERR_INVALID_ARG
+    assert lib.cce_head_prepare(ctypes.byref(hd), 0x900010, nb, None) == cce.CCE_ERR_INVALID_ARG
+    assert lib.cce_head_prepare(ctypes.byref(hd), 0x900000, nb - 1, None) == cce.CCE_ERR_WORKSPACE
+    assert lib.cce_head_prepare(ctypes.byref(head(bits=3)), 0x900000, nb, None) == cce.CCE_ERR_UNSUPPORTED
+    assert lib.cce_head_prepare(ctypes.byref(head(H=250)), 0x900000, nb, None) == cce.CCE_ERR_INVALID_ARG
 
 
 def test_workspace_sizes(lib):
