@@ -134,6 +134,9 @@ def main():
                     help="capture one step in a HIP graph and time its replays (launch-bound small M)")
     ap.add_argument("--dense", action="store_true",
                     help="a trainable dense bf16 head of the workload's shape (forward, dh and dW)")
+    ap.add_argument("--prepared", action="store_true",
+                    help="prepare the frozen head once (cce_head_prepare) before the timed steps; the steps then "
+                         "skip the per-call derivation of its per-row data")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -170,8 +173,8 @@ def main():
         w = dataclasses.replace(w, bias=args.bias, name="%s, %s head" % (w.name, args.bias))
     dev = torch.device("cuda:0")
     if args.dense:
-        if args.skip or args.group or args.sb_dtype:
-            sys.exit("--dense takes no quantization or skip options")
+        if args.skip or args.group or args.sb_dtype or args.prepared:
+            sys.exit("--dense takes no quantization, skip or preparation options")
         w = dataclasses.replace(w, name="%s shape, dense bf16 head" % w.name.split(" 4-bit")[0].split(" 8-bit")[0])
         log("generating a dense head of workload %d's shape (%s)" % (args.workload, w.name))
         inp = syn.make_dense(w.M, w.H, w.V, syn.seed_for(args.workload), softcap=w.softcap, targets=w.targets,
@@ -184,6 +187,10 @@ def main():
         log("generating workload %d (%s)" % (args.workload, w.name))
         inp = syn.make_inputs(w, syn.seed_for(args.workload))
         head = cce.head_from_numpy(inp, dev)
+        if args.prepared:
+            cce.cce_head_prepare(head)
+            torch.cuda.synchronize()
+            w = dataclasses.replace(w, name="%s, prepared head" % w.name)
         ws_f = torch.empty(cce.forward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
         ws_b = torch.empty(cce.backward_workspace_bytes(head, inp["M"]), dtype=torch.uint8, device=dev)
     M, H, V = inp["M"], inp["H"], inp["V"]
