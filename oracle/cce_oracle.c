@@ -25,7 +25,7 @@
  *      dh = sum_v coeff_v * w[v][:] (same file, scalar backward kernel's
  *      phase 1 and phase 2).
  *
- * Readings where the pages leave a step open (also listed in the design doc):
+ * Readings where the pages leave a step open:
  *   - a target outside [0, V) matches no row: its target term is 0, so
  *     logp = -lse and there is no one-hot term in the gradient;
  *   - a masked token (mask[t] == 0) has logp = lse = 0 and a zero dh row;
