@@ -375,6 +375,9 @@ def main():
         + (" (dense-equivalent: skipped pairs counted)" if args.skip else ""),
         "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),
         "tflops_6mvh": round(6.0 * M_eff * V * H / (ms * 1e-3) / 1e12, 1),
+        # the same step priced as a forward plus a recomputing backward (logits twice, dh): the rate such a
+        # design would need for this throughput, as a fraction of the peak
+        "pct_bf16_peak_6mvh": round(100.0 * 6.0 * M_eff * V * H / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
         "head_GB_per_s": round(head_gbs, 1),
         "kernel_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
         "roofline": roof,
