@@ -9,7 +9,9 @@ step is one call of cce_forward_backward: under a softcap of at most 40 its
 single pass (the logits computed once), otherwise its forward and backward
 passes after one front.  The `two_calls` field times cce_forward +
 cce_backward (the backward recomputes the logits) on the same inputs; the
-skips and the dense head always take their calls.  Each step is timed
+skips always take their calls, and a dense head (--dense) takes
+cce_dense_forward_backward alike (the single pass under a softcap of at most
+40, its dW last).  Each step is timed
 between its own pair of HIP events; the median is reported.
 
 Prints one JSON line.  `value` is supervised tokens per second of fwd+bwd.
@@ -225,20 +227,27 @@ def main():
         fwd()
         bwd()
 
-    # one call (cce_forward_backward) for a quantized head without skips: the
-    # single pass where the head allows it (0 < softcap <= 40), else its two
-    # passes after one front; the skips and the dense head take the two calls
-    combined = not args.dense and not args.skip and args.path != "calls"
+    # one call (cce_forward_backward, cce_dense_forward_backward) without
+    # skips: the single pass where the head allows it (0 < softcap <= 40), else
+    # its two passes; the skips take the two calls
+    combined = not args.skip and args.path != "calls"
     fused = combined and 0.0 < inp["softcap"] <= 40.0
     if combined:
-        ws_fb = torch.empty(cce.forward_backward_workspace_bytes(head, M), dtype=torch.uint8, device=dev)
+        nb = (cce.dense_forward_backward_workspace_bytes(head, M) if args.dense
+              else cce.forward_backward_workspace_bytes(head, M))
+        ws_fb = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     def fused_step():
-        cce.cce_forward_backward(h, head, t, None, m, workspace=ws_fb, out=(logp, lse, dh))
+        if args.dense:
+            cce.cce_dense_forward_backward(h, head, t, None, m, workspace=ws_fb, out=(logp, lse, dh), dw_out=dw)
+        else:
+            cce.cce_forward_backward(h, head, t, None, m, workspace=ws_fb, out=(logp, lse, dh))
 
     step = fused_step if combined else calls
-    log("step: %s" % (("cce_forward_backward (%s)" % ("single pass" if fused else "two passes, one front"))
-                      if combined else "cce_forward + cce_backward"))
+    fb_name = "cce_dense_forward_backward" if args.dense else "cce_forward_backward"
+    calls_name = "cce_dense_forward + cce_dense_backward" if args.dense else "cce_forward + cce_backward"
+    log("step: %s" % (("%s (%s)" % (fb_name, "single pass" if fused else "two passes"))
+                      if combined else calls_name))
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
@@ -290,7 +299,7 @@ def main():
     if combined:
         ms_calls = float(np.median(timed(replayable(calls))))
         two_calls = {"ms_per_step": round(ms_calls, 4), "tokens_per_s": round(M_eff / (ms_calls * 1e-3), 1),
-                     "tflops": round(6.0 * M_eff * V * H / (ms_calls * 1e-3) / 1e12, 1)}
+                     "tflops": round((8.0 if args.dense else 6.0) * M_eff * V * H / (ms_calls * 1e-3) / 1e12, 1)}
         log("cce_forward + cce_backward: %.3f ms/step (median)" % ms_calls)
 
     # per-kernel timing pass (same steps, events around every launch)
@@ -308,7 +317,7 @@ def main():
 
     # MFMA work per step: forward logits and dh always, the backward's logit
     # recompute unless the single pass ran (and dW for a dense head)
-    gemms = 4.0 if args.dense else (2.0 if fused else 3.0)
+    gemms = (3.0 if fused else 4.0) if args.dense else (2.0 if fused else 3.0)
     exec_flops = 2.0 * gemms * M_eff * V * H
     if args.dense:
         head_bytes = 2 * V * H
@@ -364,13 +373,14 @@ def main():
                    "g": 1.0,
                    "skip": None if not args.skip else {"block_eps": block_eps, "filter_eps": filter_eps},
                    "hip_graph": bool(args.graph),
-                   "step": ("cce_forward_backward (single pass)" if fused else
-                            ("cce_forward_backward (two passes)" if combined else "cce_forward+cce_backward"))},
+                   "step": ("%s (single pass)" % fb_name if fused else
+                            ("%s (two passes)" % fb_name if combined else calls_name))},
         "ms_fwd": round(ms_fwd, 4),
         "ms_bwd": round(ms_bwd, 4),
         "two_calls": two_calls,
         "tflops": round(tflops, 1),
-        "flops_counted": ("8*M_eff*V*H (forward, recompute, dh, dW)" if args.dense else
+        "flops_counted": (("6*M_eff*V*H (logits once, dh, dW)" if fused else "8*M_eff*V*H (forward, recompute, dh, dW)")
+                          if args.dense else
                           ("4*M_eff*V*H (logits once, dh)" if fused else "6*M_eff*V*H (logits, recompute, dh)"))
         + (" (dense-equivalent: skipped pairs counted)" if args.skip else ""),
         "pct_bf16_peak": round(100.0 * tflops / BF16_PEAK_TFLOPS, 2),

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define CCE_ABI_VERSION 7
+#define CCE_ABI_VERSION 8
 
 /* Vocabulary rows per block of block_max, and supervised tokens per token
  * tile of the backward skips (both are the kernels' tile sizes). */
@@ -298,6 +298,27 @@ cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t
                               const int32_t *targets, const uint8_t *mask,
                               const float *lse, const float *g, float *dh, float *dw,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward and backward of a dense head in one call (the two passes of page
+ * "mlx-bun 0.0.4 -> 0.0.6", src/train/flash-cce.ts, flashCceForward and
+ * flashCceBackward, with g known up front).  Outputs: logp and lse as
+ * cce_dense_forward, dh (fp32) and dw as cce_dense_backward, with g as there
+ * (NULL = all ones).  With 0 < softcap <= 40 the logits are computed once:
+ * the forward's fixed reference e^{y - cap} gives each coefficient up to the
+ * token's factor g e^{cap - lse}, every coefficient chunk is kept until lse is
+ * known, and dW is formed from them last; the workspace then holds all the
+ * chunks (about 2 M V bytes).  Other softcaps run cce_dense_forward and then
+ * cce_dense_backward on the same workspace.  dW takes every coefficient
+ * rounded to bf16 and, in the single pass, each h row times its factor
+ * rounded to bf16.  Errors as cce_dense_backward.
+ */
+size_t cce_dense_forward_backward_workspace_bytes(const cce_dense_head *head, int64_t M);
+cce_status cce_dense_forward_backward(const cce_dense_head *head, const void *h, int64_t M,
+                                      const int32_t *targets, const uint8_t *mask,
+                                      const float *g, float *logp, float *lse, float *dh,
+                                      float *dw, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /*
  * The forward without a workspace, for callers that cannot allocate device

@@ -21,7 +21,8 @@ EXPORTS = ("cce_forward", "cce_backward", "cce_forward_ex", "cce_backward_ex",
            "cce_abi_version", "cce_profile_enable", "cce_profile_read",
            "cce_dense_forward", "cce_dense_backward", "cce_dense_forward_workspace_bytes",
            "cce_dense_backward_workspace_bytes", "cce_forward_backward", "cce_forward_backward_workspace_bytes",
-           "cce_forward_static", "cce_head_prepare", "cce_head_prepare_bytes")
+           "cce_forward_static", "cce_head_prepare", "cce_head_prepare_bytes",
+           "cce_dense_forward_backward", "cce_dense_forward_backward_workspace_bytes")
 
 BLOCK_V = 256      # CCE_BLOCK_V: vocabulary rows per block of block_max
 TOKEN_TILE = 256   # CCE_TOKEN_TILE: supervised tokens per token tile of the skips
@@ -101,6 +102,10 @@ def load(path: str = LIB_PATH):
     lib.cce_dense_forward_workspace_bytes.argtypes = [DP, I64]
     lib.cce_dense_backward_workspace_bytes.restype = SZ
     lib.cce_dense_backward_workspace_bytes.argtypes = [DP, I64]
+    lib.cce_dense_forward_backward.restype = ctypes.c_int
+    lib.cce_dense_forward_backward.argtypes = [DP, P, I64, P, P, P, P, P, P, P, P, SZ, P]
+    lib.cce_dense_forward_backward_workspace_bytes.restype = SZ
+    lib.cce_dense_forward_backward_workspace_bytes.argtypes = [DP, I64]
     lib.cce_status_str.restype = ctypes.c_char_p
     lib.cce_status_str.argtypes = [ctypes.c_int]
     lib.cce_abi_version.restype = ctypes.c_int
@@ -205,6 +210,10 @@ def dense_forward_workspace_bytes(head: DenseHead, M: int) -> int:
 
 def dense_backward_workspace_bytes(head: DenseHead, M: int) -> int:
     return int(load().cce_dense_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
+
+
+def dense_forward_backward_workspace_bytes(head: DenseHead, M: int) -> int:
+    return int(load().cce_dense_forward_backward_workspace_bytes(ctypes.byref(head.c_struct()), M))
 
 
 def n_blocks(head: Head) -> int:
@@ -405,6 +414,37 @@ def cce_dense_backward(h, head: DenseHead, targets, lse, g=None, mask=None, need
     _check(lib.cce_dense_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(lse), _ptr(g),
                                   _ptr(dh), _ptr(dw), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return dh, dw
+
+
+def cce_dense_forward_backward(h, head: DenseHead, targets, g=None, mask=None, need_dw=True, workspace=None,
+                               out=None, dw_out=None):
+    """(logp, lse, dh, dW or None) in one call on a dense bf16 head; g float32
+    [M] or None (all ones).  out: (logp, lse, dh) to write into."""
+    import torch
+    lib = load()
+    M, dev = _tokens(h, head, targets, mask)
+    _expect(head.w, torch.bfloat16, dev, (head.V, head.H), "w")
+    if g is not None:
+        _expect(g, torch.float32, dev, (M,), "g")
+    if out is not None:
+        logp, lse, dh = out
+        _expect(dh, torch.float32, dev, (M, head.H), "dh")
+    else:
+        logp, lse = _fwd_out(M, dev, None)
+        dh = torch.empty((M, head.H), dtype=torch.float32, device=dev)
+    dw = None
+    if need_dw:
+        if dw_out is not None:
+            _expect(dw_out, torch.float32, dev, (head.V, head.H), "dw_out")
+            dw = dw_out
+        else:
+            dw = torch.empty((head.V, head.H), dtype=torch.float32, device=dev)
+    hs = head.c_struct()
+    ws = _workspace(lib.cce_dense_forward_backward_workspace_bytes(ctypes.byref(hs), M), dev, workspace)
+    _check(lib.cce_dense_forward_backward(ctypes.byref(hs), _ptr(h), M, _ptr(targets), _ptr(mask), _ptr(g),
+                                          _ptr(logp), _ptr(lse), _ptr(dh), _ptr(dw), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(dev)))
+    return logp, lse, dh, dw
 
 
 def dense_head_from_numpy(inp: dict, device="cuda") -> DenseHead:

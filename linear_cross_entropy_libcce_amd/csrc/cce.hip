@@ -112,6 +112,12 @@ struct Plan {
   // cce_forward_backward without the single pass: the forward's partials
   // after the backward's buffers (the backward tile merges them itself)
   size_t o_ppart, twopass_bytes;
+  // the dense head's single pass (cce_dense_forward_backward, softcap in (0,
+  // CAP_FIXED_REF_MAX]): every coefficient chunk kept until dW, whose
+  // launches follow the reduce; dh slabs, split sums, target c', per-row
+  // factors, scaled hT and one transposed chunk
+  bool dfused;
+  size_t df_coeff, df_dhp, df_tdc, df_fpart, df_fac, df_hT, df_coeffT, df_bytes;
 };
 
 // A dense bf16 head runs as an internal head of 16 "bits" per element: the
@@ -296,6 +302,16 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
     p.o_coeffT = o;
     p.bwd_bytes = align_up(o + (size_t)2 * p.ld_coeff * p.M_pad, 256);
+    p.dfused = p.cap > 0.0f && p.cap <= CAP_FIXED_REF_MAX;
+    size_t q = common;
+    p.df_coeff = q;  q = align_up(q + (size_t)p.nchunks * 2 * p.M_pad * p.ld_coeff, 256);
+    p.df_dhp = q;    q = align_up(q + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
+    p.df_tdc = q;    q = align_up(q + sizeof(float) * p.M_pad, 256);
+    p.df_fpart = q;  q = align_up(q + sizeof(float) * (size_t)p.mass_ld * p.M_pad, 256);
+    p.df_fac = q;    q = align_up(q + 2 * sizeof(float) * p.M_pad, 256);
+    p.df_hT = q;     q = align_up(q + (size_t)2 * p.H * p.M_pad, 256);
+    p.df_coeffT = q; q = align_up(q + (size_t)2 * p.ld_coeff * p.M_pad, 256);
+    p.df_bytes = q;
   }
   return p;
 }
@@ -557,7 +573,7 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
     wa.H = (int)p.H;
     wa.M_pad = (int)p.M_pad;
     wa.HT = p.HT;
-    CCE_LAUNCH("hT", st, launch_hT(st, a.haug, p.Ka / 16, p.Kb / 8, (int)p.M_pad, (int)p.H, a.cnt,
+    CCE_LAUNCH("hT", st, launch_hT(st, a.haug, p.Ka / 16, p.Kb / 8, (int)p.M_pad, (int)p.H, a.cnt, nullptr,
                                    ws_at<uint16_t>(workspace, p.o_hT)));
   }
 
@@ -574,8 +590,8 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
     ga.accumulate = c > 0;
     CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
     if (dw) {
-      CCE_LAUNCH("coeffT", st, launch_coeffT(st, a.coeff, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt, a.tok, p.V,
-                                             ga.chunk_v0, ws_at<uint16_t>(workspace, p.o_coeffT)));
+      CCE_LAUNCH("coeffT", st, launch_coeffT(st, a.coeff, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt, a.tok, nullptr,
+                                             p.V, ga.chunk_v0, ws_at<uint16_t>(workspace, p.o_coeffT)));
       wa.chunk_v0 = ga.chunk_v0;
       wa.nvt = nt;
       CCE_LAUNCH("dw_gemm", st, launch_dw(st, wa));
@@ -586,6 +602,97 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
                                                dh_dtype == CCE_DH_BF16 ? 1 : 0,
                                                ReduceTarget{a.tmass, a.mass, a.mass_ld, a.nblocks, a.full_tiles,
                                                             p.tiles, a.max_splits, 0.0f, a.tdc, nullptr, nullptr}));
+  return hip_status();
+}
+
+// The single pass of a dense head (0 < softcap <= CAP_FIXED_REF_MAX): the
+// fused tile and the dh contraction per chunk as for a quantized head, every
+// chunk kept; the split reduce then forms lse, logp, dh and each row's factor
+// g / (S + e_t); dW last, chunk by chunk, from the unnormalized coefficients
+// and hT scaled by those factors (dW_v = sum_t coefficient_tv (factor_t h_t)).
+cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                           const uint8_t *mask, const float *g, float *logp, float *lse, float *dh, float *dw,
+                           void *workspace, hipStream_t st) {
+  enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false);
+  TileArgs a = tile_args(p, head, workspace);
+  a.mass = ws_at<float>(workspace, p.df_fpart);
+  a.mass_ld = p.mass_ld;
+  a.ld_coeff = p.ld_coeff;
+  a.tdc = ws_at<float>(workspace, p.df_tdc);
+  a.full_tiles = p.chunk_tiles;
+  a.nblocks = p.fus_blocks;
+  a.max_splits = p.fus_max_splits;
+  const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
+  uint16_t *coeff0 = ws_at<uint16_t>(workspace, p.df_coeff);
+  const size_t chunk_elems = (size_t)p.M_pad * p.ld_coeff;
+
+  GemmArgs ga{};
+  ga.ksv = p.ld_coeff / 16;
+  ga.wq = head->wq;
+  ga.scales = head->scales;
+  ga.biases = head->biases;
+  ga.cnt = a.cnt;
+  ga.dh_part = ws_at<float>(workspace, p.df_dhp);
+  ga.V = p.V;
+  ga.H = (int)p.H;
+  ga.gs = p.gs;
+  ga.Gq = p.Gq;
+  ga.sbt = p.sbt;
+  ga.wpr = p.wpr;
+  ga.M_pad = (int)p.M_pad;
+  ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);
+  ga.TT = p.TT;
+  ga.HT = p.HT;
+  ga.ksplit = p.ksplit;
+  ga.nblocks = p.TT * p.HT * p.ksplit;
+  ga.small = a.small;
+  const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
+
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+    a.coeff = coeff0 + c * chunk_elems;
+    a.range_tile0 = t0;
+    a.range_tiles = nt;
+    a.chunk = c;
+    CCE_LAUNCH("tile_fused", st, launch_tile(st, p.bits, PASS_FUSED, g1, a));
+    ga.coeff = a.coeff;
+    ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_tile0 = t0;
+    ga.chunk_steps = nt * (BNT / KSTEP);
+    ga.accumulate = c > 0;
+    CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+  }
+  const int *inv = ws_at<const int>(workspace, p.o_inv);
+  const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
+  float *fac = dw ? ws_at<float>(workspace, p.df_fac) : nullptr;
+  const ReduceTarget rt{2, a.mass, a.mass_ld, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, p.cap, a.tdc,
+                        logp, lse, fac};
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, 0, rt));
+  if (dw) {
+    DwArgs wa{};
+    wa.coeffT = ws_at<const uint16_t>(workspace, p.df_coeffT);
+    wa.hT = ws_at<const uint16_t>(workspace, p.df_hT);
+    wa.cnt = a.cnt;
+    wa.dw = dw;
+    wa.V = p.V;
+    wa.ks16t = p.M_pad / 16;
+    wa.H = (int)p.H;
+    wa.M_pad = (int)p.M_pad;
+    wa.HT = p.HT;
+    CCE_LAUNCH("hT", st, launch_hT(st, a.haug, p.Ka / 16, p.Kb / 8, (int)p.M_pad, (int)p.H, a.cnt, fac,
+                                   ws_at<uint16_t>(workspace, p.df_hT)));
+    for (int c = 0; c < p.nchunks; ++c) {
+      const int t0 = c * p.chunk_tiles;
+      const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+      const int64_t v0 = (int64_t)t0 * BNT;
+      CCE_LAUNCH("coeffT", st, launch_coeffT(st, coeff0 + c * chunk_elems, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt,
+                                             a.tok, fac, p.V, v0, ws_at<uint16_t>(workspace, p.df_coeffT)));
+      wa.chunk_v0 = v0;
+      wa.nvt = nt;
+      CCE_LAUNCH("dw_gemm", st, launch_dw(st, wa));
+    }
+  }
   return hip_status();
 }
 
@@ -925,6 +1032,37 @@ cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t
   if (s != CCE_OK || M == 0) return s;
   return run_backward(&q, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, dw, workspace,
                       workspace_bytes, stream);
+}
+
+size_t cce_dense_forward_backward_workspace_bytes(const cce_dense_head *head, int64_t M) {
+  cce_head q;
+  if (check_dense(head, q) != CCE_OK || M < 0 || M > MAX_M) return 0;
+  const Plan p = make_plan(&q, M);
+  return p.dfused ? p.df_bytes : std::max(p.fwd_bytes, p.bwd_bytes);
+}
+
+cce_status cce_dense_forward_backward(const cce_dense_head *head, const void *h, int64_t M, const int32_t *targets,
+                                      const uint8_t *mask, const float *g, float *logp, float *lse, float *dh,
+                                      float *dw, void *workspace, size_t workspace_bytes, void *stream) {
+  cce_head q;
+  cce_status s = check_dense(head, q);
+  if (s == CCE_OK) s = check_tokens(h, M, targets, workspace);
+  if (s != CCE_OK || M == 0) return s;
+  if (!logp || !lse || !dh || ((uintptr_t)logp & 3) || ((uintptr_t)lse & 3) || ((uintptr_t)dh & 3) ||
+      ((uintptr_t)g & 3) || ((uintptr_t)dw & 3))
+    return CCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(&q, M);
+  if (dw && p.M_pad > MAX_DW_M_PAD) return CCE_ERR_UNSUPPORTED;
+  if (!p.dfused) {  // no fixed reference: the forward, then the backward on the same workspace
+    s = run_forward(&q, h, M, targets, mask, logp, lse, nullptr, workspace, workspace_bytes, stream);
+    if (s != CCE_OK) return s;
+    return run_backward(&q, h, M, targets, mask, lse, g, nullptr, nullptr, dh, CCE_DH_F32, dw, workspace,
+                        workspace_bytes, stream);
+  }
+  if (!workspace || workspace_bytes < p.df_bytes) return CCE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  return run_dense_fused(p, &q, h, M, targets, mask, g, logp, lse, dh, dw, workspace, st);
 }
 
 int cce_profile_enable(int on) {

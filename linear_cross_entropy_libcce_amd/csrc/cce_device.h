@@ -383,6 +383,11 @@ struct ReduceTarget {
   float cap;
   const float *tdc;    // [M_pad] c' of the target
   float *logp, *lse;   // mode 2: the outputs of the forward (the single pass has no merge launch)
+  // mode 2, dense head (or NULL): per compacted row, the token's factor
+  // g / (S + e_t) that turns the chunk's coefficients into g (1[v = t] - p_v) c'
+  // and the target's coefficient in the chunk's units, S c'_t (read by the
+  // dW launches)
+  float *fac;
 };
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16, const ReduceTarget &rt);
@@ -397,10 +402,13 @@ struct DwArgs {
   int64_t V, chunk_v0, ks16t;
   int H, M_pad, HT, nvt;   // HT: 256-column tiles of H; nvt: vocabulary tiles of the chunk
 };
+// fac (or NULL): the single pass's per-row factors (ReduceTarget::fac); hT then
+// holds each row scaled by its factor, and coeffT takes the target's
+// coefficient in the chunk's units
 void launch_hT(hipStream_t st, const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H, const int *cnt,
-               uint16_t *hT);
+               const float *fac, uint16_t *hT);
 void launch_coeffT(hipStream_t st, const uint16_t *coeff, int64_t ksv, int M_pad, int vrows, const int *cnt,
-                   const TokRec *tok, int64_t V, int64_t chunk_v0, uint16_t *coeffT);
+                   const TokRec *tok, const float *fac, int64_t V, int64_t chunk_v0, uint16_t *coeffT);
 void launch_dw(hipStream_t st, const DwArgs &a);
 
 }  // namespace cce

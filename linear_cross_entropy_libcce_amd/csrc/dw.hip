@@ -7,7 +7,9 @@
 //
 // Both operands are stored token-minor (fragment-major rows of tokens), so the
 // contraction over tokens first transposes them into token-major fragments:
-//  * k_hT, once per call: hT[d][r] = h row r (compacted, padded) column d;
+//  * k_hT, once per call: hT[d][r] = h row r (compacted, padded) column d
+//    (in the single pass: times the row's factor g / (S + e_t), rounded to
+//    bf16; rows past the supervised count are zeros);
 //  * k_coeffT, per coefficient chunk: the chunk's [token][vocab] fragments as
 //    [vocab][token] fragments, with the target's whole coefficient (kept out
 //    of the chunk, where dh adds it in fp32) written in, rounded to bf16 like
@@ -28,15 +30,21 @@ constexpr int TLD = TR + 8;    // LDS row stride of the transpose (keeps 16-byte
 // hT[d][r] for r < 256 * active tiles, d < H (haug: [M_pad][Ka] fragment-major,
 // the h part starting at K chunk kb8).
 __global__ void __launch_bounds__(256) k_hT(const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H,
-                                            const int *cnt, uint16_t *hT) {
+                                            const int *cnt, const float *fac, uint16_t *hT) {
   const int r0 = blockIdx.x * TR, d0 = blockIdx.y * TR;
   if (r0 >= active_tiles(cnt) * BM) return;
   __shared__ __attribute__((aligned(16))) uint16_t sT[TR * TLD];
   const int tid = threadIdx.x;
+  const int n = cnt[0];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + 256 * k, r = i >> 3, c = i & 7;
-    const u32x4_t x = *(const u32x4_t *)(haug + frag_slot(r0 + r, kb8 + (d0 >> 3) + c, ks16));
+    u32x4_t x = *(const u32x4_t *)(haug + frag_slot(r0 + r, kb8 + (d0 >> 3) + c, ks16));
+    if (fac) {
+      const float f = (r0 + r < n) ? fac[2 * (r0 + r)] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = pack_rne(bf16_to_f32(x[e] & 0xFFFFu) * f, bf16_to_f32(x[e] >> 16) * f);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sT[(8 * c + 2 * e) * TLD + r] = (uint16_t)(x[e] & 0xFFFFu);
@@ -53,8 +61,8 @@ __global__ void __launch_bounds__(256) k_hT(const uint16_t *haug, int64_t ks16, 
 
 // coeffT: rows = local vocabulary rows of the chunk, K = tokens (ks16t = M_pad / 16).
 __global__ void __launch_bounds__(256) k_coeffT(const uint16_t *coeff, int64_t ksv, const int *cnt,
-                                                const TokRec *tok, int64_t V, int64_t chunk_v0, uint16_t *coeffT,
-                                                int64_t ks16t) {
+                                                const TokRec *tok, const float *fac, int64_t V, int64_t chunk_v0,
+                                                uint16_t *coeffT, int64_t ks16t) {
   const int r0 = blockIdx.x * TR, c0 = blockIdx.y * TR;
   if (r0 >= active_tiles(cnt) * BM) return;
   __shared__ __attribute__((aligned(16))) uint16_t sT[TR * TLD];
@@ -73,7 +81,8 @@ __global__ void __launch_bounds__(256) k_coeffT(const uint16_t *coeff, int64_t k
   if (tid < TR) {  // the token's target column, if it falls in this block
     const TokRec rec = tok[r0 + tid];
     const int64_t vl = (int64_t)rec.tgt - chunk_v0 - c0;
-    if (rec.tgt >= 0 && (int64_t)rec.tgt < V && vl >= 0 && vl < TR) sT[vl * TLD + tid] = (uint16_t)bf16_rne(rec.tval);
+    const float tv = fac ? fac[2 * (r0 + tid) + 1] : rec.tval;
+    if (rec.tgt >= 0 && (int64_t)rec.tgt < V && vl >= 0 && vl < TR) sT[vl * TLD + tid] = (uint16_t)bf16_rne(tv);
   }
   __syncthreads();
 #pragma unroll
@@ -206,15 +215,15 @@ __global__ void __launch_bounds__(TW, 1) k_dw(DwArgs a) {
 }
 
 void launch_hT(hipStream_t st, const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H, const int *cnt,
-               uint16_t *hT) {
+               const float *fac, uint16_t *hT) {
   hipLaunchKernelGGL(k_hT, dim3((unsigned)(M_pad / TR), (unsigned)(H / TR)), dim3(256), 0, st, haug, ks16, kb8,
-                     M_pad, H, cnt, hT);
+                     M_pad, H, cnt, fac, hT);
 }
 
 void launch_coeffT(hipStream_t st, const uint16_t *coeff, int64_t ksv, int M_pad, int vrows, const int *cnt,
-                   const TokRec *tok, int64_t V, int64_t chunk_v0, uint16_t *coeffT) {
+                   const TokRec *tok, const float *fac, int64_t V, int64_t chunk_v0, uint16_t *coeffT) {
   hipLaunchKernelGGL(k_coeffT, dim3((unsigned)(M_pad / TR), (unsigned)(vrows / TR)), dim3(256), 0, st, coeff, ksv,
-                     cnt, tok, V, chunk_v0, coeffT, (int64_t)M_pad / 16);
+                     cnt, tok, fac, V, chunk_v0, coeffT, (int64_t)M_pad / 16);
 }
 
 void launch_dw(hipStream_t st, const DwArgs &a) {

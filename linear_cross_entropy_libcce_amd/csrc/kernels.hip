@@ -612,8 +612,13 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     float l = 0.0f, lp = 0.0f;
     if (r >= 0) {
       const TokRec rec = tok[r];
-      l = tg.cap + logf(S + (rec.tgt >= 0 ? expf(rec.tval - tg.cap) : 0.0f));
+      const float et = rec.tgt >= 0 ? expf(rec.tval - tg.cap) : 0.0f;
+      l = tg.cap + logf(S + et);
       lp = rec.tval - l;
+      if (tg.fac) {  // the dense head's dW: the token's factor and its target coefficient in chunk units
+        tg.fac[2 * r] = rec.g * (1.0f / (S + et));
+        tg.fac[2 * r + 1] = rec.tgt >= 0 ? S * tg.tdc[r] : 0.0f;
+      }
     }
     tg.lse[t] = l;
     tg.logp[t] = lp;

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cce.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cce_abi_version() == 7
+    assert lib.cce_abi_version() == 8
 
 
 def head(**kw):

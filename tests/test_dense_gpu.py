@@ -192,3 +192,73 @@ def test_dense_full_vocabulary_dw_rows(torch_cuda):
     worst_t = max(rel_l2(gpu[3][v], orc[3][k]) for k, v in enumerate(rows) if v in set(tg))
     say("full vocabulary dW rows: rel L2 %.3g (target rows worst %.3g)" % (e, worst_t))
     assert e <= DW_TOL and worst_t <= DW_TOL
+
+
+# ---- cce_dense_forward_backward: one call (the single pass under a softcap <= 40)
+
+def run_combined(torch, inp, g=None, need_dw=True):
+    head = cce.dense_head_from_numpy(inp)
+    h = torch.from_numpy(inp["h"].view("int16")).cuda().view(torch.bfloat16)
+    t = torch.from_numpy(inp["targets"]).cuda()
+    m = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).cuda()
+    gg = None if g is None else torch.from_numpy(np.asarray(g, np.float32)).cuda()
+    logp, lse, dh, dw = cce.cce_dense_forward_backward(h, head, t, gg, m, need_dw=need_dw)
+    torch.cuda.synchronize()
+    out = (logp.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+           dh.cpu().numpy().astype(np.float64), None if dw is None else dw.cpu().numpy().astype(np.float64))
+    del head, h, t, m, gg, logp, lse, dh, dw
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_dense_combined_against_oracle(torch_cuda, name):
+    # softcap 30: the single pass (dW from the kept chunks and hT scaled by each
+    # row's factor); softcaps 0 and 100: the forward and the backward in turn
+    M, H, V, cap, mask, tg = SMALL[name]
+    inp = syn.make_dense(M=M, H=H, V=V, seed=31, softcap=cap, mask=mask, mask_frac=0.4, targets=tg)
+    inp["targets"][3] = V + 5
+    g = np.random.default_rng(2).uniform(-2, 2, size=M)
+    gpu = run_combined(torch_cuda, inp, g=g)
+    orc = oracle.cce_dense(inp, g=g)
+    check_tokens(gpu, orc, np.arange(M), inp["mask"], "combined_" + name)
+    e = rel_l2(gpu[3], orc[3])
+    say("combined_%s: dW rel L2 %.3g" % (name, e))
+    assert e <= DW_TOL and np.all(np.isfinite(gpu[3]))
+
+
+def test_dense_combined_masked_and_without_dw(torch_cuda):
+    inp = syn.make_dense(M=40, H=128, V=500, seed=6, softcap=30.0)
+    inp["mask"] = np.zeros(40, np.uint8)
+    gpu = run_combined(torch_cuda, inp)
+    assert not np.any(gpu[0]) and not np.any(gpu[1]) and not np.any(gpu[2]) and not np.any(gpu[3])
+    inp = syn.make_dense(M=100, H=256, V=900, seed=8, softcap=30.0)
+    a = run_combined(torch_cuda, inp, need_dw=False)
+    b = run_combined(torch_cuda, inp, need_dw=True)
+    assert a[3] is None and np.array_equal(a[2], b[2]) and np.array_equal(a[0], b[0])
+    c = run_combined(torch_cuda, inp, need_dw=True)
+    for x, y in zip(b, c):
+        assert np.array_equal(x, y)
+
+
+def test_dense_combined_full_vocabulary_dw_rows(torch_cuda):
+    # the single pass at full V, H and M (four coefficient chunks, all kept
+    # until dW), 48 supervised tokens, dW rows element by element
+    M = FULL["M"]
+    inp = syn.make_dense(M=M, H=FULL["H"], V=FULL["V"], seed=44, softcap=30.0)
+    keep = np.random.default_rng(13).choice(M, size=48, replace=False)
+    inp["mask"] = np.zeros(M, np.uint8)
+    inp["mask"][keep] = 1
+    inp["targets"][keep[:6]] = 4321
+    inp["targets"][keep[6]] = FULL["V"] - 1
+    g = np.random.default_rng(14).uniform(-1.5, 1.5, size=M)
+    say("combined full vocabulary: GPU")
+    gpu = run_combined(torch_cuda, inp, g=g)
+    tg = inp["targets"][keep]
+    rows = np.unique(np.concatenate([tg, np.random.default_rng(15).choice(FULL["V"], 40, replace=False),
+                                     [0, 65535, 65536, 131072, FULL["V"] - 1]]))
+    orc = oracle.cce_dense(inp, g=g, dw_rows=rows)
+    check_tokens(gpu, orc, np.arange(M), inp["mask"], "combined_fullV")
+    e = rel_l2(gpu[3][rows], orc[3])
+    worst_t = max(rel_l2(gpu[3][v], orc[3][k]) for k, v in enumerate(rows) if v in set(tg))
+    say("combined full vocabulary dW rows: rel L2 %.3g (target rows worst %.3g)" % (e, worst_t))
+    assert e <= DW_TOL and worst_t <= DW_TOL
