@@ -118,11 +118,18 @@ struct Plan {
   // factors, scaled hT and one transposed chunk
   bool dfused;
   size_t df_coeff, df_dhp, df_tdc, df_fpart, df_fac, df_hT, df_coeffT, df_bytes;
+  // the uncapped single pass of a quantized head (cce_forward_backward, no
+  // softcap): every coefficient chunk kept until the merge has each token's
+  // largest logit; dh slabs, the (max, sum) partials, the 32-row block
+  // references and the merge's per-row (m, S, e_t)
+  bool ncfused;
+  size_t nc_coeff, nc_dhp, nc_part, nc_R, nc_nc, nc_bytes;
 };
 
 // A dense bf16 head runs as an internal head of 16 "bits" per element: the
 // 32-wide step path of the tile, no bias block, no scales.
 constexpr int DENSE_BITS = 16;
+constexpr size_t NC_MAX_BYTES = (size_t)32 << 30;  // workspace bound of the uncapped single pass
 constexpr int64_t MAX_DW_M_PAD = (int64_t)1 << 21;  // 32-bit buffer offsets of the dW operands
 
 // Layout of the head side (depends on V, H, bits and group only).
@@ -297,6 +304,17 @@ Plan make_plan(const cce_head *hd, int64_t M) {
   p.bwd_bytes = p.fus_bytes = align_up(o + sizeof(float) * (size_t)p.mass_ld * p.M_pad, 256);
   p.o_ppart = p.bwd_bytes;
   p.twopass_bytes = align_up(p.o_ppart + sizeof(float) * 2 * (2 * (size_t)p.max_splits) * p.M_pad, 256);
+  {
+    size_t q = common;
+    p.nc_coeff = q; q = align_up(q + (size_t)p.nchunks * 2 * p.M_pad * p.ld_coeff, 256);
+    p.nc_dhp = q;   q = align_up(q + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
+    p.nc_part = q;  q = align_up(q + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
+    p.nc_R = q;     q = align_up(q + sizeof(float) * (size_t)p.tiles * (BNT / 32) * p.M_pad, 256);
+    p.nc_nc = q;    q = align_up(q + sizeof(float) * 3 * p.M_pad, 256);
+    p.nc_bytes = q;
+    // the whole coefficient matrix is kept: beyond NC_MAX_BYTES the two passes run instead
+    p.ncfused = !dense && p.cap == 0.0f && p.nc_bytes <= NC_MAX_BYTES;
+  }
   if (dense) {
     p.o_hT = p.bwd_bytes;
     o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
@@ -605,6 +623,83 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
   return hip_status();
 }
 
+// The single pass of a quantized head without a softcap.  There is no fixed
+// reference, so each tile writes its coefficients -e^{z - R} against the
+// largest logit R of their 32-row vocabulary block (recorded), and its (max,
+// sum) partials over the non-target columns; every chunk is kept.  The merge
+// then gives lse, logp and each token's largest logit m, one launch scales
+// every coefficient by e^{R - m} (at most 1), and the dh contractions and the
+// split reduce proceed as for the capped single pass, against m.
+cce_status run_nc_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
+                        const uint8_t *mask, const float *g, float *logp, float *lse, void *dh, int32_t dh_dtype,
+                        void *workspace, hipStream_t st) {
+  enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false);
+  TileArgs a = tile_args(p, head, workspace);
+  a.part = ws_at<float>(workspace, p.nc_part);
+  a.ncR = ws_at<float>(workspace, p.nc_R);
+  a.ld_coeff = p.ld_coeff;
+  a.full_tiles = p.chunk_tiles;
+  a.nblocks = p.fus_blocks;
+  a.max_splits = p.fus_max_splits;
+  const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
+  uint16_t *coeff0 = ws_at<uint16_t>(workspace, p.nc_coeff);
+  const size_t chunk_elems = (size_t)p.M_pad * p.ld_coeff;
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    a.coeff = coeff0 + c * chunk_elems;
+    a.range_tile0 = t0;
+    a.range_tiles = std::min(p.chunk_tiles, p.tiles - t0);
+    a.chunk = c;
+    CCE_LAUNCH("tile_fused", st, launch_tile(st, p.bits, PASS_FUSED_NC, g1, a));
+  }
+  const int *inv = ws_at<const int>(workspace, p.o_inv);
+  const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
+  float *nc = ws_at<float>(workspace, p.nc_nc);
+  CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits,
+                                       (int)p.M_pad, inv, a.cnt, tok, logp, lse, nc));
+  CCE_LAUNCH("nc_scale", st, launch_nc_scale(st, coeff0, p.ld_coeff, p.nchunks,
+                                             p.V - (int64_t)(p.nchunks - 1) * p.ld_coeff, (int)p.M_pad, a.cnt,
+                                             a.ncR, nc));
+
+  GemmArgs ga{};
+  ga.ksv = p.ld_coeff / 16;
+  ga.wq = head->wq;
+  ga.scales = head->scales;
+  ga.biases = head->biases;
+  ga.cnt = a.cnt;
+  ga.dh_part = ws_at<float>(workspace, p.nc_dhp);
+  ga.V = p.V;
+  ga.H = (int)p.H;
+  ga.gs = p.gs;
+  ga.Gq = p.Gq;
+  ga.sbt = p.sbt;
+  ga.wpr = p.wpr;
+  ga.M_pad = (int)p.M_pad;
+  ga.max_chunk_steps = p.chunk_tiles * (BNT / KSTEP);
+  ga.TT = p.TT;
+  ga.HT = p.HT;
+  ga.ksplit = p.ksplit;
+  ga.nblocks = p.TT * p.HT * p.ksplit;
+  ga.small = a.small;
+  const dim3 g2((unsigned)(cdiv(ga.nblocks, 8) * 8));
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.chunk_tiles;
+    const int nt = std::min(p.chunk_tiles, p.tiles - t0);
+    ga.coeff = coeff0 + c * chunk_elems;
+    ga.chunk_v0 = (int64_t)t0 * BNT;
+    ga.chunk_tile0 = t0;
+    ga.chunk_steps = nt * (BNT / KSTEP);
+    ga.accumulate = c > 0;
+    CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+  }
+  ReduceTarget rt{};
+  rt.mode = 3;
+  rt.nc = nc;
+  CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, dh_dtype == CCE_DH_BF16 ? 1 : 0,
+                                               rt));
+  return hip_status();
+}
+
 // The single pass of a dense head (0 < softcap <= CAP_FIXED_REF_MAX): the
 // fused tile and the dh contraction per chunk as for a quantized head, every
 // chunk kept; the split reduce then forms lse, logp, dh and each row's factor
@@ -865,7 +960,7 @@ void *scratch_ptr() {
   return g_scratch_ptr[dev];
 }
 
-size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : p.twopass_bytes; }
+size_t fwdbwd_bytes(const Plan &p) { return p.fused ? p.fus_bytes : (p.ncfused ? p.nc_bytes : p.twopass_bytes); }
 
 }  // namespace
 
@@ -998,6 +1093,7 @@ cce_status cce_forward_backward(const cce_head *head, const void *h, int64_t M, 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   if (p.fused) return run_fused(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
+  if (p.ncfused) return run_nc_fused(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
   return run_twopass(p, head, h, M, targets, mask, g, logp, lse, dh, dh_dtype, workspace, st);
 }
 

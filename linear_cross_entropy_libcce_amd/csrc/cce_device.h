@@ -135,7 +135,10 @@ struct TileArgs {
   const uint32_t *wq;
   const int *cnt;
   TokRec *tok;           // read: lse, g, tgt; written: tval of the tokens whose target is in the tile
-  float *part;           // forward: [nwr][M_pad] x (max, sumexp)
+  float *part;           // forward: [nwr][M_pad] x (max, sumexp); uncapped single pass: the same over the
+                         // non-target columns
+  float *ncR;            // uncapped single pass: [32-row vocabulary block][M_pad] reference of each block's
+                         // coefficients (the token's largest logit in the block)
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
   int64_t V;
@@ -356,14 +359,23 @@ void launch_compact(hipStream_t st, const uint8_t *mask, int M, int M_pad, int *
 void launch_front(hipStream_t st, int bits, const FrontArgs &f);
 // Passes of the logit tile: forward partials, backward coefficients, or both
 // at once (the fused pass, softcap in (0, CAP_FIXED_REF_MAX]; quantized heads).
-enum { PASS_FWD = 0, PASS_BWD = 1, PASS_FUSED = 2 };
+enum { PASS_FWD = 0, PASS_BWD = 1, PASS_FUSED = 2, PASS_FUSED_NC = 3 };
 constexpr float CAP_FIXED_REF_MAX = 40.0f;
 void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &a);
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
                  const float *bmx, int64_t nbv, float log_eps, int block_on, uint8_t *fl);
 void launch_bmx_mask(hipStream_t st, int M, int64_t nbv, const int *inv, float *bmx);
+// nc (or NULL): the uncapped single pass's partials, which leave the target out;
+// the merge then adds the target's own term and writes (m, S, e_t) per row
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
-                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse);
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse,
+                  float *nc = nullptr);
+// The uncapped single pass: every coefficient of the ld_coeff-row chunks
+// (nchunks of them, the last holding last_rows valid rows) times
+// e^{R - m}, R its 32-row block's reference, m the token's largest logit
+// (nc); supervised rows only.
+void launch_nc_scale(hipStream_t st, uint16_t *coeff, int64_t ld_coeff, int nchunks, int64_t last_rows, int M_pad,
+                     const int *cnt, const float *ncR, const float *nc);
 void launch_dh_gemm(hipStream_t st, int bits, dim3 grid, const GemmArgs &a);
 // How the split reduce forms the target's term g (1 - p_t) c'_t w_t.
 //  mode 0: tval is the whole coefficient (the tile used -expm1(y_t - lse));
@@ -388,6 +400,10 @@ struct ReduceTarget {
   // and the target's coefficient in the chunk's units, S c'_t (read by the
   // dW launches)
   float *fac;
+  // mode 3 (the uncapped single pass): per compacted row the token's largest
+  // logit m, S (its non-target terms e^{z - m}) and e_t = e^{z_t - m}, from the
+  // merge; lse and logp are the merge's
+  const float *nc;
 };
 void launch_dh_reduce(hipStream_t st, int bits, int M, const GemmArgs &ga, const int *inv, const TokRec *tok,
                       void *dh, int out_bf16, const ReduceTarget &rt);

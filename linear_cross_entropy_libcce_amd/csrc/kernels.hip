@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(256) k_front(FrontArgs f) {
 // few supervised tokens carry hundreds of splits.
 __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, int full_tiles, int tiles,
                                                int max_splits, int M_pad, const int *inv, const int *cnt,
-                                               const TokRec *tok, int M, float *logp, float *lse) {
+                                               const TokRec *tok, int M, float *logp, float *lse, float *nc) {
   // two partials (vocabulary halves of the tile) per split, over every chunk
   // of the vocabulary the forward's launches covered
   const int nsplit = 2 * vsplit_total(nblocks, active_tiles(cnt), full_tiles, tiles, max_splits);
@@ -521,9 +521,47 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, i
     return;
   }
   const TokRec rec = tok[r];
+  if (nc) {
+    // the uncapped single pass: its partials hold the non-target terms; the
+    // target's own (its logit is at most the maximum, which spans it) is added
+    const float et = rec.tgt >= 0 ? __expf(rec.tval - mx) : 0.0f;
+    const float l = mx + logf(se + et);
+    lse[t] = l;
+    logp[t] = rec.tval - l;
+    nc[3 * r] = mx;
+    nc[3 * r + 1] = se;
+    nc[3 * r + 2] = et;
+    return;
+  }
   const float l = mx + logf(se);
   lse[t] = l;
   logp[t] = rec.tval - l;
+}
+
+// Each thread one 16-byte slot of the fragment-major chunks (8 vocabulary rows
+// of one token, in one 32-row block): slot s of a chunk is row 32 T + l % 32,
+// K chunk 2 C + l / 32, with l = s % 64, C = (s / 64) % ksv, T = s / 64 / ksv.
+__global__ void __launch_bounds__(256) k_nc_scale(uint16_t *coeff, int64_t ld_coeff, int nchunks, int64_t last_rows,
+                                                  int M_pad, const int *cnt, const float *ncR, const float *nc) {
+  const int64_t ksv = ld_coeff / 16;
+  const int64_t per_chunk = (int64_t)M_pad * ld_coeff / 8;
+  const int n = cnt[0];
+  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < per_chunk * nchunks; s += (int64_t)gridDim.x * 256) {
+    const int64_t c = s / per_chunk, sl = s - c * per_chunk;
+    const int l = (int)(sl & 63);
+    const int64_t q = sl >> 6;
+    const int64_t C = q % ksv, T = q / ksv;
+    const int64_t row = 32 * T + (l & 31);
+    const int64_t col = 8 * (2 * C + (l >> 5));  // chunk-local vocabulary row of the slot's first element
+    if (row >= n || (c == nchunks - 1 && col >= last_rows)) continue;
+    const int64_t blk = (c * ld_coeff + col) >> 5;
+    const float f = __builtin_amdgcn_exp2f((ncR[blk * M_pad + row] - nc[3 * row]) * 1.4426950408889634f);
+    u32x4_t *p = reinterpret_cast<u32x4_t *>(coeff + c * (int64_t)M_pad * ld_coeff + sl * 8);
+    u32x4_t x = *p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = pack_rne(bf16_to_f32(x[e] & 0xFFFFu) * f, bf16_to_f32(x[e] >> 16) * f);
+    *p = x;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -594,7 +632,8 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
   // single pass's split sums.  The token's contiguous run, summed by the
   // workgroup in a fixed order (every thread takes part).
   float S = 0.0f;
-  if (tg.mode != 0 && r >= 0) {
+  if (tg.mode == 3 && r >= 0) S = tg.nc[3 * r + 1];  // the uncapped single pass: from the merge
+  if ((tg.mode == 1 || tg.mode == 2) && r >= 0) {
     __shared__ float sS[4];
     const int ns = 2 * vsplit_total(tg.nblocks, act, tg.full_tiles, tg.tiles, tg.max_splits);
     float x = 0.0f;
@@ -652,6 +691,13 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
       const float inv_tot = 1.0f / (S + et);
       acc *= rec.g * inv_tot;
       rec.tval = ht ? rec.g * (S * inv_tot) * tg.tdc[r] : 0.0f;
+    } else if (tg.mode == 3) {
+      // uncapped single pass: the same against the token's largest logit m
+      // (the coefficient chunks were brought to it), c' = 1
+      const float et = tg.nc[3 * r + 2];
+      const float inv_tot = 1.0f / (S + et);
+      acc *= rec.g * inv_tot;
+      rec.tval = ht ? rec.g * (S * inv_tot) : 0.0f;
     }
     if (rec.tgt >= 0 && (int64_t)rec.tgt < a.V) {
       const uint32_t *row = a.wq + (size_t)rec.tgt * a.wpr;
@@ -711,9 +757,15 @@ void launch_front(hipStream_t st, int bits, const FrontArgs &f) {
 }
 
 void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int full_tiles, int tiles, int max_splits,
-                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse) {
+                  int M_pad, const int *inv, const int *cnt, const TokRec *tok, float *logp, float *lse, float *nc) {
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, part, nblocks, full_tiles, tiles,
-                     max_splits, M_pad, inv, cnt, tok, M, logp, lse);
+                     max_splits, M_pad, inv, cnt, tok, M, logp, lse, nc);
+}
+
+void launch_nc_scale(hipStream_t st, uint16_t *coeff, int64_t ld_coeff, int nchunks, int64_t last_rows, int M_pad,
+                     const int *cnt, const float *ncR, const float *nc) {
+  hipLaunchKernelGGL(k_nc_scale, dim3(8192), dim3(256), 0, st, coeff, ld_coeff, nchunks, last_rows, M_pad, cnt, ncR,
+                     nc);
 }
 
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,

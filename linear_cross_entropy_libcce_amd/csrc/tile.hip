@@ -60,7 +60,12 @@ constexpr float LOG2E = 1.4426950408889634f;
 // also gives every coefficient up to a per-token factor, so one pass writes
 // both the partial sums and the unnormalized coefficients -e^{c(z) - cap} c'(z)
 // (the split reduce scales them by g e^{cap - lse} once the merge has lse).
-enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2, MODE_FUSED = 3 };
+// MODE_FUSED_NC (no softcap): no fixed reference exists, so each 32-row
+// vocabulary block's coefficients -e^{z - R} are taken against the block's own
+// largest logit R (written to ncR), and the forward's (max, sum) partials run
+// over the non-target columns; once lse and the token's largest logit are known
+// a scaling launch brings every block to one reference.
+enum { MODE_FWD = 0, MODE_FWD_CAP = 1, MODE_BWD = 2, MODE_FUSED = 3, MODE_FUSED_NC = 4 };
 enum { VAR_PLAIN = 0, VAR_EXTRA = 1, VAR_SMALL = 2, VAR_SMALL32 = 3 };
 
 // One step's worth of head data for one producer thread: 16 K values of each
@@ -195,7 +200,8 @@ template <int BITS, int MODE, int VAR, bool GS32>
 __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   constexpr bool BWD = MODE == MODE_BWD;
   constexpr bool FUSED = MODE == MODE_FUSED;
-  constexpr bool COEF = BWD || FUSED;  // writes coefficients
+  constexpr bool FNC = MODE == MODE_FUSED_NC;
+  constexpr bool COEF = BWD || FUSED || FNC;  // writes coefficients
   constexpr int KW = GS32 ? 32 : 64;  // K columns per step (one quantization group)
   constexpr int NKS = KW / 16;        // MFMA k-steps per step
   constexpr bool DENSE = BITS == 16;  // bf16 head: no fold, no final scale
@@ -204,7 +210,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
   // epilogue columns per chunk: the fused pass keeps three values per column
   // live (logit, coefficient, probability term) next to the next step's
   // prefetched operands and takes 8 at a time (with 16 its step loop spilled)
-  constexpr int EW = FUSED ? 8 : 16;
+  constexpr int EW = (FUSED || FNC) ? 8 : 16;
   // the single pass reads the logit only as 2 z / cap (the capped forward
   // keeps z: its block-maximum variant needs the raw logit, and the two give
   // bit-identical lse)
@@ -532,6 +538,25 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // FNC: the block's reference, its largest logit over the valid columns
+        // (the target's included); a block past V has none and adds nothing
+        float Rb = 0.0f, Rb2 = 0.0f, esum = 0.0f;
+        bool bvalid = true;
+        if (FNC) {
+          const int64_t vbk = v0 + vcol0 + c * 32;
+          const int nvb = full ? 32 : (int)(a.V - vbk < 0 ? 0 : (a.V - vbk < 32 ? a.V - vbk : 32));
+          float mx = -INFINITY;
+#pragma unroll
+          for (int k = 0; k < 32; k += 4) {
+            const f32x4_t x = *(const f32x4_t *)(zs + lane * ZROW + k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, (k + e < nvb) ? x[e] : -INFINITY);
+          }
+          bvalid = nvb > 0;
+          Rb = bvalid ? mx : 0.0f;
+          a.ncR[(size_t)(vbk >> 5) * a.M_pad + tok0 + lane] = Rb;
+          Rb2 = Rb * LOG2E;
+        }
 #pragma unroll 1
         for (int k0 = 0; k0 < 32; k0 += EW) {
           float z[EW];
@@ -569,7 +594,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
                 a.tok[tok0 + lane].tval = rec.g * -expm1f(yt - rec.lse) * dct;
               } else {
                 a.tok[tok0 + lane].tval = yt;
-                if (COEF) a.tdc[tok0 + lane] = dct;  // the reduce forms the target's term
+                if (COEF && !FNC) a.tdc[tok0 + lane] = dct;  // the reduce forms the target's term
               }
             }
           };
@@ -625,7 +650,14 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
             // The target column is left out here; its whole term is added in
             // fp32 by k_dh_reduce.
             float cv[EW], pv[EW];
-            if (FUSED) {
+            if (FNC) {
+              // e = e^{z - R} <= 1 against the block's reference
+#pragma unroll
+              for (int k = 0; k < EW; ++k) {
+                pv[k] = __builtin_amdgcn_exp2f(fmaf(z[k], LOG2E, -Rb2));
+                cv[k] = -pv[k];
+              }
+            } else if (FUSED) {
               // c' = 4 r (1 - r); the term is taken as 4 e = exp2(c2 r + 2), so
               // the coefficient -e c' is -(4 e)(r - r^2) and the split sums
               // carry 4 S (the reduce takes the factor 4 back out, exactly)
@@ -667,7 +699,8 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               float ps = 0.0f;
 #pragma unroll
               for (int k = 0; k < EW; ++k) ps += pv[k];
-              sRun[wave][lane] += ps;  // the wave's own slot: in order, no barrier
+              if (FNC) esum += ps;  // folded into the running partial after the block
+              else sRun[wave][lane] += ps;  // the wave's own slot: in order, no barrier
             }
             uint32_t pk[EW / 2];
 #pragma unroll
@@ -684,6 +717,15 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
                 *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
                     u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
           }
+        }
+        if (FNC && bvalid) {
+          // the running (max, sum) of the token's non-target terms over this
+          // split, the block's terms brought from its reference to the maximum
+          const float mn = fmaxf(run_m, Rb);
+          const float mn2 = mn * LOG2E;
+          sRun[wave][lane] = sRun[wave][lane] * __builtin_amdgcn_exp2f(fmaf(run_m, LOG2E, -mn2)) +
+                             esum * __builtin_amdgcn_exp2f(Rb2 - mn2);
+          run_m = mn;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -781,7 +823,7 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
     const float m_out = BWD ? 0.0f : (((MODE == MODE_FWD_CAP || FUSED) && total > 0) ? a.cap : run_m);
     auto put = [&](int half, float m, float sum) {
       const int slot = 2 * (vs.slot0 + wr) + half;
-      if (COEF) {
+      if (COEF && !FNC) {
         a.mass[(size_t)(tok0 + lane) * a.mass_ld + slot] = sum;
       } else {
         float *dst = a.part + ((size_t)slot * a.M_pad + tok0 + lane) * 2;
@@ -822,9 +864,10 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
 void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &a) {
   const bool bwd = pass == PASS_BWD;
   const int mode = pass == PASS_FUSED ? MODE_FUSED
-                                      : (bwd ? MODE_BWD
-                                             : ((a.cap > 0.0f && a.cap <= CAP_FIXED_REF_MAX) ? MODE_FWD_CAP : MODE_FWD));
-  const bool extra = pass == PASS_FUSED ? false : (bwd ? a.fl != nullptr : a.bmx != nullptr);
+                   : pass == PASS_FUSED_NC
+                       ? MODE_FUSED_NC
+                       : (bwd ? MODE_BWD : ((a.cap > 0.0f && a.cap <= CAP_FIXED_REF_MAX) ? MODE_FWD_CAP : MODE_FWD));
+  const bool extra = (pass == PASS_FUSED || pass == PASS_FUSED_NC) ? false : (bwd ? a.fl != nullptr : a.bmx != nullptr);
   const bool gs32 = a.kw == 32;
   // group 32 has no small-M instantiation (the plain one is correct there)
   const int var = extra ? VAR_EXTRA : (a.small && !gs32 ? (a.small == 2 ? VAR_SMALL32 : VAR_SMALL) : VAR_PLAIN);
@@ -842,13 +885,13 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
     }                                                                                                            \
   } while (0)
   // the fused pass: no EXTRA variant (no skips, no block maxima)
-#define CCE_TILE_FUSED(B)                                                                                        \
+#define CCE_TILE_FUSED(B, MD)                                                                                    \
   do {                                                                                                           \
-    if (gs32) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);            \
-    else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_SMALL, false>), grid, dim3(TW), 0, st, a); \
+    if (gs32) hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);                    \
+    else if (var == VAR_SMALL) hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL, false>), grid, dim3(TW), 0, st, a);  \
     else if (var == VAR_SMALL32)                                                                                 \
-      hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_SMALL32, false>), grid, dim3(TW), 0, st, a);                 \
-    else hipLaunchKernelGGL((k_tile<B, MODE_FUSED, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                \
+      hipLaunchKernelGGL((k_tile<B, MD, VAR_SMALL32, false>), grid, dim3(TW), 0, st, a);                         \
+    else hipLaunchKernelGGL((k_tile<B, MD, VAR_PLAIN, false>), grid, dim3(TW), 0, st, a);                        \
   } while (0)
   if (bits == 16) {  // dense bf16 head: 32-wide steps, plain variant only
     if (mode == MODE_FUSED) hipLaunchKernelGGL((k_tile<16, MODE_FUSED, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
@@ -857,12 +900,14 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
       hipLaunchKernelGGL((k_tile<16, MODE_FWD_CAP, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
     else hipLaunchKernelGGL((k_tile<16, MODE_FWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
   } else if (bits == 4) {
-    if (mode == MODE_FUSED) CCE_TILE_FUSED(4);
+    if (mode == MODE_FUSED) CCE_TILE_FUSED(4, MODE_FUSED);
+    else if (mode == MODE_FUSED_NC) CCE_TILE_FUSED(4, MODE_FUSED_NC);
     else if (mode == MODE_BWD) CCE_TILE(4, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(4, MODE_FWD_CAP);
     else CCE_TILE(4, MODE_FWD);
   } else {
-    if (mode == MODE_FUSED) CCE_TILE_FUSED(8);
+    if (mode == MODE_FUSED) CCE_TILE_FUSED(8, MODE_FUSED);
+    else if (mode == MODE_FUSED_NC) CCE_TILE_FUSED(8, MODE_FUSED_NC);
     else if (mode == MODE_BWD) CCE_TILE(8, MODE_BWD);
     else if (mode == MODE_FWD_CAP) CCE_TILE(8, MODE_FWD_CAP);
     else CCE_TILE(8, MODE_FWD);

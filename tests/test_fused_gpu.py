@@ -67,13 +67,19 @@ CASES = {
                                                mask_frac=0.3),
     "M20_H64_V600000_8bit_cap20_two_chunks": dict(M=20, H=64, V=600000, bits=8, softcap=20.0),
     "M300_H64_V600000_4bit_cap30_two_chunks": dict(M=300, H=64, V=600000, bits=4, softcap=30.0),
-    # no softcap or one above 40: the call's two passes (the backward tiles
-    # merge the forward's partials themselves; no merge launch, one front)
+    # no softcap: the uncapped single pass (coefficients against their block's
+    # largest logit, brought to the token's maximum after the merge); a
+    # softcap above 40: the call's two passes (the backward tiles merge the
+    # forward's partials themselves; no merge launch, one front)
     "M16_H256_V4096_4bit_nocap": dict(M=16, H=256, V=4096, bits=4),
     "H512_V1000_8bit_nocap_randmask": dict(M=600, H=512, V=1000, bits=8, mask="random", mask_frac=0.3),
     "H768_V700_4bit_cap50_group32_bf16": dict(M=400, H=768, V=700, bits=4, softcap=50.0, group=32, sb_dtype="bf16"),
     "M2100_H256_V900_8bit_nocap_randmask": dict(M=2100, H=256, V=900, bits=8, mask="random", mask_frac=0.4),
     "M20_H64_V600000_8bit_nocap_two_chunks": dict(M=20, H=64, V=600000, bits=8),
+    "M40_H512_V3001_4bit_nocap_group128_f16_randmask": dict(M=40, H=512, V=3001, bits=4, group=128, sb_dtype="f16",
+                                                            mask="random", mask_frac=0.3),
+    "M300_H768_V1000_8bit_nocap_group32_zipf": dict(M=300, H=768, V=1000, bits=8, group=32, targets="zipf"),
+    "M300_H64_V600000_4bit_nocap_two_chunks": dict(M=300, H=64, V=600000, bits=4),
 }
 
 
@@ -91,9 +97,12 @@ def test_fused_against_oracle(torch_cuda, name, bias):
 
 @pytest.mark.parametrize("cap", [0.0, 50.0])
 def test_other_heads_match_the_two_calls(torch_cuda, cap):
-    # no softcap or one above 40: the call runs a forward and a backward pass,
-    # the backward tiles merging the forward's partials themselves: the same
-    # quantities as cce_forward followed by cce_backward, in another order
+    # a softcap above 40: the call runs a forward and a backward pass, the
+    # backward tiles merging the forward's partials themselves: the same
+    # quantities as cce_forward followed by cce_backward, in another order.
+    # No softcap: the uncapped single pass, whose coefficients are rounded to
+    # bf16 against their block's reference and again once brought to the
+    # token's maximum: within that rounding of the two calls
     torch = torch_cuda
     inp = syn.make_custom(M=300, H=512, V=1300, bits=8, seed=81, softcap=cap, mask="random", mask_frac=0.2,
                           bias="affine")
@@ -107,8 +116,11 @@ def test_other_heads_match_the_two_calls(torch_cuda, cap):
     dl = (logp - logp0).abs().max().item()
     ds = (lse - lse0).abs().max().item()
     rel = ((dh - dh0).norm() / dh0.norm()).item()
-    say("two passes vs two calls (cap %g): max|dlogp| %.3g max|dlse| %.3g dh rel %.3g" % (cap, dl, ds, rel))
-    assert dl <= 1e-5 and ds <= 1e-5 and rel <= 1e-5
+    say("combined call vs two calls (cap %g): max|dlogp| %.3g max|dlse| %.3g dh rel %.3g" % (cap, dl, ds, rel))
+    if cap == 0.0:
+        assert dl <= 1e-4 and ds <= 1e-4 and rel <= 5e-3
+    else:
+        assert dl <= 1e-5 and ds <= 1e-5 and rel <= 1e-5
     mk = m == 0
     assert int((logp[mk] != 0).sum()) == 0 and int((lse[mk] != 0).sum()) == 0 and int((dh[mk] != 0).sum()) == 0
 
@@ -170,10 +182,12 @@ def test_fused_repeat_runs_are_bitwise_identical(torch_cuda):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg,bias", [(3, "sym"), (3, "affine"), (2, "sym")])
+@pytest.mark.parametrize("cfg,bias", [(3, "sym"), (3, "affine"), (2, "sym"), (1, "sym"), (4, "affine")])
 def test_fused_full_size_workload_sampled(torch_cuda, cfg, bias):
-    # the softcapped workloads at full size (the launch bench.py times), one
-    # supervised token per token tile and the first and last against the oracle
+    # workloads at full size (the launches bench.py times): the softcapped ones
+    # in the single pass, workloads 1 and 4 (no softcap; 4 in three
+    # coefficient chunks) in the uncapped single pass; one supervised token per
+    # token tile and the first and last against the oracle
     import dataclasses
     w = dataclasses.replace(syn.WORKLOADS[cfg], bias="symmetric" if bias == "sym" else "affine")
     say("workload %d (%s head): generating inputs" % (cfg, bias))
