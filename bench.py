@@ -5,9 +5,9 @@ One step = forward + backward (g = 1) over one batch of the synthetic
 workload M=8192 tokens, H=2560, V=262144, 8-bit affine head (group 64),
 softcap 30 -- the largest single-GPU workload at H=2560, V=262144.  Inputs are
 resident in HBM and workspaces preallocated before the timed region.  The
-step is one call of cce_forward_backward: under a softcap of at most 40 its
-single pass (the logits computed once), otherwise its forward and backward
-passes after one front.  The `two_calls` field times cce_forward +
+step is one call of cce_forward_backward: under a softcap of at most 40, or
+with none, a single pass (the logits computed once), otherwise its forward
+and backward passes after one front.  The `two_calls` field times cce_forward +
 cce_backward (the backward recomputes the logits) on the same inputs; the
 skips always take their calls, and a dense head (--dense) takes
 cce_dense_forward_backward alike (the single pass under a softcap of at most
@@ -231,7 +231,9 @@ def main():
     # skips: the single pass where the head allows it (0 < softcap <= 40), else
     # its two passes; the skips take the two calls
     combined = not args.skip and args.path != "calls"
-    fused = combined and 0.0 < inp["softcap"] <= 40.0
+    # the logits once: a softcap in (0, 40], or none on a quantized head (its
+    # uncapped single pass)
+    fused = combined and (0.0 < inp["softcap"] <= 40.0 or (inp["softcap"] == 0.0 and not args.dense))
     if combined:
         nb = (cce.dense_forward_backward_workspace_bytes(head, M) if args.dense
               else cce.forward_backward_workspace_bytes(head, M))
