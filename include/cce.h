@@ -308,10 +308,13 @@ cce_status cce_dense_backward(const cce_dense_head *head, const void *h, int64_t
  * the forward's fixed reference e^{y - cap} gives each coefficient up to the
  * token's factor g e^{cap - lse}, every coefficient chunk is kept until lse is
  * known, and dW is formed from them last; the workspace then holds all the
- * chunks (about 2 M V bytes).  Other softcaps run cce_dense_forward and then
- * cce_dense_backward on the same workspace.  dW takes every coefficient
- * rounded to bf16 and, in the single pass, each h row times its factor
- * rounded to bf16.  Errors as cce_dense_backward.
+ * chunks (about 2 M V bytes).  Without a softcap likewise, the coefficients
+ * taken against each 32-row vocabulary block's largest logit and brought to
+ * the token's largest one before the dh and dW contractions (as
+ * cce_forward_backward does for a quantized head).  Softcaps above 40 run
+ * cce_dense_forward and then cce_dense_backward on the same workspace.  dW
+ * takes every coefficient rounded to bf16 and, in the single pass, each h row
+ * times its factor rounded to bf16.  Errors as cce_dense_backward.
  */
 size_t cce_dense_forward_backward_workspace_bytes(const cce_dense_head *head, int64_t M);
 cce_status cce_dense_forward_backward(const cce_dense_head *head, const void *h, int64_t M,

@@ -118,6 +118,7 @@ struct Plan {
   // factors, scaled hT and one transposed chunk
   bool dfused;
   size_t df_coeff, df_dhp, df_tdc, df_fpart, df_fac, df_hT, df_coeffT, df_bytes;
+  size_t df_part, df_R, df_nc;  // without a softcap: as the quantized head's uncapped single pass
   // the uncapped single pass of a quantized head (cce_forward_backward, no
   // softcap): every coefficient chunk kept until the merge has each token's
   // largest logit; dh slabs, the (max, sum) partials, the 32-row block
@@ -320,7 +321,7 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     o = align_up(p.o_hT + (size_t)2 * p.H * p.M_pad, 256);
     p.o_coeffT = o;
     p.bwd_bytes = align_up(o + (size_t)2 * p.ld_coeff * p.M_pad, 256);
-    p.dfused = p.cap > 0.0f && p.cap <= CAP_FIXED_REF_MAX;
+    p.dfused = p.cap >= 0.0f && p.cap <= CAP_FIXED_REF_MAX;
     size_t q = common;
     p.df_coeff = q;  q = align_up(q + (size_t)p.nchunks * 2 * p.M_pad * p.ld_coeff, 256);
     p.df_dhp = q;    q = align_up(q + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
@@ -329,7 +330,13 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     p.df_fac = q;    q = align_up(q + 2 * sizeof(float) * p.M_pad, 256);
     p.df_hT = q;     q = align_up(q + (size_t)2 * p.H * p.M_pad, 256);
     p.df_coeffT = q; q = align_up(q + (size_t)2 * p.ld_coeff * p.M_pad, 256);
+    if (p.cap == 0.0f) {
+      p.df_part = q; q = align_up(q + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
+      p.df_R = q;    q = align_up(q + sizeof(float) * (size_t)p.tiles * (BNT / 32) * p.M_pad, 256);
+      p.df_nc = q;   q = align_up(q + sizeof(float) * 3 * p.M_pad, 256);
+    }
     p.df_bytes = q;
+    if (p.cap == 0.0f && p.df_bytes > NC_MAX_BYTES) p.dfused = false;
   }
   return p;
 }
@@ -700,20 +707,28 @@ cce_status run_nc_fused(const Plan &p, const cce_head *head, const void *h, int6
   return hip_status();
 }
 
-// The single pass of a dense head (0 < softcap <= CAP_FIXED_REF_MAX): the
+// The single pass of a dense head (softcap in [0, CAP_FIXED_REF_MAX]): the
 // fused tile and the dh contraction per chunk as for a quantized head, every
 // chunk kept; the split reduce then forms lse, logp, dh and each row's factor
 // g / (S + e_t); dW last, chunk by chunk, from the unnormalized coefficients
 // and hT scaled by those factors (dW_v = sum_t coefficient_tv (factor_t h_t)).
+// Without a softcap the tiles write against their blocks' references and the
+// dh contractions wait for the merge and the scaling launch, as in
+// run_nc_fused.
 cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                            const uint8_t *mask, const float *g, float *logp, float *lse, float *dh, float *dw,
                            void *workspace, hipStream_t st) {
   enqueue_front(p, head, h, targets, mask, nullptr, g, workspace, st, false);
+  const bool nocap = p.cap == 0.0f;  // the uncapped variant: block references, merge, scaling
   TileArgs a = tile_args(p, head, workspace);
   a.mass = ws_at<float>(workspace, p.df_fpart);
   a.mass_ld = p.mass_ld;
   a.ld_coeff = p.ld_coeff;
   a.tdc = ws_at<float>(workspace, p.df_tdc);
+  if (nocap) {
+    a.part = ws_at<float>(workspace, p.df_part);
+    a.ncR = ws_at<float>(workspace, p.df_R);
+  }
   a.full_tiles = p.chunk_tiles;
   a.nblocks = p.fus_blocks;
   a.max_splits = p.fus_max_splits;
@@ -750,7 +765,8 @@ cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, i
     a.range_tile0 = t0;
     a.range_tiles = nt;
     a.chunk = c;
-    CCE_LAUNCH("tile_fused", st, launch_tile(st, p.bits, PASS_FUSED, g1, a));
+    CCE_LAUNCH("tile_fused", st, launch_tile(st, p.bits, nocap ? PASS_FUSED_NC : PASS_FUSED, g1, a));
+    if (nocap) continue;  // dh once every chunk is at the token's maximum
     ga.coeff = a.coeff;
     ga.chunk_v0 = (int64_t)t0 * BNT;
     ga.chunk_tile0 = t0;
@@ -761,8 +777,29 @@ cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, i
   const int *inv = ws_at<const int>(workspace, p.o_inv);
   const TokRec *tok = ws_at<const TokRec>(workspace, p.o_tok);
   float *fac = dw ? ws_at<float>(workspace, p.df_fac) : nullptr;
-  const ReduceTarget rt{2, a.mass, a.mass_ld, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, p.cap, a.tdc,
-                        logp, lse, fac};
+  ReduceTarget rt{2, a.mass, a.mass_ld, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits, p.cap, a.tdc,
+                  logp, lse, fac};
+  if (nocap) {
+    float *nc = ws_at<float>(workspace, p.df_nc);
+    CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits,
+                                         (int)p.M_pad, inv, a.cnt, tok, logp, lse, nc));
+    CCE_LAUNCH("nc_scale", st, launch_nc_scale(st, coeff0, p.ld_coeff, p.nchunks,
+                                               p.V - (int64_t)(p.nchunks - 1) * p.ld_coeff, (int)p.M_pad, a.cnt,
+                                               a.ncR, nc));
+    for (int c = 0; c < p.nchunks; ++c) {
+      const int t0 = c * p.chunk_tiles;
+      ga.coeff = coeff0 + c * chunk_elems;
+      ga.chunk_v0 = (int64_t)t0 * BNT;
+      ga.chunk_tile0 = t0;
+      ga.chunk_steps = std::min(p.chunk_tiles, p.tiles - t0) * (BNT / KSTEP);
+      ga.accumulate = c > 0;
+      CCE_LAUNCH("dh_gemm", st, launch_dh_gemm(st, p.bits, g2, ga));
+    }
+    rt = ReduceTarget{};
+    rt.mode = 3;
+    rt.nc = nc;
+    rt.fac = fac;
+  }
   CCE_LAUNCH("dh_reduce", st, launch_dh_reduce(st, p.bits, (int)M, ga, inv, tok, dh, 0, rt));
   if (dw) {
     DwArgs wa{};

@@ -662,6 +662,12 @@ __global__ void __launch_bounds__(256) k_dh_reduce(GemmArgs a, const int *inv, c
     tg.lse[t] = l;
     tg.logp[t] = lp;
   }
+  if (tg.mode == 3 && tg.fac && blockIdx.y == 0 && threadIdx.x == 0 && r >= 0) {
+    // the dense head's dW without a softcap: as above, against the token's maximum (c' = 1)
+    const TokRec rec = tok[r];
+    tg.fac[2 * r] = rec.g * (1.0f / (S + tg.nc[3 * r + 2]));
+    tg.fac[2 * r + 1] = rec.tgt >= 0 ? S : 0.0f;
+  }
   if (d >= H) return;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (r >= 0) {

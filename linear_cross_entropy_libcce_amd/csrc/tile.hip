@@ -895,6 +895,8 @@ void launch_tile(hipStream_t st, int bits, int pass, dim3 grid, const TileArgs &
   } while (0)
   if (bits == 16) {  // dense bf16 head: 32-wide steps, plain variant only
     if (mode == MODE_FUSED) hipLaunchKernelGGL((k_tile<16, MODE_FUSED, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
+    else if (mode == MODE_FUSED_NC)
+      hipLaunchKernelGGL((k_tile<16, MODE_FUSED_NC, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
     else if (mode == MODE_BWD) hipLaunchKernelGGL((k_tile<16, MODE_BWD, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);
     else if (mode == MODE_FWD_CAP)
       hipLaunchKernelGGL((k_tile<16, MODE_FWD_CAP, VAR_PLAIN, true>), grid, dim3(TW), 0, st, a);

@@ -194,7 +194,7 @@ def test_dense_full_vocabulary_dw_rows(torch_cuda):
     assert e <= DW_TOL and worst_t <= DW_TOL
 
 
-# ---- cce_dense_forward_backward: one call (the single pass under a softcap <= 40)
+# ---- cce_dense_forward_backward: one call (the single pass under a softcap <= 40 or without one)
 
 def run_combined(torch, inp, g=None, need_dw=True):
     head = cce.dense_head_from_numpy(inp)
@@ -213,7 +213,8 @@ def run_combined(torch, inp, g=None, need_dw=True):
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_dense_combined_against_oracle(torch_cuda, name):
     # softcap 30: the single pass (dW from the kept chunks and hT scaled by each
-    # row's factor); softcaps 0 and 100: the forward and the backward in turn
+    # row's factor); softcap 0: the same against block references brought to
+    # each token's maximum; softcap 100: the forward and the backward in turn
     M, H, V, cap, mask, tg = SMALL[name]
     inp = syn.make_dense(M=M, H=H, V=V, seed=31, softcap=cap, mask=mask, mask_frac=0.4, targets=tg)
     inp["targets"][3] = V + 5
@@ -240,11 +241,13 @@ def test_dense_combined_masked_and_without_dw(torch_cuda):
         assert np.array_equal(x, y)
 
 
-def test_dense_combined_full_vocabulary_dw_rows(torch_cuda):
+@pytest.mark.parametrize("cap", [30.0, 0.0])
+def test_dense_combined_full_vocabulary_dw_rows(torch_cuda, cap):
     # the single pass at full V, H and M (four coefficient chunks, all kept
-    # until dW), 48 supervised tokens, dW rows element by element
+    # until dW; without a softcap brought to each token's maximum first), 48
+    # supervised tokens, dW rows element by element
     M = FULL["M"]
-    inp = syn.make_dense(M=M, H=FULL["H"], V=FULL["V"], seed=44, softcap=30.0)
+    inp = syn.make_dense(M=M, H=FULL["H"], V=FULL["V"], seed=44, softcap=cap)
     keep = np.random.default_rng(13).choice(M, size=48, replace=False)
     inp["mask"] = np.zeros(M, np.uint8)
     inp["mask"][keep] = 1
@@ -257,7 +260,7 @@ def test_dense_combined_full_vocabulary_dw_rows(torch_cuda):
     rows = np.unique(np.concatenate([tg, np.random.default_rng(15).choice(FULL["V"], 40, replace=False),
                                      [0, 65535, 65536, 131072, FULL["V"] - 1]]))
     orc = oracle.cce_dense(inp, g=g, dw_rows=rows)
-    check_tokens(gpu, orc, np.arange(M), inp["mask"], "combined_fullV")
+    check_tokens(gpu, orc, np.arange(M), inp["mask"], "combined_fullV_cap%g" % cap)
     e = rel_l2(gpu[3][rows], orc[3])
     worst_t = max(rel_l2(gpu[3][v], orc[3][k]) for k, v in enumerate(rows) if v in set(tg))
     say("combined full vocabulary dW rows: rel L2 %.3g (target rows worst %.3g)" % (e, worst_t))
