@@ -538,30 +538,26 @@ __global__ void __launch_bounds__(256) k_merge(const float *part, int nblocks, i
   logp[t] = rec.tval - l;
 }
 
-// Each thread one 16-byte slot of the fragment-major chunks (8 vocabulary rows
-// of one token, in one 32-row block): slot s of a chunk is row 32 T + l % 32,
-// K chunk 2 C + l / 32, with l = s % 64, C = (s / 64) % ksv, T = s / 64 / ksv.
+// One thread per 16-byte slot of the fragment-major chunks: 1 KiB blocks of 64
+// slots, block (T, C) holding tokens 32 T .. + 31 and vocabulary rows 16 C ..
+// + 15 (lane l: token 32 T + l % 32, rows 16 C + 8 (l / 32) .. + 8).  Grid:
+// x = T, y = C / 4 (four blocks per workgroup, a wave each), z = chunk (the
+// chunk count stays small: the whole matrix is kept only up to 32 GiB).
 __global__ void __launch_bounds__(256) k_nc_scale(uint16_t *coeff, int64_t ld_coeff, int nchunks, int64_t last_rows,
                                                   int M_pad, const int *cnt, const float *ncR, const float *nc) {
+  const int T = blockIdx.x, c = blockIdx.z, l = threadIdx.x & 63;
+  const int row = 32 * T + (l & 31);
   const int64_t ksv = ld_coeff / 16;
-  const int64_t per_chunk = (int64_t)M_pad * ld_coeff / 8;
-  const int n = cnt[0];
-  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < per_chunk * nchunks; s += (int64_t)gridDim.x * 256) {
-    const int64_t c = s / per_chunk, sl = s - c * per_chunk;
-    const int l = (int)(sl & 63);
-    const int64_t q = sl >> 6;
-    const int64_t C = q % ksv, T = q / ksv;
-    const int64_t row = 32 * T + (l & 31);
-    const int64_t col = 8 * (2 * C + (l >> 5));  // chunk-local vocabulary row of the slot's first element
-    if (row >= n || (c == nchunks - 1 && col >= last_rows)) continue;
-    const int64_t blk = (c * ld_coeff + col) >> 5;
-    const float f = __builtin_amdgcn_exp2f((ncR[blk * M_pad + row] - nc[3 * row]) * 1.4426950408889634f);
-    u32x4_t *p = reinterpret_cast<u32x4_t *>(coeff + c * (int64_t)M_pad * ld_coeff + sl * 8);
-    u32x4_t x = *p;
+  const int64_t C = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t col = 16 * C + 8 * (l >> 5);  // chunk-local vocabulary row of the slot's first element
+  if (row >= cnt[0] || C >= ksv || col >= (c == nchunks - 1 ? last_rows : ld_coeff)) return;
+  const int64_t blk = ((int64_t)c * ld_coeff + col) >> 5;
+  const float f = __builtin_amdgcn_exp2f((ncR[blk * M_pad + row] - nc[3 * row]) * 1.4426950408889634f);
+  u32x4_t *p = reinterpret_cast<u32x4_t *>(coeff + (size_t)c * M_pad * ld_coeff + (((size_t)T * ksv + C) * 64 + l) * 8);
+  u32x4_t x = *p;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = pack_rne(bf16_to_f32(x[e] & 0xFFFFu) * f, bf16_to_f32(x[e] >> 16) * f);
-    *p = x;
-  }
+  for (int e = 0; e < 4; ++e) x[e] = pack_rne(bf16_to_f32(x[e] & 0xFFFFu) * f, bf16_to_f32(x[e] >> 16) * f);
+  *p = x;
 }
 
 // ---------------------------------------------------------------------------
@@ -770,8 +766,9 @@ void launch_merge(hipStream_t st, int M, const float *part, int nblocks, int ful
 
 void launch_nc_scale(hipStream_t st, uint16_t *coeff, int64_t ld_coeff, int nchunks, int64_t last_rows, int M_pad,
                      const int *cnt, const float *ncR, const float *nc) {
-  hipLaunchKernelGGL(k_nc_scale, dim3(8192), dim3(256), 0, st, coeff, ld_coeff, nchunks, last_rows, M_pad, cnt, ncR,
-                     nc);
+  const int64_t ksv = ld_coeff / 16;
+  const dim3 grid((unsigned)(M_pad / 32), (unsigned)((ksv + 3) / 4), (unsigned)nchunks);
+  hipLaunchKernelGGL(k_nc_scale, grid, dim3(256), 0, st, coeff, ld_coeff, nchunks, last_rows, M_pad, cnt, ncR, nc);
 }
 
 void launch_warm(hipStream_t st, int TT, int64_t tiles, const int *cnt, const int *idx, const TokRec *tok,
