@@ -322,14 +322,19 @@ Plan make_plan(const cce_head *hd, int64_t M) {
     p.o_coeffT = o;
     p.bwd_bytes = align_up(o + (size_t)2 * p.ld_coeff * p.M_pad, 256);
     p.dfused = p.cap >= 0.0f && p.cap <= CAP_FIXED_REF_MAX;
+    // with a softcap the tiles write dW's transposed operand of every chunk
+    // and dh takes the token-major chunk in turn (one chunk); without, every
+    // token-major chunk waits for the scaling and is transposed chunk by chunk
+    const size_t chunk_bytes = (size_t)2 * p.M_pad * p.ld_coeff;
+    const size_t nkeep = p.cap == 0.0f ? (size_t)p.nchunks : 1, nkeepT = p.cap == 0.0f ? 1 : (size_t)p.nchunks;
     size_t q = common;
-    p.df_coeff = q;  q = align_up(q + (size_t)p.nchunks * 2 * p.M_pad * p.ld_coeff, 256);
+    p.df_coeff = q;  q = align_up(q + nkeep * chunk_bytes, 256);
     p.df_dhp = q;    q = align_up(q + sizeof(float) * (size_t)p.ksplit * p.M_pad * p.H, 256);
     p.df_tdc = q;    q = align_up(q + sizeof(float) * p.M_pad, 256);
     p.df_fpart = q;  q = align_up(q + sizeof(float) * (size_t)p.mass_ld * p.M_pad, 256);
     p.df_fac = q;    q = align_up(q + 2 * sizeof(float) * p.M_pad, 256);
     p.df_hT = q;     q = align_up(q + (size_t)2 * p.H * p.M_pad, 256);
-    p.df_coeffT = q; q = align_up(q + (size_t)2 * p.ld_coeff * p.M_pad, 256);
+    p.df_coeffT = q; q = align_up(q + nkeepT * chunk_bytes, 256);
     if (p.cap == 0.0f) {
       p.df_part = q; q = align_up(q + sizeof(float) * 2 * (size_t)p.mass_ld * p.M_pad, 256);
       p.df_R = q;    q = align_up(q + sizeof(float) * (size_t)p.tiles * (BNT / 32) * p.M_pad, 256);
@@ -734,7 +739,9 @@ cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, i
   a.max_splits = p.fus_max_splits;
   const dim3 g1((unsigned)(cdiv(a.nblocks, 8) * 8));
   uint16_t *coeff0 = ws_at<uint16_t>(workspace, p.df_coeff);
+  uint16_t *coeffT0 = ws_at<uint16_t>(workspace, p.df_coeffT);
   const size_t chunk_elems = (size_t)p.M_pad * p.ld_coeff;
+  a.ks16t = p.M_pad / 16;
 
   GemmArgs ga{};
   ga.ksv = p.ld_coeff / 16;
@@ -761,7 +768,8 @@ cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, i
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * p.chunk_tiles;
     const int nt = std::min(p.chunk_tiles, p.tiles - t0);
-    a.coeff = coeff0 + c * chunk_elems;
+    a.coeff = nocap ? coeff0 + c * chunk_elems : coeff0;
+    a.coeffT = (!nocap && dw) ? coeffT0 + c * chunk_elems : nullptr;
     a.range_tile0 = t0;
     a.range_tiles = nt;
     a.chunk = c;
@@ -812,14 +820,21 @@ cce_status run_dense_fused(const Plan &p, const cce_head *head, const void *h, i
     wa.H = (int)p.H;
     wa.M_pad = (int)p.M_pad;
     wa.HT = p.HT;
+    // with a softcap the tiles wrote every transposed chunk but the target
+    // entries, which launch_hT sets
     CCE_LAUNCH("hT", st, launch_hT(st, a.haug, p.Ka / 16, p.Kb / 8, (int)p.M_pad, (int)p.H, a.cnt, fac,
-                                   ws_at<uint16_t>(workspace, p.df_hT)));
+                                   ws_at<uint16_t>(workspace, p.df_hT), nocap ? nullptr : a.tok,
+                                   nocap ? nullptr : coeffT0, p.ld_coeff));
     for (int c = 0; c < p.nchunks; ++c) {
       const int t0 = c * p.chunk_tiles;
       const int nt = std::min(p.chunk_tiles, p.tiles - t0);
       const int64_t v0 = (int64_t)t0 * BNT;
-      CCE_LAUNCH("coeffT", st, launch_coeffT(st, coeff0 + c * chunk_elems, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt,
-                                             a.tok, fac, p.V, v0, ws_at<uint16_t>(workspace, p.df_coeffT)));
+      if (nocap) {
+        CCE_LAUNCH("coeffT", st, launch_coeffT(st, coeff0 + c * chunk_elems, ga.ksv, (int)p.M_pad, nt * BNT, a.cnt,
+                                               a.tok, fac, p.V, v0, coeffT0));
+      } else {
+        wa.coeffT = coeffT0 + c * chunk_elems;
+      }
       wa.chunk_v0 = v0;
       wa.nvt = nt;
       CCE_LAUNCH("dw_gemm", st, launch_dw(st, wa));

@@ -141,6 +141,11 @@ struct TileArgs {
                          // coefficients (the token's largest logit in the block)
   uint16_t *coeff;       // backward: [M_pad][ld_coeff] bf16 coefficient chunk
   int64_t ld_coeff;
+  // dense head's single pass with dW, or NULL: the chunk's coefficients also
+  // as dW's operand, [ld_coeff vocabulary rows][M_pad tokens] fragment-major
+  // (ks16t = M_pad / 16), the target's entry left 0 for launch_hT to fill
+  uint16_t *coeffT;
+  int64_t ks16t;
   int64_t V;
   int G, Ka, Kb, NB, wpr, M_pad;  // NB, G: K steps of the bias block and of h (kw columns each)
   int NBr;               // K steps of the bias block's refinement half (its first half)
@@ -420,9 +425,12 @@ struct DwArgs {
 };
 // fac (or NULL): the single pass's per-row factors (ReduceTarget::fac); hT then
 // holds each row scaled by its factor, and coeffT takes the target's
-// coefficient in the chunk's units
+// coefficient in the chunk's units.  tok (or NULL): the single pass whose
+// tiles wrote every chunk's transposed coefficients (ctT, chunks of ld_coeff
+// vocabulary rows): each row's target entry is set there to fac[2r + 1].
 void launch_hT(hipStream_t st, const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H, const int *cnt,
-               const float *fac, uint16_t *hT);
+               const float *fac, uint16_t *hT, const TokRec *tok = nullptr, uint16_t *ctT = nullptr,
+               int64_t ld_coeff = 0);
 void launch_coeffT(hipStream_t st, const uint16_t *coeff, int64_t ksv, int M_pad, int vrows, const int *cnt,
                    const TokRec *tok, const float *fac, int64_t V, int64_t chunk_v0, uint16_t *coeffT);
 void launch_dw(hipStream_t st, const DwArgs &a);

@@ -30,12 +30,24 @@ constexpr int TLD = TR + 8;    // LDS row stride of the transpose (keeps 16-byte
 // hT[d][r] for r < 256 * active tiles, d < H (haug: [M_pad][Ka] fragment-major,
 // the h part starting at K chunk kb8).
 __global__ void __launch_bounds__(256) k_hT(const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H,
-                                            const int *cnt, const float *fac, uint16_t *hT) {
+                                            const int *cnt, const float *fac, uint16_t *hT, const TokRec *tok,
+                                            uint16_t *ctT, int64_t ld_coeff) {
   const int r0 = blockIdx.x * TR, d0 = blockIdx.y * TR;
   if (r0 >= active_tiles(cnt) * BM) return;
   __shared__ __attribute__((aligned(16))) uint16_t sT[TR * TLD];
   const int tid = threadIdx.x;
   const int n = cnt[0];
+  if (ctT && blockIdx.y == 0 && tid < TR) {
+    // the target entry of row r in the chunk that holds its target, rounded
+    // to bf16 like every other coefficient (targets are in [0, V) or -1)
+    const int r = r0 + tid;
+    const int tgt = tok[r].tgt;
+    if (r < n && tgt >= 0) {
+      const int64_t c = tgt / ld_coeff, vl = tgt - c * ld_coeff;
+      ctT[(size_t)c * ld_coeff * M_pad + frag_slot(vl, r >> 3, M_pad / 16) + (r & 7)] =
+          (uint16_t)bf16_rne(fac[2 * r + 1]);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + 256 * k, r = i >> 3, c = i & 7;
@@ -215,9 +227,9 @@ __global__ void __launch_bounds__(TW, 1) k_dw(DwArgs a) {
 }
 
 void launch_hT(hipStream_t st, const uint16_t *haug, int64_t ks16, int kb8, int M_pad, int H, const int *cnt,
-               const float *fac, uint16_t *hT) {
+               const float *fac, uint16_t *hT, const TokRec *tok, uint16_t *ctT, int64_t ld_coeff) {
   hipLaunchKernelGGL(k_hT, dim3((unsigned)(M_pad / TR), (unsigned)(H / TR)), dim3(256), 0, st, haug, ks16, kb8,
-                     M_pad, H, cnt, fac, hT);
+                     M_pad, H, cnt, fac, hT, tok, ctT, ld_coeff);
 }
 
 void launch_coeffT(hipStream_t st, const uint16_t *coeff, int64_t ksv, int M_pad, int vrows, const int *cnt,

@@ -716,6 +716,17 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
               for (int q = 0; q < EW / 8; ++q)
                 *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
                     u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+            if constexpr (DENSE && FUSED) {
+              // dW's operand: vocabulary row vloc + k, token tok0 + lane at
+              // element (token & 7) of its 16-byte slot; the EW rows (one
+              // 32-row block: vloc is a multiple of 8) are 8 elements apart
+              if (a.coeffT) {
+                const int t = tok0 + lane;
+                uint16_t *ct = a.coeffT + frag_slot(vloc, t >> 3, a.ks16t) + (t & 7);
+#pragma unroll
+                for (int k = 0; k < EW; ++k) ct[8 * k] = (uint16_t)((k & 1) ? pk[k / 2] >> 16 : pk[k / 2] & 0xFFFFu);
+              }
+            }
           }
         }
         if (FNC && bvalid) {
