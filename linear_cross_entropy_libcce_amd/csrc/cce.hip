@@ -641,7 +641,10 @@ cce_status run_backward(const cce_head *head, const void *h, int64_t M, const in
 // sum) partials over the non-target columns; every chunk is kept.  The merge
 // then gives lse, logp and each token's largest logit m, one launch scales
 // every coefficient by e^{R - m} (at most 1), and the dh contractions and the
-// split reduce proceed as for the capped single pass, against m.
+// split reduce proceed as for the capped single pass, against m.  The dh
+// contraction's small-M variant applies the factor itself as it stages each
+// coefficient fragment (the same arithmetic, so the same bits): no scaling
+// launch.
 cce_status run_nc_fused(const Plan &p, const cce_head *head, const void *h, int64_t M, const int32_t *targets,
                         const uint8_t *mask, const float *g, float *logp, float *lse, void *dh, int32_t dh_dtype,
                         void *workspace, hipStream_t st) {
@@ -669,11 +672,18 @@ cce_status run_nc_fused(const Plan &p, const cce_head *head, const void *h, int6
   float *nc = ws_at<float>(workspace, p.nc_nc);
   CCE_LAUNCH("merge", st, launch_merge(st, (int)M, a.part, a.nblocks, p.chunk_tiles, p.tiles, p.fus_max_splits,
                                        (int)p.M_pad, inv, a.cnt, tok, logp, lse, nc));
-  CCE_LAUNCH("nc_scale", st, launch_nc_scale(st, coeff0, p.ld_coeff, p.nchunks,
-                                             p.V - (int64_t)(p.nchunks - 1) * p.ld_coeff, (int)p.M_pad, a.cnt,
-                                             a.ncR, nc));
+  // the variant launch_dh_gemm picks for a.small (the default storage only)
+  const bool scale_in_dh = a.small != 0 && p.gs == KSTEP && p.sbt == SB_F32;
+  if (!scale_in_dh)
+    CCE_LAUNCH("nc_scale", st, launch_nc_scale(st, coeff0, p.ld_coeff, p.nchunks,
+                                               p.V - (int64_t)(p.nchunks - 1) * p.ld_coeff, (int)p.M_pad, a.cnt,
+                                               a.ncR, nc));
 
   GemmArgs ga{};
+  if (scale_in_dh) {
+    ga.ncR = a.ncR;
+    ga.nc = nc;
+  }
   ga.ksv = p.ld_coeff / 16;
   ga.wq = head->wq;
   ga.scales = head->scales;

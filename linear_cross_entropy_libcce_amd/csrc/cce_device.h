@@ -244,6 +244,13 @@ struct GemmArgs {
   int64_t fl_ld;
   int chunk_tile0;       // first vocabulary tile of the chunk
   int small;             // as in TileArgs
+  // uncapped single pass, small-M variant only (or NULL): the coefficients
+  // were written against their 32-row block's reference ncR (TileArgs::ncR)
+  // and are brought to the token's largest logit nc[3 r] as they are staged:
+  // times e^{R - m}, rounded to bf16 (rows from the supervised count on and
+  // slots past V as stored)
+  const float *ncR;
+  const float *nc;
 };
 
 // Raw buffer resource over [base, base + bytes): a lane whose byte offset is

@@ -182,6 +182,12 @@ struct DhProducer {
 
 constexpr int MAX_LIST = 2048;  // vocabulary tiles per split (a chunk holds at most 2048)
 
+// A staged coefficient fragment (small M) and the inputs of its factor.
+struct CFrag {
+  u32x4_t x;
+  float R, m;
+};
+
 template <int BITS, bool SKIP, int SMALL, int LG, int SBW>
 __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -299,10 +305,34 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     auto koff = [&](int i) { return cstep(i) * 4 * 1024; };
 
     // the coefficient fragment this wave stages for step i (small M)
+    // with a.ncR also the inputs of its factor e^{R - m}: the lane's token row
+    // and the block of its 8 vocabulary rows (R = m = 0, a factor of exactly
+    // 1, outside the supervised rows and V)
+    const bool ncs = SMALL && a.ncR != nullptr;
+    const int crow = tt * BM + (wave >> 2) * 32 + l32;
     auto cfrag_load = [&](int i) {
-      return buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, koff(i < nsteps ? i : nsteps - 1));
+      const int ii = i < nsteps ? i : nsteps - 1;
+      CFrag f;
+      f.x = buf_load16(rc, cv0 + (wave >> 2) * cstride + (wave & 3) * 1024, koff(ii));
+      f.R = f.m = 0.0f;
+      if (ncs) {
+        const int64_t v = a.chunk_v0 + (int64_t)cstep(ii) * KSTP + (wave & 3) * 16 + 8 * lh;
+        if (crow < a.cnt[0] && v < a.V) {
+          f.R = a.ncR[(size_t)(v >> 5) * a.M_pad + crow];
+          f.m = a.nc[3 * crow];
+        }
+      }
+      return f;
     };
-    u32x4_t C0, C1, C2;  // small M: staged fragments of three steps, as P0..P2
+    auto cfrag_value = [&](const CFrag &f) {
+      if (!ncs) return f.x;
+      const float s = __builtin_amdgcn_exp2f((f.R - f.m) * 1.4426950408889634f);
+      u32x4_t x = f.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = pack_rne(bf16_to_f32(x[e] & 0xFFFFu) * s, bf16_to_f32(x[e] >> 16) * s);
+      return x;
+    };
+    CFrag C0, C1, C2;  // small M: staged fragments of three steps, as P0..P2
     pr.load(a, vrow(0), P0);
     pr.load(a, vrow(1), P1);
     if (SMALL) pr.load(a, vrow(2), P2);
@@ -310,7 +340,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     pr.stage_sb(P1, sSB[1], a.sbt);
     if (SMALL) {
       if (cload) {
-        sCA[0][wave * 64 + lane] = cfrag_load(0);
+        sCA[0][wave * 64 + lane] = cfrag_value(cfrag_load(0));
         C1 = cfrag_load(1);
         C2 = cfrag_load(2);
       }
@@ -335,8 +365,8 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     // coefficient fragments likewise: a step is short there, and one step of
     // cover left both loads waited for.  The fragment is loaded before the
     // head words (loads complete in issue order for s_waitcnt).
-    auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &mid, DhRegs<BITS> &nxt, u32x4_t &cfc,
-                       u32x4_t &cfn) {
+    auto do_step = [&](int st, DhRegs<BITS> &cur, DhRegs<BITS> &mid, DhRegs<BITS> &nxt, CFrag &cfc,
+                       CFrag &cfn) {
       const int cb = st & 1;
       const int knext = koff(st + 1 < nsteps ? st + 1 : st);
       if (SMALL && cload) cfn = cfrag_load(st + 3);
@@ -372,7 +402,7 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pr.stage_sb(SMALL ? mid : nxt, sSB[cb], a.sbt);
-      if (SMALL && cload) sCA[cb ^ 1][wave * 64 + lane] = cfc;  // step st + 1's: read after the barrier
+      if (SMALL && cload) sCA[cb ^ 1][wave * 64 + lane] = cfrag_value(cfc);  // step st + 1's: read after the barrier
       __syncthreads();
     };
     int st = 0;

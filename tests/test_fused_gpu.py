@@ -72,6 +72,10 @@ CASES = {
     # softcap above 40: the call's two passes (the backward tiles merge the
     # forward's partials themselves; no merge launch, one front)
     "M16_H256_V4096_4bit_nocap": dict(M=16, H=256, V=4096, bits=4),
+    # the small-M dh contraction scales the uncapped pass's coefficients as it
+    # stages them: one and two token blocks, masked, ragged V, several splits
+    "M64_H768_V2501_4bit_nocap_randmask": dict(M=64, H=768, V=2501, bits=4, mask="random", mask_frac=0.3),
+    "M33_H512_V7000_8bit_nocap_zipf": dict(M=33, H=512, V=7000, bits=8, targets="zipf"),
     "H512_V1000_8bit_nocap_randmask": dict(M=600, H=512, V=1000, bits=8, mask="random", mask_frac=0.3),
     "H768_V700_4bit_cap50_group32_bf16": dict(M=400, H=768, V=700, bits=4, softcap=50.0, group=32, sb_dtype="bf16"),
     "M2100_H256_V900_8bit_nocap_randmask": dict(M=2100, H=256, V=900, bits=8, mask="random", mask_frac=0.4),
