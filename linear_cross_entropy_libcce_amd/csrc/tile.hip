@@ -717,14 +717,23 @@ __global__ void __launch_bounds__(TW, 1) k_tile(TileArgs a) {
                 *(u32x4_t *)(a.coeff + frag_slot(tok0 + lane, cm + q, a.ksv)) =
                     u32x4_t{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
             if constexpr (DENSE && FUSED) {
-              // dW's operand: vocabulary row vloc + k, token tok0 + lane at
-              // element (token & 7) of its 16-byte slot; the EW rows (one
-              // 32-row block: vloc is a multiple of 8) are 8 elements apart
+              // dW's operand, [vocabulary row][token] 16-byte slots of 8
+              // tokens, transposed through this wave's z scratch: columns k0
+              // .. k0 + 7 of every lane's row are read (in registers) and free.
+              // Lane 8j + i puts its value of row k into the first 16 bytes of
+              // lane 8j + k's, at element i; lane 8j + k then holds row vloc +
+              // k of tokens tok0 + 8j .. + 7, one whole slot.
               if (a.coeffT) {
-                const int t = tok0 + lane;
-                uint16_t *ct = a.coeffT + frag_slot(vloc, t >> 3, a.ks16t) + (t & 7);
+                uint16_t *zb = reinterpret_cast<uint16_t *>(zs + k0);
+                const int j8 = lane & ~7, i = lane & 7;
 #pragma unroll
-                for (int k = 0; k < EW; ++k) ct[8 * k] = (uint16_t)((k & 1) ? pk[k / 2] >> 16 : pk[k / 2] & 0xFFFFu);
+                for (int k = 0; k < EW; ++k)
+                  zb[(j8 + k) * (2 * ZROW) + i] = (uint16_t)((k & 1) ? pk[k / 2] >> 16 : pk[k / 2] & 0xFFFFu);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const u32x4_t x = *(const u32x4_t *)(zb + lane * (2 * ZROW));
+                *(u32x4_t *)(a.coeffT + frag_slot(vloc + i, (tok0 + j8) >> 3, a.ks16t)) = x;
               }
             }
           }
