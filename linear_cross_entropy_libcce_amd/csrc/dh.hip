@@ -304,10 +304,10 @@ __global__ void __launch_bounds__(TW, 1) k_dh(GemmArgs a) {
     // K offset (bytes) of step i in the fragment-major chunk
     auto koff = [&](int i) { return cstep(i) * 4 * 1024; };
 
-    // the coefficient fragment this wave stages for step i (small M)
-    // with a.ncR also the inputs of its factor e^{R - m}: the lane's token row
-    // and the block of its 8 vocabulary rows (R = m = 0, a factor of exactly
-    // 1, outside the supervised rows and V)
+    // the coefficient fragment this wave stages for step i (small M); with
+    // a.ncR also the inputs of its factor e^{R - m} for the lane's token row
+    // and the 32-row block of its 8 vocabulary rows (R = m = 0, a factor of
+    // exactly 1, outside the supervised rows and V)
     const bool ncs = SMALL && a.ncR != nullptr;
     const int crow = tt * BM + (wave >> 2) * 32 + l32;
     auto cfrag_load = [&](int i) {
