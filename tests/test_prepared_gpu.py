@@ -58,6 +58,9 @@ CASES = {
     "8bit_group128_f16_affine": dict(M=100, H=1024, V=600, bits=8, group=128, sb_dtype="f16", bias="affine"),
     "M16_8bit_cap30_affine": dict(M=16, H=2560, V=4097, bits=8, softcap=30.0, bias="affine"),
     "M40_4bit_cap30": dict(M=40, H=512, V=3000, bits=4, softcap=30.0),
+    # no softcap at small M: the dh contraction scales the coefficients as it stages them
+    "M24_8bit_nocap_affine_randmask": dict(M=24, H=768, V=5000, bits=8, bias="affine", mask="random",
+                                           mask_frac=0.25),
 }
 
 
