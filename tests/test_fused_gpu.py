@@ -4,7 +4,10 @@ With a softcap in (0, 40] the call is a single pass over the head: the
 forward's fixed reference e^{y - cap} gives every coefficient up to the
 token's factor g e^{cap - lse}, which the split reduce applies once it has
 summed the token's split sums into lse (no logit is computed twice, no merge
-launch).  Other heads run a forward and a backward pass after one front; the
+launch).  Without a softcap it is a single pass too: the coefficients against
+each 32-row vocabulary block's largest logit, brought to the token's maximum
+after the merge (at small M by the dh contraction as it stages them).  A
+softcap above 40 runs a forward and a backward pass after one front; the
 backward tiles merge the forward's partials themselves, so the results match
 the two separate calls to rounding.
 Tolerances as in test_parity_gpu.py (|dlogp|, |dlse| <= 5e-3, dh relative L2
@@ -223,8 +226,9 @@ def test_fused_small_m_on_the_full_head(torch_cuda, M, bias):
 
 GRAPH_CASES = {
     "single_pass_cap30": dict(M=300, H=512, V=2000, bits=8, softcap=30.0, mask="random", mask_frac=0.2, seed=41),
-    "two_passes_nocap": dict(M=300, H=512, V=2000, bits=4, mask="random", mask_frac=0.2, seed=42),
+    "single_pass_nocap": dict(M=300, H=512, V=2000, bits=4, mask="random", mask_frac=0.2, seed=42),
     "small_M20_cap30": dict(M=20, H=256, V=3000, bits=8, softcap=30.0, seed=43),
+    "small_M24_nocap": dict(M=24, H=256, V=3000, bits=8, mask="random", mask_frac=0.2, seed=45),
 }
 
 
@@ -258,8 +262,9 @@ def _replays_match(torch, step, outs):
 @pytest.mark.parametrize("name", list(GRAPH_CASES))
 def test_combined_call_replays_from_a_hip_graph(torch_cuda, name):
     # the combined call enqueues kernels only (no allocation, no host
-    # synchronization, no memset), in every form: the single pass, the two
-    # passes without a softcap, the small-M variants
+    # synchronization, no memset), in every form: the single pass under a
+    # softcap and without one (its scaling launch, or at small M the dh
+    # contraction's own scaling), the small-M variants
     torch = torch_cuda
     kw = dict(GRAPH_CASES[name])
     seed = kw.pop("seed")
